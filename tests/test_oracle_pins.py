@@ -1,0 +1,536 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the passage it checks. They run on the CPU only. The point of
+each one is that a plausible slip in the oracle (a dropped term, a sign, an
+index, a transposed operand, a wrong scale) makes at least one of them fail.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import accounting as acc
+from oracle import qlayer_ref as ref
+from oracle import scalar_toy
+
+from transformer_decoder_layer_qwen_amd import configs, synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def spec_of(cfg, **kw):
+    s = dict(d=cfg.d, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+             head_dim=cfg.head_dim, ffn_dim=cfg.ffn_dim, n_experts=cfg.n_experts,
+             top_k=cfg.top_k, norm_topk_prob=cfg.norm_topk_prob,
+             qkv_bias=cfg.qkv_bias, qk_norm=cfg.qk_norm, eps=cfg.rms_eps,
+             theta=cfg.rope_theta)
+    s.update(kw)
+    return ref.LayerSpec(**s)
+
+
+def f32_weights(w):
+    return {k: synth.to_f32(v) for k, v in w.items()}
+
+
+def small_cfg(**kw):
+    base = dict(name="small", d=64, n_q_heads=4, n_kv_heads=2, head_dim=16, ffn_dim=96,
+                dtype="f32", w_std=0.1, b_std=0.1, gamma_std=0.1, x_std=1.0)
+    base.update(kw)
+    return configs.LayerConfig(**base)
+
+
+# ---------------------------------------------------------------- GEMM ----
+
+def test_gemm_worked_example():
+    g = gold("gemm_example.json")
+    A, B, C = np.array(g["A"]), np.array(g["B"]), np.array(g["C"])
+    assert np.array_equal(ref.gemm(A, B), C)
+    # the same product through the [out, in] convention: W = B^T
+    assert np.array_equal(ref.linear(A, B.T), C)
+    assert acc.gemm_flops(g["m"], g["k"], g["n"]) == g["flops_2mkn"]
+    assert acc.gemm_exact_ops(g["m"], g["k"], g["n"]) == g["exact_ops"]
+
+
+def test_linear_bias_and_rows_independent():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 7))
+    W = rng.standard_normal((3, 7))
+    b = rng.standard_normal(3)
+    y = ref.linear(x, W, b)
+    for t in range(5):
+        for n in range(3):
+            assert y[t, n] == pytest.approx(sum(x[t, j] * W[n, j] for j in range(7)) + b[n],
+                                            rel=1e-13, abs=1e-13)
+
+
+# ------------------------------------------------------------- RMSNorm ----
+
+def test_rmsnorm_worked_example():
+    g = gold("rmsnorm_example.json")
+    x = np.array(g["x"])
+    assert np.mean(x * x) == g["mean_square"]
+    y = ref.rmsnorm(x, np.array(g["gamma"]), g["eps"])
+    assert np.max(np.abs(y - np.array(g["printed"]))) < 0.5 * 10 ** -g["printed_decimals"] + 1e-6
+    assert np.sqrt(g["mean_square"]) == g["denominator_approx"]
+
+
+def test_rmsnorm_properties():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((6, 32))
+    g = rng.standard_normal(32)
+    y = ref.rmsnorm(x, np.ones(32), 0.0)
+    # unit root-mean-square per row, no mean subtraction, per-row scale invariance
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, atol=1e-14)
+    assert np.allclose(ref.rmsnorm(3.5 * x, g, 0.0), ref.rmsnorm(x, g, 0.0), atol=1e-13)
+    assert not np.allclose(np.mean(y, axis=-1), 0.0)
+    # gamma scales feature j
+    assert np.allclose(ref.rmsnorm(x, g, 0.0), g * y, atol=1e-14)
+    # rows are independent
+    x2 = x.copy()
+    x2[3] *= -7
+    assert np.array_equal(ref.rmsnorm(x2, g, 1e-6)[:3], ref.rmsnorm(x, g, 1e-6)[:3])
+
+
+# ---------------------------------------------------------------- RoPE ----
+
+def test_rope_rotation_sign_and_frequency():
+    # dh = 2: one frequency omega_0 = 1 for any theta; R(a) = [[cos, -sin], [sin, cos]]
+    for theta in (1e6, 10000.0):
+        assert ref.rope_frequencies(2, theta)[0] == 1.0
+        e0 = np.array([[[1.0, 0.0]]])
+        e1 = np.array([[[0.0, 1.0]]])
+        r0 = ref.rope_rotate_half(e0, np.array([1.0]), theta)[0, 0]
+        r1 = ref.rope_rotate_half(e1, np.array([1.0]), theta)[0, 0]
+        assert np.allclose(r0, [math.cos(1), math.sin(1)], atol=1e-15)
+        assert np.allclose(r1, [-math.sin(1), math.cos(1)], atol=1e-15)
+    w = ref.rope_frequencies(128, 1e6)
+    assert w[0] == 1.0
+    assert w[32] == pytest.approx(1e-3, rel=1e-12)       # theta^(-2*32/128) = theta^(-1/2)
+    assert np.allclose(w[1:] / w[:-1], 1e6 ** (-2 / 128), rtol=1e-12)
+
+
+def test_rope_position_zero_identity_and_relative():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((1, 1, 128))
+    k = rng.standard_normal((1, 1, 128))
+    assert np.allclose(ref.rope_rotate_half(q, np.array([0.0]), 1e6), q, atol=0)
+    for p, s in ((3, 11), (100, 7), (0, 513)):
+        lhs = np.sum(ref.rope_rotate_half(q, np.array([float(p)]), 1e6)
+                     * ref.rope_rotate_half(k, np.array([float(s)]), 1e6))
+        rhs = np.sum(q * ref.rope_rotate_half(k, np.array([float(s - p)]), 1e6))
+        assert lhs == pytest.approx(rhs, rel=1e-11, abs=1e-11)
+    # norm preserving
+    r = ref.rope_rotate_half(q, np.array([77.0]), 1e6)
+    assert np.linalg.norm(r) == pytest.approx(np.linalg.norm(q), rel=1e-13)
+
+
+def test_rope_rotate_half_is_adjacent_pairs_under_permutation():
+    rng = np.random.default_rng(3)
+    dh = 16
+    t = rng.standard_normal((5, 3, dh))
+    pos = np.arange(5, dtype=float) * 3 + 1
+    half = dh // 2
+    # permutation placing pair (i, i+half) at (2i, 2i+1)
+    perm = np.empty(dh, dtype=int)
+    perm[0::2] = np.arange(half)
+    perm[1::2] = np.arange(half) + half
+    a = ref.rope_rotate_half(t, pos, 1e4)
+    b = ref.rope_adjacent(t[..., perm], pos, 1e4)
+    assert np.allclose(a[..., perm], b, atol=1e-14)
+    # and the two pairings differ on generic data (the reading matters)
+    assert not np.allclose(ref.rope_rotate_half(t, pos, 1e4), ref.rope_adjacent(t, pos, 1e4))
+
+
+# ----------------------------------------------------------- attention ----
+
+def test_gqa_group_map_matches_pages():
+    g = gold("rope_and_experiments.json")
+    a = g["gqa_groups_qwen3_8b"]
+    assert [ref.kv_group(h, a["Hq"], a["Hkv"]) for h in range(8)] == [0] * 4 + [1] * 4
+    b = g["gqa_groups_qwen3_30b_a3b"]
+    assert [ref.kv_group(h, b["Hq"], b["Hkv"]) for h in range(16)] == [0] * 8 + [1] * 8
+    assert [ref.kv_group(h, 28, 4) for h in (0, 6, 7, 27)] == [0, 0, 1, 3]
+
+
+def test_attention_probs_mask_and_gqa_equals_mha():
+    rng = np.random.default_rng(4)
+    T, Hq, Hkv, dh = 9, 6, 2, 8
+    q = rng.standard_normal((T, Hq, dh))
+    k = rng.standard_normal((T, Hkv, dh))
+    v = rng.standard_normal((T, Hkv, dh))
+    idx = np.arange(T)
+    o, P = ref.attention(q, k, v, idx, idx, Hkv, return_probs=True)
+    assert np.allclose(P.sum(-1), 1.0, atol=1e-14)
+    assert np.all(P >= 0)
+    assert np.all(P[:, np.triu_indices(T, 1)[0], np.triu_indices(T, 1)[1]] == 0.0)
+    # repeat_interleave K/V to Hq heads and run as MHA
+    k_rep = np.repeat(k, Hq // Hkv, axis=1)
+    v_rep = np.repeat(v, Hq // Hkv, axis=1)
+    o_mha = ref.attention(q, k_rep, v_rep, idx, idx, Hq)
+    assert np.allclose(o, o_mha, atol=1e-14)
+    # first query sees only itself: o = v of its group
+    for h in range(Hq):
+        assert np.allclose(o[0, h], v[0, ref.kv_group(h, Hq, Hkv)], atol=1e-15)
+
+
+def test_attention_group_routing_by_constant_values():
+    T, Hq, Hkv, dh = 4, 8, 4, 4
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((T, Hq, dh))
+    k = rng.standard_normal((T, Hkv, dh))
+    v = np.zeros((T, Hkv, dh))
+    for g in range(Hkv):
+        v[:, g, :] = g + 1.0
+    idx = np.arange(T)
+    o = ref.attention(q, k, v, idx, idx, Hkv)
+    for h in range(Hq):
+        assert np.allclose(o[:, h, :], h // 2 + 1.0, atol=1e-14)
+
+
+def test_attention_scale_two_key_closed_form():
+    # q = k1 = a*e0, k0 = 0: the visible scores of row 1 are 0 and a^2/sqrt(dh);
+    # with one-hot values the output is the probability pair itself.
+    dh, a = 16, 3.0
+    q = np.zeros((2, 1, dh)); q[1, 0, 0] = a
+    k = np.zeros((2, 1, dh)); k[1, 0, 0] = a
+    v = np.zeros((2, 1, dh)); v[0, 0, 0] = 1.0; v[1, 0, 1] = 1.0
+    o = ref.attention(q, k, v, np.arange(2), np.arange(2), 1)
+    p1 = 1.0 / (1.0 + math.exp(-a * a / math.sqrt(dh)))
+    assert o[1, 0, 1] == pytest.approx(p1, rel=1e-14)
+    assert o[1, 0, 0] == pytest.approx(1 - p1, rel=1e-14)
+
+
+def test_softmax_matches_library():
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((4, 33)) * 30
+    assert np.allclose(ref.softmax(z), scipy.special.softmax(z, axis=-1), atol=1e-15)
+
+
+# --------------------------------------------------------------- SwiGLU ----
+
+def test_silu_closed_form_points():
+    z = np.array([-40.0, -1.0, 0.0, 1.0, 2.5, 40.0])
+    s = ref.silu(z)
+    assert s[2] == 0.0
+    assert s[3] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert s[-1] == pytest.approx(40.0, rel=1e-15)
+    assert abs(s[0]) < 1e-15
+    assert np.allclose(s, z * scipy.special.expit(z), rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_gate_branch_and_down():
+    rng = np.random.default_rng(7)
+    z = rng.standard_normal((3, 8))
+    wg, wu, wd = rng.standard_normal((5, 8)), rng.standard_normal((5, 8)), rng.standard_normal((8, 5))
+    F = ref.swiglu_ffn(z, wg, wu, wd)
+    g, u = z @ wg.T, z @ wu.T
+    assert np.allclose(F, (g * scipy.special.expit(g) * u) @ wd.T, atol=1e-13)
+    # swapping the roles of gate and up changes the result (the reading matters)
+    assert not np.allclose(F, ref.swiglu_ffn(z, wu, wg, wd))
+
+
+# ------------------------------------------------------------------ MoE ----
+
+def test_topk_order_and_ties():
+    l = np.array([[0.5, 2.0, 2.0, -1.0, 3.0, 2.0]])
+    assert ref.topk_select(l, 4).tolist() == [[4, 1, 2, 5]]
+    assert ref.topk_select(l, 1).tolist() == [[4]]
+
+
+def test_router_weight_routes_agree_and_sum_to_one():
+    rng = np.random.default_rng(8)
+    logits = rng.standard_normal((50, 128)) * 2.3
+    idx = ref.topk_select(logits, 8)
+    w1 = ref.gate_weights(logits, idx, True)
+    w2 = ref.gate_weights_via_full_softmax(logits, idx)
+    assert np.allclose(w1, w2, atol=1e-15)
+    assert np.allclose(w1.sum(-1), 1.0, atol=1e-15)
+    # descending logits -> non-increasing weights
+    assert np.all(np.diff(w1, axis=-1) <= 1e-15)
+    # Qwen2 setting: raw probabilities sum to < 1
+    w3 = ref.gate_weights(logits, idx, False)
+    assert np.all(w3.sum(-1) < 1.0)
+    assert np.allclose(w3, np.take_along_axis(scipy.special.softmax(logits, -1), idx, -1))
+
+
+def _moe_weights(rng, E, mf, d):
+    return {"w_router": rng.standard_normal((E, d)),
+            "we_gate": rng.standard_normal((E, mf, d)) * 0.3,
+            "we_up": rng.standard_normal((E, mf, d)) * 0.3,
+            "we_down": rng.standard_normal((E, d, mf)) * 0.3}
+
+
+def test_moe_single_expert_is_dense_swiglu():
+    rng = np.random.default_rng(9)
+    w = _moe_weights(rng, 1, 12, 16)
+    z = rng.standard_normal((7, 16))
+    F, idx, wts, _ = ref.moe_ffn_output(z, w, 1)
+    assert np.all(idx == 0) and np.allclose(wts, 1.0)
+    assert np.allclose(F, ref.swiglu_ffn(z, w["we_gate"][0], w["we_up"][0], w["we_down"][0]),
+                       atol=1e-13)
+
+
+def test_moe_all_experts_is_softmax_weighted_sum():
+    rng = np.random.default_rng(10)
+    E, mf, d = 5, 6, 8
+    w = _moe_weights(rng, E, mf, d)
+    z = rng.standard_normal((4, d))
+    F, idx, wts, logits = ref.moe_ffn_output(z, w, E)
+    p = scipy.special.softmax(z @ w["w_router"].T, axis=-1)
+    want = sum(p[:, e:e + 1] * ref.swiglu_ffn(z, w["we_gate"][e], w["we_up"][e], w["we_down"][e])
+               for e in range(E))
+    assert np.allclose(F, want, atol=1e-13)
+
+
+def test_moe_topk_matches_bruteforce_per_token():
+    rng = np.random.default_rng(11)
+    E, k, mf, d = 16, 4, 6, 8
+    w = _moe_weights(rng, E, mf, d)
+    z = rng.standard_normal((6, d))
+    F, idx, wts, logits = ref.moe_ffn_output(z, w, k)
+    for t in range(6):
+        l = [float(np.dot(z[t], w["w_router"][e])) for e in range(E)]
+        top = sorted(range(E), key=lambda e: (-l[e], e))[:k]
+        assert idx[t].tolist() == top
+        ex = [math.exp(l[e] - l[top[0]]) for e in top]
+        s = sum(ex)
+        acc_ = np.zeros(d)
+        for i, e in enumerate(top):
+            acc_ += ex[i] / s * ref.swiglu_ffn(z[t:t + 1], w["we_gate"][e], w["we_up"][e],
+                                              w["we_down"][e])[0]
+        assert np.allclose(F[t], acc_, atol=1e-13)
+
+
+# ---------------------------------------------------- full layer / toy ----
+
+def _toy_lists(w):
+    return {k: np.asarray(v, dtype=np.float64).tolist() for k, v in w.items()}
+
+
+@pytest.mark.parametrize("variant", ["toy", "toy_qknorm", "bias_gqa"])
+def test_layer_matches_scalar_bruteforce(variant):
+    if variant == "toy":
+        cfg = configs.TOY
+    elif variant == "toy_qknorm":
+        cfg = configs.with_dims(configs.TOY, qk_norm=True, gamma_std=0.2)
+    else:
+        cfg = small_cfg(d=8, n_q_heads=4, n_kv_heads=2, head_dim=4, ffn_dim=10,
+                        qkv_bias=True, qk_norm=True, rope_theta=100.0)
+    w = f32_weights(synth.make_weights(cfg, 1000))
+    x = synth.to_f32(synth.make_prefill_input(cfg, 1001, 1, 5))
+    spec = spec_of(cfg)
+    for off in (0, 7):
+        y = ref.layer_prefill(x, w, spec, pos_offset=off)["y"][0]
+        yb = scalar_toy.toy_layer(x[0].astype(np.float64).tolist(), _toy_lists(w),
+                                  cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                                  eps=cfg.rms_eps, theta=cfg.rope_theta, pos_offset=off,
+                                  qk_norm=cfg.qk_norm, qkv_bias=cfg.qkv_bias)
+        assert np.max(np.abs(y - np.array(yb))) < 1e-13
+
+
+def test_causal_experiment_earlier_rows_bit_identical():
+    g = gold("rope_and_experiments.json")["experiment_future_change"]
+    cfg = configs.TOY
+    w = f32_weights(synth.make_weights(cfg, 1000))
+    x = synth.to_f32(synth.make_prefill_input(cfg, 1001, 1, 3)).astype(np.float64)
+    x[0, g["row"], g["col"]] = g["from"]
+    y0 = ref.layer_prefill(x, w, spec_of(cfg))["y"]
+    x[0, g["row"], g["col"]] = g["to"]
+    y1 = ref.layer_prefill(x, w, spec_of(cfg))["y"]
+    assert np.max(np.abs(y1[0, :g["row"]] - y0[0, :g["row"]])) == g["earlier_rows_max_abs_diff"]
+    assert np.max(np.abs(y1[0, g["row"]] - y0[0, g["row"]])) > 0
+
+
+def test_rope_shift_experiment():
+    g = gold("rope_and_experiments.json")["experiment_shift_positions"]
+    shift = g["to"][0] - g["from"][0]
+    for cfg in (configs.TOY, small_cfg(qk_norm=True, qkv_bias=True)):
+        w = f32_weights(synth.make_weights(cfg, 1000))
+        x = synth.to_f32(synth.make_prefill_input(cfg, 1001, 2, len(g["from"]) + 3))
+        y0 = ref.layer_prefill(x, w, spec_of(cfg), pos_offset=0)["y"]
+        y7 = ref.layer_prefill(x, w, spec_of(cfg), pos_offset=shift)["y"]
+        assert np.max(np.abs(y0 - y7)) < 1e-12
+        # changing relative distance (pos scaled) does change the output
+        if cfg.head_dim > 2:
+            assert np.max(np.abs(y0 - ref.layer_prefill(x, w, spec_of(cfg, theta=37.0))["y"])) > 1e-6
+
+
+def test_single_token_attention_branch_is_value_projection():
+    cfg = small_cfg(qkv_bias=True)
+    w = f32_weights(synth.make_weights(cfg, 1000))
+    x = synth.to_f32(synth.make_prefill_input(cfg, 1001, 1, 1)).astype(np.float64)
+    out = ref.layer_prefill(x, w, spec_of(cfg))
+    xhat = ref.rmsnorm(x[0], w["ln1_g"], cfg.rms_eps)
+    v = ref.linear(xhat, w["wv"], w["bv"]).reshape(1, cfg.n_kv_heads, cfg.head_dim)
+    o = np.concatenate([v[:, h // (cfg.n_q_heads // cfg.n_kv_heads)] for h in range(cfg.n_q_heads)], -1)
+    assert np.allclose(out["r"][0], x[0] + o @ w["wo"].astype(np.float64).T, atol=1e-13)
+
+
+def test_decode_equals_prefill_last_row():
+    for cfg in (configs.TOY, small_cfg(qk_norm=True, qkv_bias=True)):
+        spec = spec_of(cfg)
+        w = f32_weights(synth.make_weights(cfg, 1000))
+        T = 6
+        x = synth.to_f32(synth.make_prefill_input(cfg, 1001, 2, T))
+        full = ref.layer_prefill(x, w, spec, pos_offset=3)
+        part = ref.layer_prefill(x[:, :T - 1], w, spec, pos_offset=3)
+        kc = np.zeros((2, T + 2, cfg.n_kv_heads, cfg.head_dim))
+        vc = np.zeros_like(kc)
+        kc[:, :T - 1] = part["k"]
+        vc[:, :T - 1] = part["v"]
+        kc[:, T - 1:] = np.nan     # rows past the cache length are never read
+        vc[:, T - 1:] = np.nan
+        dec = ref.layer_decode(x[:, T - 1], kc, vc, np.array([T - 1, T - 1]), w, spec,
+                               pos_offset=3)
+        assert np.max(np.abs(dec["y"] - full["y"][:, T - 1])) < 1e-12
+        assert np.max(np.abs(dec["k_new"] - full["k"][:, T - 1])) < 1e-12
+        assert np.max(np.abs(dec["v_new"] - full["v"][:, T - 1])) < 1e-12
+
+
+def test_prefill_row_subset_matches_full():
+    cfg = small_cfg(qk_norm=True)
+    w = f32_weights(synth.make_weights(cfg, 1000))
+    x = synth.to_f32(synth.make_prefill_input(cfg, 1001, 2, 11))
+    full = ref.layer_prefill(x, w, spec_of(cfg))
+    rows = [0, 4, 10]
+    sub = ref.layer_prefill(x, w, spec_of(cfg), rows=rows)
+    assert np.array_equal(sub["y"], full["y"][:, rows])
+
+
+def test_moe_layer_half_single_expert_equals_dense():
+    cfg = small_cfg(n_experts=1, top_k=1, ffn_dim=24)
+    w = f32_weights(synth.make_weights(cfg, 1000))
+    r = synth.to_f32(synth.make_moe_input(cfg, 1001, 9))
+    out = ref.moe_ffn(r, w, spec_of(cfg))
+    z = ref.rmsnorm(r, w["ln2_g"], cfg.rms_eps)
+    dense = r + ref.swiglu_ffn(z, w["we_gate"][0], w["we_up"][0], w["we_down"][0])
+    assert np.allclose(out["y"], dense, atol=1e-13)
+
+
+# ---------------------------------------------------------- accounting ----
+
+def _count_layer_elements(cfg, include_norm_bias=True):
+    n = 0
+    for name, shape in synth.weight_shapes(cfg).items():
+        if not include_norm_bias and (name.endswith("_g") or name in ("bq", "bk", "bv")):
+            continue
+        n += int(np.prod(shape))
+    return n
+
+
+def test_qwen25_7b_parameter_count():
+    g = gold("param_counts.json")["qwen2.5-7b"]
+    D = g["dims"]
+    cfg = configs.QWEN25_7B
+    d, q, kv = cfg.d, cfg.q_dim, cfg.kv_dim
+    assert acc.attn_params(d, q, kv) == g["attn_per_layer"]
+    assert acc.qkv_bias_params(q, kv) == g["qkv_bias_per_layer"]
+    assert acc.mlp_params(d, cfg.ffn_dim) == g["mlp_per_layer"]
+    assert acc.norm_params(d) == g["norm_per_layer"]
+    # the synthetic layer allocates exactly these elements
+    layer = _count_layer_elements(cfg)
+    assert layer == g["attn_per_layer"] + g["qkv_bias_per_layer"] + g["mlp_per_layer"] + g["norm_per_layer"]
+    total = acc.model_params(D["L"], layer, D["V"], d, D["tied"])
+    assert total == g["total"]
+    assert total - g["embed_tokens"] == g["matmul_params"]
+    assert g["matmul_params"] - g["embed_tokens"] == g["trunk_with_final_norm"]
+    assert round(2 * g["matmul_params"] / 1e9, 2) == g["gflop_per_token"]
+    assert round(2 * g["trunk_with_final_norm"] / 1e9, 2) == g["trunk_gflop_per_token"]
+    assert round(2 * g["embed_tokens"] / 1e9, 2) == g["lm_head_gflop_per_token"]
+    nb = g["norm_and_bias_total"]
+    assert D["L"] * acc.norm_params(d) == nb["layer_norms"]
+    assert D["L"] * acc.qkv_bias_params(q, kv) == nb["qkv_bias"]
+    # the infra-view table leaves norms and bias out
+    t = g["infra_view_table"]
+    no_nb = _count_layer_elements(cfg, include_norm_bias=False)
+    assert D["L"] * acc.attn_params(d, q, kv) == t["all_attention"]
+    assert D["L"] * acc.mlp_params(d, cfg.ffn_dim) == t["all_ffn"]
+    assert acc.model_params(D["L"], no_nb, D["V"], d, False) - d == t["total"]
+    assert t["total"] + nb["layer_norms"] + nb["qkv_bias"] + nb["final_norm"] == g["total"]
+    assert round(2 * t["all_attention"] / 1e9, 2) == t["flop_per_token_g"]["attention"]
+    assert round(2 * t["all_ffn"] / 1e9, 2) == t["flop_per_token_g"]["ffn"]
+
+
+def test_qwen3_8b_layer_counts_and_flops():
+    g = gold("param_counts.json")["qwen3-8b-layer"]
+    cfg = configs.QWEN3_8B
+    assert acc.attn_params(cfg.d, cfg.q_dim, cfg.kv_dim) == g["p_attn"]
+    assert acc.mlp_params(cfg.d, cfg.ffn_dim) == g["p_mlp"]
+    assert _count_layer_elements(cfg) == g["p_layer"]
+    assert _count_layer_elements(cfg, include_norm_bias=False) == g["p_linear"]
+    T = g["T"]
+    fl = sum(acc.dense_layer_gemm_flops(T, cfg.d, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim).values())
+    assert fl == 2 * T * g["p_linear"]
+    assert round(fl / 1e9, 2) == g["linear_gflop"]
+    dense_attn = 4 * cfg.n_q_heads * T * T * cfg.head_dim
+    assert round(dense_attn / 1e9, 3) == g["dense_attention_gflop"]
+    assert acc.kv_bytes_per_token(cfg.n_kv_heads, cfg.head_dim) == g["kv_bytes_per_layer_position"]
+
+
+def test_attention_flop_constants():
+    g = gold("attention_constants.json")
+    cfg = configs.QWEN25_7B
+    per_layer = acc.attn_prefill_flops_half(1, cfg.n_q_heads, cfg.head_dim)
+    assert per_layer == g["prefill_constant_per_layer"]
+    assert 28 * per_layer == g["prefill_constant_28_layers"]
+    assert acc.attn_decode_flops(1, cfg.n_q_heads, cfg.head_dim) == g["decode_constant_per_layer"]
+    assert 28 * acc.attn_decode_flops(1, cfg.n_q_heads, cfg.head_dim) == g["decode_constant_28_layers"]
+    S = g["S_check"]
+    sum_form = sum(28 * acc.attn_decode_flops(t, cfg.n_q_heads, cfg.head_dim) for t in range(S))
+    assert float(f"{sum_form:.4e}") == g["S_check_sum_form"]
+    assert float(f"{28 * acc.attn_prefill_flops_half(S, 28, 128):.4e}") == g["S_check_square_form"]
+    # exact visible pairs: S(S+1)/2 per head
+    assert acc.attn_prefill_flops_exact(3, 1, 1) == 4 * 6
+    assert g["softmax_constant"] == 5 * 28 * 28 // 2
+    assert g["scale_constant"] == 28 * 28 // 2
+    assert round(13.05e9 / g["prefill_constant_28_layers"]) == g["crossover_S"]
+    assert acc.kv_bytes_per_token(4, 128) == g["kv_bytes_per_layer_token"]
+    assert 28 * acc.kv_bytes_per_token(4, 128) == g["kv_bytes_per_token_28_layers"]
+    for T, gb in g["per_step_read_gb"].items():
+        assert round(int(T) * g["kv_bytes_per_token_28_layers"] / 1e9, 3) == gb
+    T = g["cache_saving_T"]
+    with_cache = 13.05e9 + 401408 * T
+    without = T * 13.05e9 + 200704 * T * T
+    assert round(without / with_cache) == g["cache_saving_ratio"]
+
+
+def test_moe_parameter_counts():
+    g = gold("param_counts.json")["qwen2-57b-a14b-moe"]
+    D = g["dims"]
+    assert acc.moe_block_params(D["d"], D["e"], D["mf"], D["sf"]) - D["d"] * D["e"] \
+        - D["e"] * 3 * D["d"] * D["mf"] == g["shared_expert_with_gate"]
+    assert D["k"] * 3 * D["d"] * D["mf"] == g["routed_active_8"]
+    assert D["d"] * D["e"] == g["router"]
+    assert acc.moe_active_params(D["d"], D["e"], D["k"], D["mf"], D["sf"]) == g["ffn_active_per_layer"]
+    q = gold("param_counts.json")["qwen3-30b-a3b-layer"]
+    cfg = configs.QWEN3_30B_A3B
+    shapes = synth.weight_shapes(cfg)
+    experts = sum(int(np.prod(shapes[n])) for n in ("we_gate", "we_up", "we_down"))
+    assert round(experts / 1e6) == q["expert_params_approx_millions"]
+    assert int(np.prod(shapes["w_router"])) == 2048 * 128
+    assert acc.attn_params(cfg.d, cfg.q_dim, cfg.kv_dim) == 2048 * 4096 * 2 + 2 * 2048 * 512
+    assert acc.experts_touched(128, 8, 1) == pytest.approx(8.0)
+
+
+# ------------------------------------------------------------ hygiene ----
+
+def test_oracle_and_product_share_no_code():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for fn in os.listdir(os.path.join(root, "oracle")):
+        if fn.endswith(".py"):
+            src = open(os.path.join(root, "oracle", fn)).read()
+            assert "transformer_decoder_layer_qwen_amd" not in src, fn
+    pkg = os.path.join(root, "transformer_decoder_layer_qwen_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in src and "from oracle" not in src, fn
