@@ -1,0 +1,394 @@
+"""Layer throughput on one MI355X, plus the roofline of the dominant kernel and
+the oracle's CPU rate.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
+
+Headline workload: the Qwen2.5-7B-shaped layer, one decode step for batch 1
+with a 1024-row KV cache (bf16 weights N(0, 0.02), biases N(0, 0.02), gammas
+N(1, 0.05), cache and hidden rows N(0, 1); seeded synthetic data). One step =
+one qlayer_decode call, i.e. every stage of the layer. Two copies of the
+weights and caches alternate between steps so that the 256 MB last-level cache
+cannot serve the weight stream. `value` = tokens/s = batch / step time, timed
+with events around exactly K steps on the layer's stream.
+
+The other workloads of the config table (prefill and decode at their full
+sizes) are timed the same way and reported under "secondary", each with a
+per-stage breakdown taken from the library's stage events.
+
+One JSON line is printed on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from transformer_decoder_layer_qwen_amd import configs, synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+METRIC = "layer tokens/s (prefill & decode) + % bf16 MFMA / HBM roofline, 1 GPU"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ HIP events ----
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        import torch
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        lib.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        lib.hipEventSynchronize.argtypes = [vp]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.hipEventDestroy.argtypes = [vp]
+        lib.hipEventRecord.argtypes = [vp, vp]
+        self.lib = lib
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+# ------------------------------------------------------- algorithmic work ----
+
+def stage_work(cfg, wl, stage, cache_len=None):
+    """(algorithmic flops, algorithmic HBM bytes) of one stage of one call."""
+    d, q, kv, f, dh = cfg.d, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim, cfg.head_dim
+    N = wl.tokens
+    es = 2
+    w_bytes = {"qkv": (q + 2 * kv) * d * es + (2 * (q + 2 * kv) if cfg.qkv_bias else 0),
+               "o_proj": d * q * es, "gate_up": 2 * f * d * es, "down": d * f * es}
+    if stage in ("qkv", "o_proj", "gate_up", "down"):
+        kdim, ncols = {"qkv": (d, q + 2 * kv), "o_proj": (q, d), "gate_up": (d, 2 * f),
+                       "down": (f, d)}[stage]
+        flops = 2 * N * kdim * ncols
+        act = {"qkv": N * d * es + N * (q + 2 * kv) * 4,
+               "o_proj": N * q * es + N * d * (es + 4),
+               "gate_up": N * d * es + N * f * es,
+               "down": N * f * es + N * d * (4 + es)}[stage]
+        return flops, w_bytes[stage] + act
+    if stage == "attention":
+        if wl.kind == "prefill":
+            S = wl.seq
+            flops = wl.batch * 4 * dh * cfg.n_q_heads * S * (S + 1) // 2
+            byts = wl.batch * (S * q * es * 2 + S * 2 * kv * es)
+        else:
+            L = cache_len + 1
+            flops = wl.batch * 4 * dh * cfg.n_q_heads * L
+            byts = wl.batch * (L * 2 * kv * es + 2 * q * es)
+        return flops, byts
+    if stage == "expert_gate_up":
+        rows = N * cfg.top_k
+        flops = 2 * rows * d * 2 * f
+        touched = cfg.n_experts * (1 - (1 - cfg.top_k / cfg.n_experts) ** N)
+        return flops, touched * 2 * f * d * es + rows * (d * es + f * es)
+    if stage == "expert_down":
+        rows = N * cfg.top_k
+        flops = 2 * rows * f * d
+        touched = cfg.n_experts * (1 - (1 - cfg.top_k / cfg.n_experts) ** N)
+        return flops, touched * f * d * es + rows * (f * es + d * 4)
+    return 0, 0
+
+
+def layer_work(cfg, wl):
+    stages = ["qkv", "attention", "o_proj"] + (
+        ["expert_gate_up", "expert_down"] if cfg.is_moe else ["gate_up", "down"])
+    fl = by = 0
+    for s in stages:
+        a, b = stage_work(cfg, wl, s, cache_len=wl.seq)
+        fl += a
+        by += b
+    if cfg.is_moe:
+        by += cfg.n_experts * d_router(cfg)
+    return fl, by
+
+
+def d_router(cfg):
+    return cfg.d * 2
+
+
+# ------------------------------------------------------------- workloads ----
+
+class Setup:
+    """Device weights (n_copies) and inputs of one workload."""
+
+    def __init__(self, cid, wl, n_copies=2):
+        import torch
+        from transformer_decoder_layer_qwen_amd import binding as B
+        self.cfg = cfg = configs.CONFIGS[cid]
+        self.wl = wl
+        t0 = time.time()
+        w_np = synth.make_weights(cfg, configs.weight_seed(cid))
+        log(f"[bench] {wl.label}: weights generated in {time.time() - t0:.1f}s")
+        self.layers = []
+        for _ in range(n_copies):
+            self.layers.append(B.QLayer(cfg, B.device_weights(w_np),
+                                        max_tokens=wl.tokens if wl.kind == "prefill" else 1,
+                                        max_batch=wl.batch if wl.kind == "decode" else 1))
+        del w_np
+        self.inputs = []
+        for c in range(n_copies):
+            if wl.kind == "prefill":
+                x = B.to_device(synth.make_prefill_input(cfg, wl.seed, wl.batch, wl.seq))
+                kc = torch.zeros(wl.batch, wl.seq, cfg.n_kv_heads, cfg.head_dim,
+                                 dtype=torch.bfloat16, device="cuda")
+                self.inputs.append((x, kc, torch.zeros_like(kc), torch.empty_like(x)))
+            else:
+                x, kc, vc, lens = synth.make_decode_input(cfg, wl.seed, wl.batch, wl.seq)
+                self.inputs.append((B.to_device(x), B.to_device(kc), B.to_device(vc),
+                                    torch.from_numpy(lens).cuda(), lens.tolist(),
+                                    torch.empty(wl.batch, cfg.d, dtype=torch.bfloat16,
+                                                device="cuda")))
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        c = i % len(self.layers)
+        layer, inp = self.layers[c], self.inputs[c]
+        if self.wl.kind == "prefill":
+            x, kc, vc, y = inp
+            layer.prefill(x, kc, vc, y=y)
+        else:
+            x, kc, vc, lens, _, y = inp
+            layer.decode(x, lens, kc, vc, y=y)
+
+    def close(self):
+        for layer in self.layers:
+            layer.close()
+        self.layers, self.inputs = [], []
+
+
+def time_steps(setup, hip, steps, warmup):
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        setup.step(i)
+    torch.cuda.synchronize()
+    a, b = hip.create(2)
+    torch.cuda.synchronize()
+    hip.record(a, stream)
+    for i in range(steps):
+        setup.step(i)
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(a, b)
+    hip.destroy([a, b])
+    return ms / steps
+
+
+def time_stage(setup, hip, stage, steps):
+    """Average duration of one stage, events recorded by the library around
+    its kernels on the call's stream, over `steps` calls."""
+    import torch
+    evs = hip.create(2 * steps)
+    for i in range(steps):
+        for layer in setup.layers:
+            layer.set_stage_events(stage, evs[2 * i], evs[2 * i + 1])
+        setup.step(i)
+    torch.cuda.synchronize()
+    for layer in setup.layers:
+        layer.set_stage_events(None, None, None)
+    tot = sum(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps))
+    hip.destroy(evs)
+    return tot / steps
+
+
+def stages_of(cfg):
+    s = ["rmsnorm1", "qkv", "qkv_post", "attention", "o_proj", "rmsnorm2"]
+    s += (["router", "permute", "expert_gate_up", "expert_down", "combine"] if cfg.is_moe
+          else ["gate_up", "down"])
+    return s
+
+
+def roofline_entry(cfg, wl, stage, ms):
+    fl, by = stage_work(cfg, wl, stage, cache_len=wl.seq)
+    hbm_bound = wl.kind == "decode" or fl / max(by, 1) < 315
+    if hbm_bound:
+        ach = by / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": int(by), "kernel_ms": round(ms, 5), "stage": stage}
+    ach = fl / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops": int(fl), "kernel_ms": round(ms, 5), "stage": stage}
+
+
+def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True):
+    setup = Setup(cid, wl)
+    cfg = setup.cfg
+    ms = time_steps(setup, hip, steps, warmup)
+    out = {"workload": wl.label, "kind": wl.kind, "batch": wl.batch,
+           "seq_or_cache": wl.seq, "tokens_per_step": wl.tokens,
+           "ms_per_step": round(ms, 5), "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1)}
+    fl, by = layer_work(cfg, wl)
+    if wl.kind == "prefill":
+        out["layer_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
+        out["layer_frac_mfma"] = round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    else:
+        out["layer_gbs"] = round(by / (ms * 1e-3) / 1e9, 1)
+        out["layer_frac_hbm"] = round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if breakdown:
+        st = {}
+        for s in stages_of(cfg):
+            st[s] = round(time_stage(setup, hip, s, stage_steps), 5)
+        out["stage_ms"] = st
+        dom = max(st, key=st.get)
+        out["dominant"] = roofline_entry(cfg, wl, dom, st[dom])
+        gemms = [s for s in ("qkv", "o_proj", "gate_up", "down", "expert_gate_up",
+                             "expert_down") if s in st]
+        out["stage_roofline"] = {s: roofline_entry(cfg, wl, s, st[s]) for s in gemms + ["attention"]}
+    setup.close()
+    return out, setup
+
+
+# ------------------------------------------------------------ CPU oracle ----
+
+def cpu_baseline(seconds=12.0):
+    """The fp64 oracle, as it stands, on the headline workload: repeated decode
+    steps of the Qwen2.5-7B layer at batch 1 with a 1024-row cache."""
+    from oracle import qlayer_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    cid, wl = 2, configs.WORKLOADS[2][0]
+    cfg = configs.CONFIGS[cid]
+    w = {k: synth.to_f32(v) for k, v in synth.make_weights(cfg, configs.weight_seed(cid)).items()}
+    x, kc, vc, lens = synth.make_decode_input(cfg, wl.seed, wl.batch, wl.seq)
+    x, kc, vc = synth.to_f32(x), synth.to_f32(kc), synth.to_f32(vc)
+    spec = ref.LayerSpec(d=cfg.d, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                         head_dim=cfg.head_dim, ffn_dim=cfg.ffn_dim, qkv_bias=cfg.qkv_bias,
+                         qk_norm=cfg.qk_norm, eps=cfg.rms_eps, theta=cfg.rope_theta)
+    n = 0
+    t0 = time.time()
+    while True:
+        ref.layer_decode(x, kc, vc, lens, w, spec)
+        n += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    return {"value": round(n * wl.batch / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} decode steps of {wl.label} (fp64 NumPy oracle, weights pre-widened "
+                      f"to fp32) in {dt:.1f}s"}
+
+
+# ------------------------------------------------------------------ main ----
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-steps", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's data-parallel shards are independent, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    hip = HipEvents()
+
+    cid, wl = 2, configs.WORKLOADS[2][0]
+    head, _ = run_workload(cid, wl, hip, args.steps, args.warmup, args.stage_steps)
+    log(f"[bench] headline {head['workload']}: {head['tokens_per_s']} tok/s, "
+        f"{head['ms_per_step']} ms/step")
+    secondary = []
+    if not args.headline_only:
+        for c in (2, 3, 4, 5):
+            for w in configs.WORKLOADS[c]:
+                if (c, w.index) == (cid, wl.index):
+                    continue
+                s_steps = max(5, args.steps // 5) if w.kind == "prefill" else args.steps
+                r, _ = run_workload(c, w, hip, s_steps, max(2, args.warmup // 2),
+                                    max(3, args.stage_steps // 2))
+                log(f"[bench] {r['workload']}: {r['tokens_per_s']} tok/s, "
+                    f"{r['ms_per_step']} ms/step")
+                secondary.append(r)
+                torch.cuda.empty_cache()
+
+    cfg = configs.CONFIGS[cid]
+    dom = dict(head["dominant"])
+    roof = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = dom["stage"]
+    roof["kernel_ms"] = dom["kernel_ms"]
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.label, "batch": wl.batch, "cache_len": wl.seq, "d": cfg.d,
+                   "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "ffn_dim": cfg.ffn_dim, "qkv_bias": cfg.qkv_bias,
+                   "weight_copies_rotated": 2, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer_frac_hbm": head.get("layer_frac_hbm"),
+        "stage_ms": head.get("stage_ms"),
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

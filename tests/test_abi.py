@@ -1,0 +1,109 @@
+"""CPU checks of the C-ABI library: it loads, exports every function the
+header declares, and rejects bad arguments on the host before touching a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_decoder_layer_qwen_amd import binding as b
+from transformer_decoder_layer_qwen_amd import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlayer.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlayer_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(b.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert b.qlayer_abi_version() == 1
+
+
+def _cfg(**kw):
+    base = dict(d=256, n_q_heads=4, n_kv_heads=2, head_dim=128, ffn_dim=256, n_experts=0, top_k=0,
+                norm_topk_prob=1, qkv_bias=0, qk_norm=0, rms_eps=1e-6, rope_theta=1e6,
+                dtype=b.QL_BF16, max_tokens=64, max_batch=4)
+    base.update(kw)
+    return b.QlConfig(**base)
+
+
+def _weights(moe=False):
+    fake = 0x1000
+    names = ["ln1_g", "ln2_g", "wq", "wk", "wv", "wo"]
+    names += ["w_router", "we_gate", "we_up", "we_down"] if moe else ["w_gate", "w_up", "w_down"]
+    return b.QlWeights(**{n: fake for n in names})
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=0), b.QL_EINVAL),
+    (dict(n_q_heads=5), b.QL_EINVAL),
+    (dict(head_dim=64), b.QL_EUNSUPPORTED),
+    (dict(d=200), b.QL_EUNSUPPORTED),
+    (dict(ffn_dim=100), b.QL_EUNSUPPORTED),
+    (dict(n_q_heads=34, n_kv_heads=2), b.QL_EUNSUPPORTED),
+    (dict(max_batch=129), b.QL_EUNSUPPORTED),
+    (dict(max_tokens=0, max_batch=0), b.QL_EINVAL),
+    (dict(dtype=7), b.QL_EINVAL),
+    (dict(qkv_bias=1), b.QL_EINVAL),          # bias pointers missing
+    (dict(qk_norm=1), b.QL_EINVAL),           # QK-norm gammas missing
+    (dict(dtype=b.QL_F32, head_dim=6), b.QL_EUNSUPPORTED),
+])
+def test_create_rejects_bad_configs_on_host(kw, status):
+    h = ctypes.c_void_p()
+    st = b.load_library().qlayer_create(ctypes.byref(_cfg(**kw)), ctypes.byref(_weights()),
+                                        ctypes.byref(h))
+    assert st == status, b.qlayer_last_error()
+    assert h.value is None
+    assert b.qlayer_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_experts=20, top_k=2), b.QL_EUNSUPPORTED),
+    (dict(n_experts=16, top_k=0), b.QL_EINVAL),
+    (dict(n_experts=16, top_k=17), b.QL_EINVAL),
+    (dict(n_experts=512, top_k=8), b.QL_EUNSUPPORTED),
+    (dict(n_experts=16, top_k=2, dtype=b.QL_F32, head_dim=2), b.QL_EUNSUPPORTED),
+])
+def test_create_rejects_bad_moe_configs(kw, status):
+    h = ctypes.c_void_p()
+    st = b.load_library().qlayer_create(ctypes.byref(_cfg(**kw)), ctypes.byref(_weights(True)),
+                                        ctypes.byref(h))
+    assert st == status, b.qlayer_last_error()
+
+
+def test_null_arguments_are_rejected():
+    lib = b.load_library()
+    assert lib.qlayer_create(None, None, None) == b.QL_EINVAL
+    assert lib.qlayer_prefill(None, None, 1, 1, 0, None, None, 1, None, None) == b.QL_EINVAL
+    assert lib.qlayer_decode(None, None, 1, None, None, 0, None, None, 1, None, None) == b.QL_EINVAL
+    assert lib.qlayer_moe_ffn(None, None, 1, None, None, None, None) == b.QL_EINVAL
+    assert lib.qlayer_set_taps(None, None) == b.QL_EINVAL
+    assert lib.qlayer_destroy(None) == b.QL_OK
+    assert lib.qlayer_workspace_bytes(None) == 0
+
+
+def test_config_table_fits_the_bf16_limits():
+    for cid, cfg in configs.CONFIGS.items():
+        if cfg.dtype != "bf16":
+            continue
+        assert cfg.head_dim == 128 and cfg.d % 128 == 0 and cfg.ffn_dim % 64 == 0
+        assert cfg.n_q_heads // cfg.n_kv_heads <= 16
+        for wl in configs.WORKLOADS[cid]:
+            if wl.kind == "decode":
+                assert wl.batch <= 128

@@ -1,0 +1,368 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, on the
+same seeded inputs. Stage taps localise errors; full-size configs are checked
+on sampled rows / sequences in the launch configuration the benchmark uses.
+
+Bars: bf16 paths max|err| <= 2e-2 * RMS(reference) (per tensor), the fp32 toy
+1e-5 relative; MoE expert sets must match wherever the oracle's k-th/(k+1)-th
+logit gap exceeds 1e-3.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from harness import (ATT_BRANCH_TOL, BF16_TOL, F32_TOL, FFN_BRANCH_TOL, attention_err,  # noqa: E402
+                     branch_err, log, rel_err, rounding_err, routing_mismatch, small_cfg, small_moe_cfg,
+                     spec_of, weights_for)
+from oracle import qlayer_ref as ref  # noqa: E402
+from transformer_decoder_layer_qwen_amd import binding as B  # noqa: E402
+from transformer_decoder_layer_qwen_amd import configs, synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_guard(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    log(f"[gpu] start {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def make_layer(cfg, seed=1000, max_tokens=0, max_batch=0):
+    w_np, w32 = weights_for(cfg, seed)
+    layer = B.QLayer(cfg, B.device_weights(w_np), max_tokens=max_tokens, max_batch=max_batch)
+    return layer, w32
+
+
+def host(t):
+    return B.to_host_f32(t)
+
+
+def tdt(cfg):
+    return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+
+def run_prefill(layer, cfg, x_np, T_max, pos_offset=0):
+    B_, S, _ = x_np.shape
+    xd = B.to_device(x_np)
+    kc = torch.zeros(B_, T_max, cfg.n_kv_heads, cfg.head_dim, dtype=tdt(cfg), device="cuda")
+    vc = torch.zeros_like(kc)
+    y = layer.prefill(xd, kc, vc, pos_offset=pos_offset)
+    torch.cuda.synchronize()
+    return y, kc, vc
+
+
+# ------------------------------------------------------------- fp32 toy ----
+
+@pytest.mark.parametrize("variant", ["toy", "toy_offset7", "toy_qknorm"])
+def test_toy_prefill_f32(variant):
+    cfg = configs.TOY
+    off = 7 if variant == "toy_offset7" else 0
+    if variant == "toy_qknorm":
+        cfg = configs.with_dims(cfg, qk_norm=True, gamma_std=0.2)
+    layer, w32 = make_layer(cfg, max_tokens=16, max_batch=4)
+    x = synth.make_prefill_input(cfg, 1001, 1, 3)
+    y, kc, vc = run_prefill(layer, cfg, x, T_max=8, pos_offset=off)
+    o = ref.layer_prefill(x, w32, spec_of(cfg), pos_offset=off)
+    assert rel_err(host(y), o["y"]) <= F32_TOL
+    assert rel_err(host(kc)[:, :3], o["k"]) <= F32_TOL
+    assert rel_err(host(vc)[:, :3], o["v"]) <= F32_TOL
+    assert np.all(host(kc)[:, 3:] == 0)
+
+
+def test_toy_decode_f32():
+    cfg = configs.TOY
+    layer, w32 = make_layer(cfg, max_tokens=16, max_batch=4)
+    spec = spec_of(cfg)
+    x = synth.make_prefill_input(cfg, 1002, 2, 5)
+    part = ref.layer_prefill(x[:, :4], w32, spec)
+    T_max = 9
+    kc = np.full((2, T_max, 1, 2), np.nan, np.float32)
+    vc = np.full_like(kc, np.nan)
+    kc[:, :4] = part["k"]
+    vc[:, :4] = part["v"]
+    kd, vd = B.to_device(kc), B.to_device(vc)
+    lens = torch.tensor([4, 4], dtype=torch.int32, device="cuda")
+    y = layer.decode(B.to_device(x[:, 4]), lens, kd, vd, cache_len_host=[4, 4])
+    torch.cuda.synchronize()
+    dec = ref.layer_decode(x[:, 4], kc, vc, np.array([4, 4]), w32, spec)
+    full = ref.layer_prefill(x, w32, spec)
+    assert rel_err(host(y), dec["y"]) <= F32_TOL
+    assert rel_err(host(y), full["y"][:, 4]) <= F32_TOL
+    assert rel_err(host(kd)[:, 4], dec["k_new"]) <= F32_TOL
+    assert np.all(np.isnan(host(kd)[:, 5:]))
+
+
+# ------------------------------------------------ small bf16, stage taps ----
+
+def test_small_bf16_prefill_stages():
+    cfg = small_cfg()
+    Bn, S, T_max = 2, 300, 320
+    N = Bn * S
+    layer, w32 = make_layer(cfg, max_tokens=N, max_batch=4)
+    q_t = torch.empty(N, cfg.q_dim, dtype=torch.bfloat16, device="cuda")
+    a_t = torch.empty(N, cfg.q_dim, dtype=torch.float32, device="cuda")
+    r_t = torch.empty(N, cfg.d, dtype=torch.float32, device="cuda")
+    z_t = torch.empty(N, cfg.d, dtype=torch.bfloat16, device="cuda")
+    h_t = torch.empty(N, cfg.ffn_dim, dtype=torch.bfloat16, device="cuda")
+    layer.set_taps(q=q_t, attn=a_t, r=r_t, z=z_t, h=h_t)
+    x = synth.make_prefill_input(cfg, 1003, Bn, S)
+    y, kc, vc = run_prefill(layer, cfg, x, T_max)
+    x32 = synth.to_f32(x).reshape(N, -1).astype(np.float64)
+    o = ref.layer_prefill(x32.reshape(Bn, S, -1), w32, spec_of(cfg))
+    Hq, dh = cfg.n_q_heads, cfg.head_dim
+    yg, rg, ag = host(y).reshape(N, -1), host(r_t), host(a_t)
+    # the output bar, and the two residual branches measured on their own scale
+    e_y = rel_err(yg, o["y"].reshape(N, -1))
+    a_ref = o["r"].reshape(N, -1) - x32          # attention branch; R is fp32 (unrounded)
+    f_ref = (o["y"] - o["r"]).reshape(N, -1)      # FFN branch
+    e_att_branch = rel_err(rg - x32, a_ref)
+    e_ffn_branch = branch_err(yg, rg, f_ref)
+    log(f"y {e_y:.3e}  attention branch {e_att_branch:.3e}  ffn branch {e_ffn_branch:.3e}")
+    assert e_y <= BF16_TOL
+    assert e_att_branch <= ATT_BRANCH_TOL and e_ffn_branch <= FFN_BRANCH_TOL
+    # Q/K/V: projections, QK-norm, RoPE; one bf16 rounding each
+    errs = {"q": rounding_err(host(q_t), o["q"].reshape(N, -1)),
+            "k": rounding_err(host(kc)[:, :S], o["k"]),
+            "v": rounding_err(host(vc)[:, :S], o["v"]),
+            "k-untouched": float(np.abs(host(kc)[:, S:]).max())}
+    # each later stage fed the GPU's own inputs
+    qg = host(q_t).reshape(Bn, S, Hq, dh)
+    kg, vg = host(kc)[:, :S], host(vc)[:, :S]
+    att = np.stack([ref.attention(qg[b], kg[b], vg[b], np.arange(S), np.arange(S),
+                                  cfg.n_kv_heads).reshape(S, -1) for b in range(Bn)])
+    errs["attention"] = attention_err(ag, att.reshape(N, -1), vg)
+    errs["o_proj"] = rounding_err(rg - x32, ref.linear(ag, w32["wo"]), rel=0.0, noise=1e-4)
+    errs["rmsnorm2"] = rounding_err(host(z_t), ref.rmsnorm(rg, w32["ln2_g"], cfg.rms_eps))
+    errs["swiglu"] = rounding_err(host(h_t), ref.swiglu_hidden(host(z_t), w32["w_gate"],
+                                                               w32["w_up"]))
+    ffn_iso = ref.linear(host(h_t), w32["w_down"])
+    errs["down"] = rounding_err(yg, rg + ffn_iso)
+    log(f"stage checks (<= 1 passes): { {k: round(v, 3) for k, v in errs.items()} }")
+    for k, v in errs.items():
+        if k == "k-untouched":
+            assert v == 0.0
+        else:
+            assert v <= 1.0, (k, v)
+
+
+def test_small_bf16_decode_ragged_lengths():
+    cfg = small_cfg()
+    lens = [5, 100, 257]
+    Bn, T_max = len(lens), 300
+    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=4)
+    q_t = torch.empty(Bn, cfg.q_dim, dtype=torch.bfloat16, device="cuda")
+    a_t = torch.empty(Bn, cfg.q_dim, dtype=torch.float32, device="cuda")
+    r_t = torch.empty(Bn, cfg.d, dtype=torch.float32, device="cuda")
+    layer.set_taps(q=q_t, attn=a_t, r=r_t)
+    x, kc, vc, _ = synth.make_decode_input(cfg, 1004, Bn, max(lens), T_max=T_max)
+    for b, L in enumerate(lens):  # shorter sequences: rows past their length are canaries
+        kc[b, L:] = synth.BF16_NAN_BITS
+        vc[b, L:] = synth.BF16_NAN_BITS
+    kd, vd = B.to_device(kc), B.to_device(vc)
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    y = layer.decode(B.to_device(x), ld, kd, vd, cache_len_host=lens)
+    torch.cuda.synchronize()
+    x32 = synth.to_f32(x).astype(np.float64)
+    dec = ref.layer_decode(x32, synth.to_f32(kc), synth.to_f32(vc), np.array(lens), w32,
+                           spec_of(cfg))
+    assert rel_err(host(y), dec["y"]) <= BF16_TOL
+    assert rel_err(host(r_t) - x32, dec["r"] - x32) <= ATT_BRANCH_TOL
+    assert branch_err(host(y), host(r_t), dec["y"] - dec["r"]) <= FFN_BRANCH_TOL
+    assert rounding_err(host(q_t), dec["q"].reshape(Bn, -1)) <= 1.0
+    for b, L in enumerate(lens):
+        assert rounding_err(host(kd)[b, L], dec["k_new"][b]) <= 1.0
+        assert rounding_err(host(vd)[b, L], dec["v_new"][b]) <= 1.0
+        assert np.all(np.isnan(host(kd)[b, L + 1:]))          # nothing else written
+        assert np.array_equal(host(kd)[b, :L], synth.to_f32(kc[b, :L]))
+    # attention kernel alone, fed the GPU's own queries and cache
+    qg = host(q_t).reshape(Bn, cfg.n_q_heads, cfg.head_dim)
+    for b, L in enumerate(lens):
+        o = ref.attention(qg[b:b + 1], host(kd)[b, :L + 1], host(vd)[b, :L + 1], np.array([L]),
+                          np.arange(L + 1), cfg.n_kv_heads)
+        assert attention_err(host(a_t)[b], o.reshape(-1), host(vd)[b, :L + 1]) <= 1.0
+    # O projection alone
+    assert rounding_err(host(r_t) - x32, ref.linear(host(a_t), w32["wo"]), rel=0.0,
+                        noise=1e-4) <= 1.0
+
+
+def test_decode_out_of_range_length_is_contained():
+    cfg = small_cfg()
+    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=4)
+    T_max = 16
+    x, kc, vc, _ = synth.make_decode_input(cfg, 1005, 2, 8, T_max=T_max)
+    kd, vd = B.to_device(kc), B.to_device(vc)
+    with pytest.raises(B.QLayerError) as e:
+        layer.decode(B.to_device(x), torch.tensor([8, 16], dtype=torch.int32, device="cuda"),
+                     kd, vd, cache_len_host=[8, 16])
+    assert e.value.status == B.QL_ECACHE_FULL
+    # without the host copy the kernels contain it: NaN output, no write
+    before = host(kd).copy()
+    y = layer.decode(B.to_device(x), torch.tensor([8, 16], dtype=torch.int32, device="cuda"),
+                     kd, vd)
+    torch.cuda.synchronize()
+    yh = host(y)
+    assert np.all(np.isfinite(yh[0])) and np.all(np.isnan(yh[1]))
+    after = host(kd)
+    assert np.array_equal(after[1], before[1], equal_nan=True)
+
+
+# --------------------------------------------------------- small MoE ----
+
+@pytest.mark.parametrize("N", [37, 300, 700])
+def test_small_moe_ffn(N):
+    cfg = small_moe_cfg()
+    layer, w32 = make_layer(cfg, max_tokens=max(N, 8), max_batch=4)
+    r = synth.make_moe_input(cfg, 1006, N)
+    idx_t = torch.empty(N, cfg.top_k, dtype=torch.int32, device="cuda")
+    w_t = torch.empty(N, cfg.top_k, dtype=torch.float32, device="cuda")
+    lg_t = torch.empty(N, cfg.n_experts, dtype=torch.float32, device="cuda")
+    z_t = torch.empty(N, cfg.d, dtype=torch.bfloat16, device="cuda")
+    layer.set_taps(logits=lg_t, z=z_t)
+    y = layer.moe_ffn(B.to_device(r), topk_idx=idx_t, topk_w=w_t)
+    torch.cuda.synchronize()
+    r32 = synth.to_f32(r).astype(np.float64)
+    o = ref.moe_ffn(r32, w32, spec_of(cfg))
+    assert rel_err(host(lg_t), o["logits"]) <= 1e-4
+    idx_g, w_g = idx_t.cpu().numpy(), w_t.cpu().numpy()
+    bad, checked = routing_mismatch(idx_g, o["logits"], cfg.top_k)
+    assert checked > 0.9 * N and bad.size == 0, bad
+    # the GPU's gate weights: softmax over its own selected logits, sum 1
+    sel = np.take_along_axis(host(lg_t).astype(np.float64), idx_g.astype(np.int64), -1)
+    assert rounding_err(w_g, ref.softmax(sel, -1), rel=1e-5, noise=1e-6) <= 1.0
+    assert np.all(np.diff(np.take_along_axis(host(lg_t), idx_g.astype(np.int64), -1), axis=-1) <= 0)
+    same = np.all(np.sort(idx_g, -1) == np.sort(o["idx"], -1), -1)
+    yg = host(y)
+    assert rel_err(yg[same], o["y"][same]) <= BF16_TOL
+    assert branch_err(yg[same], r32[same], o["f"][same]) <= FFN_BRANCH_TOL
+    # expert path alone: the GPU's z and routing through the oracle's experts
+    zg = host(z_t).astype(np.float64)
+    f_iso = np.zeros_like(r32)
+    for i in range(cfg.top_k):
+        for e in np.unique(idx_g[:, i]):
+            t = np.nonzero(idx_g[:, i] == e)[0]
+            f_iso[t] += w_g[t, i:i + 1] * ref.swiglu_ffn(zg[t], w32["we_gate"][e], w32["we_up"][e],
+                                                        w32["we_down"][e])
+    assert branch_err(yg, r32, f_iso) <= 1e-2
+
+
+def test_small_moe_layer_prefill():
+    cfg = small_moe_cfg()
+    Bn, S = 1, 200
+    layer, w32 = make_layer(cfg, max_tokens=Bn * S, max_batch=4)
+    x = synth.make_prefill_input(cfg, 1007, Bn, S)
+    y, kc, vc = run_prefill(layer, cfg, x, T_max=S)
+    o = ref.layer_prefill(synth.to_f32(x), w32, spec_of(cfg))
+    assert rel_err(host(y), o["y"]) <= BF16_TOL
+
+
+# ----------------------------------------------------- GPU invariants ----
+
+def test_gpu_causal_future_change_leaves_earlier_rows_bit_identical():
+    for cfg in (configs.TOY, small_cfg()):
+        layer, _ = make_layer(cfg, max_tokens=64, max_batch=4)
+        S = 3 if cfg.dtype == "f32" else 41
+        x = synth.to_f32(synth.make_prefill_input(cfg, 1008, 1, S)).copy()
+        x[0, S - 1, 0] = 1.0
+        enc = (lambda a: synth.f32_to_bf16_bits(a)) if cfg.dtype == "bf16" else (lambda a: a)
+        y0 = host(run_prefill(layer, cfg, enc(x), T_max=S)[0])
+        x[0, S - 1, 0] = -3.0
+        y1 = host(run_prefill(layer, cfg, enc(x), T_max=S)[0])
+        assert np.array_equal(y0[0, :S - 1], y1[0, :S - 1])
+        assert not np.array_equal(y0[0, S - 1], y1[0, S - 1])
+
+
+def test_gpu_rope_shift_and_determinism():
+    cfg = small_cfg()
+    layer, _ = make_layer(cfg, max_tokens=256, max_batch=4)
+    x = synth.make_prefill_input(cfg, 1009, 2, 100)
+    y0 = host(run_prefill(layer, cfg, x, T_max=100, pos_offset=0)[0])
+    y0b = host(run_prefill(layer, cfg, x, T_max=100, pos_offset=0)[0])
+    y7 = host(run_prefill(layer, cfg, x, T_max=100, pos_offset=7)[0])
+    assert np.array_equal(y0, y0b)
+    assert rel_err(y7, y0) <= BF16_TOL
+
+
+def test_gpu_decode_matches_prefill_last_row():
+    cfg = small_cfg()
+    T = 130
+    layer, _ = make_layer(cfg, max_tokens=2 * T, max_batch=4)
+    x = synth.make_prefill_input(cfg, 1010, 2, T)
+    y_full = host(run_prefill(layer, cfg, x, T_max=T + 4)[0])
+    _, kc, vc = run_prefill(layer, cfg, np.ascontiguousarray(x[:, :T - 1]), T_max=T + 4)
+    lens = torch.tensor([T - 1, T - 1], dtype=torch.int32, device="cuda")
+    y_dec = host(layer.decode(B.to_device(np.ascontiguousarray(x[:, T - 1])), lens, kc, vc))
+    assert rel_err(y_dec, y_full[:, T - 1]) <= BF16_TOL
+
+
+# --------------------------------------------- full sizes, sampled outputs ----
+
+FULL = [(cid, wl) for cid in (2, 3, 4, 5) for wl in configs.WORKLOADS[cid]]
+
+
+@pytest.mark.parametrize("cid,wl", FULL, ids=[w.label.replace(" ", "_") for _, w in FULL])
+def test_full_size(cid, wl):
+    cfg = configs.CONFIGS[cid]
+    log(f"[gpu] {wl.label}: generating inputs (seed {wl.seed})")
+    spec = spec_of(cfg)
+    if wl.kind == "prefill":
+        layer, w32 = make_layer(cfg, seed=configs.weight_seed(cid), max_tokens=wl.tokens,
+                                max_batch=1)
+        r_t = torch.empty(wl.tokens, cfg.d, dtype=torch.float32, device="cuda")
+        layer.set_taps(r=r_t)
+        x = synth.make_prefill_input(cfg, wl.seed, wl.batch, wl.seq)
+        y, kc, vc = run_prefill(layer, cfg, x, T_max=wl.seq)
+        rows = sorted({0, 1, 127, 128, wl.seq // 2 + 3, wl.seq - 2, wl.seq - 1})
+        x32 = synth.to_f32(x).astype(np.float64)
+        o = ref.layer_prefill(x32, w32, spec, rows=rows)
+        got = host(y)[:, rows]
+        rg = host(r_t).reshape(wl.batch, wl.seq, -1)[:, rows]
+        e = rel_err(got, o["y"])
+        ea = rel_err(rg - x32[:, rows], o["r"] - x32[:, rows])
+        ef = branch_err(got, rg, o["f"])
+        ek = rounding_err(host(kc), o["k"])
+        log(f"[gpu] {wl.label}: y {e:.2e}  attention branch {ea:.2e}  ffn branch {ef:.2e}  "
+            f"k-cache {ek:.2f} (<=1)")
+        assert e <= BF16_TOL
+        assert ea <= ATT_BRANCH_TOL and ef <= FFN_BRANCH_TOL and ek <= 1.0
+    else:
+        layer, w32 = make_layer(cfg, seed=configs.weight_seed(cid), max_tokens=1,
+                                max_batch=wl.batch)
+        x, kc, vc, lens = synth.make_decode_input(cfg, wl.seed, wl.batch, wl.seq)
+        kd, vd = B.to_device(kc), B.to_device(vc)
+        y = layer.decode(B.to_device(x), torch.from_numpy(lens).cuda(), kd, vd,
+                         cache_len_host=lens.tolist())
+        torch.cuda.synchronize()
+        sel = sorted({0, wl.batch // 2, wl.batch - 1})
+        o = ref.layer_decode(synth.to_f32(x[sel]), synth.to_f32(kc[sel]), synth.to_f32(vc[sel]),
+                             lens[sel], w32, spec)
+        e = rel_err(host(y)[sel], o["y"])
+        ek = rounding_err(host(kd)[sel, wl.seq], o["k_new"])
+        log(f"[gpu] {wl.label}: y {e:.2e}  new k row {ek:.2f} (<=1)")
+        assert e <= BF16_TOL and ek <= 1.0
+
+
+def test_full_size_moe_ffn_routing():
+    cfg = configs.QWEN3_30B_A3B
+    N = 4096
+    layer, w32 = make_layer(cfg, seed=configs.weight_seed(5), max_tokens=N, max_batch=1)
+    r = synth.make_moe_input(cfg, 5099, N)
+    idx_t = torch.empty(N, cfg.top_k, dtype=torch.int32, device="cuda")
+    w_t = torch.empty(N, cfg.top_k, dtype=torch.float32, device="cuda")
+    y = layer.moe_ffn(B.to_device(r), topk_idx=idx_t, topk_w=w_t)
+    torch.cuda.synchronize()
+    r32 = synth.to_f32(r)
+    z = ref.rmsnorm(r32, w32["ln2_g"], cfg.rms_eps)
+    logits = ref.router_logits(z, w32["w_router"])
+    bad, checked = routing_mismatch(idx_t.cpu().numpy(), logits, cfg.top_k)
+    log(f"[gpu] moe routing: {checked} tokens checked (gap > 1e-3), {bad.size} mismatches")
+    assert bad.size == 0 and checked > 0.95 * N
+    rows = np.arange(0, N, 97)
+    o = ref.moe_ffn(r32[rows], w32, spec_of(cfg))
+    e = rel_err(host(y)[rows], o["y"])
+    ef = branch_err(host(y)[rows], r32[rows], o["f"])
+    log(f"[gpu] moe ffn N={N}: y {e:.2e}  branch {ef:.2e}")
+    assert e <= BF16_TOL and ef <= FFN_BRANCH_TOL

@@ -1,0 +1,214 @@
+// Causal GQA attention for prefill, head_dim 128, tiled online softmax on MFMA.
+//
+// For query head h of sequence b, rows t and keys u <= t:
+//   o_t = sum_u softmax_u(q_t . k_u / sqrt(dh)) v_u,  KV head g = h / (Hq/Hkv)
+// ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §7-§9; "Qwen2.5-7B 结构拆解"
+// §05, §05.2: the KV head is indexed, never copied; §05.4: tiles above the
+// diagonal are skipped in both products). The [S, S] probability matrix is
+// never written to memory ("推理系统 03" §12).
+//
+// Block = 4 waves = 128 query rows of one (sequence, head); a wave owns 32
+// rows. Key tiles of 64 rows stream through LDS, double-buffered.
+// Scores are formed transposed, S^T = K Q^T, with 32x32x16 MFMAs: the query
+// is the MFMA column, so a lane owns one query and its running max / sum
+// need only one cross-lane exchange per tile. P^T stays in registers and is
+// the B operand of O^T += V^T P^T; V is stored transposed in LDS (pitch 68
+// elements, which spreads the 16 rows read together over distinct banks).
+// K rows keep 16-byte chunks XOR-swizzled by (key & 7). The output stays fp32
+// (it feeds the O projection as a bf16 hi + lo pair).
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kDh = 128;
+constexpr int kBQ = 128;      // queries per block
+constexpr int kBK = 64;       // keys per tile
+constexpr int kVtPitch = 68;  // bf16 elements per transposed-V row
+constexpr int kKElems = kBK * kDh;
+constexpr int kVElems = kDh * kVtPitch;
+constexpr int kStage = kKElems + kVElems;
+
+__global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs p) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int hi = lane >> 5;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = h / (p.n_q_heads / p.n_kv_heads);
+  const int q0 = qt * kBQ;
+  const int S = p.S;
+  const int my_q = q0 + wave * 32 + col;
+  const int wave_qmax = q0 + wave * 32 + 31;
+
+  // Q^T fragments (B operand): lane (query col, group hi) holds dh [16s+8hi, +8)
+  bf16x8 qf[8];
+  {
+    const bf16* qrow = p.q + (size_t)(b * S + min(my_q, S - 1)) * p.ldq + h * kDh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = load_bf16x8(qrow + 16 * s + 8 * hi);
+  }
+
+  const size_t kv_row_stride = (size_t)p.n_kv_heads * kDh;
+  const bf16* kbase = p.k_cache + ((size_t)b * p.T_max) * kv_row_stride + g * kDh;
+  const bf16* vbase = p.v_cache + ((size_t)b * p.T_max) * kv_row_stride + g * kDh;
+  const int kend = min(q0 + kBQ, S);  // keys needed by this block
+  const int ntiles = (kend + kBK - 1) / kBK;
+
+  // tile-load assignment
+  //   K: chunk = tid + 256*i, key = chunk >> 4, 16-byte piece c = chunk & 15
+  //   V: 8-wide dh piece c = tid & 15, keys 4*(tid>>4) .. +3
+  const int vc = tid & 15;
+  const int vk = (tid >> 4) * 4;
+  u32x4 rk[4], rv[4];
+  auto gload = [&](int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = tid + 256 * i;
+      const int key = k0 + (ch >> 4);
+      rk[i] = key < S ? *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kv_row_stride +
+                                                         (ch & 15) * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = k0 + vk + j;
+      rv[j] = key < S ? *reinterpret_cast<const u32x4*>(vbase + (size_t)key * kv_row_stride +
+                                                         vc * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto lstore = [&](int st) {
+    bf16* Ks = lds + st * kStage;
+    bf16* Vt = Ks + kKElems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = tid + 256 * i;
+      const int key = ch >> 4, c = ch & 15;
+      *reinterpret_cast<u32x4*>(Ks + key * kDh + ((c ^ (key & 7)) * 8)) = rk[i];
+    }
+    const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&rv[0]);
+    const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&rv[1]);
+    const bf16x8 v2 = *reinterpret_cast<const bf16x8*>(&rv[2]);
+    const bf16x8 v3 = *reinterpret_cast<const bf16x8*>(&rv[3]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bf16x4 t = {v0[e], v1[e], v2[e], v3[e]};
+      *reinterpret_cast<bf16x4*>(Vt + (vc * 8 + e) * kVtPitch + vk) = t;
+    }
+  };
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int st = kt & 1;
+    const bool more = kt + 1 < ntiles;
+    if (more) gload(kt + 1);
+    const int k0 = kt * kBK;
+    if (k0 <= wave_qmax) {  // otherwise every key of the tile is in this wave's future
+      const bf16* Ks = lds + st * kStage;
+      const bf16* Vt = Ks + kKElems;
+      f32x16 sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+        const int key = 32 * t + col;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int c = 2 * s + hi;
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(Ks + key * kDh + ((c ^ (key & 7)) * 8));
+          sc[t] = mfma_32x32x16(kf, qf[s], sc[t]);
+        }
+      }
+      // scale, mask, tile max. Register r of half t holds key 32t + 8(r/4) + 4hi + r%4.
+      const bool need_mask = (k0 + kBK - 1 > q0 + wave * 32) || (k0 + kBK > S);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sc[t][r] * p.scale_log2;
+          if (need_mask) {
+            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key > my_q || key >= S) x = -INFINITY;
+          }
+          sc[t][r] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      const float m_new = fmaxf(m_run, mt);  // finite: key 0 is visible to every query
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float lsum = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = exp2f(sc[t][r] - m_new);
+          lsum += pv;
+          pf[2 * t + (r >> 3)][r & 7] = (bf16)pv;
+        }
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]; k-step u covers keys
+      // 32(u/2) + 16(u%2) + {4hi..4hi+3, 8+4hi..8+4hi+3} in slot order.
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kb = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16* vr = Vt + (32 * dt + col) * kVtPitch + kb;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+          const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vr + 8);
+          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          acc_o[dt] = mfma_32x32x16(vf, pf[u], acc_o[dt]);
+        }
+      }
+    }
+    if (more) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  if (my_q >= S) return;
+  const float inv = 1.0f / l_tot;
+  float* orow = p.out + (size_t)(b * S + my_q) * p.ldo + h * kDh;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 v = {acc_o[dt][4 * c + 0] * inv, acc_o[dt][4 * c + 1] * inv,
+                       acc_o[dt][4 * c + 2] * inv, acc_o[dt][4 * c + 3] * inv};
+      *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * c + 4 * hi) = v;
+    }
+}
+
+}  // namespace
+
+hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
+  if (a.B <= 0 || a.S <= 0) return hipSuccess;
+  const int nqt = (a.S + kBQ - 1) / kBQ;
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3(nqt, a.n_q_heads, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}

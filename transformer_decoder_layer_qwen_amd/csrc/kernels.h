@@ -1,0 +1,155 @@
+// Host-side launchers of the layer's kernels (internal to the library).
+// Every launcher enqueues on `s`, returns the launch status and never
+// synchronises. Shapes are validated by the caller (qlayer.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+typedef __bf16 bf16;
+
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 256;
+
+// ---- RMSNorm (rows x d) ----
+hipError_t ql_rmsnorm_bf16(const bf16* x, const bf16* gamma, bf16* out, float* out_f32, int rows,
+                           int d, float eps, hipStream_t s);
+// bf16 rows -> fp32 normalised rows only
+hipError_t ql_rmsnorm_bf16_to_f32(const bf16* x, const bf16* gamma, float* out, int rows, int d,
+                                  float eps, hipStream_t s);
+hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, float* out_f32,
+                                 int rows, int d, float eps, hipStream_t s);
+hipError_t ql_rmsnorm_f32(const float* x, const float* gamma, float* out, int rows, int d,
+                          float eps, hipStream_t s);
+
+// ---- prefill GEMMs, C[M,N] = A[M,K] B[N,K]^T (N % 128 == 0, K % 64 == 0) ----
+// QKV: out[M, q+2kv] fp32 = A [Wq; Wk; Wv]^T + [bq; bk; bv] (biases may be NULL);
+// A (and the O projection's A) is fp32, used as a bf16 hi + lo pair.
+hipError_t ql_gemm_qkv(const float* A, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
+                       int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
+                       float* out, hipStream_t s);
+hipError_t ql_gemm_resid_f32(const float* A, int M, const bf16* B, int N, int K,
+                             const bf16* resid, float* out, hipStream_t s);
+hipError_t ql_gemm_resid_out(const bf16* A, int M, const bf16* B, int N, int K,
+                             const float* resid, bf16* out, hipStream_t s);
+hipError_t ql_gemm_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
+                          bf16* out, hipStream_t s);
+hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
+                          int mf, int d, const int* tile_expert, const int* tile_row0,
+                          const int* tile_rows, const int* num_tiles, int max_tiles, int bm,
+                          bf16* H, hipStream_t s);
+hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
+                            const int* tile_row0, const int* tile_rows, const int* num_tiles,
+                            int max_tiles, int bm, float* out, hipStream_t s);
+
+// ---- decode GEMMs with M <= 128 rows (N % 16 == 0, K % 32 == 0) ----
+hipError_t ql_skinny_qkv(const float* X, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
+                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
+                         float* out, hipStream_t s);
+hipError_t ql_skinny_resid_f32(const float* X, int M, const bf16* W, int N, int K,
+                               const bf16* resid, float* out, hipStream_t s);
+hipError_t ql_skinny_resid_out(const bf16* X, int M, const bf16* W, int N, int K,
+                               const float* resid, bf16* out, hipStream_t s);
+hipError_t ql_skinny_swiglu(const bf16* X, int M, const bf16* Wg, const bf16* Wu, int F, int K,
+                            bf16* out, hipStream_t s);
+
+// ---- QK-norm + RoPE + cache write ----
+struct QkvPostArgs {
+  const float* qkv;      // [rows, ld_qkv] fp32 projections (bias added)
+  int ld_qkv;
+  int rows;              // prefill: B*S; decode: B
+  int seq;               // prefill: S (row n -> sequence n / S, cache row n % S)
+  const int* cache_len;  // decode: [B] cache row of the new token; NULL for prefill
+  int T_max;
+  int pos_offset;
+  int n_q_heads, n_kv_heads, head_dim;
+  float eps, theta;
+  const void* q_norm_g;  // NULL -> no QK-norm
+  const void* k_norm_g;
+  void* q_out;           // [rows, Hq*dh]
+  void* k_cache;         // [B, T_max, Hkv, dh]
+  void* v_cache;
+};
+hipError_t ql_qkv_post_bf16(const QkvPostArgs& a, hipStream_t s);
+hipError_t ql_qkv_post_f32(const QkvPostArgs& a, hipStream_t s);
+
+// ---- attention ----
+struct AttnPrefillArgs {
+  const bf16* q;         // [B*S, ldq]
+  const bf16* k_cache;   // [B, T_max, Hkv, dh]
+  const bf16* v_cache;
+  float* out;            // [B*S, ldo] fp32
+  const float* qf;       // fp32 variants of the same buffers (QL_F32)
+  const float* kf;
+  const float* vf;
+  float* outf;
+  int ldq, ldo;
+  int B, S, T_max;
+  int n_q_heads, n_kv_heads, head_dim;
+  float scale_log2;      // log2(e) / sqrt(dh)
+};
+hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s);
+hipError_t ql_attn_prefill_f32(const AttnPrefillArgs& a, hipStream_t s);
+
+struct AttnDecodeArgs {
+  const bf16* q;         // [B, ldq]
+  const bf16* k_cache;   // [B, T_max, Hkv, dh]
+  const bf16* v_cache;
+  float* out;            // [B, ldo] fp32
+  const float* qf;
+  const float* kf;
+  const float* vf;
+  float* outf;
+  const int* cache_len;  // [B] device
+  int ldq, ldo;
+  int B, T_max;
+  int n_q_heads, n_kv_heads, head_dim;
+  int chunk, nsplit;     // keys per split, number of splits
+  float* part_o;         // [B, Hq, nsplit, dh]
+  float* part_ml;        // [B, Hq, nsplit, 2]
+  float scale_log2;
+};
+hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s);
+hipError_t ql_attn_decode_f32(const AttnDecodeArgs& a, hipStream_t s);
+
+// ---- fp32 GEMM for small layers: mode 0 bias, 1 residual, 2 SwiGLU ----
+// out[m * ldo + n]; mode 1 reads add[m * ldo + n], mode 0 add[n] (may be NULL)
+hipError_t ql_gemm_f32_generic(int mode, const float* A, const float* B, const float* B2, int M,
+                               int N, int K, const float* add, float* out, int ldo, hipStream_t s);
+
+// ---- MoE routing ----
+struct RouterArgs {
+  const float* zf;   // [N, d] fp32 RMSNorm2 output
+  const bf16* wr;    // [E, d]
+  int N, d, E, k;
+  int norm_topk;
+  float* logits;     // [N, E] or NULL
+  int* idx;          // [N, k]
+  float* w;          // [N, k]
+};
+hipError_t ql_router_topk(const RouterArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int* idx;    // [N, k]
+  int N, k, E, bm;
+  int* hist;         // [ceil(N/256), E]
+  int* blkoff;       // [ceil(N/256), E]
+  int* offsets;      // [E + 1]
+  int* tile_expert;  // [max_tiles]
+  int* tile_row0;
+  int* tile_rows;
+  int* num_tiles;    // [1]
+  int* slot_token;   // [N*k]
+  int* pos_of;       // [N, k]
+};
+hipError_t ql_moe_permute(const PermuteArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* out_slot;  // [N*k, d]
+  const int* pos_of;      // [N, k]
+  const float* w;         // [N, k]
+  int N, k, d;
+  bf16* y;                // [N, d]
+};
+hipError_t ql_moe_combine(const CombineArgs& a, const void* resid, int resid_is_f32,
+                          hipStream_t s);

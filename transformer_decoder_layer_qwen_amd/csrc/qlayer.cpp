@@ -1,0 +1,657 @@
+// Host side of the C ABI declared in include/qlayer.h: argument checks, the
+// per-handle device workspace and the order of kernel launches for one layer.
+//
+// Prefill / decode, per call on the caller's stream:
+//   RMSNorm1 -> QKV projection (+bias) -> QK-norm + RoPE + cache write ->
+//   attention -> O projection + residual (R, fp32) -> RMSNorm2 ->
+//   dense: gate/up + SwiGLU -> down + residual (Y)
+//   MoE:   router + top-k -> permutation -> grouped gate/up + SwiGLU ->
+//          grouped down -> weighted combine + residual (Y)
+// ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §2-§10; "Qwen2.5-7B 结构
+// 拆解" §09.1 for the decode step and §10.2 for the MoE FFN.)
+#include "../../include/qlayer.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ql_status fail(ql_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr int kMaxSplits = 32;
+constexpr int kMinMoeTile = 32;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct ql_handle {
+  ql_config cfg;
+  ql_weights w;
+  int device;
+  int es;  // element bytes of the config dtype
+  int q_dim, kv_dim, qkv_dim, G;
+  int rows;  // workspace rows: max(max_tokens, max_batch)
+  char* ws;
+  size_t ws_bytes;
+  // workspace slices
+  void* xhat;
+  float* qkv;
+  void* q;
+  void* attn;
+  float* r;
+  void* z;
+  float* zf;
+  void* h;
+  float* part_o;
+  float* part_ml;
+  float* logits;
+  int* idx;
+  float* topw;
+  int* hist;
+  int* blkoff;
+  int* offsets;
+  int* tile_expert;
+  int* tile_row0;
+  int* tile_rows;
+  int* num_tiles;
+  int* slot_token;
+  int* pos_of;
+  void* hm;
+  float* out_slot;
+  int max_tiles;
+  ql_taps taps;
+  int ev_stage;
+  hipEvent_t ev_start, ev_stop;
+};
+
+namespace {
+
+#define QL_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(QL_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));            \
+  } while (0)
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Stage markers for qlayer_set_stage_events.
+ql_status mark(ql_handle* h, int stage, bool begin, hipStream_t s) {
+  if (h->ev_stage == QL_STAGE_NONE || h->ev_stage != stage) return QL_OK;
+  QL_HIP(hipEventRecord(begin ? h->ev_start : h->ev_stop, s));
+  return QL_OK;
+}
+
+#define QL_STAGE(h, st, s, body)               \
+  do {                                         \
+    ql_status m_ = mark(h, st, true, s);       \
+    if (m_ != QL_OK) return m_;                \
+    body;                                      \
+    m_ = mark(h, st, false, s);                \
+    if (m_ != QL_OK) return m_;                \
+  } while (0)
+
+ql_status validate(const ql_config* c, const ql_weights* w) {
+  if (!c || !w) return fail(QL_EINVAL, "config and weights must not be NULL");
+  if (c->d <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->ffn_dim <= 0)
+    return fail(QL_EINVAL, "dimensions must be positive");
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(QL_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_q_heads,
+                c->n_kv_heads);
+  if (c->max_tokens < 0 || c->max_batch < 0 || (c->max_tokens == 0 && c->max_batch == 0))
+    return fail(QL_EINVAL, "max_tokens / max_batch must be non-negative and not both 0");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f))
+    return fail(QL_EINVAL, "rms_eps must be >= 0 and rope_theta > 0");
+  if (c->dtype != QL_BF16 && c->dtype != QL_F32) return fail(QL_EINVAL, "unknown dtype %d", c->dtype);
+  if (!w->ln1_g || !w->ln2_g || !w->wq || !w->wk || !w->wv || !w->wo)
+    return fail(QL_EINVAL, "attention weights and norm gammas must not be NULL");
+  if (c->qkv_bias && (!w->bq || !w->bk || !w->bv))
+    return fail(QL_EINVAL, "qkv_bias set but a bias pointer is NULL");
+  if (c->qk_norm && (!w->q_norm_g || !w->k_norm_g))
+    return fail(QL_EINVAL, "qk_norm set but a QK-norm gamma is NULL");
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (c->n_experts > 0) {
+    if (c->dtype != QL_BF16) return fail(QL_EUNSUPPORTED, "MoE layers need dtype QL_BF16");
+    if (c->n_experts % 16 || c->n_experts > kMaxExperts)
+      return fail(QL_EUNSUPPORTED, "n_experts must be a multiple of 16 and <= %d", kMaxExperts);
+    if (c->top_k < 1 || c->top_k > std::min(c->n_experts, kMaxTopK))
+      return fail(QL_EINVAL, "top_k must be in [1, min(n_experts, %d)]", kMaxTopK);
+    if (!w->w_router || !w->we_gate || !w->we_up || !w->we_down)
+      return fail(QL_EINVAL, "MoE weights must not be NULL");
+  } else {
+    if (c->n_experts < 0) return fail(QL_EINVAL, "n_experts must be >= 0");
+    if (!w->w_gate || !w->w_up || !w->w_down)
+      return fail(QL_EINVAL, "dense FFN weights must not be NULL");
+  }
+  if (c->dtype == QL_BF16) {
+    if (c->head_dim != 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs head_dim == 128");
+    if (c->d % 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs d %% 128 == 0");
+    if (c->ffn_dim % 64) return fail(QL_EUNSUPPORTED, "QL_BF16 needs ffn_dim %% 64 == 0");
+    if (G > 16) return fail(QL_EUNSUPPORTED, "QL_BF16 needs n_q_heads / n_kv_heads <= 16");
+    if (c->max_batch > 128) return fail(QL_EUNSUPPORTED, "QL_BF16 decode needs max_batch <= 128");
+  } else {
+    if (!is_pow2(c->head_dim) || c->head_dim < 2 || c->head_dim > 128)
+      return fail(QL_EUNSUPPORTED, "QL_F32 needs a power-of-two head_dim in [2, 128]");
+  }
+  return QL_OK;
+}
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(std::max<size_t>(bytes, 1));
+    return p;
+  }
+};
+
+// Lays the workspace out (base == nullptr only measures it).
+size_t layout(ql_handle* h, char* base) {
+  const ql_config& c = h->cfg;
+  const size_t N = (size_t)h->rows;
+  const size_t es = (size_t)h->es;
+  Carve k{base};
+  h->xhat = k.take<void>(N * c.d * 4);  // fp32: feeds the QKV GEMM as bf16 hi + lo
+  h->qkv = k.take<float>(N * h->qkv_dim * 4);
+  h->q = k.take<void>(N * h->q_dim * es);
+  h->attn = k.take<void>(N * h->q_dim * 4);  // fp32: feeds the O GEMM as bf16 hi + lo
+  h->r = k.take<float>(N * c.d * 4);
+  h->z = k.take<void>(N * c.d * es);
+  const size_t B = (size_t)std::max(c.max_batch, 0);
+  h->part_o = k.take<float>(B * c.n_q_heads * kMaxSplits * c.head_dim * 4);
+  h->part_ml = k.take<float>(B * c.n_q_heads * kMaxSplits * 2 * 4);
+  if (c.n_experts > 0) {
+    const size_t E = c.n_experts, K = c.top_k, NK = N * K;
+    const size_t nblk = (N + 255) / 256;
+    h->max_tiles = (int)((NK + kMinMoeTile - 1) / kMinMoeTile + E);
+    h->zf = k.take<float>(N * c.d * 4);
+    h->logits = k.take<float>(N * E * 4);
+    h->idx = k.take<int>(NK * 4);
+    h->topw = k.take<float>(NK * 4);
+    h->hist = k.take<int>(nblk * E * 4);
+    h->blkoff = k.take<int>(nblk * E * 4);
+    h->offsets = k.take<int>((E + 1) * 4);
+    h->tile_expert = k.take<int>(h->max_tiles * 4);
+    h->tile_row0 = k.take<int>(h->max_tiles * 4);
+    h->tile_rows = k.take<int>(h->max_tiles * 4);
+    h->num_tiles = k.take<int>(4);
+    h->slot_token = k.take<int>(NK * 4);
+    h->pos_of = k.take<int>(NK * 4);
+    h->hm = k.take<void>(NK * c.ffn_dim * 2);
+    h->out_slot = k.take<float>(NK * c.d * 4);
+  } else {
+    h->h = k.take<void>(N * c.ffn_dim * es);
+  }
+  return k.off;
+}
+
+float scale_log2(int dh) { return 1.4426950408889634f / std::sqrt((float)dh); }
+
+ql_status copy_taps(ql_handle* h, int N, hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const size_t es = h->es;
+  if (h->taps.q)
+    QL_HIP(hipMemcpyAsync(h->taps.q, h->q, (size_t)N * h->q_dim * es, hipMemcpyDeviceToDevice, s));
+  if (h->taps.attn)
+    QL_HIP(hipMemcpyAsync(h->taps.attn, h->attn, (size_t)N * h->q_dim * 4,
+                          hipMemcpyDeviceToDevice, s));
+  if (h->taps.r)
+    QL_HIP(hipMemcpyAsync(h->taps.r, h->r, (size_t)N * c.d * 4, hipMemcpyDeviceToDevice, s));
+  if (h->taps.z)
+    QL_HIP(hipMemcpyAsync(h->taps.z, h->z, (size_t)N * c.d * es, hipMemcpyDeviceToDevice, s));
+  if (h->taps.h && c.n_experts == 0)
+    QL_HIP(hipMemcpyAsync(h->taps.h, h->h, (size_t)N * c.ffn_dim * es, hipMemcpyDeviceToDevice,
+                          s));
+  if (h->taps.logits && c.n_experts > 0)
+    QL_HIP(hipMemcpyAsync(h->taps.logits, h->logits, (size_t)N * c.n_experts * 4,
+                          hipMemcpyDeviceToDevice, s));
+  return QL_OK;
+}
+
+// y = resid + MoE(z); z bf16 and zf fp32 hold RMSNorm2 of the residual rows.
+ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf16* y,
+                   hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const ql_weights& w = h->w;
+  RouterArgs ra{};
+  ra.zf = h->zf;
+  ra.wr = static_cast<const bf16*>(w.w_router);
+  ra.N = N;
+  ra.d = c.d;
+  ra.E = c.n_experts;
+  ra.k = c.top_k;
+  ra.norm_topk = c.norm_topk_prob;
+  ra.logits = h->logits;
+  ra.idx = h->idx;
+  ra.w = h->topw;
+  QL_STAGE(h, QL_STAGE_ROUTER, s, QL_HIP(ql_router_topk(ra, s)));
+
+  // rows per expert tile: 128 when experts see many rows, 32 for decode-sized batches
+  const int bm = ((long long)N * c.top_k >= 64LL * c.n_experts) ? 128 : kMinMoeTile;
+  const int max_tiles = (int)(((long long)N * c.top_k + bm - 1) / bm + c.n_experts);
+  PermuteArgs pa{};
+  pa.idx = h->idx;
+  pa.N = N;
+  pa.k = c.top_k;
+  pa.E = c.n_experts;
+  pa.bm = bm;
+  pa.hist = h->hist;
+  pa.blkoff = h->blkoff;
+  pa.offsets = h->offsets;
+  pa.tile_expert = h->tile_expert;
+  pa.tile_row0 = h->tile_row0;
+  pa.tile_rows = h->tile_rows;
+  pa.num_tiles = h->num_tiles;
+  pa.slot_token = h->slot_token;
+  pa.pos_of = h->pos_of;
+  QL_STAGE(h, QL_STAGE_PERMUTE, s, QL_HIP(ql_moe_permute(pa, s)));
+
+  QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
+           QL_HIP(ql_gemm_moe_gu(static_cast<const bf16*>(h->z), h->slot_token,
+                                 static_cast<const bf16*>(w.we_gate),
+                                 static_cast<const bf16*>(w.we_up), c.ffn_dim, c.d,
+                                 h->tile_expert, h->tile_row0, h->tile_rows, h->num_tiles,
+                                 max_tiles, bm, static_cast<bf16*>(h->hm), s)));
+  QL_STAGE(h, QL_STAGE_EXPERT_DOWN, s,
+           QL_HIP(ql_gemm_moe_down(static_cast<const bf16*>(h->hm),
+                                   static_cast<const bf16*>(w.we_down), c.ffn_dim, c.d,
+                                   h->tile_expert, h->tile_row0, h->tile_rows, h->num_tiles,
+                                   max_tiles, bm, h->out_slot, s)));
+  CombineArgs ca{};
+  ca.out_slot = h->out_slot;
+  ca.pos_of = h->pos_of;
+  ca.w = h->topw;
+  ca.N = N;
+  ca.k = c.top_k;
+  ca.d = c.d;
+  ca.y = y;
+  QL_STAGE(h, QL_STAGE_COMBINE, s, QL_HIP(ql_moe_combine(ca, resid, resid_is_f32, s)));
+  return QL_OK;
+}
+
+// ---- bf16 layer halves -------------------------------------------------------
+
+ql_status attn_half_bf16(ql_handle* h, const bf16* x, int N, bool decode, int B, int S,
+                         const int* cache_len, int pos_offset, void* kc, void* vc, int T_max,
+                         hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const ql_weights& w = h->w;
+  float* xhat = static_cast<float*>(h->xhat);
+  QL_STAGE(h, QL_STAGE_RMSNORM1, s,
+           QL_HIP(ql_rmsnorm_bf16_to_f32(x, static_cast<const bf16*>(w.ln1_g), xhat, N, c.d,
+                                         c.rms_eps, s)));
+  ql_status mst = mark(h, QL_STAGE_QKV, true, s);
+  if (mst != QL_OK) return mst;
+  const bf16* bq = c.qkv_bias ? static_cast<const bf16*>(w.bq) : nullptr;
+  const bf16* bk = c.qkv_bias ? static_cast<const bf16*>(w.bk) : nullptr;
+  const bf16* bv = c.qkv_bias ? static_cast<const bf16*>(w.bv) : nullptr;
+  if (decode)
+    QL_HIP(ql_skinny_qkv(xhat, N, static_cast<const bf16*>(w.wq), static_cast<const bf16*>(w.wk),
+                         static_cast<const bf16*>(w.wv), h->q_dim, h->kv_dim, c.d, bq, bk, bv,
+                         h->qkv, s));
+  else
+    QL_HIP(ql_gemm_qkv(xhat, N, static_cast<const bf16*>(w.wq), static_cast<const bf16*>(w.wk),
+                       static_cast<const bf16*>(w.wv), h->q_dim, h->kv_dim, c.d, bq, bk, bv,
+                       h->qkv, s));
+  mst = mark(h, QL_STAGE_QKV, false, s);
+  if (mst != QL_OK) return mst;
+  QkvPostArgs qa{};
+  qa.qkv = h->qkv;
+  qa.ld_qkv = h->qkv_dim;
+  qa.rows = N;
+  qa.seq = S;
+  qa.cache_len = decode ? cache_len : nullptr;
+  qa.T_max = T_max;
+  qa.pos_offset = pos_offset;
+  qa.n_q_heads = c.n_q_heads;
+  qa.n_kv_heads = c.n_kv_heads;
+  qa.head_dim = c.head_dim;
+  qa.eps = c.rms_eps;
+  qa.theta = c.rope_theta;
+  qa.q_norm_g = c.qk_norm ? w.q_norm_g : nullptr;
+  qa.k_norm_g = c.qk_norm ? w.k_norm_g : nullptr;
+  qa.q_out = h->q;
+  qa.k_cache = kc;
+  qa.v_cache = vc;
+  QL_STAGE(h, QL_STAGE_QKV_POST, s, QL_HIP(ql_qkv_post_bf16(qa, s)));
+
+  if (decode) {
+    AttnDecodeArgs da{};
+    da.q = static_cast<const bf16*>(h->q);
+    da.k_cache = static_cast<const bf16*>(kc);
+    da.v_cache = static_cast<const bf16*>(vc);
+    da.out = static_cast<float*>(h->attn);
+    da.cache_len = cache_len;
+    da.ldq = h->q_dim;
+    da.ldo = h->q_dim;
+    da.B = B;
+    da.T_max = T_max;
+    da.n_q_heads = c.n_q_heads;
+    da.n_kv_heads = c.n_kv_heads;
+    da.head_dim = c.head_dim;
+    const int groups = B * c.n_kv_heads;
+    int nsplit = std::max(1, std::min(kMaxSplits, (512 + groups - 1) / groups));
+    int chunk = (T_max + nsplit - 1) / nsplit;
+    chunk = (chunk + 63) / 64 * 64;
+    nsplit = (T_max + chunk - 1) / chunk;
+    da.chunk = chunk;
+    da.nsplit = nsplit;
+    da.part_o = h->part_o;
+    da.part_ml = h->part_ml;
+    da.scale_log2 = scale_log2(c.head_dim);
+    QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
+    QL_STAGE(h, QL_STAGE_O_PROJ, s,
+             QL_HIP(ql_skinny_resid_f32(static_cast<const float*>(h->attn), N,
+                                        static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
+                                        s)));
+  } else {
+    AttnPrefillArgs pa{};
+    pa.q = static_cast<const bf16*>(h->q);
+    pa.k_cache = static_cast<const bf16*>(kc);
+    pa.v_cache = static_cast<const bf16*>(vc);
+    pa.out = static_cast<float*>(h->attn);
+    pa.ldq = h->q_dim;
+    pa.ldo = h->q_dim;
+    pa.B = B;
+    pa.S = S;
+    pa.T_max = T_max;
+    pa.n_q_heads = c.n_q_heads;
+    pa.n_kv_heads = c.n_kv_heads;
+    pa.head_dim = c.head_dim;
+    pa.scale_log2 = scale_log2(c.head_dim);
+    QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_prefill_bf16(pa, s)));
+    QL_STAGE(h, QL_STAGE_O_PROJ, s,
+             QL_HIP(ql_gemm_resid_f32(static_cast<const float*>(h->attn), N,
+                                      static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
+                                      s)));
+  }
+  return QL_OK;
+}
+
+ql_status ffn_half_bf16(ql_handle* h, int N, bool decode, bf16* y, hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const ql_weights& w = h->w;
+  bf16* z = static_cast<bf16*>(h->z);
+  QL_STAGE(h, QL_STAGE_RMSNORM2, s,
+           QL_HIP(ql_rmsnorm_f32in_bf16(h->r, static_cast<const bf16*>(w.ln2_g), z,
+                                        c.n_experts > 0 ? h->zf : nullptr, N, c.d, c.rms_eps,
+                                        s)));
+  if (c.n_experts > 0) return moe_core(h, N, h->r, 1, y, s);
+  bf16* hh = static_cast<bf16*>(h->h);
+  if (decode) {
+    QL_STAGE(h, QL_STAGE_GATE_UP, s,
+             QL_HIP(ql_skinny_swiglu(z, N, static_cast<const bf16*>(w.w_gate),
+                                     static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, s)));
+    QL_STAGE(h, QL_STAGE_DOWN, s,
+             QL_HIP(ql_skinny_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d,
+                                        c.ffn_dim, h->r, y, s)));
+  } else {
+    QL_STAGE(h, QL_STAGE_GATE_UP, s,
+             QL_HIP(ql_gemm_swiglu(z, N, static_cast<const bf16*>(w.w_gate),
+                                   static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, s)));
+    QL_STAGE(h, QL_STAGE_DOWN, s,
+             QL_HIP(ql_gemm_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d, c.ffn_dim,
+                                      h->r, y, s)));
+  }
+  return QL_OK;
+}
+
+// ---- fp32 layer (small shapes) ---------------------------------------------
+
+ql_status layer_f32(ql_handle* h, const float* x, int N, bool decode, int B, int S,
+                    const int* cache_len, int pos_offset, void* kc, void* vc, int T_max, float* y,
+                    hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const ql_weights& w = h->w;
+  float* xhat = static_cast<float*>(h->xhat);
+  QL_HIP(ql_rmsnorm_f32(x, static_cast<const float*>(w.ln1_g), xhat, N, c.d, c.rms_eps, s));
+  const float* wq = static_cast<const float*>(w.wq);
+  const float* wk = static_cast<const float*>(w.wk);
+  const float* wv = static_cast<const float*>(w.wv);
+  const float* bq = c.qkv_bias ? static_cast<const float*>(w.bq) : nullptr;
+  const float* bk = c.qkv_bias ? static_cast<const float*>(w.bk) : nullptr;
+  const float* bv = c.qkv_bias ? static_cast<const float*>(w.bv) : nullptr;
+  QL_HIP(ql_gemm_f32_generic(0, xhat, wq, nullptr, N, h->q_dim, c.d, bq, h->qkv, h->qkv_dim, s));
+  QL_HIP(ql_gemm_f32_generic(0, xhat, wk, nullptr, N, h->kv_dim, c.d, bk, h->qkv + h->q_dim,
+                             h->qkv_dim, s));
+  QL_HIP(ql_gemm_f32_generic(0, xhat, wv, nullptr, N, h->kv_dim, c.d, bv,
+                             h->qkv + h->q_dim + h->kv_dim, h->qkv_dim, s));
+  QkvPostArgs qa{};
+  qa.qkv = h->qkv;
+  qa.ld_qkv = h->qkv_dim;
+  qa.rows = N;
+  qa.seq = S;
+  qa.cache_len = decode ? cache_len : nullptr;
+  qa.T_max = T_max;
+  qa.pos_offset = pos_offset;
+  qa.n_q_heads = c.n_q_heads;
+  qa.n_kv_heads = c.n_kv_heads;
+  qa.head_dim = c.head_dim;
+  qa.eps = c.rms_eps;
+  qa.theta = c.rope_theta;
+  qa.q_norm_g = c.qk_norm ? w.q_norm_g : nullptr;
+  qa.k_norm_g = c.qk_norm ? w.k_norm_g : nullptr;
+  qa.q_out = h->q;
+  qa.k_cache = kc;
+  qa.v_cache = vc;
+  QL_HIP(ql_qkv_post_f32(qa, s));
+  float* attn = static_cast<float*>(h->attn);
+  if (decode) {
+    AttnDecodeArgs da{};
+    da.qf = static_cast<const float*>(h->q);
+    da.kf = static_cast<const float*>(kc);
+    da.vf = static_cast<const float*>(vc);
+    da.outf = attn;
+    da.cache_len = cache_len;
+    da.ldq = h->q_dim;
+    da.ldo = h->q_dim;
+    da.B = B;
+    da.T_max = T_max;
+    da.n_q_heads = c.n_q_heads;
+    da.n_kv_heads = c.n_kv_heads;
+    da.head_dim = c.head_dim;
+    QL_HIP(ql_attn_decode_f32(da, s));
+  } else {
+    AttnPrefillArgs pa{};
+    pa.qf = static_cast<const float*>(h->q);
+    pa.kf = static_cast<const float*>(kc);
+    pa.vf = static_cast<const float*>(vc);
+    pa.outf = attn;
+    pa.ldq = h->q_dim;
+    pa.ldo = h->q_dim;
+    pa.B = B;
+    pa.S = S;
+    pa.T_max = T_max;
+    pa.n_q_heads = c.n_q_heads;
+    pa.n_kv_heads = c.n_kv_heads;
+    pa.head_dim = c.head_dim;
+    QL_HIP(ql_attn_prefill_f32(pa, s));
+  }
+  QL_HIP(ql_gemm_f32_generic(1, attn, static_cast<const float*>(w.wo), nullptr, N, c.d, h->q_dim,
+                             x, h->r, c.d, s));
+  float* z = static_cast<float*>(h->z);
+  QL_HIP(ql_rmsnorm_f32(h->r, static_cast<const float*>(w.ln2_g), z, N, c.d, c.rms_eps, s));
+  float* hh = static_cast<float*>(h->h);
+  QL_HIP(ql_gemm_f32_generic(2, z, static_cast<const float*>(w.w_gate),
+                             static_cast<const float*>(w.w_up), N, c.ffn_dim, c.d, nullptr, hh,
+                             c.ffn_dim, s));
+  QL_HIP(ql_gemm_f32_generic(1, hh, static_cast<const float*>(w.w_down), nullptr, N, c.d,
+                             c.ffn_dim, h->r, y, c.d, s));
+  return QL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlayer_last_error(void) { return g_last_error.c_str(); }
+
+int qlayer_abi_version(void) { return QLAYER_ABI_VERSION; }
+
+ql_status qlayer_create(const ql_config* cfg, const ql_weights* w, ql_handle** out) {
+  if (!out) return fail(QL_EINVAL, "out must not be NULL");
+  *out = nullptr;
+  ql_status st = validate(cfg, w);
+  if (st != QL_OK) return st;
+  ql_handle* h = new ql_handle();
+  h->cfg = *cfg;
+  h->w = *w;
+  h->es = cfg->dtype == QL_BF16 ? 2 : 4;
+  h->q_dim = cfg->n_q_heads * cfg->head_dim;
+  h->kv_dim = cfg->n_kv_heads * cfg->head_dim;
+  h->qkv_dim = h->q_dim + 2 * h->kv_dim;
+  h->G = cfg->n_q_heads / cfg->n_kv_heads;
+  h->rows = std::max(std::max(cfg->max_tokens, cfg->max_batch), 1);
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(QL_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  }
+  h->ws_bytes = layout(h, nullptr);
+  e = hipMalloc(reinterpret_cast<void**>(&h->ws), h->ws_bytes);
+  if (e != hipSuccess) {
+    delete h;
+    return fail(QL_ENOMEM, "workspace of %zu bytes: %s", h->ws_bytes, hipGetErrorString(e));
+  }
+  layout(h, h->ws);
+  *out = h;
+  return QL_OK;
+}
+
+ql_status qlayer_destroy(ql_handle* h) {
+  if (!h) return QL_OK;
+  hipError_t e = hipDeviceSynchronize();
+  hipError_t f = hipFree(h->ws);
+  delete h;
+  if (e != hipSuccess) return fail(QL_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  if (f != hipSuccess) return fail(QL_EHIP, "hipFree: %s", hipGetErrorString(f));
+  return QL_OK;
+}
+
+size_t qlayer_workspace_bytes(const ql_handle* h) { return h ? h->ws_bytes : 0; }
+
+ql_status qlayer_set_taps(ql_handle* h, const ql_taps* taps) {
+  if (!h) return fail(QL_EINVAL, "handle must not be NULL");
+  if (taps) h->taps = *taps;
+  else std::memset(&h->taps, 0, sizeof(h->taps));
+  return QL_OK;
+}
+
+ql_status qlayer_set_stage_events(ql_handle* h, int stage, void* start_event, void* stop_event) {
+  if (!h) return fail(QL_EINVAL, "handle must not be NULL");
+  if (stage < QL_STAGE_NONE || stage > QL_STAGE_COMBINE)
+    return fail(QL_EINVAL, "unknown stage %d", stage);
+  if (stage == QL_STAGE_NONE || !start_event || !stop_event) {
+    h->ev_stage = QL_STAGE_NONE;
+    h->ev_start = h->ev_stop = nullptr;
+    return QL_OK;
+  }
+  h->ev_stage = stage;
+  h->ev_start = static_cast<hipEvent_t>(start_event);
+  h->ev_stop = static_cast<hipEvent_t>(stop_event);
+  return QL_OK;
+}
+
+ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offset, void* k_cache,
+                         void* v_cache, int T_max, void* y, void* stream) {
+  if (!h || !x || !k_cache || !v_cache || !y)
+    return fail(QL_EINVAL, "prefill: NULL argument");
+  if (B <= 0 || S <= 0) return fail(QL_EINVAL, "prefill: B and S must be positive");
+  if ((long long)B * S > h->cfg.max_tokens)
+    return fail(QL_EINVAL, "prefill: B*S = %lld exceeds max_tokens %d", (long long)B * S,
+                h->cfg.max_tokens);
+  if (S > T_max) return fail(QL_EINVAL, "prefill: S (%d) > T_max (%d)", S, T_max);
+  if (x == y) return fail(QL_EINVAL, "prefill: y must not alias x");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int N = B * S;
+  ql_status st;
+  if (h->cfg.dtype == QL_F32) {
+    st = layer_f32(h, static_cast<const float*>(x), N, false, B, S, nullptr, pos_offset, k_cache,
+                   v_cache, T_max, static_cast<float*>(y), s);
+  } else {
+    st = attn_half_bf16(h, static_cast<const bf16*>(x), N, false, B, S, nullptr, pos_offset,
+                        k_cache, v_cache, T_max, s);
+    if (st == QL_OK) st = ffn_half_bf16(h, N, false, static_cast<bf16*>(y), s);
+  }
+  if (st == QL_OK) st = copy_taps(h, N, s);
+  return st;
+}
+
+ql_status qlayer_decode(ql_handle* h, const void* x, int B, const int* cache_len,
+                        const int* cache_len_host, int pos_offset, void* k_cache, void* v_cache,
+                        int T_max, void* y, void* stream) {
+  if (!h || !x || !cache_len || !k_cache || !v_cache || !y)
+    return fail(QL_EINVAL, "decode: NULL argument");
+  if (B <= 0) return fail(QL_EINVAL, "decode: B must be positive");
+  if (B > h->cfg.max_batch)
+    return fail(QL_EINVAL, "decode: B = %d exceeds max_batch %d", B, h->cfg.max_batch);
+  if (T_max <= 0) return fail(QL_EINVAL, "decode: T_max must be positive");
+  if (x == y) return fail(QL_EINVAL, "decode: y must not alias x");
+  if (cache_len_host)
+    for (int b = 0; b < B; ++b)
+      if (cache_len_host[b] < 0 || cache_len_host[b] + 1 > T_max)
+        return fail(QL_ECACHE_FULL, "decode: cache_len[%d] = %d does not fit T_max = %d", b,
+                    cache_len_host[b], T_max);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ql_status st;
+  if (h->cfg.dtype == QL_F32) {
+    st = layer_f32(h, static_cast<const float*>(x), B, true, B, 1, cache_len, pos_offset, k_cache,
+                   v_cache, T_max, static_cast<float*>(y), s);
+  } else {
+    st = attn_half_bf16(h, static_cast<const bf16*>(x), B, true, B, 1, cache_len, pos_offset,
+                        k_cache, v_cache, T_max, s);
+    if (st == QL_OK) st = ffn_half_bf16(h, B, true, static_cast<bf16*>(y), s);
+  }
+  if (st == QL_OK) st = copy_taps(h, B, s);
+  return st;
+}
+
+ql_status qlayer_moe_ffn(ql_handle* h, const void* r, int N, void* y, int* topk_idx,
+                         float* topk_w, void* stream) {
+  if (!h || !r || !y) return fail(QL_EINVAL, "moe_ffn: NULL argument");
+  if (h->cfg.n_experts <= 0) return fail(QL_EUNSUPPORTED, "moe_ffn: the handle has a dense FFN");
+  if (N <= 0) return fail(QL_EINVAL, "moe_ffn: N must be positive");
+  if (N > h->rows) return fail(QL_EINVAL, "moe_ffn: N = %d exceeds %d rows", N, h->rows);
+  if (r == y) return fail(QL_EINVAL, "moe_ffn: y must not alias r");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ql_config& c = h->cfg;
+  QL_HIP(ql_rmsnorm_bf16(static_cast<const bf16*>(r), static_cast<const bf16*>(h->w.ln2_g),
+                         static_cast<bf16*>(h->z), h->zf, N, c.d, c.rms_eps, s));
+  ql_status st = moe_core(h, N, r, 0, static_cast<bf16*>(y), s);
+  if (st != QL_OK) return st;
+  const size_t nk = (size_t)N * c.top_k;
+  if (topk_idx)
+    QL_HIP(hipMemcpyAsync(topk_idx, h->idx, nk * 4, hipMemcpyDeviceToDevice, s));
+  if (topk_w) QL_HIP(hipMemcpyAsync(topk_w, h->topw, nk * 4, hipMemcpyDeviceToDevice, s));
+  if (h->taps.logits)
+    QL_HIP(hipMemcpyAsync(h->taps.logits, h->logits, (size_t)N * c.n_experts * 4,
+                          hipMemcpyDeviceToDevice, s));
+  if (h->taps.z)
+    QL_HIP(hipMemcpyAsync(h->taps.z, h->z, (size_t)N * c.d * 2, hipMemcpyDeviceToDevice, s));
+  return QL_OK;
+}
+
+}  // extern "C"
