@@ -6,14 +6,18 @@ the oracle's CPU rate.
 Headline workload: the Qwen2.5-7B-shaped layer, one decode step for batch 1
 with a 1024-row KV cache (bf16 weights N(0, 0.02), biases N(0, 0.02), gammas
 N(1, 0.05), cache and hidden rows N(0, 1); seeded synthetic data). One step =
-one qlayer_decode call, i.e. every stage of the layer. Two copies of the
+one qlayer_decode call, i.e. every stage of the layer. The timed loop replays
+a HIP graph that holds one call per weight copy, as consecutive layers of a
+model run inside one decode-step graph (--eager launches each call directly). Two copies of the
 weights and caches alternate between steps so that the 256 MB last-level cache
 cannot serve the weight stream. `value` = tokens/s = batch / step time, timed
 with events around exactly K steps on the layer's stream.
 
 The other workloads of the config table (prefill and decode at their full
 sizes) are timed the same way and reported under "secondary", each with a
-per-stage breakdown taken from the library's stage events.
+per-stage breakdown taken from the library's stage events (eager calls, each
+queued behind a short spin kernel so that host launch latency stays outside
+the measured windows).
 
 One JSON line is printed on stdout.
 """
@@ -37,6 +41,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 METRIC = "layer tokens/s (prefill & decode) + % bf16 MFMA / HBM roofline, 1 GPU"
+SPACER_CYCLES = 2_000_000   # spin queued ahead of each stage-timed call
 
 
 def log(msg):
@@ -185,6 +190,25 @@ class Setup:
                                                 device="cuda")))
         torch.cuda.synchronize()
 
+    def capture(self):
+        """One HIP graph holding one full call on each weight copy in turn --
+        the way consecutive layers of a model run inside one decode-step
+        graph. One replay = len(layers) steps."""
+        import torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(len(self.layers)):   # warm the captured code paths
+                self.step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in range(len(self.layers)):
+                self.step(c)
+        torch.cuda.synchronize()
+        return g
+
     def step(self, i):
         c = i % len(self.layers)
         layer, inp = self.layers[c], self.inputs[c]
@@ -201,17 +225,27 @@ class Setup:
         self.layers, self.inputs = [], []
 
 
-def time_steps(setup, hip, steps, warmup):
+def time_steps(setup, hip, steps, warmup, graph=None):
+    """Mean time of one call over exactly `steps` calls (a graph replay runs
+    one call per weight copy), HIP events around the whole timed region on
+    the stream the calls run on."""
     import torch
-    stream = torch.cuda.current_stream().cuda_stream
-    for i in range(warmup):
-        setup.step(i)
+    n = len(setup.layers)
+    if graph is not None:
+        assert steps % n == 0, "steps must be a multiple of the number of weight copies"
+        run, calls = (lambda i: graph.replay()), steps // n
+        wcalls = max(1, warmup // n)
+    else:
+        run, calls, wcalls = setup.step, steps, warmup
+    for i in range(wcalls):
+        run(i)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
     a, b = hip.create(2)
     torch.cuda.synchronize()
     hip.record(a, stream)
-    for i in range(steps):
-        setup.step(i)
+    for i in range(calls):
+        run(i)
     hip.record(b, stream)
     torch.cuda.synchronize()
     ms = hip.elapsed_ms(a, b)
@@ -220,13 +254,17 @@ def time_steps(setup, hip, steps, warmup):
 
 
 def time_stage(setup, hip, stage, steps):
-    """Average duration of one stage, events recorded by the library around
-    its kernels on the call's stream, over `steps` calls."""
+    """Mean duration of one stage: the library records events immediately
+    before its first and after its last kernel, on the call's stream. Each
+    call is queued behind a bounded spin kernel, so the host has enqueued the
+    whole call before the GPU reaches it and no host launch gap falls inside
+    the window."""
     import torch
     evs = hip.create(2 * steps)
     for i in range(steps):
         for layer in setup.layers:
             layer.set_stage_events(stage, evs[2 * i], evs[2 * i + 1])
+        torch.cuda._sleep(SPACER_CYCLES)
         setup.step(i)
     torch.cuda.synchronize()
     for layer in setup.layers:
@@ -236,8 +274,11 @@ def time_stage(setup, hip, stage, steps):
     return tot / steps
 
 
-def stages_of(cfg):
-    s = ["rmsnorm1", "qkv", "qkv_post", "attention", "o_proj", "rmsnorm2"]
+def stages_of(cfg, kind):
+    # decode fuses RMSNorm1 into the QKV projection and the QK-norm / RoPE /
+    # cache append into the attention kernel
+    s = (["rmsnorm1", "qkv", "qkv_post"] if kind == "prefill" else ["qkv"])
+    s += ["attention", "o_proj", "rmsnorm2"]
     s += (["router", "permute", "expert_gate_up", "expert_down", "combine"] if cfg.is_moe
           else ["gate_up", "down"])
     return s
@@ -257,11 +298,13 @@ def roofline_entry(cfg, wl, stage, ms):
             "algorithmic_flops": int(fl), "kernel_ms": round(ms, 5), "stage": stage}
 
 
-def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True):
+def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_graph=True):
     setup = Setup(cid, wl)
     cfg = setup.cfg
-    ms = time_steps(setup, hip, steps, warmup)
-    out = {"workload": wl.label, "kind": wl.kind, "batch": wl.batch,
+    graph = setup.capture() if use_graph else None
+    ms = time_steps(setup, hip, steps, warmup, graph)
+    del graph
+    out = {"workload": wl.label, "kind": wl.kind, "batch": wl.batch, "hip_graph": use_graph,
            "seq_or_cache": wl.seq, "tokens_per_step": wl.tokens,
            "ms_per_step": round(ms, 5), "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1)}
     fl, by = layer_work(cfg, wl)
@@ -273,7 +316,7 @@ def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True):
         out["layer_frac_hbm"] = round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if breakdown:
         st = {}
-        for s in stages_of(cfg):
+        for s in stages_of(cfg, wl.kind):
             st[s] = round(time_stage(setup, hip, s, stage_steps), 5)
         out["stage_ms"] = st
         dom = max(st, key=st.get)
@@ -328,6 +371,9 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-steps", type=int, default=10)
+    ap.add_argument("--eager", action="store_true", help="no HIP graph replay")
+    ap.add_argument("--only", default=None,
+                    help="time one workload CID:INDEX of the config table instead of the headline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -341,7 +387,15 @@ def main():
     hip = HipEvents()
 
     cid, wl = 2, configs.WORKLOADS[2][0]
-    head, _ = run_workload(cid, wl, hip, args.steps, args.warmup, args.stage_steps)
+    if args.only:
+        c, i = (int(v) for v in args.only.split(":"))
+        w = [x for x in configs.WORKLOADS[c] if x.index == i][0]
+        r, _ = run_workload(c, w, hip, args.steps, args.warmup, args.stage_steps,
+                            use_graph=not args.eager)
+        print(json.dumps(r), flush=True)
+        return
+    head, _ = run_workload(cid, wl, hip, args.steps, args.warmup, args.stage_steps,
+                           use_graph=not args.eager)
     log(f"[bench] headline {head['workload']}: {head['tokens_per_s']} tok/s, "
         f"{head['ms_per_step']} ms/step")
     secondary = []
@@ -350,9 +404,9 @@ def main():
             for w in configs.WORKLOADS[c]:
                 if (c, w.index) == (cid, wl.index):
                     continue
-                s_steps = max(5, args.steps // 5) if w.kind == "prefill" else args.steps
+                s_steps = max(6, args.steps // 5 // 2 * 2) if w.kind == "prefill" else args.steps
                 r, _ = run_workload(c, w, hip, s_steps, max(2, args.warmup // 2),
-                                    max(3, args.stage_steps // 2))
+                                    max(3, args.stage_steps // 2), use_graph=not args.eager)
                 log(f"[bench] {r['workload']}: {r['tokens_per_s']} tok/s, "
                     f"{r['ms_per_step']} ms/step")
                 secondary.append(r)

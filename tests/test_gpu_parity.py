@@ -366,3 +366,41 @@ def test_full_size_moe_ffn_routing():
     ef = branch_err(host(y)[rows], r32[rows], o["f"])
     log(f"[gpu] moe ffn N={N}: y {e:.2e}  branch {ef:.2e}")
     assert e <= BF16_TOL and ef <= FFN_BRANCH_TOL
+
+
+def test_hip_graph_replay_matches_eager():
+    """A captured call replays to the eager result, replay after replay, with
+    eager work in between (no memset nodes are ever captured)."""
+    cfg = small_cfg()
+    layer, _ = make_layer(cfg, max_tokens=256, max_batch=8)
+    x = B.to_device(synth.make_prefill_input(cfg, 1011, 2, 90))
+    kc = torch.zeros(2, 96, cfg.n_kv_heads, cfg.head_dim, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    y_eager = layer.prefill(x, kc, vc).clone()
+    xd, kd, vd, lens = synth.make_decode_input(cfg, 1012, 3, 40, T_max=48)
+    xd, kd, vd = B.to_device(xd), B.to_device(kd), B.to_device(vd)
+    lens = torch.from_numpy(lens).cuda()
+    yd_eager = layer.decode(xd, lens, kd, vd).clone()
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_eager)
+    yd = torch.empty_like(yd_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.prefill(x, kc, vc, y=y)
+        layer.decode(xd, lens, kd, vd, y=yd)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.prefill(x, kc, vc, y=y)
+        layer.decode(xd, lens, kd, vd, y=yd)
+    for rep in range(4):
+        y.zero_()
+        yd.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), rep
+        assert torch.equal(yd, yd_eager), rep
+        layer.decode(xd, lens, kd, vd)          # eager work between replays
+        torch.cuda.synchronize()

@@ -26,7 +26,7 @@ DEVICE_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
-HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__"]
+HOST_FLAGS = [f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-fPIC"]
 
 
 def _run(cmd):

@@ -43,13 +43,18 @@ hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const 
                             int max_tiles, int bm, float* out, hipStream_t s);
 
 // ---- decode GEMMs with M <= 128 rows (N % 16 == 0, K % 32 == 0) ----
-hipError_t ql_skinny_qkv(const float* X, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
-                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
-                         float* out, hipStream_t s);
+// out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x, gamma bf16;
+// RMSNorm's 1/rms and the QKV bias are applied by the consumer)
+hipError_t ql_skinny_qkv_raw(const bf16* x, const bf16* gamma, int M, const bf16* Wq,
+                             const bf16* Wk, const bf16* Wv, int q, int kv, int K, float* out,
+                             hipStream_t s);
+// out[M, N] fp32 = resid + X W^T (X fp32, used as a bf16 hi + lo pair)
 hipError_t ql_skinny_resid_f32(const float* X, int M, const bf16* W, int N, int K,
                                const bf16* resid, float* out, hipStream_t s);
+// out[M, N] bf16 = resid + X W^T
 hipError_t ql_skinny_resid_out(const bf16* X, int M, const bf16* W, int N, int K,
                                const float* resid, bf16* out, hipStream_t s);
+// out[M, F] = SiLU(X Wg^T) * (X Wu^T)
 hipError_t ql_skinny_swiglu(const bf16* X, int M, const bf16* Wg, const bf16* Wu, int F, int K,
                             bf16* out, hipStream_t s);
 
@@ -92,9 +97,23 @@ hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s);
 hipError_t ql_attn_prefill_f32(const AttnPrefillArgs& a, hipStream_t s);
 
 struct AttnDecodeArgs {
-  const bf16* q;         // [B, ldq]
+  const bf16* q;         // unused by the fused bf16 kernel
   const bf16* k_cache;   // [B, T_max, Hkv, dh]
   const bf16* v_cache;
+  bf16* k_cache_w;       // same caches, written at row cache_len[b]
+  bf16* v_cache_w;
+  const float* qkv_raw;  // [B, ld_raw] raw sums of (x * gamma1) [Wq; Wk; Wv]^T
+  int ld_raw;
+  const bf16* x;         // [B, d] layer input (for RMSNorm1's 1/rms)
+  int d;
+  const bf16* bq;        // QKV bias or NULL
+  const bf16* bk;
+  const bf16* bv;
+  const bf16* q_norm_g;  // QK-norm gammas or NULL
+  const bf16* k_norm_g;
+  float eps, theta;
+  int pos_offset;
+  bf16* q_out;           // [B, Hq*dh] rotated queries (optional copy)
   float* out;            // [B, ldo] fp32
   const float* qf;
   const float* kf;

@@ -292,106 +292,9 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
   return QL_OK;
 }
 
-// ---- bf16 layer halves -------------------------------------------------------
+// ---- bf16 layer -------------------------------------------------------------
 
-ql_status attn_half_bf16(ql_handle* h, const bf16* x, int N, bool decode, int B, int S,
-                         const int* cache_len, int pos_offset, void* kc, void* vc, int T_max,
-                         hipStream_t s) {
-  const ql_config& c = h->cfg;
-  const ql_weights& w = h->w;
-  float* xhat = static_cast<float*>(h->xhat);
-  QL_STAGE(h, QL_STAGE_RMSNORM1, s,
-           QL_HIP(ql_rmsnorm_bf16_to_f32(x, static_cast<const bf16*>(w.ln1_g), xhat, N, c.d,
-                                         c.rms_eps, s)));
-  ql_status mst = mark(h, QL_STAGE_QKV, true, s);
-  if (mst != QL_OK) return mst;
-  const bf16* bq = c.qkv_bias ? static_cast<const bf16*>(w.bq) : nullptr;
-  const bf16* bk = c.qkv_bias ? static_cast<const bf16*>(w.bk) : nullptr;
-  const bf16* bv = c.qkv_bias ? static_cast<const bf16*>(w.bv) : nullptr;
-  if (decode)
-    QL_HIP(ql_skinny_qkv(xhat, N, static_cast<const bf16*>(w.wq), static_cast<const bf16*>(w.wk),
-                         static_cast<const bf16*>(w.wv), h->q_dim, h->kv_dim, c.d, bq, bk, bv,
-                         h->qkv, s));
-  else
-    QL_HIP(ql_gemm_qkv(xhat, N, static_cast<const bf16*>(w.wq), static_cast<const bf16*>(w.wk),
-                       static_cast<const bf16*>(w.wv), h->q_dim, h->kv_dim, c.d, bq, bk, bv,
-                       h->qkv, s));
-  mst = mark(h, QL_STAGE_QKV, false, s);
-  if (mst != QL_OK) return mst;
-  QkvPostArgs qa{};
-  qa.qkv = h->qkv;
-  qa.ld_qkv = h->qkv_dim;
-  qa.rows = N;
-  qa.seq = S;
-  qa.cache_len = decode ? cache_len : nullptr;
-  qa.T_max = T_max;
-  qa.pos_offset = pos_offset;
-  qa.n_q_heads = c.n_q_heads;
-  qa.n_kv_heads = c.n_kv_heads;
-  qa.head_dim = c.head_dim;
-  qa.eps = c.rms_eps;
-  qa.theta = c.rope_theta;
-  qa.q_norm_g = c.qk_norm ? w.q_norm_g : nullptr;
-  qa.k_norm_g = c.qk_norm ? w.k_norm_g : nullptr;
-  qa.q_out = h->q;
-  qa.k_cache = kc;
-  qa.v_cache = vc;
-  QL_STAGE(h, QL_STAGE_QKV_POST, s, QL_HIP(ql_qkv_post_bf16(qa, s)));
-
-  if (decode) {
-    AttnDecodeArgs da{};
-    da.q = static_cast<const bf16*>(h->q);
-    da.k_cache = static_cast<const bf16*>(kc);
-    da.v_cache = static_cast<const bf16*>(vc);
-    da.out = static_cast<float*>(h->attn);
-    da.cache_len = cache_len;
-    da.ldq = h->q_dim;
-    da.ldo = h->q_dim;
-    da.B = B;
-    da.T_max = T_max;
-    da.n_q_heads = c.n_q_heads;
-    da.n_kv_heads = c.n_kv_heads;
-    da.head_dim = c.head_dim;
-    const int groups = B * c.n_kv_heads;
-    int nsplit = std::max(1, std::min(kMaxSplits, (512 + groups - 1) / groups));
-    int chunk = (T_max + nsplit - 1) / nsplit;
-    chunk = (chunk + 63) / 64 * 64;
-    nsplit = (T_max + chunk - 1) / chunk;
-    da.chunk = chunk;
-    da.nsplit = nsplit;
-    da.part_o = h->part_o;
-    da.part_ml = h->part_ml;
-    da.scale_log2 = scale_log2(c.head_dim);
-    QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
-    QL_STAGE(h, QL_STAGE_O_PROJ, s,
-             QL_HIP(ql_skinny_resid_f32(static_cast<const float*>(h->attn), N,
-                                        static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
-                                        s)));
-  } else {
-    AttnPrefillArgs pa{};
-    pa.q = static_cast<const bf16*>(h->q);
-    pa.k_cache = static_cast<const bf16*>(kc);
-    pa.v_cache = static_cast<const bf16*>(vc);
-    pa.out = static_cast<float*>(h->attn);
-    pa.ldq = h->q_dim;
-    pa.ldo = h->q_dim;
-    pa.B = B;
-    pa.S = S;
-    pa.T_max = T_max;
-    pa.n_q_heads = c.n_q_heads;
-    pa.n_kv_heads = c.n_kv_heads;
-    pa.head_dim = c.head_dim;
-    pa.scale_log2 = scale_log2(c.head_dim);
-    QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_prefill_bf16(pa, s)));
-    QL_STAGE(h, QL_STAGE_O_PROJ, s,
-             QL_HIP(ql_gemm_resid_f32(static_cast<const float*>(h->attn), N,
-                                      static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
-                                      s)));
-  }
-  return QL_OK;
-}
-
-ql_status ffn_half_bf16(ql_handle* h, int N, bool decode, bf16* y, hipStream_t s) {
+ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_t s) {
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
   bf16* z = static_cast<bf16*>(h->z);
@@ -417,6 +320,124 @@ ql_status ffn_half_bf16(ql_handle* h, int N, bool decode, bf16* y, hipStream_t s
                                       h->r, y, s)));
   }
   return QL_OK;
+}
+
+// Prefill: RMSNorm1 -> QKV GEMM (+bias) -> QK-norm/RoPE/cache -> attention ->
+// O GEMM + residual -> FFN half.
+ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset, void* kc,
+                       void* vc, int T_max, bf16* y, hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const ql_weights& w = h->w;
+  const int N = B * S;
+  float* xhat = static_cast<float*>(h->xhat);
+  QL_STAGE(h, QL_STAGE_RMSNORM1, s,
+           QL_HIP(ql_rmsnorm_bf16_to_f32(x, static_cast<const bf16*>(w.ln1_g), xhat, N, c.d,
+                                         c.rms_eps, s)));
+  const bf16* bq = c.qkv_bias ? static_cast<const bf16*>(w.bq) : nullptr;
+  const bf16* bk = c.qkv_bias ? static_cast<const bf16*>(w.bk) : nullptr;
+  const bf16* bv = c.qkv_bias ? static_cast<const bf16*>(w.bv) : nullptr;
+  QL_STAGE(h, QL_STAGE_QKV, s,
+           QL_HIP(ql_gemm_qkv(xhat, N, static_cast<const bf16*>(w.wq),
+                              static_cast<const bf16*>(w.wk), static_cast<const bf16*>(w.wv),
+                              h->q_dim, h->kv_dim, c.d, bq, bk, bv, h->qkv, s)));
+  QkvPostArgs qa{};
+  qa.qkv = h->qkv;
+  qa.ld_qkv = h->qkv_dim;
+  qa.rows = N;
+  qa.seq = S;
+  qa.cache_len = nullptr;
+  qa.T_max = T_max;
+  qa.pos_offset = pos_offset;
+  qa.n_q_heads = c.n_q_heads;
+  qa.n_kv_heads = c.n_kv_heads;
+  qa.head_dim = c.head_dim;
+  qa.eps = c.rms_eps;
+  qa.theta = c.rope_theta;
+  qa.q_norm_g = c.qk_norm ? w.q_norm_g : nullptr;
+  qa.k_norm_g = c.qk_norm ? w.k_norm_g : nullptr;
+  qa.q_out = h->q;
+  qa.k_cache = kc;
+  qa.v_cache = vc;
+  QL_STAGE(h, QL_STAGE_QKV_POST, s, QL_HIP(ql_qkv_post_bf16(qa, s)));
+  AttnPrefillArgs pa{};
+  pa.q = static_cast<const bf16*>(h->q);
+  pa.k_cache = static_cast<const bf16*>(kc);
+  pa.v_cache = static_cast<const bf16*>(vc);
+  pa.out = static_cast<float*>(h->attn);
+  pa.ldq = h->q_dim;
+  pa.ldo = h->q_dim;
+  pa.B = B;
+  pa.S = S;
+  pa.T_max = T_max;
+  pa.n_q_heads = c.n_q_heads;
+  pa.n_kv_heads = c.n_kv_heads;
+  pa.head_dim = c.head_dim;
+  pa.scale_log2 = scale_log2(c.head_dim);
+  QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_prefill_bf16(pa, s)));
+  QL_STAGE(h, QL_STAGE_O_PROJ, s,
+           QL_HIP(ql_gemm_resid_f32(static_cast<const float*>(h->attn), N,
+                                    static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r, s)));
+  return ffn_dense_or_moe(h, N, false, y, s);
+}
+
+// Decode: QKV projection of x * gamma1 (raw sums) -> attention with RMSNorm1
+// scale, QK-norm, RoPE and the cache append fused in -> O projection +
+// residual -> FFN half.
+ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, int pos_offset,
+                      void* kc, void* vc, int T_max, bf16* y, hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const ql_weights& w = h->w;
+  QL_STAGE(h, QL_STAGE_QKV, s,
+           QL_HIP(ql_skinny_qkv_raw(x, static_cast<const bf16*>(w.ln1_g), B,
+                                    static_cast<const bf16*>(w.wq), static_cast<const bf16*>(w.wk),
+                                    static_cast<const bf16*>(w.wv), h->q_dim, h->kv_dim, c.d,
+                                    h->qkv, s)));
+  AttnDecodeArgs da{};
+  da.k_cache = static_cast<const bf16*>(kc);
+  da.v_cache = static_cast<const bf16*>(vc);
+  da.k_cache_w = static_cast<bf16*>(kc);
+  da.v_cache_w = static_cast<bf16*>(vc);
+  da.qkv_raw = h->qkv;
+  da.ld_raw = h->qkv_dim;
+  da.x = x;
+  da.d = c.d;
+  if (c.qkv_bias) {
+    da.bq = static_cast<const bf16*>(w.bq);
+    da.bk = static_cast<const bf16*>(w.bk);
+    da.bv = static_cast<const bf16*>(w.bv);
+  }
+  if (c.qk_norm) {
+    da.q_norm_g = static_cast<const bf16*>(w.q_norm_g);
+    da.k_norm_g = static_cast<const bf16*>(w.k_norm_g);
+  }
+  da.eps = c.rms_eps;
+  da.theta = c.rope_theta;
+  da.pos_offset = pos_offset;
+  da.q_out = static_cast<bf16*>(h->q);
+  da.out = static_cast<float*>(h->attn);
+  da.cache_len = cache_len;
+  da.ldo = h->q_dim;
+  da.B = B;
+  da.T_max = T_max;
+  da.n_q_heads = c.n_q_heads;
+  da.n_kv_heads = c.n_kv_heads;
+  da.head_dim = c.head_dim;
+  const int groups = B * c.n_kv_heads;
+  int nsplit = std::max(1, std::min(kMaxSplits, (512 + groups - 1) / groups));
+  int chunk = (T_max + nsplit - 1) / nsplit;
+  chunk = (chunk + 63) / 64 * 64;
+  nsplit = (T_max + chunk - 1) / chunk;
+  da.chunk = chunk;
+  da.nsplit = nsplit;
+  da.part_o = h->part_o;
+  da.part_ml = h->part_ml;
+  da.scale_log2 = scale_log2(c.head_dim);
+  QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
+  QL_STAGE(h, QL_STAGE_O_PROJ, s,
+           QL_HIP(ql_skinny_resid_f32(static_cast<const float*>(h->attn), B,
+                                      static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
+                                      s)));
+  return ffn_dense_or_moe(h, B, true, y, s);
 }
 
 // ---- fp32 layer (small shapes) ---------------------------------------------
@@ -592,9 +613,8 @@ ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offs
     st = layer_f32(h, static_cast<const float*>(x), N, false, B, S, nullptr, pos_offset, k_cache,
                    v_cache, T_max, static_cast<float*>(y), s);
   } else {
-    st = attn_half_bf16(h, static_cast<const bf16*>(x), N, false, B, S, nullptr, pos_offset,
-                        k_cache, v_cache, T_max, s);
-    if (st == QL_OK) st = ffn_half_bf16(h, N, false, static_cast<bf16*>(y), s);
+    st = prefill_bf16(h, static_cast<const bf16*>(x), B, S, pos_offset, k_cache, v_cache, T_max,
+                      static_cast<bf16*>(y), s);
   }
   if (st == QL_OK) st = copy_taps(h, N, s);
   return st;
@@ -621,9 +641,8 @@ ql_status qlayer_decode(ql_handle* h, const void* x, int B, const int* cache_len
     st = layer_f32(h, static_cast<const float*>(x), B, true, B, 1, cache_len, pos_offset, k_cache,
                    v_cache, T_max, static_cast<float*>(y), s);
   } else {
-    st = attn_half_bf16(h, static_cast<const bf16*>(x), B, true, B, 1, cache_len, pos_offset,
-                        k_cache, v_cache, T_max, s);
-    if (st == QL_OK) st = ffn_half_bf16(h, B, true, static_cast<bf16*>(y), s);
+    st = decode_bf16(h, static_cast<const bf16*>(x), B, cache_len, pos_offset, k_cache, v_cache,
+                     T_max, static_cast<bf16*>(y), s);
   }
   if (st == QL_OK) st = copy_taps(h, B, s);
   return st;

@@ -1,4 +1,4 @@
-// RMSNorm over the feature axis, one wave64 per row.
+// RMSNorm over the feature axis.
 //
 // out_j = gamma_j * x_j / sqrt(mean_k x_k^2 + eps), the mean of squares taken
 // in fp32 ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层", §3). Rows are
@@ -12,6 +12,80 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;
 
+// V consecutive elements of T <-> float[V] with one vector memory access.
+template <class T, int V> QL_DEV void loadv(const T* p, float* f) {
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int i = 0; i < V; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
+      f[i] = v[0]; f[i + 1] = v[1]; f[i + 2] = v[2]; f[i + 3] = v[3];
+    }
+  } else if constexpr (V == 8) {
+    unpack8(*reinterpret_cast<const bf16x8*>(p), f);
+  } else {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = (float)v[i];
+  }
+}
+template <class T, int V> QL_DEV void storev(T* p, const float* f) {
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int i = 0; i < V; i += 4)
+      *reinterpret_cast<f32x4*>(p + i) = f32x4{f[i], f[i + 1], f[i + 2], f[i + 3]};
+  } else if constexpr (V == 8) {
+    *reinterpret_cast<bf16x8*>(p) = pack8(f);
+  } else {
+    const bf16x4 v = {(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3]};
+    *reinterpret_cast<bf16x4*>(p) = v;
+  }
+}
+
+// One block of 256 threads per row; thread t owns the V-wide pieces t, t+256,
+// ... (PER of them), all loaded before the reduction so one row costs about
+// one memory round trip.
+template <class TIn, class TG, class TOut, int PER>
+__global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict__ x,
+                                                          const TG* __restrict__ gamma,
+                                                          TOut* __restrict__ out,
+                                                          float* __restrict__ out_f32, int d,
+                                                          float eps) {
+  constexpr int V = 16 / sizeof(TIn);
+  __shared__ float wsum[4];
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const TIn* xr = x + row * d;
+  float v[PER][V], g[PER][V];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = (tid + 256 * i) * V;
+    if (c < d) {
+      loadv<TIn, V>(xr + c, v[i]);
+      loadv<TG, V>(gamma + c, g[i]);
+#pragma unroll
+      for (int j = 0; j < V; ++j) ss += v[i][j] * v[i][j];
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = (tid + 256 * i) * V;
+    if (c < d) {
+      float o[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) o[j] = g[i][j] * (v[i][j] * inv);
+      storev<TOut, V>(out + row * d + c, o);
+      if (out_f32) storev<float, V>(out_f32 + row * d + c, o);
+    }
+  }
+}
+
+// Any d: one wave per row, strided scalar accesses.
 template <class TIn, class TG, class TOut>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
                                                       const TG* __restrict__ gamma,
@@ -24,40 +98,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
   const TIn* xr = x + (size_t)row * d;
   TOut* orow = out + (size_t)row * d;
   float ss = 0.f;
-  constexpr bool kVec = sizeof(TIn) == 2 && sizeof(TG) == 2;
-  if (kVec && (d % 512) == 0) {
-    // 16-byte loads: lane covers 8 consecutive features per 512-wide stripe.
-    const int nv = d / 512;
-    float v[8];
-    for (int i = 0; i < nv; ++i) {
-      unpack8(load_bf16x8(reinterpret_cast<const bf16*>(xr) + i * 512 + lane * 8), v);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
-    }
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-    for (int i = 0; i < nv; ++i) {
-      const int c = i * 512 + lane * 8;
-      float g[8], o[8];
-      unpack8(load_bf16x8(reinterpret_cast<const bf16*>(xr) + c), v);
-      unpack8(load_bf16x8(reinterpret_cast<const bf16*>(gamma) + c), g);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = g[j] * (v[j] * inv);
-      if constexpr (sizeof(TOut) == 2) {
-        store_bf16x8(reinterpret_cast<bf16*>(orow) + c, pack8(o));
-      } else {
-        float* of = reinterpret_cast<float*>(orow) + c;
-        *reinterpret_cast<f32x4*>(of) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(of + 4) = f32x4{o[4], o[5], o[6], o[7]};
-      }
-      if (out_f32) {
-        float* of = out_f32 + (size_t)row * d + c;
-        *reinterpret_cast<f32x4*>(of) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(of + 4) = f32x4{o[4], o[5], o[6], o[7]};
-      }
-    }
-    return;
-  }
   for (int c = lane; c < d; c += 64) {
     const float v = to_f32(xr[c]);
     ss += v * v;
@@ -75,6 +115,21 @@ template <class TIn, class TG, class TOut>
 hipError_t launch(const TIn* x, const TG* gamma, TOut* out, float* out_f32, int rows, int d,
                   float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  constexpr int V = 16 / sizeof(TIn);
+  const int per = (d + 256 * V - 1) / (256 * V);
+  if (d % V == 0 && per <= 8) {
+#define QL_RMS_CASE(P)                                                                    \
+  if (per <= P) {                                                                         \
+    hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, P>), dim3(rows), dim3(256), 0, s, \
+                       x, gamma, out, out_f32, d, eps);                                   \
+    return hipGetLastError();                                                             \
+  }
+    QL_RMS_CASE(1)
+    QL_RMS_CASE(2)
+    QL_RMS_CASE(4)
+    QL_RMS_CASE(8)
+#undef QL_RMS_CASE
+  }
   const int blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   hipLaunchKernelGGL((rmsnorm_kernel<TIn, TG, TOut>), dim3(blocks), dim3(256), 0, s, x, gamma,
                      out, out_f32, rows, d, eps);
