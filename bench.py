@@ -274,11 +274,16 @@ def time_stage(setup, hip, stage, steps):
     return tot / steps
 
 
-def stages_of(cfg, kind):
+GEMV_MAX_ROWS = 4   # dense decode with this many rows or fewer folds RMSNorm2 into gate/up
+
+
+def stages_of(cfg, kind, batch):
     # decode fuses RMSNorm1 into the QKV projection and the QK-norm / RoPE /
     # cache append into the attention kernel
     s = (["rmsnorm1", "qkv", "qkv_post"] if kind == "prefill" else ["qkv"])
-    s += ["attention", "o_proj", "rmsnorm2"]
+    s += ["attention", "o_proj"]
+    if not (kind == "decode" and not cfg.is_moe and batch <= GEMV_MAX_ROWS):
+        s += ["rmsnorm2"]
     s += (["router", "permute", "expert_gate_up", "expert_down", "combine"] if cfg.is_moe
           else ["gate_up", "down"])
     return s
@@ -316,7 +321,7 @@ def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_g
         out["layer_frac_hbm"] = round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if breakdown:
         st = {}
-        for s in stages_of(cfg, wl.kind):
+        for s in stages_of(cfg, wl.kind, wl.batch):
             st[s] = round(time_stage(setup, hip, s, stage_steps), 5)
         out["stage_ms"] = st
         dom = max(st, key=st.get)

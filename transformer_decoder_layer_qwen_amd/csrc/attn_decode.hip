@@ -5,8 +5,10 @@
 // causal halving for the single query; §05.2: the Hq/Hkv query heads of a
 // group read the same K/V bytes, so the group pays for them once.)
 //
-// Split-K: grid (splits, Hkv, B). A block reads one key range of one KV head
-// once and serves all G = Hq/Hkv query heads of the group:
+// Split-K: grid (splits, Hkv, B), 4 or 8 waves per block. A block reads
+// one key range of one KV head once and serves all G = Hq/Hkv query heads of
+// the group; its waves take 16-key tiles round-robin, each keeping the next
+// tile's loads in flight while it works on the current one:
 //   * scores: S^T[key][head] = K Q^T with 16x16x32 MFMAs, K rows loaded
 //     straight from the cache with 16-byte loads (A operand), the G queries
 //     padded to 16 columns (B operand, held in registers);
@@ -15,17 +17,21 @@
 //   * P V on the vector ALUs: lane (dh piece of 8, key sub-group) loads its
 //     V rows with 16-byte loads and accumulates G x 8 fp32 outputs; P and the
 //     per-head rescale factors go through a per-wave LDS scratch.
-// Each block writes an unnormalised partial (m, l, o[128]) per head; the
-// combine kernel merges the splits (with a single split the block writes the
-// normalised output itself).
+// The waves merge in LDS. With one split the block writes the normalised
+// output; otherwise it writes an unnormalised partial (m, l, o[128]) per head
+// and a small combine kernel merges the splits (a cross-block merge inside
+// the kernel would need device-scope fences, which write back and invalidate
+// the whole L2 of the XCD on this GPU and cost far more than a launch).
 //
 // Prologue (fused QK-norm / RoPE / cache append): the Q/K/V projection hands
-// over raw sums of (x * gamma1) W^T. Each block computes RMSNorm1's 1/rms for
-// its row, forms q for its G heads (scale, bias, QK-norm, rotate_half RoPE at
-// position cache_len + pos_offset) and keeps them in LDS; the block whose key
-// range contains the new row also forms that row's k and v, appends them to
-// the cache and uses them from LDS ("Qwen2.5-7B 结构拆解" §09.1; "推理系统 03：
-// 逐项算清一个真实 Qwen3 Transformer 层" §5, §6, §12).
+// over raw sums of (x * gamma1) W^T, and 1/rms of x (or the block computes it
+// from x). Each block forms q for its G heads (scale, bias, QK-norm,
+// rotate_half RoPE at position cache_len + pos_offset) and keeps them in LDS;
+// the block whose key range contains the new row also forms that row's k and
+// v, appends them to the cache and uses them from LDS ("Qwen2.5-7B 结构拆解"
+// §09.1; "推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §5, §6, §12).
+// The cache, K/V tile, projection and bias loads are all issued before the
+// prologue's arithmetic.
 #include "common.h"
 #include "kernels.h"
 
@@ -33,16 +39,18 @@ namespace {
 
 constexpr int kDh = 128;
 
-template <int G>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p) {
-  __shared__ float p_lds[4][16 * 16];  // per wave: P[key 16][head 16]
-  __shared__ float a_lds[4][16];       // per wave: rescale per head
-  __shared__ float w_o[4][G * kDh];    // cross-wave partial outputs
-  __shared__ float w_m[4][16];
-  __shared__ float w_l[4][16];
+// NW waves per block (4 or 8); wave w takes keys kbeg + 16 w + 16 NW i.
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeArgs p) {
+  constexpr int kQS = 16 / NW;            // query-head slots per wave in the prologue
+  __shared__ float p_lds[NW][16 * 16];    // per wave: P[key 16][head 16]
+  __shared__ float a_lds[NW][16];         // per wave: rescale per head
+  __shared__ float w_o[NW][G * kDh];      // cross-wave partial outputs
+  __shared__ float w_m[NW][16];
+  __shared__ float w_l[NW][16];
   __shared__ __attribute__((aligned(16))) bf16 q_lds[16][kDh];    // rows >= G stay zero
   __shared__ __attribute__((aligned(16))) bf16 kv_new[2][kDh];    // appended K and V row
-  __shared__ float red4[4];
+  __shared__ float red[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -53,27 +61,95 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
   const int g = blockIdx.y;
   const int b = blockIdx.z;
 
+  // ---- every load goes out before any of them is waited on ----
+  // Nothing here depends on cache_len[b]: the first tile is loaded up to the
+  // split's end within T_max and masked once the length is known, the
+  // projection / bias / norm loads are unconditional (absent biases and norms
+  // read a harmless valid address and are masked to 0 / 1).
   const int L = p.cache_len[b];
+  const int kbeg = split * p.chunk;
+  const int kcap = min(kbeg + p.chunk, p.T_max);
+  const size_t row_stride = (size_t)p.n_kv_heads * kDh;
+  const bf16* kb_ = p.k_cache + (size_t)b * p.T_max * row_stride + g * kDh;
+  const bf16* vb_ = p.v_cache + (size_t)b * p.T_max * row_stride + g * kDh;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // A wave's tile: keys k0 .. k0+15. K: lane (key col, k-group grp) loads dh
+  // [32 s + 8 grp, +8) of key k0 + col; V: keys k0 + 4 grp + j, dh piece col.
+  auto load_tile = [&](int k0, int lim, u32x4 (&kt)[4], u32x4 (&vt)[4]) {
+    const int krow = k0 + col;
+    const bool kv = krow < lim;
+    const bf16* kr = kb_ + (size_t)(kv ? krow : kbeg) * row_stride;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      kt[s] = kv ? *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * grp) : zero4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = k0 + 4 * grp + j;
+      vt[j] = key < lim ? *reinterpret_cast<const u32x4*>(vb_ + (size_t)key * row_stride + col * 8)
+                        : zero4;
+    }
+  };
+  u32x4 kcur[4], vcur[4];
+  load_tile(kbeg + 16 * wave, kcap, kcur, vcur);
+
+  const int qd = p.n_q_heads * kDh;
+  const int kvd = p.n_kv_heads * kDh;
+  const float* raw = p.qkv_raw + (size_t)b * p.ld_raw;
+  // slots 0 .. kQS-1: query heads wave + NW i of the group; kQS, kQS+1: the new K and V row
+  constexpr int kSlots = kQS + 2;
+  float hv[kSlots][2], hb[kSlots][2];
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    const int hq = g * G + wave + NW * i;
+    const int c0 = i < kQS ? (wave + NW * i < G ? hq * kDh : 0)
+                           : (i == kQS ? qd + g * kDh : qd + kvd + g * kDh);
+    hv[i][0] = raw[c0 + lane];
+    hv[i][1] = raw[c0 + lane + 64];
+    const bf16* bias = i < kQS ? p.bq : (i == kQS ? p.bk : p.bv);
+    const int bc = i < kQS ? c0 : g * kDh;
+    const bf16* bsrc = bias ? bias + bc : p.x;
+    const float b0 = to_f32(bsrc[lane]), b1 = to_f32(bsrc[lane + 64]);
+    hb[i][0] = bias ? b0 : 0.f;
+    hb[i][1] = bias ? b1 : 0.f;
+  }
+  const float inv_given = p.inv_rms ? p.inv_rms[b] : 0.f;
+  const bool qkn = p.q_norm_g != nullptr;
+  const bf16* qgs = qkn ? p.q_norm_g : p.x;
+  const bf16* kgs = qkn ? p.k_norm_g : p.x;
+  const float qg0r = to_f32(qgs[lane]), qg1r = to_f32(qgs[lane + 64]);
+  const float kg0r = to_f32(kgs[lane]), kg1r = to_f32(kgs[lane + 64]);
+  const float qg0 = qkn ? qg0r : 1.f, qg1 = qkn ? qg1r : 1.f;
+  const float kg0 = qkn ? kg0r : 1.f, kg1 = qkn ? kg1r : 1.f;
+
   const bool valid = L >= 0 && L < p.T_max;
   const int nkeys = valid ? L + 1 : 0;
-  const int kbeg = split * p.chunk;
   const int kend = min(kbeg + p.chunk, nkeys);
+  const bool has_new = valid && kbeg <= L && L < kend;
+  // rows of the first tile past the live keys may hold anything (a NaN would
+  // survive a zero softmax weight in P V): zero their V
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (kbeg + 16 * wave + 4 * grp + j >= kend) vcur[j] = zero4;
 
   // ---- prologue: RMSNorm1 scale, q heads, the appended K/V row ----
-  {
+  float inv = inv_given;
+  if (!p.inv_rms) {
     const bf16* xr = p.x + (size_t)b * p.d;
     float ss = 0.f;
-    for (int c = tid * 8; c < p.d; c += 256 * 8) {
+    for (int c = tid * 8; c < p.d; c += NW * 64 * 8) {
       float f[8];
       unpack8(load_bf16x8(xr + c), f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
     }
     ss = wave_sum(ss);
-    if (lane == 0) red4[wave] = ss;
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += red[w];
+    inv = 1.0f / sqrtf(t / (float)p.d + p.eps);
   }
-  __syncthreads();
-  const float inv = 1.0f / sqrtf((red4[0] + red4[1] + red4[2] + red4[3]) / (float)p.d + p.eps);
   float sn, cs;
   {
     const double pos = (double)L + (double)p.pos_offset;
@@ -83,23 +159,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
     ang -= two_pi * rint(ang / two_pi);
     sincosf((float)ang, &sn, &cs);
   }
-  const int qd = p.n_q_heads * kDh;
-  const int kvd = p.n_kv_heads * kDh;
-  const float* raw = p.qkv_raw + (size_t)b * p.ld_raw;
   // one head's 128 values: lane owns (lane, lane + 64); scale, bias, norm, rotate
-  auto head_vec = [&](int col0, const bf16* bias, const bf16* gam, bool rotate, float& o0,
-                      float& o1) {
-    float x0 = inv * raw[col0 + lane];
-    float x1 = inv * raw[col0 + lane + 64];
-    if (bias) {
-      x0 += to_f32(bias[lane]);
-      x1 += to_f32(bias[lane + 64]);
-    }
-    if (gam) {
+  auto head_vec = [&](int i, bool norm, float g0, float g1, bool rotate, float& o0, float& o1) {
+    float x0 = inv * hv[i][0] + hb[i][0];
+    float x1 = inv * hv[i][1] + hb[i][1];
+    if (norm) {
       const float hs = wave_sum(x0 * x0 + x1 * x1);
       const float hinv = 1.0f / sqrtf(hs / (float)kDh + p.eps);
-      x0 = to_f32(gam[lane]) * (x0 * hinv);
-      x1 = to_f32(gam[lane + 64]) * (x1 * hinv);
+      x0 = g0 * (x0 * hinv);
+      x1 = g1 * (x1 * hinv);
     }
     if (rotate) {
       o0 = x0 * cs - x1 * sn;
@@ -109,12 +177,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
       o1 = x1;
     }
   };
-  for (int hh = wave; hh < 16; hh += 4) {
+#pragma unroll
+  for (int i = 0; i < kQS; ++i) {
+    const int hh = wave + NW * i;
     float r0 = 0.f, r1 = 0.f;
     if (hh < G) {
-      const int hq = g * G + hh;
-      head_vec(hq * kDh, p.bq ? p.bq + hq * kDh : nullptr, p.q_norm_g, true, r0, r1);
+      head_vec(i, qkn, qg0, qg1, true, r0, r1);
       if (split == 0 && p.q_out) {
+        const int hq = g * G + hh;
         const float nv = valid ? 0.f : __builtin_nanf("");
         p.q_out[(size_t)b * qd + hq * kDh + lane] = (bf16)(r0 + nv);
         p.q_out[(size_t)b * qd + hq * kDh + lane + 64] = (bf16)(r1 + nv);
@@ -123,11 +193,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
     q_lds[hh][lane] = (bf16)r0;
     q_lds[hh][lane + 64] = (bf16)r1;
   }
-  const bool has_new = valid && kbeg <= L && L < kend;
   if (has_new && wave == 0) {
     float k0, k1, v0, v1;
-    head_vec(qd + g * kDh, p.bk ? p.bk + g * kDh : nullptr, p.k_norm_g, true, k0, k1);
-    head_vec(qd + kvd + g * kDh, p.bv ? p.bv + g * kDh : nullptr, nullptr, false, v0, v1);
+    head_vec(kQS, qkn, kg0, kg1, true, k0, k1);
+    head_vec(kQS + 1, false, 1.f, 1.f, false, v0, v1);
     const size_t crow = ((size_t)b * p.T_max + L) * kvd + g * kDh;
     const bf16 bk0 = (bf16)k0, bk1 = (bf16)k1, bv0 = (bf16)v0, bv1 = (bf16)v1;
     p.k_cache_w[crow + lane] = bk0;
@@ -145,9 +214,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
   bf16x8 qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(&q_lds[col][32 * s + 8 * grp]);
-  const size_t row_stride = (size_t)p.n_kv_heads * kDh;
-  const bf16* kb_ = p.k_cache + (size_t)b * p.T_max * row_stride + g * kDh;
-  const bf16* vb_ = p.v_cache + (size_t)b * p.T_max * row_stride + g * kDh;
 
   float acc[G][8];
 #pragma unroll
@@ -157,29 +223,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
   float m_run = -INFINITY;  // for head `col`
   float l_run = 0.f;
 
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  for (int k0 = kbeg + 16 * wave; k0 < kend; k0 += 64) {
-    // scores for keys k0 .. k0+15
-    const int krow = k0 + col;
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-    {
-      const bool kv = krow < kend;
-      const bool knew = has_new && krow == L;
-      const bf16* kr = knew ? kv_new[0] : kb_ + (size_t)(kv ? krow : kbeg) * row_stride;
+  for (int k0 = kbeg + 16 * wave; k0 < kend; k0 += 16 * NW) {
+    // the next tile's loads overlap this tile's arithmetic
+    u32x4 knext[4], vnext[4];
+    load_tile(k0 + 16 * NW, kend, knext, vnext);
+    // the appended row comes from LDS (its cache write may still be in flight)
+    if (has_new) {
+      if (k0 + col == L) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 kraw = kv ? *reinterpret_cast<const u32x4*>(kr + 32 * s + 8 * grp) : zero4;
-        sc = mfma_16x16x32(*reinterpret_cast<const bf16x8*>(&kraw), qf[s], sc);
+        for (int s = 0; s < 4; ++s)
+          kcur[s] = *reinterpret_cast<const u32x4*>(&kv_new[0][32 * s + 8 * grp]);
       }
-    }
-    // V rows this lane accumulates: keys k0 + 4*grp + j, dh piece col
-    u32x4 vraw[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + 4 * grp + j;
-      const bf16* vr = (has_new && key == L) ? kv_new[1] : vb_ + (size_t)key * row_stride;
-      vraw[j] = key < kend ? *reinterpret_cast<const u32x4*>(vr + col * 8) : zero4;
+      for (int j = 0; j < 4; ++j)
+        if (k0 + 4 * grp + j == L) vcur[j] = *reinterpret_cast<const u32x4*>(&kv_new[1][col * 8]);
     }
+    // scores for keys k0 .. k0+15
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sc = mfma_16x16x32(*reinterpret_cast<const bf16x8*>(&kcur[s]), qf[s], sc);
     // lane holds S^T[key 4*grp + r][head col]
     float mt = -INFINITY;
 #pragma unroll
@@ -216,7 +278,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float v[8];
-      unpack8(*reinterpret_cast<const bf16x8*>(&vraw[j]), v);
+      unpack8(*reinterpret_cast<const bf16x8*>(&vcur[j]), v);
       const float* pr = &p_lds[wave][(4 * grp + j) * 16];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -227,6 +289,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kcur[s] = knext[s];
+      vcur[s] = vnext[s];
+    }
   }
 
   // reduce the 4 key sub-groups of the wave (lanes col, col+16, col+32, col+48)
@@ -248,18 +315,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
     w_l[wave][col] = l_run;
   }
   __syncthreads();
-
-  // merge the 4 waves; write this split's partial for each head of the group
-  for (int i = tid; i < G * kDh; i += 256) {
+  // merge the waves; write this split's partial for each head of the group
+  for (int i = tid; i < G * kDh; i += NW * 64) {
     const int h = i / kDh;
     const int d = i % kDh;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, w_m[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, w_m[w][h]);
     float o = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         if (w_m[w][h] == -INFINITY) continue;
         const float f = exp2f(w_m[w][h] - M);
         o += w_o[w][h * kDh + d] * f;
@@ -280,44 +346,71 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnDecodeArgs p
   }
 }
 
+// Merge the splits of one (sequence, head): every partial is loaded at once
+// (the loads are independent), the maxima and sums go through LDS.
 __global__ __launch_bounds__(128) void attn_decode_combine_kernel(const AttnDecodeArgs p) {
+  __shared__ float s_m[kMaxDecodeSplits], s_l[kMaxDecodeSplits];
   const int bh = blockIdx.x;  // b * Hq + head
   const int b = bh / p.n_q_heads;
   const int d = threadIdx.x;
+  const size_t base = (size_t)bh * p.nsplit;
+  float ov[kMaxDecodeSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxDecodeSplits; ++s)
+    ov[s] = s < p.nsplit ? p.part_o[(base + s) * kDh + d] : 0.f;
+  if (d < p.nsplit) {
+    s_m[d] = p.part_ml[(base + d) * 2];
+    s_l[d] = p.part_ml[(base + d) * 2 + 1];
+  }
   const int L = p.cache_len[b];
   const bool valid = L >= 0 && L < p.T_max;
-  const size_t base = (size_t)bh * p.nsplit;
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.part_ml[(base + s) * 2]);
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, s_m[s]);
   float o = 0.f, l = 0.f;
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float m = p.part_ml[(base + s) * 2];
+#pragma unroll
+  for (int s = 0; s < kMaxDecodeSplits; ++s) {
+    if (s >= p.nsplit) break;
+    const float m = s_m[s];
     if (m == -INFINITY) continue;
     const float f = exp2f(m - M);
-    o += p.part_o[(base + s) * kDh + d] * f;
-    l += p.part_ml[(base + s) * 2 + 1] * f;
+    o += ov[s] * f;
+    l += s_l[s] * f;
   }
   const float out = valid ? o / l : __builtin_nanf("");
   p.out[(size_t)b * p.ldo + (size_t)(bh % p.n_q_heads) * kDh + d] = out;
+}
+
+template <int G>
+hipError_t launch_g(const AttnDecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.nsplit, a.n_kv_heads, a.B);
+  switch (a.waves) {
+    case 4: hipLaunchKernelGGL((attn_decode_kernel<G, 4>), grid, dim3(256), 0, s, a); break;
+    case 8:
+      if constexpr (G <= 8) {
+        hipLaunchKernelGGL((attn_decode_kernel<G, 8>), grid, dim3(512), 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  const dim3 grid(a.nsplit, a.n_kv_heads, a.B);
+  hipError_t e;
   switch (a.n_q_heads / a.n_kv_heads) {
-#define QL_G(V)                                                                     \
-  case V:                                                                           \
-    hipLaunchKernelGGL(attn_decode_kernel<V>, grid, dim3(256), 0, s, a);           \
-    break;
+#define QL_G(V) \
+  case V: e = launch_g<V>(a, s); break;
     QL_G(1) QL_G(2) QL_G(3) QL_G(4) QL_G(5) QL_G(6) QL_G(7) QL_G(8)
     QL_G(9) QL_G(10) QL_G(11) QL_G(12) QL_G(13) QL_G(14) QL_G(15) QL_G(16)
 #undef QL_G
     default:
       return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q_heads), dim3(128), 0, s, a);
   return hipGetLastError();

@@ -58,6 +58,26 @@ hipError_t ql_skinny_resid_out(const bf16* X, int M, const bf16* W, int N, int K
 hipError_t ql_skinny_swiglu(const bf16* X, int M, const bf16* Wg, const bf16* Wu, int F, int K,
                             bf16* out, hipStream_t s);
 
+// ---- decode GEMVs for M <= kGemvMaxRows rows (N % 2 == 0, K % 8 == 0) ----
+// Same contracts as the skinny forms above; fp32 X is used unsplit.
+constexpr int kGemvMaxRows = 4;
+bool ql_gemv_ok(int M, int N, int K);
+// (the QKV form also writes RMSNorm's 1/rms of each x row to inv_rms[M] if non-NULL)
+hipError_t ql_gemv_qkv_raw(const bf16* x, const bf16* gamma, int M, const bf16* Wq,
+                           const bf16* Wk, const bf16* Wv, int q, int kv, int K, float* out,
+                           float eps, float* inv_rms, hipStream_t s);
+hipError_t ql_gemv_resid_f32(const float* X, int M, const bf16* W, int N, int K,
+                             const bf16* resid, float* out, hipStream_t s);
+hipError_t ql_gemv_resid_out(const bf16* X, int M, const bf16* W, int N, int K,
+                             const float* resid, bf16* out, hipStream_t s);
+hipError_t ql_gemv_swiglu(const bf16* X, int M, const bf16* Wg, const bf16* Wu, int F, int K,
+                          bf16* out, hipStream_t s);
+// out[M, F] = SiLU(Z Wg^T) * (Z Wu^T), Z = RMSNorm(R) * gamma computed on the fly
+// (R fp32 [M, K])
+hipError_t ql_gemv_rmsnorm_swiglu(const float* R, const bf16* gamma, float eps, int M,
+                                  const bf16* Wg, const bf16* Wu, int F, int K, bf16* out,
+                                  hipStream_t s);
+
 // ---- QK-norm + RoPE + cache write ----
 struct QkvPostArgs {
   const float* qkv;      // [rows, ld_qkv] fp32 projections (bias added)
@@ -126,8 +146,11 @@ struct AttnDecodeArgs {
   int chunk, nsplit;     // keys per split, number of splits
   float* part_o;         // [B, Hq, nsplit, dh]
   float* part_ml;        // [B, Hq, nsplit, 2]
+  int waves;             // waves per block: 4 or 8 (8 needs G <= 8)
+  const float* inv_rms;  // [B] RMSNorm1 1/rms of x, or NULL (computed from x)
   float scale_log2;
 };
+constexpr int kMaxDecodeSplits = 32;  // nsplit <= this
 hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s);
 hipError_t ql_attn_decode_f32(const AttnDecodeArgs& a, hipStream_t s);
 

@@ -36,7 +36,6 @@ ql_status fail(ql_status st, const char* fmt, ...) {
   return st;
 }
 
-constexpr int kMaxSplits = 32;
 constexpr int kMinMoeTile = 32;
 constexpr size_t kAlign = 256;
 
@@ -64,6 +63,7 @@ struct ql_handle {
   void* h;
   float* part_o;
   float* part_ml;
+  float* inv_rms;   // [rows] RMSNorm1 1/rms handed from the QKV GEMV to attention
   float* logits;
   int* idx;
   float* topw;
@@ -181,8 +181,9 @@ size_t layout(ql_handle* h, char* base) {
   h->r = k.take<float>(N * c.d * 4);
   h->z = k.take<void>(N * c.d * es);
   const size_t B = (size_t)std::max(c.max_batch, 0);
-  h->part_o = k.take<float>(B * c.n_q_heads * kMaxSplits * c.head_dim * 4);
-  h->part_ml = k.take<float>(B * c.n_q_heads * kMaxSplits * 2 * 4);
+  h->part_o = k.take<float>(B * c.n_q_heads * kMaxDecodeSplits * c.head_dim * 4);
+  h->part_ml = k.take<float>(B * c.n_q_heads * kMaxDecodeSplits * 2 * 4);
+  h->inv_rms = k.take<float>(N * 4);
   if (c.n_experts > 0) {
     const size_t E = c.n_experts, K = c.top_k, NK = N * K;
     const size_t nblk = (N + 255) / 256;
@@ -298,19 +299,33 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
   bf16* z = static_cast<bf16*>(h->z);
-  QL_STAGE(h, QL_STAGE_RMSNORM2, s,
-           QL_HIP(ql_rmsnorm_f32in_bf16(h->r, static_cast<const bf16*>(w.ln2_g), z,
-                                        c.n_experts > 0 ? h->zf : nullptr, N, c.d, c.rms_eps,
-                                        s)));
+  const bf16* g2 = static_cast<const bf16*>(w.ln2_g);
+  // few rows on the dense path: RMSNorm2 rides inside the gate/up projection
+  // (z is then only formed when a tap asks for it)
+  const bool gemv = decode && c.n_experts == 0 && ql_gemv_ok(N, c.ffn_dim, c.d) &&
+                    ql_gemv_ok(N, c.d, c.ffn_dim);
+  if (!gemv || h->taps.z)
+    QL_STAGE(h, QL_STAGE_RMSNORM2, s,
+             QL_HIP(ql_rmsnorm_f32in_bf16(h->r, g2, z, c.n_experts > 0 ? h->zf : nullptr, N,
+                                          c.d, c.rms_eps, s)));
   if (c.n_experts > 0) return moe_core(h, N, h->r, 1, y, s);
   bf16* hh = static_cast<bf16*>(h->h);
   if (decode) {
-    QL_STAGE(h, QL_STAGE_GATE_UP, s,
-             QL_HIP(ql_skinny_swiglu(z, N, static_cast<const bf16*>(w.w_gate),
-                                     static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, s)));
-    QL_STAGE(h, QL_STAGE_DOWN, s,
-             QL_HIP(ql_skinny_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d,
-                                        c.ffn_dim, h->r, y, s)));
+    const bf16* wg = static_cast<const bf16*>(w.w_gate);
+    const bf16* wu = static_cast<const bf16*>(w.w_up);
+    const bf16* wd = static_cast<const bf16*>(w.w_down);
+    if (gemv) {
+      QL_STAGE(h, QL_STAGE_GATE_UP, s,
+               QL_HIP(ql_gemv_rmsnorm_swiglu(h->r, g2, c.rms_eps, N, wg, wu, c.ffn_dim, c.d, hh,
+                                             s)));
+      QL_STAGE(h, QL_STAGE_DOWN, s,
+               QL_HIP(ql_gemv_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
+    } else {
+      QL_STAGE(h, QL_STAGE_GATE_UP, s,
+               QL_HIP(ql_skinny_swiglu(z, N, wg, wu, c.ffn_dim, c.d, hh, s)));
+      QL_STAGE(h, QL_STAGE_DOWN, s,
+               QL_HIP(ql_skinny_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
+    }
   } else {
     QL_STAGE(h, QL_STAGE_GATE_UP, s,
              QL_HIP(ql_gemm_swiglu(z, N, static_cast<const bf16*>(w.w_gate),
@@ -387,11 +402,16 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
                       void* kc, void* vc, int T_max, bf16* y, hipStream_t s) {
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
+  const bool gemv = ql_gemv_ok(B, h->qkv_dim, c.d) && ql_gemv_ok(B, c.d, h->q_dim);
+  const bf16* g1 = static_cast<const bf16*>(w.ln1_g);
+  const bf16* wq = static_cast<const bf16*>(w.wq);
+  const bf16* wk = static_cast<const bf16*>(w.wk);
+  const bf16* wv = static_cast<const bf16*>(w.wv);
   QL_STAGE(h, QL_STAGE_QKV, s,
-           QL_HIP(ql_skinny_qkv_raw(x, static_cast<const bf16*>(w.ln1_g), B,
-                                    static_cast<const bf16*>(w.wq), static_cast<const bf16*>(w.wk),
-                                    static_cast<const bf16*>(w.wv), h->q_dim, h->kv_dim, c.d,
-                                    h->qkv, s)));
+           QL_HIP(gemv ? ql_gemv_qkv_raw(x, g1, B, wq, wk, wv, h->q_dim, h->kv_dim, c.d, h->qkv,
+                                         c.rms_eps, h->inv_rms, s)
+                       : ql_skinny_qkv_raw(x, g1, B, wq, wk, wv, h->q_dim, h->kv_dim, c.d,
+                                           h->qkv, s)));
   AttnDecodeArgs da{};
   da.k_cache = static_cast<const bf16*>(kc);
   da.v_cache = static_cast<const bf16*>(vc);
@@ -422,21 +442,29 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
   da.n_q_heads = c.n_q_heads;
   da.n_kv_heads = c.n_kv_heads;
   da.head_dim = c.head_dim;
+  // Launch shape: ~512 blocks over (split, KV head, sequence); with few
+  // groups the blocks get 8 waves (one 16-key tile per wave for short caches:
+  // every K/V load is issued at kernel start), else 4. The split length is a
+  // whole number of tiles per wave.
   const int groups = B * c.n_kv_heads;
-  int nsplit = std::max(1, std::min(kMaxSplits, (512 + groups - 1) / groups));
+  const int waves = (groups <= 16 && h->G <= 8) ? 8 : 4;
+  int nsplit = std::max(1, std::min(kMaxDecodeSplits, (512 + groups - 1) / groups));
   int chunk = (T_max + nsplit - 1) / nsplit;
-  chunk = (chunk + 63) / 64 * 64;
+  chunk = (chunk + 16 * waves - 1) / (16 * waves) * (16 * waves);
   nsplit = (T_max + chunk - 1) / chunk;
+  da.waves = waves;
   da.chunk = chunk;
   da.nsplit = nsplit;
   da.part_o = h->part_o;
   da.part_ml = h->part_ml;
+  da.inv_rms = gemv ? h->inv_rms : nullptr;
   da.scale_log2 = scale_log2(c.head_dim);
   QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
+  const float* attn = static_cast<const float*>(h->attn);
+  const bf16* wo = static_cast<const bf16*>(w.wo);
   QL_STAGE(h, QL_STAGE_O_PROJ, s,
-           QL_HIP(ql_skinny_resid_f32(static_cast<const float*>(h->attn), B,
-                                      static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
-                                      s)));
+           QL_HIP(gemv ? ql_gemv_resid_f32(attn, B, wo, c.d, h->q_dim, x, h->r, s)
+                       : ql_skinny_resid_f32(attn, B, wo, c.d, h->q_dim, x, h->r, s)));
   return ffn_dense_or_moe(h, B, true, y, s);
 }
 
