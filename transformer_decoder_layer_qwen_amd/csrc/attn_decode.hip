@@ -5,33 +5,33 @@
 // causal halving for the single query; §05.2: the Hq/Hkv query heads of a
 // group read the same K/V bytes, so the group pays for them once.)
 //
-// Split-K: grid (splits, Hkv, B), 4 or 8 waves per block. A block reads
-// one key range of one KV head once and serves all G = Hq/Hkv query heads of
-// the group; its waves take 16-key tiles round-robin, each keeping the next
-// tile's loads in flight while it works on the current one:
+// One wave per (key split, KV head, sequence). The wave reads its key range of
+// one KV head once and serves all G = Hq/Hkv query heads of the group, 16 keys
+// (a tile) at a time, with the next tile's loads in flight during the current
+// tile's arithmetic:
 //   * scores: S^T[key][head] = K Q^T with 16x16x32 MFMAs, K rows loaded
 //     straight from the cache with 16-byte loads (A operand), the G queries
 //     padded to 16 columns (B operand, held in registers);
 //   * online softmax per head (column): max over 16 keys = 4 registers and
-//     two lane exchanges;
-//   * P V on the vector ALUs: lane (dh piece of 8, key sub-group) loads its
-//     V rows with 16-byte loads and accumulates G x 8 fp32 outputs; P and the
-//     per-head rescale factors go through a per-wave LDS scratch.
-// The waves merge in LDS. With one split the block writes the normalised
-// output; otherwise it writes an unnormalised partial (m, l, o[128]) per head
-// and a small combine kernel merges the splits (a cross-block merge inside
-// the kernel would need device-scope fences, which write back and invalidate
-// the whole L2 of the XCD on this GPU and cost far more than a launch).
+//     two lane exchanges; P goes through LDS;
+//   * P V on the vector ALUs: lane (dh piece col of 8 values, head group grp)
+//     owns heads grp, grp + 4, ... and sums over all 16 keys of the tile, so
+//     no cross-lane reduction is needed at the end.
+// With one split the wave writes the normalised output; otherwise it writes an
+// unnormalised partial (m, l, o[128]) per head and the combine kernel merges
+// the splits. (A merge inside the kernel would need device-scope fences,
+// which write back and invalidate the whole L2 of the XCD on this GPU and cost
+// far more than a second launch.) Short caches get one tile per wave, so every
+// K/V byte a wave needs is requested when the wave starts.
 //
 // Prologue (fused QK-norm / RoPE / cache append): the Q/K/V projection hands
-// over raw sums of (x * gamma1) W^T, and 1/rms of x (or the block computes it
-// from x). Each block forms q for its G heads (scale, bias, QK-norm,
-// rotate_half RoPE at position cache_len + pos_offset) and keeps them in LDS;
-// the block whose key range contains the new row also forms that row's k and
-// v, appends them to the cache and uses them from LDS ("Qwen2.5-7B 结构拆解"
-// §09.1; "推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §5, §6, §12).
-// The cache, K/V tile, projection and bias loads are all issued before the
-// prologue's arithmetic.
+// over raw sums of (x * gamma1) W^T, and 1/rms of x (or the wave computes it
+// from x). The wave forms q for its G heads (scale, bias, QK-norm,
+// rotate_half RoPE at position cache_len + pos_offset) into LDS; the wave
+// whose key range contains the new row also forms that row's k and v, appends
+// them to the cache and uses them from LDS ("Qwen2.5-7B 结构拆解" §09.1;
+// "推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §5, §6, §12). All cache,
+// projection, bias and norm loads are issued before any is waited on.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,22 +39,16 @@ namespace {
 
 constexpr int kDh = 128;
 
-// NW waves per block (4 or 8); wave w takes keys kbeg + 16 w + 16 NW i.
-template <int G, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeArgs p) {
-  constexpr int kQS = 16 / NW;            // query-head slots per wave in the prologue
-  __shared__ float p_lds[NW][16 * 16];    // per wave: P[key 16][head 16]
-  __shared__ float a_lds[NW][16];         // per wave: rescale per head
-  __shared__ float w_o[NW][G * kDh];      // cross-wave partial outputs
-  __shared__ float w_m[NW][16];
-  __shared__ float w_l[NW][16];
-  __shared__ __attribute__((aligned(16))) bf16 q_lds[16][kDh];    // rows >= G stay zero
-  __shared__ __attribute__((aligned(16))) bf16 kv_new[2][kDh];    // appended K and V row
-  __shared__ float red[NW];
+template <int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attn_decode_kernel(const AttnDecodeArgs p) {
+  constexpr int HPL = (G + 3) / 4;  // heads per lane in P V
+  __shared__ float p_lds[16 * 16];  // P[key 16][head 16]
+  __shared__ float a_lds[16];       // per-head rescale, then per-head l
+  __shared__ __attribute__((aligned(16))) bf16 q_lds[16][kDh];  // rows >= G stay zero
+  __shared__ __attribute__((aligned(16))) bf16 kv_new[2][kDh];  // appended K and V row
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[16][kDh];  // the tile's V rows
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int col = lane & 15;
   const int grp = lane >> 4;
   const int split = blockIdx.x;
@@ -63,7 +57,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
 
   // ---- every load goes out before any of them is waited on ----
   // Nothing here depends on cache_len[b]: the first tile is loaded up to the
-  // split's end within T_max and masked once the length is known, the
+  // split's end within T_max and masked once the length is known; the
   // projection / bias / norm loads are unconditional (absent biases and norms
   // read a harmless valid address and are masked to 0 / 1).
   const int L = p.cache_len[b];
@@ -73,8 +67,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
   const bf16* kb_ = p.k_cache + (size_t)b * p.T_max * row_stride + g * kDh;
   const bf16* vb_ = p.v_cache + (size_t)b * p.T_max * row_stride + g * kDh;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  // A wave's tile: keys k0 .. k0+15. K: lane (key col, k-group grp) loads dh
-  // [32 s + 8 grp, +8) of key k0 + col; V: keys k0 + 4 grp + j, dh piece col.
+  // tile at key k0: K lane (key col, k-group grp) holds dh [32 s + 8 grp, +8)
+  // of key k0 + col; V lane holds dh piece col of keys k0 + 4 grp + j
   auto load_tile = [&](int k0, int lim, u32x4 (&kt)[4], u32x4 (&vt)[4]) {
     const int krow = k0 + col;
     const bool kv = krow < lim;
@@ -90,24 +84,20 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
     }
   };
   u32x4 kcur[4], vcur[4];
-  load_tile(kbeg + 16 * wave, kcap, kcur, vcur);
+  load_tile(kbeg, kcap, kcur, vcur);
 
   const int qd = p.n_q_heads * kDh;
   const int kvd = p.n_kv_heads * kDh;
   const float* raw = p.qkv_raw + (size_t)b * p.ld_raw;
-  // slots 0 .. kQS-1: query heads wave + NW i of the group; kQS, kQS+1: the new K and V row
-  constexpr int kSlots = kQS + 2;
-  float hv[kSlots][2], hb[kSlots][2];
+  // slots 0 .. G-1: the group's query heads; G, G+1: the new K and V row
+  float hv[G + 2][2], hb[G + 2][2];
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    const int hq = g * G + wave + NW * i;
-    const int c0 = i < kQS ? (wave + NW * i < G ? hq * kDh : 0)
-                           : (i == kQS ? qd + g * kDh : qd + kvd + g * kDh);
+  for (int i = 0; i < G + 2; ++i) {
+    const int c0 = i < G ? (g * G + i) * kDh : (i == G ? qd + g * kDh : qd + kvd + g * kDh);
     hv[i][0] = raw[c0 + lane];
     hv[i][1] = raw[c0 + lane + 64];
-    const bf16* bias = i < kQS ? p.bq : (i == kQS ? p.bk : p.bv);
-    const int bc = i < kQS ? c0 : g * kDh;
-    const bf16* bsrc = bias ? bias + bc : p.x;
+    const bf16* bias = i < G ? p.bq : (i == G ? p.bk : p.bv);
+    const bf16* bsrc = bias ? bias + (i < G ? c0 : g * kDh) : p.x;
     const float b0 = to_f32(bsrc[lane]), b1 = to_f32(bsrc[lane + 64]);
     hb[i][0] = bias ? b0 : 0.f;
     hb[i][1] = bias ? b1 : 0.f;
@@ -118,43 +108,34 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
   const bf16* kgs = qkn ? p.k_norm_g : p.x;
   const float qg0r = to_f32(qgs[lane]), qg1r = to_f32(qgs[lane + 64]);
   const float kg0r = to_f32(kgs[lane]), kg1r = to_f32(kgs[lane + 64]);
-  const float qg0 = qkn ? qg0r : 1.f, qg1 = qkn ? qg1r : 1.f;
-  const float kg0 = qkn ? kg0r : 1.f, kg1 = qkn ? kg1r : 1.f;
+  const double omega = p.rope_omega[lane];
 
   const bool valid = L >= 0 && L < p.T_max;
   const int nkeys = valid ? L + 1 : 0;
   const int kend = min(kbeg + p.chunk, nkeys);
   const bool has_new = valid && kbeg <= L && L < kend;
-  // rows of the first tile past the live keys may hold anything (a NaN would
-  // survive a zero softmax weight in P V): zero their V
+  // first-tile rows past the live keys may hold anything (a NaN would survive
+  // a zero softmax weight in P V): zero their V
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if (kbeg + 16 * wave + 4 * grp + j >= kend) vcur[j] = zero4;
+    if (kbeg + 4 * grp + j >= kend) vcur[j] = zero4;
 
   // ---- prologue: RMSNorm1 scale, q heads, the appended K/V row ----
   float inv = inv_given;
   if (!p.inv_rms) {
     const bf16* xr = p.x + (size_t)b * p.d;
     float ss = 0.f;
-    for (int c = tid * 8; c < p.d; c += NW * 64 * 8) {
+    for (int c = lane * 8; c < p.d; c += 64 * 8) {
       float f[8];
       unpack8(load_bf16x8(xr + c), f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
     }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    float t = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) t += red[w];
-    inv = 1.0f / sqrtf(t / (float)p.d + p.eps);
+    inv = 1.0f / sqrtf(wave_sum(ss) / (float)p.d + p.eps);
   }
   float sn, cs;
   {
-    const double pos = (double)L + (double)p.pos_offset;
-    const double omega = exp2(-2.0 * (double)lane / (double)kDh * log2((double)p.theta));
-    double ang = pos * omega;
+    double ang = ((double)L + (double)p.pos_offset) * omega;
     const double two_pi = 6.283185307179586476925286766559;
     ang -= two_pi * rint(ang / two_pi);
     sincosf((float)ang, &sn, &cs);
@@ -178,11 +159,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
     }
   };
 #pragma unroll
-  for (int i = 0; i < kQS; ++i) {
-    const int hh = wave + NW * i;
+  for (int hh = 0; hh < 16; ++hh) {
     float r0 = 0.f, r1 = 0.f;
     if (hh < G) {
-      head_vec(i, qkn, qg0, qg1, true, r0, r1);
+      head_vec(hh, qkn, qg0r, qg1r, true, r0, r1);
       if (split == 0 && p.q_out) {
         const int hq = g * G + hh;
         const float nv = valid ? 0.f : __builtin_nanf("");
@@ -193,10 +173,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
     q_lds[hh][lane] = (bf16)r0;
     q_lds[hh][lane + 64] = (bf16)r1;
   }
-  if (has_new && wave == 0) {
+  if (has_new) {
     float k0, k1, v0, v1;
-    head_vec(kQS, qkn, kg0, kg1, true, k0, k1);
-    head_vec(kQS + 1, false, 1.f, 1.f, false, v0, v1);
+    head_vec(G, qkn, kg0r, kg1r, true, k0, k1);
+    head_vec(G + 1, false, 1.f, 1.f, false, v0, v1);
     const size_t crow = ((size_t)b * p.T_max + L) * kvd + g * kDh;
     const bf16 bk0 = (bf16)k0, bk1 = (bf16)k1, bv0 = (bf16)v0, bv1 = (bf16)v1;
     p.k_cache_w[crow + lane] = bk0;
@@ -208,25 +188,28 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
     kv_new[1][lane] = bv0;
     kv_new[1][lane + 64] = bv1;
   }
-  __syncthreads();
+  // LDS traffic of one wave is processed in order; the barrier only keeps the
+  // compiler from moving LDS accesses across it
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
   // Q^T fragments: lane (head col, group grp) holds dh [32s + 8grp, +8)
   bf16x8 qf[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(&q_lds[col][32 * s + 8 * grp]);
 
-  float acc[G][8];
+  float acc[HPL][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int i = 0; i < HPL; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
   float m_run = -INFINITY;  // for head `col`
   float l_run = 0.f;
 
-  for (int k0 = kbeg + 16 * wave; k0 < kend; k0 += 16 * NW) {
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
     // the next tile's loads overlap this tile's arithmetic
     u32x4 knext[4], vnext[4];
-    load_tile(k0 + 16 * NW, kend, knext, vnext);
+    load_tile(k0 + 16, kend, knext, vnext);
     // the appended row comes from LDS (its cache write may still be in flight)
     if (has_new) {
       if (k0 + col == L) {
@@ -238,6 +221,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
       for (int j = 0; j < 4; ++j)
         if (k0 + 4 * grp + j == L) vcur[j] = *reinterpret_cast<const u32x4*>(&kv_new[1][col * 8]);
     }
+    // V rows to LDS: row 4 grp + j, dh piece col
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&v_lds[4 * grp + j][col * 8]) = vcur[j];
     // scores for keys k0 .. k0+15
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -261,31 +247,40 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
     for (int r = 0; r < 4; ++r) {
       const float pv = exp2f(sc[r] - m_new);
       ps += pv;
-      p_lds[wave][(4 * grp + r) * 16 + col] = pv;
+      p_lds[(4 * grp + r) * 16 + col] = pv;
     }
     ps += __shfl_xor(ps, 16, kWave);
     ps += __shfl_xor(ps, 32, kWave);
     l_run = l_run * alpha + ps;
-    if (grp == 0) a_lds[wave][col] = alpha;
+    if (grp == 0) a_lds[col] = alpha;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = a_lds[wave][h];
+    for (int i = 0; i < HPL; ++i) {
+      // heads >= G (padding columns) are computed but never stored; reading
+      // them unconditionally keeps the loop free of divergent loads
+      const int h = grp + 4 * i;
+      const float al = a_lds[h];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
+      for (int e = 0; e < 8; ++e) acc[i][e] *= al;
     }
+    // four keys at a time (the scheduling barrier bounds how many LDS reads
+    // the compiler hoists, and with them the register count)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v[8];
-      unpack8(*reinterpret_cast<const bf16x8*>(&vcur[j]), v);
-      const float* pr = &p_lds[wave][(4 * grp + j) * 16];
+    for (int kq = 0; kq < 16; kq += 4) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pw = pr[h];
+      for (int key = kq; key < kq + 4; ++key) {
+        float v[8];
+        unpack8(*reinterpret_cast<const bf16x8*>(&v_lds[key][col * 8]), v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] += pw * v[e];
+        for (int i = 0; i < HPL; ++i) {
+          const int h = grp + 4 * i;
+          const float pw = p_lds[key * 16 + h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[i][e] += pw * v[e];
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -296,122 +291,153 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(const AttnDecodeAr
     }
   }
 
-  // reduce the 4 key sub-groups of the wave (lanes col, col+16, col+32, col+48)
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[h][e];
-        v += __shfl_xor(v, 16, kWave);
-        v += __shfl_xor(v, 32, kWave);
-        acc[h][e] = v;
-      }
+  // per-head m and l (held by lanes grp 0, col = head) to every lane via LDS
   if (grp == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w_o[wave][h * kDh + col * 8 + e] = acc[h][e];
-    w_m[wave][col] = m_run;
-    w_l[wave][col] = l_run;
+    a_lds[col] = l_run;
+    p_lds[col] = m_run;
   }
-  __syncthreads();
-  // merge the waves; write this split's partial for each head of the group
-  for (int i = tid; i < G * kDh; i += NW * 64) {
-    const int h = i / kDh;
-    const int d = i % kDh;
-    float M = -INFINITY;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, w_m[w][h]);
-    float o = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        if (w_m[w][h] == -INFINITY) continue;
-        const float f = exp2f(w_m[w][h] - M);
-        o += w_o[w][h * kDh + d] * f;
-        l += w_l[w][h] * f;
-      }
-    }
+  for (int i = 0; i < HPL; ++i) {
+    const int h = grp + 4 * i;
+    if (h >= G) continue;
+    const int hq = g * G + h;
     if (p.nsplit == 1) {  // the only split: normalise here
-      p.out[(size_t)b * p.ldo + (size_t)(g * G + h) * kDh + d] =
-          valid ? o / l : __builtin_nanf("");
-      continue;
-    }
-    const size_t slot = ((size_t)b * p.n_q_heads + g * G + h) * p.nsplit + split;
-    p.part_o[slot * kDh + d] = o;
-    if (d == 0) {
-      p.part_ml[slot * 2 + 0] = M;
-      p.part_ml[slot * 2 + 1] = l;
+      const float rl = valid ? 1.0f / a_lds[h] : __builtin_nanf("");
+      float* o = p.out + (size_t)b * p.ldo + (size_t)hq * kDh + col * 8;
+      f32x4 o0, o1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o0[e] = acc[i][e] * rl;
+        o1[e] = acc[i][e + 4] * rl;
+      }
+      *reinterpret_cast<f32x4*>(o) = o0;
+      *reinterpret_cast<f32x4*>(o + 4) = o1;
+    } else {
+      const size_t slot = ((size_t)b * p.n_q_heads + hq) * p.nsplit + split;
+      float* o = p.part_o + slot * kDh + col * 8;
+      f32x4 o0, o1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o0[e] = acc[i][e];
+        o1[e] = acc[i][e + 4];
+      }
+      *reinterpret_cast<f32x4*>(o) = o0;
+      *reinterpret_cast<f32x4*>(o + 4) = o1;
+      if (col == 0) {
+        p.part_ml[slot * 2 + 0] = p_lds[h];
+        p.part_ml[slot * 2 + 1] = a_lds[h];
+      }
     }
   }
 }
 
-// Merge the splits of one (sequence, head): every partial is loaded at once
-// (the loads are independent), the maxima and sums go through LDS.
-__global__ __launch_bounds__(128) void attn_decode_combine_kernel(const AttnDecodeArgs p) {
+// Merge the splits of one (sequence, head). 512 threads: thread t owns output
+// element t % 128 and the splits s = t / 128 (mod 4). The partial outputs of
+// the first 128 splits and all split maxima / sums are requested together, so
+// the merge waits on memory once; weights go through LDS.
+constexpr int kCombineThreads = 512;
+constexpr int kCombineBatch = 32;  // partial outputs in flight per thread
+__global__ __launch_bounds__(kCombineThreads) void attn_decode_combine_kernel(const AttnDecodeArgs p) {
+  constexpr int kQ = kCombineThreads / kDh;  // split residues per element
+  constexpr int kW = kCombineThreads / 64;
   __shared__ float s_m[kMaxDecodeSplits], s_l[kMaxDecodeSplits];
+  __shared__ float red[kW];
+  __shared__ float qsum[kQ][kDh];
   const int bh = blockIdx.x;  // b * Hq + head
   const int b = bh / p.n_q_heads;
-  const int d = threadIdx.x;
-  const size_t base = (size_t)bh * p.nsplit;
-  float ov[kMaxDecodeSplits];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int d = t & (kDh - 1);
+  const int q = t / kDh;
+  const int ns = p.nsplit;
+  const size_t base = (size_t)bh * ns;
+  float ov[kCombineBatch];
 #pragma unroll
-  for (int s = 0; s < kMaxDecodeSplits; ++s)
-    ov[s] = s < p.nsplit ? p.part_o[(base + s) * kDh + d] : 0.f;
-  if (d < p.nsplit) {
-    s_m[d] = p.part_ml[(base + d) * 2];
-    s_l[d] = p.part_ml[(base + d) * 2 + 1];
+  for (int u = 0; u < kCombineBatch; ++u) {
+    const int s = q + kQ * u;
+    ov[u] = s < ns ? p.part_o[(base + s) * kDh + d] : 0.f;
+  }
+  float mx = -INFINITY;
+  for (int s = t; s < ns; s += kCombineThreads) {
+    const float m = p.part_ml[(base + s) * 2];
+    s_m[s] = m;
+    s_l[s] = p.part_ml[(base + s) * 2 + 1];
+    mx = fmaxf(mx, m);
   }
   const int L = p.cache_len[b];
-  const bool valid = L >= 0 && L < p.T_max;
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, s_m[s]);
-  float o = 0.f, l = 0.f;
+  float M = red[0];
 #pragma unroll
-  for (int s = 0; s < kMaxDecodeSplits; ++s) {
-    if (s >= p.nsplit) break;
+  for (int w = 1; w < kW; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+  // split weights (in place of the maxima) and the total l
+  float lsum = 0.f;
+  for (int s = t; s < ns; s += kCombineThreads) {
     const float m = s_m[s];
-    if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    o += ov[s] * f;
-    l += s_l[s] * f;
+    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
+    s_m[s] = w;
+    lsum += w * s_l[s];
   }
-  const float out = valid ? o / l : __builtin_nanf("");
-  p.out[(size_t)b * p.ldo + (size_t)(bh % p.n_q_heads) * kDh + d] = out;
-}
-
-template <int G>
-hipError_t launch_g(const AttnDecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.nsplit, a.n_kv_heads, a.B);
-  switch (a.waves) {
-    case 4: hipLaunchKernelGGL((attn_decode_kernel<G, 4>), grid, dim3(256), 0, s, a); break;
-    case 8:
-      if constexpr (G <= 8) {
-        hipLaunchKernelGGL((attn_decode_kernel<G, 8>), grid, dim3(512), 0, s, a);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  lsum = wave_sum(lsum);
+  if (lane == 0) red[wave] = lsum;
+  __syncthreads();
+  float l = 0.f;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) l += red[w];
+  float o = 0.f;
+#pragma unroll
+  for (int u = 0; u < kCombineBatch; ++u) {
+    const int s = q + kQ * u;
+    if (s < ns) o += ov[u] * s_m[s];
   }
-  return hipGetLastError();
+  for (int s0 = q + kQ * kCombineBatch; s0 < ns; s0 += kQ * kCombineBatch) {
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int s = s0 + kQ * u;
+      ov[u] = s < ns ? p.part_o[(base + s) * kDh + d] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int s = s0 + kQ * u;
+      if (s < ns) o += ov[u] * s_m[s];
+    }
+  }
+  qsum[q][d] = o;
+  __syncthreads();
+  if (q == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) tot += qsum[i][d];
+    const bool valid = L >= 0 && L < p.T_max;
+    p.out[(size_t)b * p.ldo + (size_t)(bh % p.n_q_heads) * kDh + d] =
+        valid ? tot / l : __builtin_nanf("");
+  }
 }
 
 }  // namespace
 
 hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  hipError_t e;
+  if (a.nsplit < 1 || a.nsplit > kMaxDecodeSplits) return hipErrorInvalidValue;
+  const dim3 grid(a.nsplit, a.n_kv_heads, a.B);
   switch (a.n_q_heads / a.n_kv_heads) {
-#define QL_G(V) \
-  case V: e = launch_g<V>(a, s); break;
+#define QL_G(V)                                                                 \
+  case V:                                                                       \
+    hipLaunchKernelGGL(attn_decode_kernel<V>, grid, dim3(64), 0, s, a);        \
+    break;
     QL_G(1) QL_G(2) QL_G(3) QL_G(4) QL_G(5) QL_G(6) QL_G(7) QL_G(8)
     QL_G(9) QL_G(10) QL_G(11) QL_G(12) QL_G(13) QL_G(14) QL_G(15) QL_G(16)
 #undef QL_G
     default:
       return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q_heads), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q_heads), dim3(kCombineThreads),
+                     0, s, a);
   return hipGetLastError();
 }

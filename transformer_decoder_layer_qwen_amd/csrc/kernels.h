@@ -146,11 +146,11 @@ struct AttnDecodeArgs {
   int chunk, nsplit;     // keys per split, number of splits
   float* part_o;         // [B, Hq, nsplit, dh]
   float* part_ml;        // [B, Hq, nsplit, 2]
-  int waves;             // waves per block: 4 or 8 (8 needs G <= 8)
   const float* inv_rms;  // [B] RMSNorm1 1/rms of x, or NULL (computed from x)
+  const double* rope_omega;  // [head_dim / 2] RoPE frequencies theta^(-2i/dh)
   float scale_log2;
 };
-constexpr int kMaxDecodeSplits = 32;  // nsplit <= this
+constexpr int kMaxDecodeSplits = 1024;  // nsplit <= this
 hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s);
 hipError_t ql_attn_decode_f32(const AttnDecodeArgs& a, hipStream_t s);
 

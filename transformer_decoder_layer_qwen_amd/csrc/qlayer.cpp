@@ -18,6 +18,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 #include <string>
 
 #include "kernels.h"
@@ -64,6 +65,7 @@ struct ql_handle {
   float* part_o;
   float* part_ml;
   float* inv_rms;   // [rows] RMSNorm1 1/rms handed from the QKV GEMV to attention
+  double* rope_omega;  // [head_dim / 2] RoPE frequencies
   float* logits;
   int* idx;
   float* topw;
@@ -157,6 +159,23 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
   return QL_OK;
 }
 
+// Decode attention launch shape: about kDecodeTargetWaves waves over
+// (key split, KV head, sequence), at least one 16-key tile per split.
+constexpr int kDecodeTargetWaves = 2048;
+int decode_splits(int groups, int T_max, int* chunk) {
+  int ns = (kDecodeTargetWaves + groups - 1) / groups;
+  ns = std::max(1, std::min({ns, kMaxDecodeSplits, (T_max + 15) / 16}));
+  int ch = (T_max + ns - 1) / ns;
+  ch = (ch + 15) / 16 * 16;
+  *chunk = ch;
+  return (T_max + ch - 1) / ch;
+}
+// Upper bound of B * nsplit over every batch size (sizes the split partials).
+size_t decode_split_slots(const ql_config& c) {
+  const int hkv = std::max(c.n_kv_heads, 1);
+  return (size_t)std::max(c.max_batch, 0) + (kDecodeTargetWaves + hkv - 1) / hkv;
+}
+
 struct Carve {
   char* base;
   size_t off = 0;
@@ -181,8 +200,10 @@ size_t layout(ql_handle* h, char* base) {
   h->r = k.take<float>(N * c.d * 4);
   h->z = k.take<void>(N * c.d * es);
   const size_t B = (size_t)std::max(c.max_batch, 0);
-  h->part_o = k.take<float>(B * c.n_q_heads * kMaxDecodeSplits * c.head_dim * 4);
-  h->part_ml = k.take<float>(B * c.n_q_heads * kMaxDecodeSplits * 2 * 4);
+  const size_t slots = decode_split_slots(c);
+  h->part_o = k.take<float>(slots * c.n_q_heads * c.head_dim * 4);
+  h->part_ml = k.take<float>(slots * c.n_q_heads * 2 * 4);
+  h->rope_omega = k.take<double>((size_t)std::max(c.head_dim / 2, 1) * 8);
   h->inv_rms = k.take<float>(N * 4);
   if (c.n_experts > 0) {
     const size_t E = c.n_experts, K = c.top_k, NK = N * K;
@@ -442,21 +463,13 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
   da.n_q_heads = c.n_q_heads;
   da.n_kv_heads = c.n_kv_heads;
   da.head_dim = c.head_dim;
-  // Launch shape: ~512 blocks over (split, KV head, sequence); with few
-  // groups the blocks get 8 waves (one 16-key tile per wave for short caches:
-  // every K/V load is issued at kernel start), else 4. The split length is a
-  // whole number of tiles per wave.
-  const int groups = B * c.n_kv_heads;
-  const int waves = (groups <= 16 && h->G <= 8) ? 8 : 4;
-  int nsplit = std::max(1, std::min(kMaxDecodeSplits, (512 + groups - 1) / groups));
-  int chunk = (T_max + nsplit - 1) / nsplit;
-  chunk = (chunk + 16 * waves - 1) / (16 * waves) * (16 * waves);
-  nsplit = (T_max + chunk - 1) / chunk;
-  da.waves = waves;
+  int chunk = 0;
+  const int nsplit = decode_splits(B * c.n_kv_heads, T_max, &chunk);
   da.chunk = chunk;
   da.nsplit = nsplit;
   da.part_o = h->part_o;
   da.part_ml = h->part_ml;
+  da.rope_omega = h->rope_omega;
   da.inv_rms = gemv ? h->inv_rms : nullptr;
   da.scale_log2 = scale_log2(c.head_dim);
   QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
@@ -586,6 +599,17 @@ ql_status qlayer_create(const ql_config* cfg, const ql_weights* w, ql_handle** o
     return fail(QL_ENOMEM, "workspace of %zu bytes: %s", h->ws_bytes, hipGetErrorString(e));
   }
   layout(h, h->ws);
+  if (cfg->dtype == QL_BF16) {
+    std::vector<double> om(cfg->head_dim / 2);
+    for (int i = 0; i < cfg->head_dim / 2; ++i)
+      om[i] = std::pow((double)cfg->rope_theta, -2.0 * i / (double)cfg->head_dim);
+    e = hipMemcpy(h->rope_omega, om.data(), om.size() * sizeof(double), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      hipFree(h->ws);
+      delete h;
+      return fail(QL_EHIP, "RoPE table upload: %s", hipGetErrorString(e));
+    }
+  }
   *out = h;
   return QL_OK;
 }
