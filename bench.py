@@ -277,6 +277,23 @@ def time_stage(setup, hip, stage, steps):
 GEMV_MAX_ROWS = 4   # dense decode with this many rows or fewer folds RMSNorm2 into gate/up
 
 
+def time_empty_span(hip, steps):
+    """Mean span of two events recorded back to back behind the same spin
+    kernel: the fixed cost that every stage span carries on top of its
+    kernels. Stage times below are reported with it subtracted."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = hip.create(2 * steps)
+    for i in range(steps):
+        torch.cuda._sleep(SPACER_CYCLES)
+        hip.record(evs[2 * i], stream)
+        hip.record(evs[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    tot = sum(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps))
+    hip.destroy(evs)
+    return tot / steps
+
+
 def stages_of(cfg, kind, batch):
     # decode fuses RMSNorm1 into the QKV projection and the QK-norm / RoPE /
     # cache append into the attention kernel
@@ -289,13 +306,32 @@ def stages_of(cfg, kind, batch):
     return s
 
 
+# HBM bytes per launch from rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), scaled by what the same counters read for a plain 256 MiB device copy
+# (FETCH_SIZE 131085.4 KiB, WRITE_SIZE 262144.0 KiB). Keyed by (workload, stage); an entry
+# is only valid for the kernel source it was taken on, named beside it.
+PMC_FETCH_SCALE = 262144.0 / 131085.4
+PMC_WRITE_SCALE = 262144.0 / 262144.0
+PMC_TRAFFIC_KIB = {
+    # profiles/gemv_gate_up_qwen25_7b_decode_b1_hbm_counters.txt (csrc/gemv.hip as of e72cee5)
+    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132731.3, 296.2),
+}
+
+
+def pmc_traffic(wl, stage):
+    t = PMC_TRAFFIC_KIB.get((wl.label, stage))
+    if t is None:
+        return None
+    return int((t[0] * PMC_FETCH_SCALE + t[1] * PMC_WRITE_SCALE) * 1024)
+
+
 def roofline_entry(cfg, wl, stage, ms):
     fl, by = stage_work(cfg, wl, stage, cache_len=wl.seq)
     hbm_bound = wl.kind == "decode" or fl / max(by, 1) < 315
     if hbm_bound:
         ach = by / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": pmc_traffic(wl, stage),
                 "algorithmic_bytes": int(by), "kernel_ms": round(ms, 5), "stage": stage}
     ach = fl / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -321,9 +357,11 @@ def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_g
         out["layer_frac_hbm"] = round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if breakdown:
         st = {}
+        empty = time_empty_span(hip, max(stage_steps, 8))
         for s in stages_of(cfg, wl.kind, wl.batch):
-            st[s] = round(time_stage(setup, hip, s, stage_steps), 5)
+            st[s] = round(max(time_stage(setup, hip, s, stage_steps) - empty, 1e-6), 5)
         out["stage_ms"] = st
+        out["event_span_overhead_ms"] = round(empty, 5)
         dom = max(st, key=st.get)
         out["dominant"] = roofline_entry(cfg, wl, dom, st[dom])
         gemms = [s for s in ("qkv", "o_proj", "gate_up", "down", "expert_gate_up",
@@ -379,16 +417,28 @@ def main():
     ap.add_argument("--eager", action="store_true", help="no HIP graph replay")
     ap.add_argument("--only", default=None,
                     help="time one workload CID:INDEX of the config table instead of the headline")
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (a known-size reference "
+                         "for the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer's data-parallel shards are independent, see the design notes)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: "
+              "data-parallel ranks each run their own sequences with no exchange, so the "
+              "per-GPU kernels are exactly the ones measured here", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_ref:
+        n = args.copy_ref << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy reference: 5 copies of {n} bytes")
+        return
     hip = HipEvents()
 
     cid, wl = 2, configs.WORKLOADS[2][0]

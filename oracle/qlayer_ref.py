@@ -19,8 +19,7 @@ Sources (page title, then the section each function follows):
 [P4] "Transformer 的 Infra 视角" (inference-learning-path.pages.dev)
 [P5] "第七章 模型容量与参数量推导" (starbuckoverflow.cn)
 
-Readings where the pages are silent or disagree (each is also listed in the
-design notes of the repository):
+Readings where the pages are silent or disagree:
 
 * RoPE pairs coordinate i with i + dh/2 (rotate_half, [P3 §6]); [P1 §05.3]
   pairs (2i, 2i+1). ``rope_adjacent`` keeps the [P1] form only to pin the
