@@ -14,8 +14,8 @@
 // need only one cross-lane exchange per tile. P^T stays in registers and is
 // the B operand of O^T += V^T P^T; V is stored transposed in LDS (pitch 68
 // elements, which spreads the 16 rows read together over distinct banks).
-// K rows keep 16-byte chunks XOR-swizzled by (key & 7). The output stays fp32
-// (it feeds the O projection as a bf16 hi + lo pair).
+// K rows keep 16-byte chunks XOR-swizzled by (key & 7). The fp32 output is
+// stored as a bf16 pair hi + lo, the form in which the O projection reads it.
 #include "common.h"
 #include "kernels.h"
 
@@ -193,14 +193,22 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (my_q >= S) return;
   const float inv = 1.0f / l_tot;
-  float* orow = p.out + (size_t)(b * S + my_q) * p.ldo + h * kDh;
+  // the fp32 output as a bf16 pair: hi = RNE(o) at column c, lo = RNE(o - hi)
+  // at column c + lo_off (the O projection multiplies both)
+  bf16* orow = p.out + (size_t)(b * S + my_q) * p.ldo + h * kDh;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const f32x4 v = {acc_o[dt][4 * c + 0] * inv, acc_o[dt][4 * c + 1] * inv,
-                       acc_o[dt][4 * c + 2] * inv, acc_o[dt][4 * c + 3] * inv};
-      *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * c + 4 * hi) = v;
+      bf16x4 vh, vl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = acc_o[dt][4 * c + e] * inv;
+        vh[e] = (bf16)v;
+        vl[e] = (bf16)(v - (float)vh[e]);
+      }
+      *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * c + 4 * hi) = vh;
+      *reinterpret_cast<bf16x4*>(orow + p.lo_off + 32 * dt + 8 * c + 4 * hi) = vl;
     }
 }
 

@@ -1,0 +1,560 @@
+// Large-tile bf16 GEMM on MFMA for the prefill projections, C = A * B^T.
+//
+// A is [M, Ka] (token rows), B is [N, Kb] (a weight in the [out, in] storage
+// convention of "Qwen2.5-7B 结构拆解" §03.1); both K-contiguous. Token rows never
+// interact in a projection (§03.2 of the same page), so M = B*S rows form one
+// GEMM. Ka is Kb, or 2 Kb when A carries an fp32 activation as a bf16 pair
+// [hi | lo] (hi = RNE(a), lo = RNE(a - hi)): then the k loop runs over 2 Kb and
+// reads B at k mod Kb, which sums hi*W + lo*W with the activation kept to about
+// 16 significant bits. Used for the projections of the RMSNorm1 output and of
+// the attention output.
+//
+// Design (gfx950, wave64):
+// * tile 256 x 256 x 64; 4 or 8 waves, each owning 128 x 128 (or 128 x 64) of
+//   the tile as 32x32x16 MFMAs with fp32 accumulators.
+// * global -> LDS directly (global_load_lds_dwordx4: 16 B per lane, lane i
+//   writes 16 i bytes past a wave-uniform LDS base); each load instruction
+//   moves 8 whole 128-byte rows (full cache lines). Two stages: stage t+1 is
+//   requested while stage t is multiplied.
+// * LDS rows are 32 bf16 (4 chunks of 16 B), chunks XOR-swizzled by row (swz)
+//   so fragment reads are free of bank conflicts. A direct load cannot
+//   scatter, so each lane picks the global chunk that belongs at its fixed
+//   LDS slot.
+// * split-K over blockIdx.y when the tile grid alone is too small for the
+//   chip: each split writes an fp32 partial tile and a second kernel sums the
+//   partials and applies the epilogue.
+// * epilogue through LDS, half a tile at a time (the ring is reused): every
+//   thread then handles 8 consecutive columns of one row, so stores are
+//   16/32-byte contiguous and SwiGLU can pair a gate column with its up column.
+//
+// Epilogues (one rounding at the stored tensor):
+//   BIAS      out_f32 = acc (+ bias)            Q/K/V projection (+QKV bias)
+//   RESID_F32 out_f32 = resid_bf16 + acc        R = X + O W_O^T
+//   RESID_OUT out     = bf16(resid_f32 + acc)   Y = R + H W_down^T
+//   SWIGLU    out     = bf16(SiLU(g) * u)       B tile = [128 W_gate rows | 128 W_up rows]
+// With split-K each split stores its fp32 partial tile and the reduce kernel
+// applies the epilogue.
+// ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §4, §9, §10.)
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU };
+
+constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2;
+constexpr int kGroupM = 4;  // tile rows per L2 group
+constexpr int kStageBytes = (BM + BN) * BK * 2;       // 64 KiB
+constexpr int kChunks = (BM + BN) * BK / 8;            // 16-byte chunks per stage
+constexpr int kRowChunks = BK / 8;                     // chunks per LDS row
+constexpr int kPitch = BN + 4;                         // fp32 epilogue tile pitch
+constexpr int kEpiBytes = (BM / 2) * kPitch * 4;       // half a tile
+constexpr int kLdsBytes = NSTAGE * kStageBytes > kEpiBytes ? NSTAGE * kStageBytes : kEpiBytes;
+
+struct G2Args {
+  const bf16* A;
+  int lda, M, Ka;
+  const bf16* B;
+  const bf16* B2;  // BIAS: rows [seg1, seg2) come from B2, [seg2, N) from B3; SWIGLU: up
+  const bf16* B3;
+  int seg1, seg2;
+  int ldb, Kb;
+  int tiles_m, tiles_n, splits, ksteps_per_split;
+  float* out_f32;
+  bf16* out_bf16;
+  int ldo;
+  const bf16* bias;
+  const bf16* bias2;
+  const bf16* bias3;
+  const bf16* resid_bf16;
+  const float* resid_f32;
+  int ldr;
+  float* part;  // [splits][M][tiles_n * BN]
+};
+
+// LDS slot of chunk c of row r is c ^ swz(r). A 16-byte read by the lanes of
+// one MFMA fragment touches 16 consecutive rows (from a multiple of 16) at one
+// chunk; with 128-byte rows this puts them on 16 distinct 16-byte positions of
+// a 256-byte bank line, so the read is free of bank conflicts.
+QL_DEV int swz(int r) { return (r >> 1) & 7; }
+
+// Typed address-space casts for the direct-to-LDS load builtin.
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+QL_DEV void load_lds16(const bf16* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+QL_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// PART: write this split's fp32 partial tile instead of MODE's epilogue.
+// NW waves (4 or 8): waves are 2 (rows) x NW/2 (columns); a wave owns
+// 128 x (256 / (NW/2)) of the tile. With 8 waves two share each SIMD, so one
+// wave's MFMAs run while the other waits on LDS or the barrier.
+template <int MODE, bool PART, int NW, bool DMA>
+__global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) {
+  constexpr int NT = NW * 64;           // threads
+  constexpr int WNW = NW / 2;           // waves along N
+  constexpr int WCOLS = BN / WNW;       // columns per wave
+  constexpr int TJ = WCOLS / 32;        // 32-wide MFMA tiles per wave along N
+  constexpr int LPT = kChunks / NT;     // direct loads per thread per stage
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+
+  // XCD-aware tile order. Consecutive block ids go to the 8 XCDs round-robin,
+  // each XCD with its own L2; so block b works on item (b % 8) * chunk + b / 8
+  // of the work list, and every XCD walks a contiguous stretch of it. The list
+  // orders (split, tile) split-major, tiles in groups of kGroupM tile rows x
+  // all tile columns, column-major inside a group: the ~32 blocks an XCD runs
+  // at once share 4 A tiles and 8 B tiles, which its L2 then serves.
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int total = ntiles * p.splits;
+  const int chunk = (total + 7) / 8;
+  const int w = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
+  if (w >= total) return;
+  const int split = w / ntiles;
+  const int pid = w % ntiles;
+  const int group = pid / (kGroupM * p.tiles_n);
+  const int first_m = group * kGroupM;
+  const int gsize = min(p.tiles_m - first_m, kGroupM);
+  const int in_group = pid % (kGroupM * p.tiles_n);
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * BM;
+  const int rows_valid = min(BM, p.M - m0);
+  constexpr bool kDual = MODE == G2_SWIGLU;
+  const int n0 = tn * (kDual ? BN / 2 : BN);  // first output column of the tile
+
+  // QKV: a 256-column tile lies inside one of the three weight matrices
+  const bf16* Bw = p.B;
+  const bf16* bias = p.bias;
+  int nb = n0;
+  if constexpr (MODE == G2_BIAS) {
+    if (n0 >= p.seg2) {
+      Bw = p.B3;
+      bias = p.bias3;
+      nb = n0 - p.seg2;
+    } else if (n0 >= p.seg1) {
+      Bw = p.B2;
+      bias = p.bias2;
+      nb = n0 - p.seg1;
+    }
+  }
+
+  // Direct-load plan: per stage the block fills kChunks 16-byte LDS chunks (A
+  // first, then B); load j of wave w covers chunks (NW j + w) * 64 + lane, i.e.
+  // 8 whole 128-byte rows, each one full cache line of A or B.
+  const bf16* src[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) {
+    const int P = (NW * j + wave) * 64 + lane;
+    const int Q = P & (kChunks / 2 - 1);
+    const int row = Q / kRowChunks;
+    const int c = (Q % kRowChunks) ^ swz(row);
+    if (j < LPT / 2) {
+      const int rr = min(row, rows_valid - 1);  // rows past M re-read a valid row
+      src[j] = p.A + (size_t)(m0 + rr) * p.lda + c * 8;
+    } else {
+      const bf16* base;
+      if constexpr (kDual) {
+        base = row < BN / 2 ? p.B + (size_t)(n0 + row) * p.ldb
+                            : p.B2 + (size_t)(n0 + row - BN / 2) * p.ldb;
+      } else {
+        base = Bw + (size_t)(nb + row) * p.ldb;
+      }
+      src[j] = base + c * 8;
+    }
+  }
+  const int ks0 = split * p.ksteps_per_split;
+  const int nk = min(p.ksteps_per_split, p.Ka / BK - ks0);
+
+  auto issue = [&](int kt) {  // stage kt of this split -> ring slot kt % NSTAGE
+    const int ka = (ks0 + kt) * BK;
+    int kb = ka;
+    if (kb >= p.Kb) kb -= p.Kb;  // [hi | lo] A: B is read twice
+    char* slot = smem + (kt % NSTAGE) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j)
+      load_lds16(src[j] + (j < LPT / 2 ? ka : kb), slot + (NW * j + wave) * 1024);
+  };
+  // register-staged alternative: global -> VGPRs, later VGPRs -> LDS
+  u32x4 stg[DMA ? 1 : LPT];
+  auto gload = [&](int kt) {
+    const int ka = (ks0 + kt) * BK;
+    int kb = ka;
+    if (kb >= p.Kb) kb -= p.Kb;
+#pragma unroll
+    for (int j = 0; j < (DMA ? 0 : LPT); ++j)
+      stg[j] = *reinterpret_cast<const u32x4*>(src[j] + (j < LPT / 2 ? ka : kb));
+  };
+  auto swrite = [&](int kt) {
+    char* slot = smem + (kt % NSTAGE) * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < (DMA ? 0 : LPT); ++j)
+      *reinterpret_cast<u32x4*>(slot + (NW * j + wave) * 1024 + lane * 16) = stg[j];
+  };
+
+  f32x16 acc[4][TJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment read offsets (bytes within a stage) for k16 step ks
+  const int fr = lane & 31;
+  const int fk = lane >> 5;
+  constexpr int KS = BK / 16;  // 16-deep MFMA steps per stage
+  int aoff[KS][4], boff[KS][TJ];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = 2 * ks + fk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wm * 128 + 32 * i + fr;
+      aoff[ks][i] = (ra * kRowChunks + (c ^ swz(ra))) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int rb = wn * WCOLS + 32 * j + fr;
+      boff[ks][j] = kStageBytes / 2 + (rb * kRowChunks + (c ^ swz(rb))) * 16;
+    }
+  }
+
+  // One stage: the fragments of k steps (0, 1) are read, then those of (2, 3)
+  // are requested before the MFMAs of (0, 1) run, so only the first reads of
+  // a stage sit in front of its MFMAs.
+  auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][4], bf16x8 (&bfr)[2][TJ]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
+    }
+  };
+  auto mma2 = [&](const bf16x8 (&af)[2][4], const bf16x8 (&bfr)[2][TJ]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+  };
+  static_assert(KS == 4, "two halves of two k steps per stage");
+  auto compute = [&](int kt) {
+    const char* st = smem + (kt % NSTAGE) * kStageBytes;
+    bf16x8 a0[2][4], b0[2][TJ], a1[2][4], b1[2][TJ];
+    read2(st, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    read2(st, 2, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma2(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma2(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (DMA) {
+    // Two stages; stage kt+1 is requested right after the barrier that
+    // publishes stage kt and lands while stage kt is multiplied.
+    if (nk > 0) issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();  // this wave's part of stage kt (the only stage in flight)
+      // every wave's part of stage kt has landed and every wave is done with
+      // the other slot; the acquire fence keeps the LDS reads below it
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (kt + 1 < nk) issue(kt + 1);
+      compute(kt);
+    }
+  } else {
+    // Registers hold stage kt+1 while stage kt is multiplied; they go to the
+    // other LDS slot after the MFMAs, then stage kt+2 is requested.
+    if (nk > 0) {
+      gload(0);
+      swrite(0);
+    }
+    if (nk > 1) gload(1);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      compute(kt);
+      if (kt + 1 < nk) swrite(kt + 1);
+      if (kt + 2 < nk) gload(kt + 2);
+      __syncthreads();
+    }
+  }
+  __syncthreads();  // the ring is reused for the epilogue
+
+  // ---- epilogue: half a tile (one wm row of waves) at a time through LDS ----
+  float* C = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            C[row * kPitch + wn * WCOLS + 32 * j + (lane & 31)] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+    const int rbase = half * 128;
+    if constexpr (PART) {
+      const int ldp = p.tiles_n * BN;
+      float* dst = p.part + (size_t)split * p.M * ldp;
+      const int seg = tid & 31;
+      for (int r = tid >> 5; r < 128; r += NT / 32) {
+        if (rbase + r >= rows_valid) break;
+        const float* c = C + r * kPitch + seg * 8;
+        float* o = dst + (size_t)(m0 + rbase + r) * ldp + tn * BN + seg * 8;
+        *reinterpret_cast<f32x4*>(o) = *reinterpret_cast<const f32x4*>(c);
+        *reinterpret_cast<f32x4*>(o + 4) = *reinterpret_cast<const f32x4*>(c + 4);
+      }
+    } else if constexpr (kDual) {
+      const int seg = tid & 15;
+      for (int r = tid >> 4; r < 128; r += NT / 16) {
+        if (rbase + r >= rows_valid) break;
+        const float* g = C + r * kPitch + seg * 8;
+        const float* u = g + BN / 2;
+        float h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = silu_f32(g[e]) * u[e];
+        store_bf16x8(p.out_bf16 + (size_t)(m0 + rbase + r) * p.ldo + n0 + seg * 8, pack8(h));
+      }
+    } else {
+      const int seg = tid & 31;
+      const int col = n0 + seg * 8;
+      float badd[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) badd[e] = 0.f;
+      if constexpr (MODE == G2_BIAS) {
+        if (bias) unpack8(load_bf16x8(bias + nb + seg * 8), badd);
+      }
+      for (int r = tid >> 5; r < 128; r += NT / 32) {
+        if (rbase + r >= rows_valid) break;
+        const float* c = C + r * kPitch + seg * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = c[e] + badd[e];
+        const size_t row = (size_t)(m0 + rbase + r);
+        if constexpr (MODE == G2_RESID_F32) {
+          float x[8];
+          unpack8(load_bf16x8(p.resid_bf16 + row * p.ldr + col), x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += x[e];
+        }
+        if constexpr (MODE == G2_RESID_OUT) {
+          const float* rr = p.resid_f32 + row * p.ldr + col;
+          const f32x4 r0 = *reinterpret_cast<const f32x4*>(rr);
+          const f32x4 r1 = *reinterpret_cast<const f32x4*>(rr + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] += r0[e];
+            v[e + 4] += r1[e];
+          }
+          store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
+        } else {
+          float* o = p.out_f32 + row * p.ldo + col;
+          *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Sum of the split-K partials + the epilogue of MODE; one thread per 8 output
+// columns of one row.
+template <int MODE>
+__global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
+  constexpr bool kDual = MODE == G2_SWIGLU;
+  const int ldp = p.tiles_n * BN;
+  const int segs = (kDual ? p.tiles_n * BN / 2 : p.tiles_n * BN) / 8;  // per row
+  const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (idx >= (size_t)p.M * segs) return;
+  const int row = (int)(idx / segs);
+  const int seg = (int)(idx % segs);
+  const size_t pstride = (size_t)p.M * ldp;
+  if constexpr (kDual) {
+    const int tn = seg / (BN / 16), c = (seg % (BN / 16)) * 8;
+    const float* pg = p.part + (size_t)row * ldp + tn * BN + c;
+    float g[8] = {}, u[8] = {};
+    for (int s = 0; s < p.splits; ++s) {
+      const float* q = pg + s * pstride;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        g[e] += q[e];
+        u[e] += q[e + BN / 2];
+      }
+    }
+    float h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = silu_f32(g[e]) * u[e];
+    store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + seg * 8, pack8(h));
+  } else {
+    const int col = seg * 8;
+    const float* pc = p.part + (size_t)row * ldp + col;
+    float v[8] = {};
+    for (int s = 0; s < p.splits; ++s) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(pc + s * pstride);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(pc + s * pstride + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] += a[e];
+        v[e + 4] += b[e];
+      }
+    }
+    if constexpr (MODE == G2_BIAS) {
+      const bf16* bias = p.bias;
+      int nb = col;
+      if (col >= p.seg2) {
+        bias = p.bias3;
+        nb = col - p.seg2;
+      } else if (col >= p.seg1) {
+        bias = p.bias2;
+        nb = col - p.seg1;
+      }
+      if (bias) {
+        float b8[8];
+        unpack8(load_bf16x8(bias + nb), b8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += b8[e];
+      }
+    }
+    if constexpr (MODE == G2_RESID_F32) {
+      float x[8];
+      unpack8(load_bf16x8(p.resid_bf16 + (size_t)row * p.ldr + col), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += x[e];
+    }
+    if constexpr (MODE == G2_RESID_OUT) {
+      const float* rr = p.resid_f32 + (size_t)row * p.ldr + col;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += rr[e];
+      store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + col, pack8(v));
+    } else {
+      float* o = p.out_f32 + (size_t)row * p.ldo + col;
+      *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+  }
+}
+
+constexpr int kWaves = 8;
+
+template <int MODE, int NW = kWaves, bool DMA = true>
+hipError_t run(G2Args a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  const int nks = a.Ka / BK;
+  a.splits = a.splits < 1 ? 1 : (a.splits > nks ? nks : a.splits);
+  a.ksteps_per_split = (nks + a.splits - 1) / a.splits;
+  a.splits = (nks + a.ksteps_per_split - 1) / a.ksteps_per_split;
+  const int total = a.tiles_m * a.tiles_n * a.splits;
+  const dim3 grid(8 * ((total + 7) / 8));
+  if (a.splits == 1) {
+    hipLaunchKernelGGL((gemm2_kernel<MODE, false, NW, DMA>), grid, dim3(NW * 64), 0, s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gemm2_kernel<MODE, true, NW, DMA>), grid, dim3(NW * 64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int segs = (MODE == G2_SWIGLU ? a.tiles_n * BN / 2 : a.tiles_n * BN) / 8;
+  const size_t threads = (size_t)a.M * segs;
+  hipLaunchKernelGGL(gemm2_reduce_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+G2Args base(const bf16* A, int M, int Ka, const bf16* B, int Kb, int splits, void* part) {
+  G2Args a{};
+  a.A = A;
+  a.lda = Ka;
+  a.M = M;
+  a.Ka = Ka;
+  a.B = B;
+  a.ldb = Kb;
+  a.Kb = Kb;
+  a.seg1 = a.seg2 = 0x7fffffff;
+  a.splits = splits;
+  a.part = static_cast<float*>(part);
+  return a;
+}
+
+}  // namespace
+
+size_t ql_gemm2_part_bytes(int M, int b_rows, int splits) {
+  return splits <= 1 ? 0 : (size_t)splits * M * ((b_rows + BN - 1) / BN) * BN * 4;
+}
+
+bool ql_gemm2_ok(int N, int Kb, bool dual) {
+  return Kb % BK == 0 && (dual ? N % (BN / 2) == 0 : N % BN == 0);
+}
+
+hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
+                        int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
+                        float* out, int splits, void* part, hipStream_t s) {
+  G2Args a = base(A2, M, 2 * K, Wq, K, splits, part);
+  a.B2 = Wk;
+  a.B3 = Wv;
+  a.seg1 = q;
+  a.seg2 = q + kv;
+  a.bias = bq;
+  a.bias2 = bk;
+  a.bias3 = bv;
+  a.out_f32 = out;
+  a.ldo = q + 2 * kv;
+  a.tiles_n = (q + 2 * kv) / BN;
+  return run<G2_BIAS>(a, s);
+}
+
+hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
+                              const bf16* resid, float* out, int splits, void* part,
+                              hipStream_t s) {
+  G2Args a = base(A2, M, 2 * K, W, K, splits, part);
+  a.resid_bf16 = resid;
+  a.ldr = N;
+  a.out_f32 = out;
+  a.ldo = N;
+  a.tiles_n = N / BN;
+  return run<G2_RESID_F32>(a, s);
+}
+
+hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
+                              const float* resid, bf16* out, int splits, void* part,
+                              hipStream_t s) {
+  G2Args a = base(A, M, K, W, K, splits, part);
+  a.resid_f32 = resid;
+  a.ldr = N;
+  a.out_bf16 = out;
+  a.ldo = N;
+  a.tiles_n = N / BN;
+  return run<G2_RESID_OUT>(a, s);
+}
+
+hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
+                           bf16* out, int splits, void* part, hipStream_t s) {
+  G2Args a = base(A, M, K, Wg, K, splits, part);
+  a.B2 = Wu;
+  a.out_bf16 = out;
+  a.ldo = F;
+  a.tiles_n = F / (BN / 2);
+  return run<G2_SWIGLU>(a, s);
+}

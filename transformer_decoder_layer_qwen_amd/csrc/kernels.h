@@ -17,6 +17,11 @@ hipError_t ql_rmsnorm_bf16(const bf16* x, const bf16* gamma, bf16* out, float* o
 // bf16 rows -> fp32 normalised rows only
 hipError_t ql_rmsnorm_bf16_to_f32(const bf16* x, const bf16* gamma, float* out, int rows, int d,
                                   float eps, hipStream_t s);
+// bf16 rows -> normalised rows as a bf16 pair per row: [hi (d) | lo (d)]
+hipError_t ql_rmsnorm_bf16_to_hilo(const bf16* x, const bf16* gamma, bf16* out, int rows, int d,
+                                   float eps, hipStream_t s);
+// [rows][hi (cols) | lo (cols)] -> fp32 hi + lo
+hipError_t ql_hilo_to_f32(const bf16* hl, int rows, int cols, float* out, hipStream_t s);
 hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, float* out_f32,
                                  int rows, int d, float eps, hipStream_t s);
 hipError_t ql_rmsnorm_f32(const float* x, const float* gamma, float* out, int rows, int d,
@@ -41,6 +46,23 @@ hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, 
 hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
                             int max_tiles, int bm, float* out, hipStream_t s);
+
+// ---- prefill GEMMs, 256 x 256 tiles (N % 256 == 0, or F % 128 for SwiGLU; K % 32) ----
+// A2 = [hi | lo] bf16 pair of an fp32 activation, [M, 2K]. splits > 1 runs split-K
+// through `part` (ql_gemm2_part_bytes(M, weight rows read per call, splits) bytes).
+size_t ql_gemm2_part_bytes(int M, int b_rows, int splits);
+bool ql_gemm2_ok(int N, int Kb, bool dual);
+hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
+                        int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
+                        float* out, int splits, void* part, hipStream_t s);
+hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
+                              const bf16* resid, float* out, int splits, void* part,
+                              hipStream_t s);
+hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
+                              const float* resid, bf16* out, int splits, void* part,
+                              hipStream_t s);
+hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
+                           bf16* out, int splits, void* part, hipStream_t s);
 
 // ---- decode GEMMs with M <= 128 rows (N % 16 == 0, K % 32 == 0) ----
 // out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x, gamma bf16;
@@ -103,7 +125,8 @@ struct AttnPrefillArgs {
   const bf16* q;         // [B*S, ldq]
   const bf16* k_cache;   // [B, T_max, Hkv, dh]
   const bf16* v_cache;
-  float* out;            // [B*S, ldo] fp32
+  bf16* out;             // [B*S, ldo] fp32 output as bf16 hi (column c) + lo (c + lo_off)
+  int lo_off;
   const float* qf;       // fp32 variants of the same buffers (QL_F32)
   const float* kf;
   const float* vf;

@@ -65,6 +65,8 @@ struct ql_handle {
   float* part_o;
   float* part_ml;
   float* inv_rms;   // [rows] RMSNorm1 1/rms handed from the QKV GEMV to attention
+  void* g2part;     // split-K partial tiles of the prefill GEMMs
+  bool attn_hilo;   // the attention buffer holds a [hi | lo] bf16 pair (prefill)
   double* rope_omega;  // [head_dim / 2] RoPE frequencies
   float* logits;
   int* idx;
@@ -148,8 +150,10 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
   }
   if (c->dtype == QL_BF16) {
     if (c->head_dim != 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs head_dim == 128");
-    if (c->d % 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs d %% 128 == 0");
-    if (c->ffn_dim % 64) return fail(QL_EUNSUPPORTED, "QL_BF16 needs ffn_dim %% 64 == 0");
+    if (c->d % 256) return fail(QL_EUNSUPPORTED, "QL_BF16 needs d %% 256 == 0");
+    if ((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim % 256)
+      return fail(QL_EUNSUPPORTED, "QL_BF16 needs (Hq + 2 Hkv) * head_dim %% 256 == 0");
+    if (c->ffn_dim % 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs ffn_dim %% 128 == 0");
     if (G > 16) return fail(QL_EUNSUPPORTED, "QL_BF16 needs n_q_heads / n_kv_heads <= 16");
     if (c->max_batch > 128) return fail(QL_EUNSUPPORTED, "QL_BF16 decode needs max_batch <= 128");
   } else {
@@ -157,6 +161,26 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
       return fail(QL_EUNSUPPORTED, "QL_F32 needs a power-of-two head_dim in [2, 128]");
   }
   return QL_OK;
+}
+
+// Prefill GEMM split-K: enough (tile, split) blocks for about one per CU,
+// each split keeping at least 512 of K.
+constexpr int kGemmTargetBlocks = 256;
+int gemm2_splits(int M, int b_rows, int K) {
+  const int tiles = ((M + 255) / 256) * ((b_rows + 255) / 256);
+  int sp = std::max(1, kGemmTargetBlocks / std::max(tiles, 1));
+  return std::max(1, std::min(sp, K / 512));
+}
+// Partial-tile bytes for the four dense prefill GEMMs at M rows (the largest).
+size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
+  size_t b = 0;
+  b = std::max(b, ql_gemm2_part_bytes(M, qkv_dim, gemm2_splits(M, qkv_dim, 2 * c.d)));
+  b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, 2 * q_dim)));
+  if (c.n_experts == 0) {
+    b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, c.d)));
+    b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, c.ffn_dim)));
+  }
+  return b;
 }
 
 // Decode attention launch shape: about kDecodeTargetWaves waves over
@@ -193,10 +217,10 @@ size_t layout(ql_handle* h, char* base) {
   const size_t N = (size_t)h->rows;
   const size_t es = (size_t)h->es;
   Carve k{base};
-  h->xhat = k.take<void>(N * c.d * 4);  // fp32: feeds the QKV GEMM as bf16 hi + lo
+  h->xhat = k.take<void>(N * c.d * 4);  // [hi | lo] bf16 pair of the fp32 RMSNorm1 output
   h->qkv = k.take<float>(N * h->qkv_dim * 4);
   h->q = k.take<void>(N * h->q_dim * es);
-  h->attn = k.take<void>(N * h->q_dim * 4);  // fp32: feeds the O GEMM as bf16 hi + lo
+  h->attn = k.take<void>(N * h->q_dim * 4);  // prefill: [hi | lo] bf16 pair; decode: fp32
   h->r = k.take<float>(N * c.d * 4);
   h->z = k.take<void>(N * c.d * es);
   const size_t B = (size_t)std::max(c.max_batch, 0);
@@ -205,6 +229,9 @@ size_t layout(ql_handle* h, char* base) {
   h->part_ml = k.take<float>(slots * c.n_q_heads * 2 * 4);
   h->rope_omega = k.take<double>((size_t)std::max(c.head_dim / 2, 1) * 8);
   h->inv_rms = k.take<float>(N * 4);
+  h->g2part = c.dtype == QL_BF16 ? k.take<void>(gemm2_part_bytes(c, h->q_dim, h->qkv_dim,
+                                                                 std::max(c.max_tokens, 0)))
+                                 : nullptr;
   if (c.n_experts > 0) {
     const size_t E = c.n_experts, K = c.top_k, NK = N * K;
     const size_t nblk = (N + 255) / 256;
@@ -237,9 +264,14 @@ ql_status copy_taps(ql_handle* h, int N, hipStream_t s) {
   const size_t es = h->es;
   if (h->taps.q)
     QL_HIP(hipMemcpyAsync(h->taps.q, h->q, (size_t)N * h->q_dim * es, hipMemcpyDeviceToDevice, s));
-  if (h->taps.attn)
-    QL_HIP(hipMemcpyAsync(h->taps.attn, h->attn, (size_t)N * h->q_dim * 4,
-                          hipMemcpyDeviceToDevice, s));
+  if (h->taps.attn) {
+    if (h->attn_hilo)
+      QL_HIP(ql_hilo_to_f32(static_cast<const bf16*>(h->attn), N, h->q_dim,
+                            static_cast<float*>(h->taps.attn), s));
+    else
+      QL_HIP(hipMemcpyAsync(h->taps.attn, h->attn, (size_t)N * h->q_dim * 4,
+                            hipMemcpyDeviceToDevice, s));
+  }
   if (h->taps.r)
     QL_HIP(hipMemcpyAsync(h->taps.r, h->r, (size_t)N * c.d * 4, hipMemcpyDeviceToDevice, s));
   if (h->taps.z)
@@ -348,12 +380,15 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
                QL_HIP(ql_skinny_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
     }
   } else {
+    const int sgu = gemm2_splits(N, 2 * c.ffn_dim, c.d);
+    const int sdn = gemm2_splits(N, c.d, c.ffn_dim);
     QL_STAGE(h, QL_STAGE_GATE_UP, s,
-             QL_HIP(ql_gemm_swiglu(z, N, static_cast<const bf16*>(w.w_gate),
-                                   static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, s)));
+             QL_HIP(ql_gemm2_swiglu(z, N, static_cast<const bf16*>(w.w_gate),
+                                    static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, sgu,
+                                    h->g2part, s)));
     QL_STAGE(h, QL_STAGE_DOWN, s,
-             QL_HIP(ql_gemm_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d, c.ffn_dim,
-                                      h->r, y, s)));
+             QL_HIP(ql_gemm2_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d,
+                                       c.ffn_dim, h->r, y, sdn, h->g2part, s)));
   }
   return QL_OK;
 }
@@ -365,17 +400,18 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
   const int N = B * S;
-  float* xhat = static_cast<float*>(h->xhat);
+  bf16* xhat = static_cast<bf16*>(h->xhat);  // [N, 2d]: hi | lo
   QL_STAGE(h, QL_STAGE_RMSNORM1, s,
-           QL_HIP(ql_rmsnorm_bf16_to_f32(x, static_cast<const bf16*>(w.ln1_g), xhat, N, c.d,
-                                         c.rms_eps, s)));
+           QL_HIP(ql_rmsnorm_bf16_to_hilo(x, static_cast<const bf16*>(w.ln1_g), xhat, N, c.d,
+                                          c.rms_eps, s)));
   const bf16* bq = c.qkv_bias ? static_cast<const bf16*>(w.bq) : nullptr;
   const bf16* bk = c.qkv_bias ? static_cast<const bf16*>(w.bk) : nullptr;
   const bf16* bv = c.qkv_bias ? static_cast<const bf16*>(w.bv) : nullptr;
   QL_STAGE(h, QL_STAGE_QKV, s,
-           QL_HIP(ql_gemm_qkv(xhat, N, static_cast<const bf16*>(w.wq),
-                              static_cast<const bf16*>(w.wk), static_cast<const bf16*>(w.wv),
-                              h->q_dim, h->kv_dim, c.d, bq, bk, bv, h->qkv, s)));
+           QL_HIP(ql_gemm2_qkv(xhat, N, static_cast<const bf16*>(w.wq),
+                               static_cast<const bf16*>(w.wk), static_cast<const bf16*>(w.wv),
+                               h->q_dim, h->kv_dim, c.d, bq, bk, bv, h->qkv,
+                               gemm2_splits(N, h->qkv_dim, 2 * c.d), h->g2part, s)));
   QkvPostArgs qa{};
   qa.qkv = h->qkv;
   qa.ld_qkv = h->qkv_dim;
@@ -399,9 +435,10 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   pa.q = static_cast<const bf16*>(h->q);
   pa.k_cache = static_cast<const bf16*>(kc);
   pa.v_cache = static_cast<const bf16*>(vc);
-  pa.out = static_cast<float*>(h->attn);
+  pa.out = static_cast<bf16*>(h->attn);  // [N, 2q]: hi | lo
+  pa.lo_off = h->q_dim;
   pa.ldq = h->q_dim;
-  pa.ldo = h->q_dim;
+  pa.ldo = 2 * h->q_dim;
   pa.B = B;
   pa.S = S;
   pa.T_max = T_max;
@@ -410,9 +447,11 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   pa.head_dim = c.head_dim;
   pa.scale_log2 = scale_log2(c.head_dim);
   QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_prefill_bf16(pa, s)));
+  h->attn_hilo = true;
   QL_STAGE(h, QL_STAGE_O_PROJ, s,
-           QL_HIP(ql_gemm_resid_f32(static_cast<const float*>(h->attn), N,
-                                    static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r, s)));
+           QL_HIP(ql_gemm2_resid_f32(static_cast<const bf16*>(h->attn), N,
+                                     static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
+                                     gemm2_splits(N, c.d, 2 * h->q_dim), h->g2part, s)));
   return ffn_dense_or_moe(h, N, false, y, s);
 }
 
@@ -473,6 +512,7 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
   da.inv_rms = gemv ? h->inv_rms : nullptr;
   da.scale_log2 = scale_log2(c.head_dim);
   QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
+  h->attn_hilo = false;
   const float* attn = static_cast<const float*>(h->attn);
   const bf16* wo = static_cast<const bf16*>(w.wo);
   QL_STAGE(h, QL_STAGE_O_PROJ, s,
@@ -486,6 +526,7 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
 ql_status layer_f32(ql_handle* h, const float* x, int N, bool decode, int B, int S,
                     const int* cache_len, int pos_offset, void* kc, void* vc, int T_max, float* y,
                     hipStream_t s) {
+  h->attn_hilo = false;
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
   float* xhat = static_cast<float*>(h->xhat);

@@ -4,7 +4,9 @@
 // in fp32 ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层", §3). Rows are
 // independent. The output is bf16 or fp32; an optional second output keeps
 // the fp32 value next to a bf16 one (the MoE router takes its top-k decision
-// from fp32 inputs).
+// from fp32 inputs). HILO stores the fp32 result as a bf16 pair per row,
+// [hi | lo] with hi = RNE(o), lo = RNE(o - hi), the form in which the QKV
+// projection reads it.
 #include "common.h"
 #include "kernels.h"
 
@@ -44,7 +46,7 @@ template <class T, int V> QL_DEV void storev(T* p, const float* f) {
 // One block of 256 threads per row; thread t owns the V-wide pieces t, t+256,
 // ... (PER of them), all loaded before the reduction so one row costs about
 // one memory round trip.
-template <class TIn, class TG, class TOut, int PER>
+template <class TIn, class TG, class TOut, int PER, bool HILO>
 __global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict__ x,
                                                           const TG* __restrict__ gamma,
                                                           TOut* __restrict__ out,
@@ -79,14 +81,23 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict_
       float o[V];
 #pragma unroll
       for (int j = 0; j < V; ++j) o[j] = g[i][j] * (v[i][j] * inv);
-      storev<TOut, V>(out + row * d + c, o);
-      if (out_f32) storev<float, V>(out_f32 + row * d + c, o);
+      if constexpr (HILO) {
+        float lo[V];
+        TOut* orow = out + row * 2 * d;
+#pragma unroll
+        for (int j = 0; j < V; ++j) lo[j] = o[j] - (float)(bf16)o[j];
+        storev<TOut, V>(orow + c, o);
+        storev<TOut, V>(orow + d + c, lo);
+      } else {
+        storev<TOut, V>(out + row * d + c, o);
+        if (out_f32) storev<float, V>(out_f32 + row * d + c, o);
+      }
     }
   }
 }
 
 // Any d: one wave per row, strided scalar accesses.
-template <class TIn, class TG, class TOut>
+template <class TIn, class TG, class TOut, bool HILO>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
                                                       const TG* __restrict__ gamma,
                                                       TOut* __restrict__ out,
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
   const TIn* xr = x + (size_t)row * d;
-  TOut* orow = out + (size_t)row * d;
+  TOut* orow = out + (size_t)row * (HILO ? 2 * d : d);
   float ss = 0.f;
   for (int c = lane; c < d; c += 64) {
     const float v = to_f32(xr[c]);
@@ -107,11 +118,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
   for (int c = lane; c < d; c += 64) {
     const float o = to_f32(gamma[c]) * (to_f32(xr[c]) * inv);
     orow[c] = from_f32<TOut>(o);
-    if (out_f32) out_f32[(size_t)row * d + c] = o;
+    if constexpr (HILO) orow[d + c] = from_f32<TOut>(o - to_f32(from_f32<TOut>(o)));
+    else if (out_f32) out_f32[(size_t)row * d + c] = o;
   }
 }
 
-template <class TIn, class TG, class TOut>
+template <class TIn, class TG, class TOut, bool HILO = false>
 hipError_t launch(const TIn* x, const TG* gamma, TOut* out, float* out_f32, int rows, int d,
                   float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
@@ -120,7 +132,7 @@ hipError_t launch(const TIn* x, const TG* gamma, TOut* out, float* out_f32, int 
   if (d % V == 0 && per <= 8) {
 #define QL_RMS_CASE(P)                                                                    \
   if (per <= P) {                                                                         \
-    hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, P>), dim3(rows), dim3(256), 0, s, \
+    hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, P, HILO>), dim3(rows), dim3(256), 0, s, \
                        x, gamma, out, out_f32, d, eps);                                   \
     return hipGetLastError();                                                             \
   }
@@ -131,7 +143,7 @@ hipError_t launch(const TIn* x, const TG* gamma, TOut* out, float* out_f32, int 
 #undef QL_RMS_CASE
   }
   const int blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((rmsnorm_kernel<TIn, TG, TOut>), dim3(blocks), dim3(256), 0, s, x, gamma,
+  hipLaunchKernelGGL((rmsnorm_kernel<TIn, TG, TOut, HILO>), dim3(blocks), dim3(256), 0, s, x, gamma,
                      out, out_f32, rows, d, eps);
   return hipGetLastError();
 }
@@ -145,6 +157,28 @@ hipError_t ql_rmsnorm_bf16(const bf16* x, const bf16* gamma, bf16* out, float* o
 hipError_t ql_rmsnorm_bf16_to_f32(const bf16* x, const bf16* gamma, float* out, int rows, int d,
                                   float eps, hipStream_t s) {
   return launch<bf16, bf16, float>(x, gamma, out, nullptr, rows, d, eps, s);
+}
+hipError_t ql_rmsnorm_bf16_to_hilo(const bf16* x, const bf16* gamma, bf16* out, int rows, int d,
+                                   float eps, hipStream_t s) {
+  return launch<bf16, bf16, bf16, true>(x, gamma, out, nullptr, rows, d, eps, s);
+}
+
+namespace {
+__global__ __launch_bounds__(256) void hilo_to_f32_kernel(const bf16* __restrict__ hl, int rows,
+                                                          int cols, float* __restrict__ out) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * cols) return;
+  const size_t r = i / cols, c = i % cols;
+  out[i] = (float)hl[r * 2 * cols + c] + (float)hl[r * 2 * cols + cols + c];
+}
+}  // namespace
+
+hipError_t ql_hilo_to_f32(const bf16* hl, int rows, int cols, float* out, hipStream_t s) {
+  const size_t n = (size_t)rows * cols;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(hilo_to_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, hl,
+                     rows, cols, out);
+  return hipGetLastError();
 }
 hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, float* out_f32,
                                  int rows, int d, float eps, hipStream_t s) {
