@@ -28,6 +28,8 @@ constexpr int kVtPitch = 68;  // bf16 elements per transposed-V row
 constexpr int kKElems = kBK * kDh;
 constexpr int kVElems = kDh * kVtPitch;
 constexpr int kStage = kKElems + kVElems;
+constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
+constexpr int kPairMinBlocks = 256;  // the CU count
 
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * kStage];
@@ -36,10 +38,18 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   const int wave = tid >> 6;
   const int col = lane & 31;
   const int hi = lane >> 5;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / (p.n_q_heads / p.n_kv_heads);
+  // Causal work grows with the query tile, so with p.pair a block takes tile
+  // nqt-1-x and then tile x: every block then does about the same work.
+  // Otherwise a block takes one tile, the longest first.
+  const int nqt = (p.S + kBQ - 1) / kBQ;
+  const int qt_first = p.pair ? nqt - 1 - (int)blockIdx.x : (int)(gridDim.x - 1 - blockIdx.x);
+  const int npass = (p.pair && (int)blockIdx.x < qt_first) ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+  if (pass > 0) __syncthreads();  // the LDS ring is reused
+  const int qt = pass == 0 ? qt_first : (int)blockIdx.x;
   const int q0 = qt * kBQ;
   const int S = p.S;
   const int my_q = q0 + wave * 32 + col;
@@ -67,6 +77,21 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   u32x4 rk[4], rv[4];
   auto gload = [&](int kt) {
     const int k0 = kt * kBK;
+    if (k0 + kBK <= S) {  // whole tile inside the sequence: no per-lane checks
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = tid + 256 * i;
+        rk[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(k0 + (ch >> 4)) * kv_row_stride +
+                                                 (ch & 15) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        rv[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(k0 + vk + j) * kv_row_stride +
+                                                 vc * 8);
+      return;
+    }
+    // ragged last tile: rows past S are zero (they may hold anything, and a
+    // NaN would survive a zero softmax weight in P V)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = tid + 256 * i;
@@ -120,7 +145,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
     const bool more = kt + 1 < ntiles;
     if (more) gload(kt + 1);
     const int k0 = kt * kBK;
-    if (k0 <= wave_qmax) {  // otherwise every key of the tile is in this wave's future
+    // skip tiles whose every key is in this wave's future (wave-uniform)
+    if (__builtin_amdgcn_readfirstlane(k0 <= wave_qmax)) {
       const bf16* Ks = lds + st * kStage;
       const bf16* Vt = Ks + kKElems;
       f32x16 sc[2];
@@ -137,40 +163,53 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
           sc[t] = mfma_32x32x16(kf, qf[s], sc[t]);
         }
       }
-      // scale, mask, tile max. Register r of half t holds key 32t + 8(r/4) + 4hi + r%4.
-      const bool need_mask = (k0 + kBK - 1 > q0 + wave * 32) || (k0 + kBK > S);
+      // mask, tile max (raw scores; the scale is positive and applied in the
+      // exponent). Register r of half t holds key 32t + 8(r/4) + 4hi + r%4.
+      // The mask test is wave-uniform (readfirstlane), so the common unmasked
+      // tile carries no per-element code.
+      const bool need_mask = __builtin_amdgcn_readfirstlane(
+          (k0 + kBK - 1 > q0 + wave * 32) || (k0 + kBK > S));
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+            sc[t][r] = (key > my_q || key >= S) ? -INFINITY : sc[t][r];
+          }
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sc[t][r] * p.scale_log2;
-          if (need_mask) {
-            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key > my_q || key >= S) x = -INFINITY;
-          }
-          sc[t][r] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-      const float m_new = fmaxf(m_run, mt);  // finite: key 0 is visible to every query
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[t][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * p.scale_log2;
+      // Lazy rescaling: the reference maximum only moves when a score exceeds
+      // it by more than kSlack (log2 units), so p <= 2^kSlack and the output
+      // is unchanged (numerator and denominator use the same reference); the
+      // rescale of the accumulators runs only when some lane moved.
+      const bool grow = mt > m_run + kSlack;  // first tile: m_run = -inf
+      if (__any(grow)) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      }
       float lsum = 0.f;
       bf16x8 pf[4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = exp2f(sc[t][r] - m_new);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[t][r], p.scale_log2, -m_run));
           lsum += pv;
           pf[2 * t + (r >> 3)][r & 7] = (bf16)pv;
         }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      l_run += lsum;
       // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]; k-step u covers keys
       // 32(u/2) + 16(u%2) + {4hi..4hi+3, 8+4hi..8+4hi+3} in slot order.
 #pragma unroll
@@ -191,7 +230,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  if (my_q >= S) return;
+  if (my_q >= S) continue;
   const float inv = 1.0f / l_tot;
   // the fp32 output as a bf16 pair: hi = RNE(o) at column c, lo = RNE(o - hi)
   // at column c + lo_off (the O projection multiplies both)
@@ -210,6 +249,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
       *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * c + 4 * hi) = vh;
       *reinterpret_cast<bf16x4*>(orow + p.lo_off + 32 * dt + 8 * c + 4 * hi) = vl;
     }
+  }  // pass
 }
 
 }  // namespace
@@ -217,6 +257,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
 hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   const int nqt = (a.S + kBQ - 1) / kBQ;
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3(nqt, a.n_q_heads, a.B), dim3(256), 0, s, a);
+  // pair query tiles when the unpaired grid would still give every CU at
+  // least two blocks
+  AttnPrefillArgs b = a;
+  b.pair = (long)nqt * a.n_q_heads * a.B >= 2L * kPairMinBlocks;
+  const int gx = b.pair ? (nqt + 1) / 2 : nqt;
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3(gx, a.n_q_heads, a.B), dim3(256), 0, s, b);
   return hipGetLastError();
 }

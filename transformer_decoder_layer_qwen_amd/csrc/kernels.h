@@ -135,6 +135,7 @@ struct AttnPrefillArgs {
   int B, S, T_max;
   int n_q_heads, n_kv_heads, head_dim;
   float scale_log2;      // log2(e) / sqrt(dh)
+  int pair;              // set by the launcher: a block takes query tiles nqt-1-x and x
 };
 hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s);
 hipError_t ql_attn_prefill_f32(const AttnPrefillArgs& a, hipStream_t s);
