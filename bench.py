@@ -297,7 +297,8 @@ def time_empty_span(hip, steps):
 def stages_of(cfg, kind, batch):
     # decode fuses RMSNorm1 into the QKV projection and the QK-norm / RoPE /
     # cache append into the attention kernel
-    s = (["rmsnorm1", "qkv", "qkv_post"] if kind == "prefill" else ["qkv"])
+    # (prefill: the QKV GEMM's epilogue does QK-norm, RoPE and the cache write)
+    s = (["rmsnorm1", "qkv"] if kind == "prefill" else ["qkv"])
     s += ["attention", "o_proj"]
     if not (kind == "decode" and not cfg.is_moe and batch <= GEMV_MAX_ROWS):
         s += ["rmsnorm2"]

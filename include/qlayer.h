@@ -81,7 +81,7 @@ typedef enum { QL_BF16 = 0, QL_F32 = 1 } ql_dtype;
  * max_tokens   largest B*S of qlayer_prefill and largest N of qlayer_moe_ffn
  * max_batch    largest B of qlayer_decode
  *
- * QL_BF16 shape limits: head_dim == 128, d % 256 == 0, (Hq + 2 Hkv) * dh % 256 == 0,
+ * QL_BF16 shape limits: head_dim == 128, d % 256 == 0, Hq and Hkv even,
  * ffn_dim % 128 == 0, Hq/Hkv <= 16, max_batch <= 128, and with experts
  * n_experts <= 256.
  */

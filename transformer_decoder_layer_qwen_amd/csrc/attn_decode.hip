@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   {
     double ang = ((double)L + (double)p.pos_offset) * omega;
     const double two_pi = 6.283185307179586476925286766559;
-    ang -= two_pi * rint(ang / two_pi);
+    ang -= two_pi * rint(ang * (1.0 / two_pi));
     sincosf((float)ang, &sn, &cs);
   }
   // one head's 128 values: lane owns (lane, lane + 64); scale, bias, norm, rotate

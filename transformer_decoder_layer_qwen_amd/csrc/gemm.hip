@@ -337,58 +337,6 @@ GemmArgs base_args(const bf16* A, int lda, int M, const bf16* B, int ldb, int K)
 
 }  // namespace
 
-hipError_t ql_gemm_qkv(const float* A, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
-                       int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
-                       float* out, hipStream_t s) {
-  const int N = q + 2 * kv;
-  GemmArgs a = base_args(nullptr, K, M, Wq, K, K);
-  a.Af = A;
-  a.B2 = Wk;
-  a.B3 = Wv;
-  a.seg1 = q;
-  a.seg2 = q + kv;
-  a.bias = bq;
-  a.bias2 = bk;
-  a.bias3 = bv;
-  a.out_f32 = out;
-  a.ldo = N;
-  a.tiles_n = N / 128;
-  return launch<128, 128, 64, 64, GM_F32_BIAS, true>(a, (M + 127) / 128, s);
-}
-
-hipError_t ql_gemm_resid_f32(const float* A, int M, const bf16* B, int N, int K,
-                             const bf16* resid, float* out, hipStream_t s) {
-  GemmArgs a = base_args(nullptr, K, M, B, K, K);
-  a.Af = A;
-  a.resid_bf16 = resid;
-  a.ldr = N;
-  a.out_f32 = out;
-  a.ldo = N;
-  a.tiles_n = N / 128;
-  return launch<128, 128, 64, 64, GM_RESID_F32, true>(a, (M + 127) / 128, s);
-}
-
-hipError_t ql_gemm_resid_out(const bf16* A, int M, const bf16* B, int N, int K,
-                             const float* resid, bf16* out, hipStream_t s) {
-  GemmArgs a = base_args(A, K, M, B, K, K);
-  a.resid_f32 = resid;
-  a.ldr = N;
-  a.out_bf16 = out;
-  a.ldo = N;
-  a.tiles_n = N / 128;
-  return launch<128, 128, 64, 64, GM_RESID_OUT>(a, (M + 127) / 128, s);
-}
-
-hipError_t ql_gemm_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                          bf16* out, hipStream_t s) {
-  GemmArgs a = base_args(A, K, M, Wg, K, K);
-  a.B2 = Wu;
-  a.out_bf16 = out;
-  a.ldo = F;
-  a.tiles_n = F / 64;
-  return launch<128, 128, 64, 64, GM_SWIGLU>(a, (M + 127) / 128, s);
-}
-
 hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
                           int mf, int d, const int* tile_expert, const int* tile_row0,
                           const int* tile_rows, const int* num_tiles, int max_tiles, int bm,

@@ -28,7 +28,7 @@
 //   16/32-byte contiguous and SwiGLU can pair a gate column with its up column.
 //
 // Epilogues (one rounding at the stored tensor):
-//   BIAS      out_f32 = acc (+ bias)            Q/K/V projection (+QKV bias)
+//   BIAS      Q/K/V projection: + bias, QK-norm, RoPE; q -> q_out, k/v -> cache
 //   RESID_F32 out_f32 = resid_bf16 + acc        R = X + O W_O^T
 //   RESID_OUT out     = bf16(resid_f32 + acc)   Y = R + H W_down^T
 //   SWIGLU    out     = bf16(SiLU(g) * u)       B tile = [128 W_gate rows | 128 W_up rows]
@@ -70,7 +70,71 @@ struct G2Args {
   const float* resid_f32;
   int ldr;
   float* part;  // [splits][M][tiles_n * BN]
+  // BIAS (the QKV projection): per-head QK-norm, RoPE and the cache write
+  // fused into the epilogue
+  int S, pos_offset, T_max, n_q_heads, n_kv_heads;
+  float eps;
+  const double* omega;  // [64] RoPE frequencies
+  const bf16* q_norm_g;
+  const bf16* k_norm_g;
+  bf16* q_out;          // [M, Hq*128]
+  bf16* k_cache;        // [B, T_max, Hkv, 128]
+  bf16* v_cache;
 };
+
+// QKV epilogue for 8 columns [col, col + 8) of token row `row`, bias added.
+// The 16 lanes of an aligned lane group hold one head (128 columns), so the
+// per-head sum of squares of QK-norm is a 16-lane reduction and the RoPE
+// partner of column i (i + 64) sits 8 lanes away. q goes to q_out; k and v go
+// to cache row (row % S) of sequence row / S. ("推理系统 03：逐项算清一个真实 Qwen3
+// Transformer 层" §5 QK-norm, §6 rotate_half RoPE with omega_i = theta^(-2i/dh),
+// §12 the cache keeps post-norm, post-RoPE keys.)
+QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
+  const int qd = p.n_q_heads * 128, kvd = p.n_kv_heads * 128;
+  int part = 0, c = col;
+  if (col >= qd + kvd) {
+    part = 2;
+    c = col - qd - kvd;
+  } else if (col >= qd) {
+    part = 1;
+    c = col - qd;
+  }
+  const int head = c >> 7, d0 = c & 127;
+  const int b = (int)(row / p.S), t = (int)(row % p.S);
+  if (part < 2) {
+    const bf16* gam = part == 0 ? p.q_norm_g : p.k_norm_g;
+    if (gam) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+      ss = group_sum(ss, 16);
+      const float inv = 1.0f / sqrtf(ss / 128.f + p.eps);
+      float g[8];
+      unpack8(load_bf16x8(gam + d0), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = g[e] * (v[e] * inv);
+    }
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = __shfl_xor(v[e], 8, kWave);
+    const double pos = (double)t + (double)p.pos_offset;
+    const double two_pi = 6.283185307179586476925286766559;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double ang = pos * p.omega[(d0 + e) & 63];
+      ang -= two_pi * rint(ang * (1.0 / two_pi));
+      float sn, cs;
+      sincosf((float)ang, &sn, &cs);
+      v[e] = d0 < 64 ? v[e] * cs - o[e] * sn : v[e] * cs + o[e] * sn;
+    }
+  }
+  if (part == 0) {
+    store_bf16x8(p.q_out + row * qd + c, pack8(v));
+  } else {
+    bf16* cache = part == 1 ? p.k_cache : p.v_cache;
+    store_bf16x8(cache + (((size_t)b * p.T_max + t) * p.n_kv_heads + head) * 128 + d0, pack8(v));
+  }
+}
 
 // LDS slot of chunk c of row r is c ^ swz(r). A 16-byte read by the lanes of
 // one MFMA fragment touches 16 consecutive rows (from a multiple of 16) at one
@@ -353,6 +417,10 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = c[e] + badd[e];
         const size_t row = (size_t)(m0 + rbase + r);
+        if constexpr (MODE == G2_BIAS) {
+          qkv_finish(p, row, col, v);
+          continue;
+        }
         if constexpr (MODE == G2_RESID_F32) {
           float x[8];
           unpack8(load_bf16x8(p.resid_bf16 + row * p.ldr + col), x);
@@ -437,6 +505,8 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] += b8[e];
       }
+      qkv_finish(p, (size_t)row, col, v);
+      return;
     }
     if constexpr (MODE == G2_RESID_F32) {
       float x[8];
@@ -510,8 +580,20 @@ bool ql_gemm2_ok(int N, int Kb, bool dual) {
 
 hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
-                        float* out, int splits, void* part, hipStream_t s) {
+                        const QkvFinish& f, int splits, void* part, hipStream_t s) {
   G2Args a = base(A2, M, 2 * K, Wq, K, splits, part);
+  a.S = f.S;
+  a.pos_offset = f.pos_offset;
+  a.T_max = f.T_max;
+  a.n_q_heads = q / 128;
+  a.n_kv_heads = kv / 128;
+  a.eps = f.eps;
+  a.omega = f.omega;
+  a.q_norm_g = f.q_norm_g;
+  a.k_norm_g = f.k_norm_g;
+  a.q_out = f.q_out;
+  a.k_cache = f.k_cache;
+  a.v_cache = f.v_cache;
   a.B2 = Wk;
   a.B3 = Wv;
   a.seg1 = q;
@@ -519,7 +601,6 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
   a.bias = bq;
   a.bias2 = bk;
   a.bias3 = bv;
-  a.out_f32 = out;
   a.ldo = q + 2 * kv;
   a.tiles_n = (q + 2 * kv) / BN;
   return run<G2_BIAS>(a, s);

@@ -304,14 +304,6 @@ hipError_t ql_gemv_resid_out(const bf16* X, int M, const bf16* W, int N, int K,
   return launch<GV_RESID_OUT, GX_BF16>(a, M, s);
 }
 
-hipError_t ql_gemv_swiglu(const bf16* X, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                          bf16* out, hipStream_t s) {
-  GemvArgs a = base(X, K, Wg, F);
-  a.W2 = Wu;
-  a.out_bf16 = out;
-  return launch<GV_SWIGLU, GX_BF16>(a, M, s);
-}
-
 hipError_t ql_gemv_rmsnorm_swiglu(const float* R, const bf16* gamma, float eps, int M,
                                   const bf16* Wg, const bf16* Wu, int F, int K, bf16* out,
                                   hipStream_t s) {

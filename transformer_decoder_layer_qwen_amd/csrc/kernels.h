@@ -14,9 +14,6 @@ constexpr int kMaxExperts = 256;
 // ---- RMSNorm (rows x d) ----
 hipError_t ql_rmsnorm_bf16(const bf16* x, const bf16* gamma, bf16* out, float* out_f32, int rows,
                            int d, float eps, hipStream_t s);
-// bf16 rows -> fp32 normalised rows only
-hipError_t ql_rmsnorm_bf16_to_f32(const bf16* x, const bf16* gamma, float* out, int rows, int d,
-                                  float eps, hipStream_t s);
 // bf16 rows -> normalised rows as a bf16 pair per row: [hi (d) | lo (d)]
 hipError_t ql_rmsnorm_bf16_to_hilo(const bf16* x, const bf16* gamma, bf16* out, int rows, int d,
                                    float eps, hipStream_t s);
@@ -27,18 +24,7 @@ hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, f
 hipError_t ql_rmsnorm_f32(const float* x, const float* gamma, float* out, int rows, int d,
                           float eps, hipStream_t s);
 
-// ---- prefill GEMMs, C[M,N] = A[M,K] B[N,K]^T (N % 128 == 0, K % 64 == 0) ----
-// QKV: out[M, q+2kv] fp32 = A [Wq; Wk; Wv]^T + [bq; bk; bv] (biases may be NULL);
-// A (and the O projection's A) is fp32, used as a bf16 hi + lo pair.
-hipError_t ql_gemm_qkv(const float* A, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
-                       int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
-                       float* out, hipStream_t s);
-hipError_t ql_gemm_resid_f32(const float* A, int M, const bf16* B, int N, int K,
-                             const bf16* resid, float* out, hipStream_t s);
-hipError_t ql_gemm_resid_out(const bf16* A, int M, const bf16* B, int N, int K,
-                             const float* resid, bf16* out, hipStream_t s);
-hipError_t ql_gemm_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                          bf16* out, hipStream_t s);
+// ---- MoE expert GEMMs over routed row tiles (mf % 64 == 0, d % 128 == 0) ----
 hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
                           int mf, int d, const int* tile_expert, const int* tile_row0,
                           const int* tile_rows, const int* num_tiles, int max_tiles, int bm,
@@ -52,9 +38,22 @@ hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const 
 // through `part` (ql_gemm2_part_bytes(M, weight rows read per call, splits) bytes).
 size_t ql_gemm2_part_bytes(int M, int b_rows, int splits);
 bool ql_gemm2_ok(int N, int Kb, bool dual);
+// QKV projection of [B*S] token rows with bias, per-head QK-norm, RoPE at
+// position (row % S) + pos_offset, q to q_out [M, q] and k, v to cache row
+// row % S of sequence row / S (q, kv multiples of 256; head_dim 128)
+struct QkvFinish {
+  int S, pos_offset, T_max;
+  float eps;
+  const double* omega;   // [64]
+  const bf16* q_norm_g;  // or NULL
+  const bf16* k_norm_g;
+  bf16* q_out;
+  bf16* k_cache;
+  bf16* v_cache;
+};
 hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
-                        float* out, int splits, void* part, hipStream_t s);
+                        const QkvFinish& f, int splits, void* part, hipStream_t s);
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
                               const bf16* resid, float* out, int splits, void* part,
                               hipStream_t s);
@@ -92,15 +91,13 @@ hipError_t ql_gemv_resid_f32(const float* X, int M, const bf16* W, int N, int K,
                              const bf16* resid, float* out, hipStream_t s);
 hipError_t ql_gemv_resid_out(const bf16* X, int M, const bf16* W, int N, int K,
                              const float* resid, bf16* out, hipStream_t s);
-hipError_t ql_gemv_swiglu(const bf16* X, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                          bf16* out, hipStream_t s);
 // out[M, F] = SiLU(Z Wg^T) * (Z Wu^T), Z = RMSNorm(R) * gamma computed on the fly
 // (R fp32 [M, K])
 hipError_t ql_gemv_rmsnorm_swiglu(const float* R, const bf16* gamma, float eps, int M,
                                   const bf16* Wg, const bf16* Wu, int F, int K, bf16* out,
                                   hipStream_t s);
 
-// ---- QK-norm + RoPE + cache write ----
+// ---- QK-norm + RoPE + cache write (fp32 layer) ----
 struct QkvPostArgs {
   const float* qkv;      // [rows, ld_qkv] fp32 projections (bias added)
   int ld_qkv;
@@ -117,7 +114,6 @@ struct QkvPostArgs {
   void* k_cache;         // [B, T_max, Hkv, dh]
   void* v_cache;
 };
-hipError_t ql_qkv_post_bf16(const QkvPostArgs& a, hipStream_t s);
 hipError_t ql_qkv_post_f32(const QkvPostArgs& a, hipStream_t s);
 
 // ---- attention ----

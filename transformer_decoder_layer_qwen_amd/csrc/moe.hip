@@ -24,10 +24,18 @@
 
 namespace {
 
-constexpr int kTok = 16;  // tokens per router block
+constexpr int kTok = 16;  // tokens per router block (the MFMA's N)
+constexpr int kRW = 8;    // waves per router block; they split K
 
-__global__ __launch_bounds__(256) void router_topk_kernel(const RouterArgs p) {
-  extern __shared__ float logit_lds[];  // [kTok][E]
+// logits[t][e] = z_t . w_e with z fp32 (a bf16 hi + lo pair on the MFMA) and
+// w bf16; wave w sums K range [w d/8, (w+1) d/8) for every expert tile, KU
+// 32-deep k steps per round with all of the round's loads in flight; the
+// waves' partial logits meet in LDS. Then one wave per token picks the top k
+// (descending logit, ties to the lower expert index) and forms the weights.
+// MT: expert tiles held per wave (E <= 16 MT); KU: k steps per round.
+template <int MT, int KU>
+__global__ __launch_bounds__(kRW * 64) void router_topk_kernel(const RouterArgs p) {
+  extern __shared__ float part[];  // [kRW / 2][kTok][E]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -37,63 +45,88 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const RouterArgs p) {
   const int E = p.E;
   const int etiles = E / 16;
 
-  // B operand: z^T split into hi/lo bf16; lane (token col, group grp)
+  // B operand: z^T; lane (token col, k group grp)
   const int tok = t0 + col;
   const bool tv = tok < p.N;
-  const float* zr = p.zf + (size_t)(tv ? tok : 0) * p.d + 8 * grp;
+  const int kw = p.d / kRW;  // K per wave (a multiple of 32: d % 256 == 0)
+  const float* zr = p.zf + (size_t)(tv ? tok : 0) * p.d + wave * kw + 8 * grp;
+  const bf16* wr = p.wr + (size_t)col * p.d + wave * kw + 8 * grp;
 
-  for (int et0 = wave; et0 < etiles; et0 += 8) {
-    // two expert tiles per pass (et0 and et0 + 4) share the z fragments
-    const int et1 = et0 + 4;
-    const bool two = et1 < etiles;
-    const bf16* w0 = p.wr + (size_t)(et0 * 16 + col) * p.d + 8 * grp;
-    const bf16* w1 = p.wr + (size_t)((two ? et1 : et0) * 16 + col) * p.d + 8 * grp;
-    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < p.d; k += 32) {
-      float zv[8];
-      if (tv) {
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zr + k);
-        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zr + k + 4);
-        zv[0] = z0[0]; zv[1] = z0[1]; zv[2] = z0[2]; zv[3] = z0[3];
-        zv[4] = z1[0]; zv[5] = z1[1]; zv[6] = z1[2]; zv[7] = z1[3];
-      } else {
+  f32x4 acc[MT];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) zv[i] = 0.f;
-      }
+  for (int et = 0; et < MT; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < kw; k += 32 * KU) {
+    f32x4 z[KU][2];
+    bf16x8 wf[KU][MT];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      if (k + 32 * u >= kw) break;  // the wave's K range ends inside the round
+      z[u][0] = *reinterpret_cast<const f32x4*>(zr + k + 32 * u);
+      z[u][1] = *reinterpret_cast<const f32x4*>(zr + k + 32 * u + 4);
+#pragma unroll
+      for (int et = 0; et < MT; ++et)
+        if (et < etiles) wf[u][et] = load_bf16x8(wr + (size_t)et * 16 * p.d + k + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      if (k + 32 * u >= kw) break;
       bf16x8 zh, zl;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        zh[i] = (bf16)zv[i];
-        zl[i] = (bf16)(zv[i] - (float)zh[i]);
+      for (int i = 0; i < 4; ++i) {
+        const float v0 = tv ? z[u][0][i] : 0.f, v1 = tv ? z[u][1][i] : 0.f;
+        zh[i] = (bf16)v0;
+        zl[i] = (bf16)(v0 - (float)zh[i]);
+        zh[i + 4] = (bf16)v1;
+        zl[i + 4] = (bf16)(v1 - (float)zh[i + 4]);
       }
-      const bf16x8 wf0 = load_bf16x8(w0 + k);
-      a0 = mfma_16x16x32(wf0, zh, a0);
-      a0 = mfma_16x16x32(wf0, zl, a0);
-      if (two) {
-        const bf16x8 wf1 = load_bf16x8(w1 + k);
-        a1 = mfma_16x16x32(wf1, zh, a1);
-        a1 = mfma_16x16x32(wf1, zl, a1);
-      }
-    }
-    // lane holds D[expert 4*grp + r][token col]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      logit_lds[col * E + et0 * 16 + 4 * grp + r] = a0[r];
-      if (two) logit_lds[col * E + et1 * 16 + 4 * grp + r] = a1[r];
+      for (int et = 0; et < MT; ++et) {
+        if (et < etiles) {
+          acc[et] = mfma_16x16x32(wf[u][et], zh, acc[et]);
+          acc[et] = mfma_16x16x32(wf[u][et], zl, acc[et]);
+        }
+      }
     }
+  }
+  // lane holds D[expert 16 et + 4 grp + r][token col]; the upper half of the
+  // waves parks its partials, the lower half adds its own, then slot sums
+  constexpr int kHalf = kRW / 2;
+  if (wave >= kHalf) {
+#pragma unroll
+    for (int et = 0; et < MT; ++et)
+      if (et < etiles)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          part[((wave - kHalf) * kTok + col) * E + et * 16 + 4 * grp + r] = acc[et][r];
+  }
+  __syncthreads();
+  if (wave < kHalf) {
+#pragma unroll
+    for (int et = 0; et < MT; ++et)
+      if (et < etiles)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          part[(wave * kTok + col) * E + et * 16 + 4 * grp + r] += acc[et][r];
+  }
+  __syncthreads();
+  for (int i = tid; i < kTok * E; i += kRW * 64) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kHalf; ++w) v += part[w * kTok * E + i];
+    part[i] = v;  // slot 0 now holds the logits; each i is read and written by one thread
   }
   __syncthreads();
 
-  // top-k: one wave per token; lane holds experts lane, lane+64, ...
+  // top-k: one wave per token; lane holds experts lane, lane + 64, ...
   const int per = (E + 63) / 64;
-  for (int tl = wave; tl < kTok; tl += 4) {
+  for (int tl = wave; tl < kTok; tl += kRW) {
     const int t = t0 + tl;
     if (t >= p.N) break;
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + 64 * j;
-      v[j] = (j < per && e < E) ? logit_lds[tl * E + e] : -INFINITY;
+      v[j] = (j < per && e < E) ? part[tl * E + e] : -INFINITY;
     }
     if (p.logits) {
 #pragma unroll
@@ -110,8 +143,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const RouterArgs p) {
     for (int j = 0; j < 4; ++j) den_all += (v[j] == -INFINITY) ? 0.f : __expf(v[j] - mx);
     den_all = wave_sum(den_all);
 
-    float sel_v[kMaxTopK];
-    int sel_i[kMaxTopK];
+    // selection i lands in lane i (k <= 32 < 64 lanes)
+    float my_v = -INFINITY, top = -INFINITY;
+    int my_i = 0;
     for (int i = 0; i < p.k; ++i) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
@@ -135,21 +169,22 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const RouterArgs p) {
       // NaN logits compare false everywhere: keep the index in range so the
       // permutation never addresses outside its tables
       if (bi < 0 || bi >= E) bi = i % E;
-      sel_v[i] = bv;
-      sel_i[i] = bi;
+      if (i == 0) top = bv;
+      if (lane == i) {
+        my_v = bv;
+        my_i = bi;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (lane + 64 * j == bi) v[j] = -INFINITY;
     }
-    if (lane == 0) {
-      float den = 0.f;
-      for (int i = 0; i < p.k; ++i) den += __expf(sel_v[i] - sel_v[0]);
-      for (int i = 0; i < p.k; ++i) {
-        const float w = p.norm_topk ? __expf(sel_v[i] - sel_v[0]) / den
-                                    : __expf(sel_v[i] - mx) / den_all;
-        p.idx[(size_t)t * p.k + i] = sel_i[i];
-        p.w[(size_t)t * p.k + i] = w;
-      }
+    const bool mine = lane < p.k;
+    const float ew = mine ? __expf(my_v - top) : 0.f;
+    const float den = wave_sum(ew);
+    if (mine) {
+      const float w = p.norm_topk ? ew / den : __expf(my_v - mx) / den_all;
+      p.idx[(size_t)t * p.k + lane] = my_i;
+      p.w[(size_t)t * p.k + lane] = w;
     }
   }
 }
@@ -253,8 +288,12 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const CombineArgs p, c
 hipError_t ql_router_topk(const RouterArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
   const int blocks = (a.N + kTok - 1) / kTok;
-  hipLaunchKernelGGL(router_topk_kernel, dim3(blocks), dim3(256), kTok * a.E * sizeof(float), s,
-                     a);
+  const size_t lds = (size_t)(kRW / 2) * kTok * a.E * sizeof(float);
+  const int et = a.E / 16;
+  if (et <= 2) hipLaunchKernelGGL((router_topk_kernel<2, 4>), dim3(blocks), dim3(kRW * 64), lds, s, a);
+  else if (et <= 4) hipLaunchKernelGGL((router_topk_kernel<4, 4>), dim3(blocks), dim3(kRW * 64), lds, s, a);
+  else if (et <= 8) hipLaunchKernelGGL((router_topk_kernel<8, 2>), dim3(blocks), dim3(kRW * 64), lds, s, a);
+  else hipLaunchKernelGGL((router_topk_kernel<16, 1>), dim3(blocks), dim3(kRW * 64), lds, s, a);
   return hipGetLastError();
 }
 

@@ -1,4 +1,6 @@
-// Per-head QK-RMSNorm, rotate_half RoPE and the KV-cache write.
+// Per-head QK-RMSNorm, rotate_half RoPE and the KV-cache write, fp32 layer.
+// (The bf16 prefill does the same in the QKV GEMM's epilogue; bf16 decode in
+// the attention prologue.)
 //
 // Input: the projected rows qkv[n, Hq*dh + 2*Hkv*dh] in fp32 (bias already
 // added by the projection). For each token row and each head:
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
   const double omega = exp2(-2.0 * (double)i / (double)p.head_dim * log2((double)p.theta));
   double ang = pos * omega;
   const double two_pi = 6.283185307179586476925286766559;
-  ang -= two_pi * rint(ang / two_pi);
+  ang -= two_pi * rint(ang * (1.0 / two_pi));
   float sn, cs;
   sincosf((float)ang, &sn, &cs);
 
@@ -88,72 +90,6 @@ __global__ __launch_bounds__(256) void qkv_post_kernel(QkvPostArgs p) {
   }
 }
 
-// head_dim 128: one wave per (token row, head); lane i owns the pair
-// (i, i + 64). Q heads come first, then one wave per KV head writes both the
-// rotated K row and the V row.
-__global__ __launch_bounds__(256) void qkv_post_head_kernel(QkvPostArgs p) {
-  constexpr int kDh = 128;
-  const int lane = threadIdx.x & 63;
-  const int slots = p.n_q_heads + p.n_kv_heads;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= p.rows * slots) return;
-  const int n = item / slots;
-  const int slot = item % slots;
-  int b, crow;
-  if (p.cache_len) {
-    b = n;
-    crow = p.cache_len[b];
-  } else {
-    b = n / p.seq;
-    crow = n % p.seq;
-  }
-  const bool in_range = crow >= 0 && crow < p.T_max;
-  const int qd = p.n_q_heads * kDh;
-  const int kvd = p.n_kv_heads * kDh;
-  const bool is_q = slot < p.n_q_heads;
-  const int h = is_q ? slot : slot - p.n_q_heads;
-  if (!is_q && !in_range) return;  // never write outside the cache
-  const float* src = p.qkv + (size_t)n * p.ld_qkv;
-  const float* hs = src + (is_q ? h * kDh : qd + h * kDh);
-  float x0 = hs[lane];
-  float x1 = hs[lane + 64];
-  float vv0 = 0.f, vv1 = 0.f;
-  if (!is_q) {
-    vv0 = src[qd + kvd + h * kDh + lane];
-    vv1 = src[qd + kvd + h * kDh + lane + 64];
-  }
-  const double pos = (double)crow + (double)p.pos_offset;
-  const double omega = exp2(-2.0 * (double)lane / (double)kDh * log2((double)p.theta));
-  double ang = pos * omega;
-  const double two_pi = 6.283185307179586476925286766559;
-  ang -= two_pi * rint(ang / two_pi);
-  float sn, cs;
-  sincosf((float)ang, &sn, &cs);
-  const bf16* gam = static_cast<const bf16*>(is_q ? p.q_norm_g : p.k_norm_g);
-  if (gam) {
-    const float ss = wave_sum(x0 * x0 + x1 * x1);
-    const float inv = 1.0f / sqrtf(ss / (float)kDh + p.eps);
-    x0 = to_f32(gam[lane]) * (x0 * inv);
-    x1 = to_f32(gam[lane + 64]) * (x1 * inv);
-  }
-  float r0 = x0 * cs - x1 * sn;
-  float r1 = x0 * sn + x1 * cs;
-  if (is_q) {
-    if (!in_range) r0 = r1 = __builtin_nanf("");
-    bf16* dst = static_cast<bf16*>(p.q_out) + (size_t)n * qd + h * kDh;
-    dst[lane] = (bf16)r0;
-    dst[lane + 64] = (bf16)r1;
-  } else {
-    const size_t cache_row = ((size_t)b * p.T_max + crow) * (size_t)kvd + h * kDh;
-    bf16* kd = static_cast<bf16*>(p.k_cache) + cache_row;
-    bf16* vd = static_cast<bf16*>(p.v_cache) + cache_row;
-    kd[lane] = (bf16)r0;
-    kd[lane + 64] = (bf16)r1;
-    vd[lane] = (bf16)vv0;
-    vd[lane + 64] = (bf16)vv1;
-  }
-}
-
 template <class T>
 hipError_t launch(const QkvPostArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
@@ -166,11 +102,4 @@ hipError_t launch(const QkvPostArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t ql_qkv_post_bf16(const QkvPostArgs& a, hipStream_t s) {
-  if (a.head_dim != 128) return launch<bf16>(a, s);
-  const long long items = (long long)a.rows * (a.n_q_heads + a.n_kv_heads);
-  if (items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(qkv_post_head_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
 hipError_t ql_qkv_post_f32(const QkvPostArgs& a, hipStream_t s) { return launch<float>(a, s); }

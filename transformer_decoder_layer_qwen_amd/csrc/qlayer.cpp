@@ -151,8 +151,8 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
   if (c->dtype == QL_BF16) {
     if (c->head_dim != 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs head_dim == 128");
     if (c->d % 256) return fail(QL_EUNSUPPORTED, "QL_BF16 needs d %% 256 == 0");
-    if ((c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim % 256)
-      return fail(QL_EUNSUPPORTED, "QL_BF16 needs (Hq + 2 Hkv) * head_dim %% 256 == 0");
+    if (c->n_q_heads % 2 || c->n_kv_heads % 2)
+      return fail(QL_EUNSUPPORTED, "QL_BF16 needs even n_q_heads and n_kv_heads");
     if (c->ffn_dim % 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs ffn_dim %% 128 == 0");
     if (G > 16) return fail(QL_EUNSUPPORTED, "QL_BF16 needs n_q_heads / n_kv_heads <= 16");
     if (c->max_batch > 128) return fail(QL_EUNSUPPORTED, "QL_BF16 decode needs max_batch <= 128");
@@ -407,30 +407,23 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   const bf16* bq = c.qkv_bias ? static_cast<const bf16*>(w.bq) : nullptr;
   const bf16* bk = c.qkv_bias ? static_cast<const bf16*>(w.bk) : nullptr;
   const bf16* bv = c.qkv_bias ? static_cast<const bf16*>(w.bv) : nullptr;
+  // QKV projection with QK-norm, RoPE and the cache write in its epilogue
+  QkvFinish f{};
+  f.S = S;
+  f.pos_offset = pos_offset;
+  f.T_max = T_max;
+  f.eps = c.rms_eps;
+  f.omega = h->rope_omega;
+  f.q_norm_g = c.qk_norm ? static_cast<const bf16*>(w.q_norm_g) : nullptr;
+  f.k_norm_g = c.qk_norm ? static_cast<const bf16*>(w.k_norm_g) : nullptr;
+  f.q_out = static_cast<bf16*>(h->q);
+  f.k_cache = static_cast<bf16*>(kc);
+  f.v_cache = static_cast<bf16*>(vc);
   QL_STAGE(h, QL_STAGE_QKV, s,
            QL_HIP(ql_gemm2_qkv(xhat, N, static_cast<const bf16*>(w.wq),
                                static_cast<const bf16*>(w.wk), static_cast<const bf16*>(w.wv),
-                               h->q_dim, h->kv_dim, c.d, bq, bk, bv, h->qkv,
+                               h->q_dim, h->kv_dim, c.d, bq, bk, bv, f,
                                gemm2_splits(N, h->qkv_dim, 2 * c.d), h->g2part, s)));
-  QkvPostArgs qa{};
-  qa.qkv = h->qkv;
-  qa.ld_qkv = h->qkv_dim;
-  qa.rows = N;
-  qa.seq = S;
-  qa.cache_len = nullptr;
-  qa.T_max = T_max;
-  qa.pos_offset = pos_offset;
-  qa.n_q_heads = c.n_q_heads;
-  qa.n_kv_heads = c.n_kv_heads;
-  qa.head_dim = c.head_dim;
-  qa.eps = c.rms_eps;
-  qa.theta = c.rope_theta;
-  qa.q_norm_g = c.qk_norm ? w.q_norm_g : nullptr;
-  qa.k_norm_g = c.qk_norm ? w.k_norm_g : nullptr;
-  qa.q_out = h->q;
-  qa.k_cache = kc;
-  qa.v_cache = vc;
-  QL_STAGE(h, QL_STAGE_QKV_POST, s, QL_HIP(ql_qkv_post_bf16(qa, s)));
   AttnPrefillArgs pa{};
   pa.q = static_cast<const bf16*>(h->q);
   pa.k_cache = static_cast<const bf16*>(kc);

@@ -154,10 +154,6 @@ hipError_t ql_rmsnorm_bf16(const bf16* x, const bf16* gamma, bf16* out, float* o
                            int d, float eps, hipStream_t s) {
   return launch<bf16, bf16, bf16>(x, gamma, out, out_f32, rows, d, eps, s);
 }
-hipError_t ql_rmsnorm_bf16_to_f32(const bf16* x, const bf16* gamma, float* out, int rows, int d,
-                                  float eps, hipStream_t s) {
-  return launch<bf16, bf16, float>(x, gamma, out, nullptr, rows, d, eps, s);
-}
 hipError_t ql_rmsnorm_bf16_to_hilo(const bf16* x, const bf16* gamma, bf16* out, int rows, int d,
                                    float eps, hipStream_t s) {
   return launch<bf16, bf16, bf16, true>(x, gamma, out, nullptr, rows, d, eps, s);
