@@ -44,9 +44,8 @@ enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU };
 
 constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2;
 constexpr int kGroupM = 4;  // tile rows per L2 group
-constexpr int kStageBytes = (BM + BN) * BK * 2;       // 64 KiB
-constexpr int kChunks = (BM + BN) * BK / 8;            // 16-byte chunks per stage
-constexpr int kRowChunks = BK / 8;                     // chunks per LDS row
+constexpr int kStageBytes = (BM + BN) * BK * 2;       // 64 KiB (256-row tiles)
+constexpr int kRowChunks = BK / 8;                     // 16-byte chunks per LDS row
 constexpr int kPitch = BN + 4;                         // fp32 epilogue tile pitch
 constexpr int kEpiBytes = (BM / 2) * kPitch * 4;       // half a tile
 constexpr int kLdsBytes = NSTAGE * kStageBytes > kEpiBytes ? NSTAGE * kStageBytes : kEpiBytes;
@@ -159,44 +158,56 @@ QL_DEV void wait_vmcnt() {
 }
 
 // PART: write this split's fp32 partial tile instead of MODE's epilogue.
-// NW waves (4 or 8): waves are 2 (rows) x NW/2 (columns); a wave owns
-// 128 x (256 / (NW/2)) of the tile. With 8 waves two share each SIMD, so one
-// wave's MFMAs run while the other waits on LDS or the barrier.
-template <int MODE, bool PART, int NW, bool DMA>
-__global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) {
+// BMT = 256: 8 waves as 2 (rows) x 4 (columns), a wave owns 128 x 64; two
+// waves share each SIMD, so one wave's MFMAs run while the other waits.
+// (BMT = 128 would be 4 waves as 1 x 4.)
+template <int MODE, bool PART, int BMT>
+__global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G2Args p) {
+  constexpr int NW = BMT / 32;          // waves
   constexpr int NT = NW * 64;           // threads
-  constexpr int WNW = NW / 2;           // waves along N
+  constexpr int WMW = BMT / 128;        // waves along M
+  constexpr int WNW = NW / WMW;         // waves along N
   constexpr int WCOLS = BN / WNW;       // columns per wave
   constexpr int TJ = WCOLS / 32;        // 32-wide MFMA tiles per wave along N
-  constexpr int LPT = kChunks / NT;     // direct loads per thread per stage
+  constexpr int AC = BMT * kRowChunks;  // A chunks per stage
+  constexpr int CH = AC + BN * kRowChunks;
+  constexpr int LPT = CH / NT;          // direct loads per thread per stage
+  constexpr int LPA = AC / NT;          // ... of which A
+  constexpr int SB = CH * 16;           // stage bytes
+  constexpr bool kDual = MODE == G2_SWIGLU;
+  static_assert(CH % NT == 0 && AC % NT == 0, "whole loads per thread");
+  static_assert(NSTAGE * SB <= kLdsBytes, "LDS ring");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
 
-  // XCD-aware tile order. Consecutive block ids go to the 8 XCDs round-robin,
-  // each XCD with its own L2; so block b works on item (b % 8) * chunk + b / 8
-  // of the work list, and every XCD walks a contiguous stretch of it. The list
-  // orders (split, tile) split-major, tiles in groups of kGroupM tile rows x
-  // all tile columns, column-major inside a group: the ~32 blocks an XCD runs
-  // at once share 4 A tiles and 8 B tiles, which its L2 then serves.
-  const int ntiles = p.tiles_m * p.tiles_n;
-  const int total = ntiles * p.splits;
-  const int chunk = (total + 7) / 8;
-  const int w = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
-  if (w >= total) return;
-  const int split = w / ntiles;
-  const int pid = w % ntiles;
-  const int group = pid / (kGroupM * p.tiles_n);
-  const int first_m = group * kGroupM;
-  const int gsize = min(p.tiles_m - first_m, kGroupM);
-  const int in_group = pid % (kGroupM * p.tiles_n);
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int m0 = tm * BM;
-  const int rows_valid = min(BM, p.M - m0);
-  constexpr bool kDual = MODE == G2_SWIGLU;
+  int split = 0, tn, m0, rows_valid;
+  {
+    // XCD-aware tile order. Consecutive block ids go to the 8 XCDs
+    // round-robin, each XCD with its own L2; so block b works on item
+    // (b % 8) * chunk + b / 8 of the work list, and every XCD walks a
+    // contiguous stretch of it. The list orders (split, tile) split-major,
+    // tiles in groups of kGroupM tile rows x all tile columns, column-major
+    // inside a group: the blocks an XCD runs at once share a few A and B
+    // tiles, which its L2 then serves.
+    const int ntiles = p.tiles_m * p.tiles_n;
+    const int total = ntiles * p.splits;
+    const int chunk = (total + 7) / 8;
+    const int w = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
+    if (w >= total) return;
+    split = w / ntiles;
+    const int pid = w % ntiles;
+    const int group = pid / (kGroupM * p.tiles_n);
+    const int first_m = group * kGroupM;
+    const int gsize = min(p.tiles_m - first_m, kGroupM);
+    const int in_group = pid % (kGroupM * p.tiles_n);
+    const int tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+    m0 = tm * BMT;
+    rows_valid = min(BMT, p.M - m0);
+  }
   const int n0 = tn * (kDual ? BN / 2 : BN);  // first output column of the tile
 
   // QKV: a 256-column tile lies inside one of the three weight matrices
@@ -215,18 +226,19 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
     }
   }
 
-  // Direct-load plan: per stage the block fills kChunks 16-byte LDS chunks (A
+  // Direct-load plan: per stage the block fills CH 16-byte LDS chunks (A
   // first, then B); load j of wave w covers chunks (NW j + w) * 64 + lane, i.e.
   // 8 whole 128-byte rows, each one full cache line of A or B.
   const bf16* src[LPT];
 #pragma unroll
   for (int j = 0; j < LPT; ++j) {
     const int P = (NW * j + wave) * 64 + lane;
-    const int Q = P & (kChunks / 2 - 1);
+    const bool is_a = j < LPA;
+    const int Q = is_a ? P : P - AC;
     const int row = Q / kRowChunks;
     const int c = (Q % kRowChunks) ^ swz(row);
-    if (j < LPT / 2) {
-      const int rr = min(row, rows_valid - 1);  // rows past M re-read a valid row
+    if (is_a) {
+      const int rr = min(row, rows_valid - 1);  // rows past the tile re-read a valid row
       src[j] = p.A + (size_t)(m0 + rr) * p.lda + c * 8;
     } else {
       const bf16* base;
@@ -246,26 +258,10 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
     const int ka = (ks0 + kt) * BK;
     int kb = ka;
     if (kb >= p.Kb) kb -= p.Kb;  // [hi | lo] A: B is read twice
-    char* slot = smem + (kt % NSTAGE) * kStageBytes;
+    char* slot = smem + (kt % NSTAGE) * SB;
 #pragma unroll
     for (int j = 0; j < LPT; ++j)
-      load_lds16(src[j] + (j < LPT / 2 ? ka : kb), slot + (NW * j + wave) * 1024);
-  };
-  // register-staged alternative: global -> VGPRs, later VGPRs -> LDS
-  u32x4 stg[DMA ? 1 : LPT];
-  auto gload = [&](int kt) {
-    const int ka = (ks0 + kt) * BK;
-    int kb = ka;
-    if (kb >= p.Kb) kb -= p.Kb;
-#pragma unroll
-    for (int j = 0; j < (DMA ? 0 : LPT); ++j)
-      stg[j] = *reinterpret_cast<const u32x4*>(src[j] + (j < LPT / 2 ? ka : kb));
-  };
-  auto swrite = [&](int kt) {
-    char* slot = smem + (kt % NSTAGE) * kStageBytes;
-#pragma unroll
-    for (int j = 0; j < (DMA ? 0 : LPT); ++j)
-      *reinterpret_cast<u32x4*>(slot + (NW * j + wave) * 1024 + lane * 16) = stg[j];
+      load_lds16(src[j] + (j < LPA ? ka : kb), slot + (NW * j + wave) * 1024);
   };
 
   f32x16 acc[4][TJ];
@@ -292,7 +288,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int rb = wn * WCOLS + 32 * j + fr;
-      boff[ks][j] = kStageBytes / 2 + (rb * kRowChunks + (c ^ swz(rb))) * 16;
+      boff[ks][j] = AC * 16 + (rb * kRowChunks + (c ^ swz(rb))) * 16;
     }
   }
 
@@ -319,8 +315,19 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
   };
   static_assert(KS == 4, "two halves of two k steps per stage");
-  auto compute = [&](int kt) {
-    const char* st = smem + (kt % NSTAGE) * kStageBytes;
+
+  // Two stages; stage kt+1 is requested right after the barrier that publishes
+  // stage kt and lands while stage kt is multiplied.
+  if (nk > 0) issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();  // this wave's part of stage kt (the only stage in flight)
+    // every wave's part of stage kt has landed and every wave is done with
+    // the other slot. A bare s_barrier: __syncthreads' release fence adds
+    // nothing here; the acquire fence keeps the LDS reads below it.
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (kt + 1 < nk) issue(kt + 1);
+    const char* st = smem + (kt % NSTAGE) * SB;
     bf16x8 a0[2][4], b0[2][TJ], a1[2][4], b1[2][TJ];
     read2(st, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
@@ -330,42 +337,13 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
     __builtin_amdgcn_sched_barrier(0);
     mma2(a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-  };
-  if constexpr (DMA) {
-    // Two stages; stage kt+1 is requested right after the barrier that
-    // publishes stage kt and lands while stage kt is multiplied.
-    if (nk > 0) issue(0);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<0>();  // this wave's part of stage kt (the only stage in flight)
-      // every wave's part of stage kt has landed and every wave is done with
-      // the other slot; the acquire fence keeps the LDS reads below it
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      if (kt + 1 < nk) issue(kt + 1);
-      compute(kt);
-    }
-  } else {
-    // Registers hold stage kt+1 while stage kt is multiplied; they go to the
-    // other LDS slot after the MFMAs, then stage kt+2 is requested.
-    if (nk > 0) {
-      gload(0);
-      swrite(0);
-    }
-    if (nk > 1) gload(1);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      compute(kt);
-      if (kt + 1 < nk) swrite(kt + 1);
-      if (kt + 2 < nk) gload(kt + 2);
-      __syncthreads();
-    }
   }
   __syncthreads();  // the ring is reused for the epilogue
 
-  // ---- epilogue: half a tile (one wm row of waves) at a time through LDS ----
+  // ---- epilogue: 128 rows (one row of waves) at a time through LDS ----
   float* C = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int half = 0; half < WMW; ++half) {
     if (wm == half) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -396,10 +374,10 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
         if (rbase + r >= rows_valid) break;
         const float* g = C + r * kPitch + seg * 8;
         const float* u = g + BN / 2;
-        float h[8];
+        float hv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = silu_f32(g[e]) * u[e];
-        store_bf16x8(p.out_bf16 + (size_t)(m0 + rbase + r) * p.ldo + n0 + seg * 8, pack8(h));
+        for (int e = 0; e < 8; ++e) hv[e] = silu_f32(g[e]) * u[e];
+        store_bf16x8(p.out_bf16 + (size_t)(m0 + rbase + r) * p.ldo + n0 + seg * 8, pack8(hv));
       }
     } else {
       const int seg = tid & 31;
@@ -437,7 +415,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4) void gemm2_kernel(const G2Args p) 
             v[e + 4] += r1[e];
           }
           store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
-        } else {
+        } else {  // RESID_F32: fp32 rows
           float* o = p.out_f32 + row * p.ldo + col;
           *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
           *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -527,9 +505,7 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
   }
 }
 
-constexpr int kWaves = 8;
-
-template <int MODE, int NW = kWaves, bool DMA = true>
+template <int MODE>
 hipError_t run(G2Args a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   a.tiles_m = (a.M + BM - 1) / BM;
@@ -540,10 +516,10 @@ hipError_t run(G2Args a, hipStream_t s) {
   const int total = a.tiles_m * a.tiles_n * a.splits;
   const dim3 grid(8 * ((total + 7) / 8));
   if (a.splits == 1) {
-    hipLaunchKernelGGL((gemm2_kernel<MODE, false, NW, DMA>), grid, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((gemm2_kernel<MODE, false, 256>), grid, dim3(512), 0, s, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((gemm2_kernel<MODE, true, NW, DMA>), grid, dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm2_kernel<MODE, true, 256>), grid, dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int segs = (MODE == G2_SWIGLU ? a.tiles_n * BN / 2 : a.tiles_n * BN) / 8;
@@ -639,3 +615,4 @@ hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu,
   a.tiles_n = F / (BN / 2);
   return run<G2_SWIGLU>(a, s);
 }
+
