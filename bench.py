@@ -295,12 +295,14 @@ def time_empty_span(hip, steps):
 
 
 def stages_of(cfg, kind, batch):
-    # decode fuses RMSNorm1 into the QKV projection and the QK-norm / RoPE /
-    # cache append into the attention kernel
-    # (prefill: the QKV GEMM's epilogue does QK-norm, RoPE and the cache write)
-    s = (["rmsnorm1", "qkv"] if kind == "prefill" else ["qkv"])
+    # decode with at most GEMV_MAX_ROWS sequences fuses RMSNorm1 into the QKV
+    # projection, QK-norm / RoPE / cache append into attention and (dense FFN)
+    # RMSNorm2 into gate/up; prefill and larger decode batches run RMSNorm1 on
+    # its own and do QK-norm, RoPE and the cache write in the QKV epilogue
+    gemv = kind == "decode" and batch <= GEMV_MAX_ROWS
+    s = (["qkv"] if gemv else ["rmsnorm1", "qkv"])
     s += ["attention", "o_proj"]
-    if not (kind == "decode" and not cfg.is_moe and batch <= GEMV_MAX_ROWS):
+    if not (gemv and not cfg.is_moe):
         s += ["rmsnorm2"]
     s += (["router", "permute", "expert_gate_up", "expert_down", "combine"] if cfg.is_moe
           else ["gate_up", "down"])
@@ -314,7 +316,7 @@ def stages_of(cfg, kind, batch):
 PMC_FETCH_SCALE = 262144.0 / 131085.4
 PMC_WRITE_SCALE = 262144.0 / 262144.0
 PMC_TRAFFIC_KIB = {
-    # profiles/gemv_gate_up_qwen25_7b_decode_b1_hbm_counters.txt (csrc/gemv.hip as of e72cee5)
+    # profiles/gemv_gate_up_qwen25_7b_decode_b1_hbm_counters.md (csrc/gemv.hip as of e72cee5)
     ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132731.3, 296.2),
 }
 

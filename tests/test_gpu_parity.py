@@ -149,11 +149,14 @@ def test_small_bf16_prefill_stages():
             assert v <= 1.0, (k, v)
 
 
-def test_small_bf16_decode_ragged_lengths():
+# up to 4 sequences take the VALU GEMV path, more the MFMA tiles; lengths
+# include an empty cache (0) and a full one (T_max - 1)
+@pytest.mark.parametrize("lens", [[5, 100, 257], [0, 5, 100, 257, 31, 128, 299]],
+                         ids=["gemv_B3", "mfma_B7"])
+def test_small_bf16_decode_ragged_lengths(lens):
     cfg = small_cfg()
-    lens = [5, 100, 257]
     Bn, T_max = len(lens), 300
-    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=4)
+    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=8)
     q_t = torch.empty(Bn, cfg.q_dim, dtype=torch.bfloat16, device="cuda")
     a_t = torch.empty(Bn, cfg.q_dim, dtype=torch.float32, device="cuda")
     r_t = torch.empty(Bn, cfg.d, dtype=torch.float32, device="cuda")
@@ -189,23 +192,25 @@ def test_small_bf16_decode_ragged_lengths():
                         noise=1e-4) <= 1.0
 
 
-def test_decode_out_of_range_length_is_contained():
+@pytest.mark.parametrize("lens", [[8, 16], [8, 16, 3, 0, 5, 7]], ids=["gemv_B2", "mfma_B6"])
+def test_decode_out_of_range_length_is_contained(lens):
     cfg = small_cfg()
-    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=4)
+    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=8)
     T_max = 16
-    x, kc, vc, _ = synth.make_decode_input(cfg, 1005, 2, 8, T_max=T_max)
+    Bn = len(lens)
+    x, kc, vc, _ = synth.make_decode_input(cfg, 1005, Bn, 8, T_max=T_max)
     kd, vd = B.to_device(kc), B.to_device(vc)
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
     with pytest.raises(B.QLayerError) as e:
-        layer.decode(B.to_device(x), torch.tensor([8, 16], dtype=torch.int32, device="cuda"),
-                     kd, vd, cache_len_host=[8, 16])
+        layer.decode(B.to_device(x), ld, kd, vd, cache_len_host=lens)
     assert e.value.status == B.QL_ECACHE_FULL
     # without the host copy the kernels contain it: NaN output, no write
     before = host(kd).copy()
-    y = layer.decode(B.to_device(x), torch.tensor([8, 16], dtype=torch.int32, device="cuda"),
-                     kd, vd)
+    y = layer.decode(B.to_device(x), ld, kd, vd)
     torch.cuda.synchronize()
     yh = host(y)
-    assert np.all(np.isfinite(yh[0])) and np.all(np.isnan(yh[1]))
+    assert np.all(np.isnan(yh[1]))
+    assert np.all(np.isfinite(np.delete(yh, 1, axis=0)))
     after = host(kd)
     assert np.array_equal(after[1], before[1], equal_nan=True)
 

@@ -32,6 +32,11 @@
 // them to the cache and uses them from LDS ("Qwen2.5-7B 结构拆解" §09.1;
 // "推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §5, §6, §12). All cache,
 // projection, bias and norm loads are issued before any is waited on.
+// QR: the projection already finished q and appended the new row (larger
+// batches, where the projection runs on MFMA tiles); the wave only attends.
+//
+// Output: fp32, or (out_hilo) the bf16 pair hi = RNE(o), lo = RNE(o - hi)
+// that the O projection takes as its A operand.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,7 +44,21 @@ namespace {
 
 constexpr int kDh = 128;
 
-template <int G>
+// 8 output values of one head -> fp32 or the bf16 hi/lo pair
+QL_DEV void store_out8(const AttnDecodeArgs& p, size_t idx, const float (&v)[8]) {
+  if (p.out_hilo) {
+    float lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lo[e] = v[e] - (float)(bf16)v[e];
+    store_bf16x8(p.out_hilo + idx, pack8(v));
+    store_bf16x8(p.out_hilo + idx + p.lo_off, pack8(lo));
+  } else {
+    *reinterpret_cast<f32x4*>(p.out + idx) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p.out + idx + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+template <int G, bool QR>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attn_decode_kernel(const AttnDecodeArgs p) {
   constexpr int HPL = (G + 3) / 4;  // heads per lane in P V
   __shared__ float p_lds[16 * 16];  // P[key 16][head 16]
@@ -88,115 +107,129 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
 
   const int qd = p.n_q_heads * kDh;
   const int kvd = p.n_kv_heads * kDh;
-  const float* raw = p.qkv_raw + (size_t)b * p.ld_raw;
-  // slots 0 .. G-1: the group's query heads; G, G+1: the new K and V row
-  float hv[G + 2][2], hb[G + 2][2];
+  // Q^T fragments: lane (head col, group grp) holds dh [32s + 8grp, +8)
+  bf16x8 qf[4];
+  if constexpr (QR) {  // finished queries; columns >= G are zero padding
+    const bf16* qrow = p.q_in + (size_t)b * qd + (size_t)(g * G + min(col, G - 1)) * kDh;
 #pragma unroll
-  for (int i = 0; i < G + 2; ++i) {
-    const int c0 = i < G ? (g * G + i) * kDh : (i == G ? qd + g * kDh : qd + kvd + g * kDh);
-    hv[i][0] = raw[c0 + lane];
-    hv[i][1] = raw[c0 + lane + 64];
-    const bf16* bias = i < G ? p.bq : (i == G ? p.bk : p.bv);
-    const bf16* bsrc = bias ? bias + (i < G ? c0 : g * kDh) : p.x;
-    const float b0 = to_f32(bsrc[lane]), b1 = to_f32(bsrc[lane + 64]);
-    hb[i][0] = bias ? b0 : 0.f;
-    hb[i][1] = bias ? b1 : 0.f;
+    for (int s = 0; s < 4; ++s) qf[s] = load_bf16x8(qrow + 32 * s + 8 * grp);
+    if (col >= G) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qf[s] = bf16x8{};
+    }
   }
-  const float inv_given = p.inv_rms ? p.inv_rms[b] : 0.f;
-  const bool qkn = p.q_norm_g != nullptr;
-  const bf16* qgs = qkn ? p.q_norm_g : p.x;
-  const bf16* kgs = qkn ? p.k_norm_g : p.x;
-  const float qg0r = to_f32(qgs[lane]), qg1r = to_f32(qgs[lane + 64]);
-  const float kg0r = to_f32(kgs[lane]), kg1r = to_f32(kgs[lane + 64]);
-  const double omega = p.rope_omega[lane];
-
   const bool valid = L >= 0 && L < p.T_max;
   const int nkeys = valid ? L + 1 : 0;
   const int kend = min(kbeg + p.chunk, nkeys);
-  const bool has_new = valid && kbeg <= L && L < kend;
+  const bool has_new = !QR && valid && kbeg <= L && L < kend;
   // first-tile rows past the live keys may hold anything (a NaN would survive
-  // a zero softmax weight in P V): zero their V
+  // a zero softmax weight in P V): zero their V, once every load is out
+  auto zero_dead_v = [&]() {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (kbeg + 4 * grp + j >= kend) vcur[j] = zero4;
-
-  // ---- prologue: RMSNorm1 scale, q heads, the appended K/V row ----
-  float inv = inv_given;
-  if (!p.inv_rms) {
-    const bf16* xr = p.x + (size_t)b * p.d;
-    float ss = 0.f;
-    for (int c = lane * 8; c < p.d; c += 64 * 8) {
-      float f[8];
-      unpack8(load_bf16x8(xr + c), f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
-    }
-    inv = 1.0f / sqrtf(wave_sum(ss) / (float)p.d + p.eps);
-  }
-  float sn, cs;
-  {
-    double ang = ((double)L + (double)p.pos_offset) * omega;
-    const double two_pi = 6.283185307179586476925286766559;
-    ang -= two_pi * rint(ang * (1.0 / two_pi));
-    sincosf((float)ang, &sn, &cs);
-  }
-  // one head's 128 values: lane owns (lane, lane + 64); scale, bias, norm, rotate
-  auto head_vec = [&](int i, bool norm, float g0, float g1, bool rotate, float& o0, float& o1) {
-    float x0 = inv * hv[i][0] + hb[i][0];
-    float x1 = inv * hv[i][1] + hb[i][1];
-    if (norm) {
-      const float hs = wave_sum(x0 * x0 + x1 * x1);
-      const float hinv = 1.0f / sqrtf(hs / (float)kDh + p.eps);
-      x0 = g0 * (x0 * hinv);
-      x1 = g1 * (x1 * hinv);
-    }
-    if (rotate) {
-      o0 = x0 * cs - x1 * sn;
-      o1 = x0 * sn + x1 * cs;
-    } else {
-      o0 = x0;
-      o1 = x1;
-    }
+    for (int j = 0; j < 4; ++j)
+      if (kbeg + 4 * grp + j >= kend) vcur[j] = zero4;
   };
-#pragma unroll
-  for (int hh = 0; hh < 16; ++hh) {
-    float r0 = 0.f, r1 = 0.f;
-    if (hh < G) {
-      head_vec(hh, qkn, qg0r, qg1r, true, r0, r1);
-      if (split == 0 && p.q_out) {
-        const int hq = g * G + hh;
-        const float nv = valid ? 0.f : __builtin_nanf("");
-        p.q_out[(size_t)b * qd + hq * kDh + lane] = (bf16)(r0 + nv);
-        p.q_out[(size_t)b * qd + hq * kDh + lane + 64] = (bf16)(r1 + nv);
-      }
-    }
-    q_lds[hh][lane] = (bf16)r0;
-    q_lds[hh][lane + 64] = (bf16)r1;
-  }
-  if (has_new) {
-    float k0, k1, v0, v1;
-    head_vec(G, qkn, kg0r, kg1r, true, k0, k1);
-    head_vec(G + 1, false, 1.f, 1.f, false, v0, v1);
-    const size_t crow = ((size_t)b * p.T_max + L) * kvd + g * kDh;
-    const bf16 bk0 = (bf16)k0, bk1 = (bf16)k1, bv0 = (bf16)v0, bv1 = (bf16)v1;
-    p.k_cache_w[crow + lane] = bk0;
-    p.k_cache_w[crow + lane + 64] = bk1;
-    p.v_cache_w[crow + lane] = bv0;
-    p.v_cache_w[crow + lane + 64] = bv1;
-    kv_new[0][lane] = bk0;
-    kv_new[0][lane + 64] = bk1;
-    kv_new[1][lane] = bv0;
-    kv_new[1][lane + 64] = bv1;
-  }
-  // LDS traffic of one wave is processed in order; the barrier only keeps the
-  // compiler from moving LDS accesses across it
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if constexpr (QR) zero_dead_v();
 
-  // Q^T fragments: lane (head col, group grp) holds dh [32s + 8grp, +8)
-  bf16x8 qf[4];
+  if constexpr (!QR) {
+    const float* raw = p.qkv_raw + (size_t)b * p.ld_raw;
+    // slots 0 .. G-1: the group's query heads; G, G+1: the new K and V row
+    float hv[G + 2][2], hb[G + 2][2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(&q_lds[col][32 * s + 8 * grp]);
+    for (int i = 0; i < G + 2; ++i) {
+      const int c0 = i < G ? (g * G + i) * kDh : (i == G ? qd + g * kDh : qd + kvd + g * kDh);
+      hv[i][0] = raw[c0 + lane];
+      hv[i][1] = raw[c0 + lane + 64];
+      const bf16* bias = i < G ? p.bq : (i == G ? p.bk : p.bv);
+      const bf16* bsrc = bias ? bias + (i < G ? c0 : g * kDh) : p.x;
+      const float b0 = to_f32(bsrc[lane]), b1 = to_f32(bsrc[lane + 64]);
+      hb[i][0] = bias ? b0 : 0.f;
+      hb[i][1] = bias ? b1 : 0.f;
+    }
+    const float inv_given = p.inv_rms ? p.inv_rms[b] : 0.f;
+    const bool qkn = p.q_norm_g != nullptr;
+    const bf16* qgs = qkn ? p.q_norm_g : p.x;
+    const bf16* kgs = qkn ? p.k_norm_g : p.x;
+    const float qg0r = to_f32(qgs[lane]), qg1r = to_f32(qgs[lane + 64]);
+    const float kg0r = to_f32(kgs[lane]), kg1r = to_f32(kgs[lane + 64]);
+    const double omega = p.rope_omega[lane];
+    zero_dead_v();
+
+    // ---- prologue: RMSNorm1 scale, q heads, the appended K/V row ----
+    float inv = inv_given;
+    if (!p.inv_rms) {
+      const bf16* xr = p.x + (size_t)b * p.d;
+      float ss = 0.f;
+      for (int c = lane * 8; c < p.d; c += 64 * 8) {
+        float f[8];
+        unpack8(load_bf16x8(xr + c), f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+      }
+      inv = 1.0f / sqrtf(wave_sum(ss) / (float)p.d + p.eps);
+    }
+    float sn, cs;
+    {
+      double ang = ((double)L + (double)p.pos_offset) * omega;
+      const double two_pi = 6.283185307179586476925286766559;
+      ang -= two_pi * rint(ang * (1.0 / two_pi));
+      sincosf((float)ang, &sn, &cs);
+    }
+    // one head's 128 values: lane owns (lane, lane + 64); scale, bias, norm, rotate
+    auto head_vec = [&](int i, bool norm, float g0, float g1, bool rotate, float& o0, float& o1) {
+      float x0 = inv * hv[i][0] + hb[i][0];
+      float x1 = inv * hv[i][1] + hb[i][1];
+      if (norm) {
+        const float hs = wave_sum(x0 * x0 + x1 * x1);
+        const float hinv = 1.0f / sqrtf(hs / (float)kDh + p.eps);
+        x0 = g0 * (x0 * hinv);
+        x1 = g1 * (x1 * hinv);
+      }
+      if (rotate) {
+        o0 = x0 * cs - x1 * sn;
+        o1 = x0 * sn + x1 * cs;
+      } else {
+        o0 = x0;
+        o1 = x1;
+      }
+    };
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      float r0 = 0.f, r1 = 0.f;
+      if (hh < G) {
+        head_vec(hh, qkn, qg0r, qg1r, true, r0, r1);
+        if (split == 0 && p.q_out) {
+          const int hq = g * G + hh;
+          const float nv = valid ? 0.f : __builtin_nanf("");
+          p.q_out[(size_t)b * qd + hq * kDh + lane] = (bf16)(r0 + nv);
+          p.q_out[(size_t)b * qd + hq * kDh + lane + 64] = (bf16)(r1 + nv);
+        }
+      }
+      q_lds[hh][lane] = (bf16)r0;
+      q_lds[hh][lane + 64] = (bf16)r1;
+    }
+    if (has_new) {
+      float k0, k1, v0, v1;
+      head_vec(G, qkn, kg0r, kg1r, true, k0, k1);
+      head_vec(G + 1, false, 1.f, 1.f, false, v0, v1);
+      const size_t crow = ((size_t)b * p.T_max + L) * kvd + g * kDh;
+      const bf16 bk0 = (bf16)k0, bk1 = (bf16)k1, bv0 = (bf16)v0, bv1 = (bf16)v1;
+      p.k_cache_w[crow + lane] = bk0;
+      p.k_cache_w[crow + lane + 64] = bk1;
+      p.v_cache_w[crow + lane] = bv0;
+      p.v_cache_w[crow + lane + 64] = bv1;
+      kv_new[0][lane] = bk0;
+      kv_new[0][lane + 64] = bk1;
+      kv_new[1][lane] = bv0;
+      kv_new[1][lane + 64] = bv1;
+    }
+    // LDS traffic of one wave is processed in order; the barrier only keeps the
+    // compiler from moving LDS accesses across it
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(&q_lds[col][32 * s + 8 * grp]);
+  }
 
   float acc[HPL][8];
 #pragma unroll
@@ -305,15 +338,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
     const int hq = g * G + h;
     if (p.nsplit == 1) {  // the only split: normalise here
       const float rl = valid ? 1.0f / a_lds[h] : __builtin_nanf("");
-      float* o = p.out + (size_t)b * p.ldo + (size_t)hq * kDh + col * 8;
-      f32x4 o0, o1;
+      float o[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o0[e] = acc[i][e] * rl;
-        o1[e] = acc[i][e + 4] * rl;
-      }
-      *reinterpret_cast<f32x4*>(o) = o0;
-      *reinterpret_cast<f32x4*>(o + 4) = o1;
+      for (int e = 0; e < 8; ++e) o[e] = acc[i][e] * rl;
+      store_out8(p, (size_t)b * p.ldo + (size_t)hq * kDh + col * 8, o);
     } else {
       const size_t slot = ((size_t)b * p.n_q_heads + hq) * p.nsplit + split;
       float* o = p.part_o + slot * kDh + col * 8;
@@ -413,8 +441,15 @@ __global__ __launch_bounds__(kCombineThreads) void attn_decode_combine_kernel(co
 #pragma unroll
     for (int i = 0; i < kQ; ++i) tot += qsum[i][d];
     const bool valid = L >= 0 && L < p.T_max;
-    p.out[(size_t)b * p.ldo + (size_t)(bh % p.n_q_heads) * kDh + d] =
-        valid ? tot / l : __builtin_nanf("");
+    const float v = valid ? tot / l : __builtin_nanf("");
+    const size_t idx = (size_t)b * p.ldo + (size_t)(bh % p.n_q_heads) * kDh + d;
+    if (p.out_hilo) {
+      const bf16 hi = (bf16)v;
+      p.out_hilo[idx] = hi;
+      p.out_hilo[idx + p.lo_off] = (bf16)(v - (float)hi);
+    } else {
+      p.out[idx] = v;
+    }
   }
 }
 
@@ -425,9 +460,12 @@ hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.nsplit < 1 || a.nsplit > kMaxDecodeSplits) return hipErrorInvalidValue;
   const dim3 grid(a.nsplit, a.n_kv_heads, a.B);
   switch (a.n_q_heads / a.n_kv_heads) {
-#define QL_G(V)                                                                 \
-  case V:                                                                       \
-    hipLaunchKernelGGL(attn_decode_kernel<V>, grid, dim3(64), 0, s, a);        \
+#define QL_G(V)                                                                      \
+  case V:                                                                            \
+    if (a.q_in)                                                                      \
+      hipLaunchKernelGGL((attn_decode_kernel<V, true>), grid, dim3(64), 0, s, a);   \
+    else                                                                             \
+      hipLaunchKernelGGL((attn_decode_kernel<V, false>), grid, dim3(64), 0, s, a);  \
     break;
     QL_G(1) QL_G(2) QL_G(3) QL_G(4) QL_G(5) QL_G(6) QL_G(7) QL_G(8)
     QL_G(9) QL_G(10) QL_G(11) QL_G(12) QL_G(13) QL_G(14) QL_G(15) QL_G(16)

@@ -42,13 +42,11 @@ namespace {
 
 enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU };
 
-constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kGroupM = 4;  // tile rows per L2 group
-constexpr int kStageBytes = (BM + BN) * BK * 2;       // 64 KiB (256-row tiles)
 constexpr int kRowChunks = BK / 8;                     // 16-byte chunks per LDS row
 constexpr int kPitch = BN + 4;                         // fp32 epilogue tile pitch
-constexpr int kEpiBytes = (BM / 2) * kPitch * 4;       // half a tile
-constexpr int kLdsBytes = NSTAGE * kStageBytes > kEpiBytes ? NSTAGE * kStageBytes : kEpiBytes;
+constexpr int kEpiBytes = 128 * kPitch * 4;            // 128 rows of the output tile
 
 struct G2Args {
   const bf16* A;
@@ -72,6 +70,7 @@ struct G2Args {
   // BIAS (the QKV projection): per-head QK-norm, RoPE and the cache write
   // fused into the epilogue
   int S, pos_offset, T_max, n_q_heads, n_kv_heads;
+  const int* cache_len;  // decode: row b is sequence b at cache row cache_len[b]
   float eps;
   const double* omega;  // [64] RoPE frequencies
   const bf16* q_norm_g;
@@ -85,9 +84,12 @@ struct G2Args {
 // The 16 lanes of an aligned lane group hold one head (128 columns), so the
 // per-head sum of squares of QK-norm is a 16-lane reduction and the RoPE
 // partner of column i (i + 64) sits 8 lanes away. q goes to q_out; k and v go
-// to cache row (row % S) of sequence row / S. ("推理系统 03：逐项算清一个真实 Qwen3
+// to cache row (row % S) of sequence row / S (prefill), or to cache row
+// cache_len[row] of sequence row (decode; nothing is written to the cache
+// when that length is outside [0, T_max)). ("推理系统 03：逐项算清一个真实 Qwen3
 // Transformer 层" §5 QK-norm, §6 rotate_half RoPE with omega_i = theta^(-2i/dh),
 // §12 the cache keeps post-norm, post-RoPE keys.)
+template <bool DEC>
 QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
   const int qd = p.n_q_heads * 128, kvd = p.n_kv_heads * 128;
   int part = 0, c = col;
@@ -99,7 +101,14 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
     c = col - qd;
   }
   const int head = c >> 7, d0 = c & 127;
-  const int b = (int)(row / p.S), t = (int)(row % p.S);
+  int b, t;
+  if constexpr (DEC) {
+    b = (int)row;
+    t = p.cache_len[b];
+  } else {
+    b = (int)(row / p.S);
+    t = (int)(row % p.S);
+  }
   if (part < 2) {
     const bf16* gam = part == 0 ? p.q_norm_g : p.k_norm_g;
     if (gam) {
@@ -129,7 +138,7 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
   }
   if (part == 0) {
     store_bf16x8(p.q_out + row * qd + c, pack8(v));
-  } else {
+  } else if (!DEC || (t >= 0 && t < p.T_max)) {
     bf16* cache = part == 1 ? p.k_cache : p.v_cache;
     store_bf16x8(cache + (((size_t)b * p.T_max + t) * p.n_kv_heads + head) * 128 + d0, pack8(v));
   }
@@ -159,9 +168,18 @@ QL_DEV void wait_vmcnt() {
 
 // PART: write this split's fp32 partial tile instead of MODE's epilogue.
 // BMT = 256: 8 waves as 2 (rows) x 4 (columns), a wave owns 128 x 64; two
-// waves share each SIMD, so one wave's MFMAs run while the other waits.
-// (BMT = 128 would be 4 waves as 1 x 4.)
-template <int MODE, bool PART, int BMT>
+// waves share each SIMD, so one wave's MFMAs run while the other waits. Two
+// ring stages (2 x 64 KiB).
+// BMT = 128: 4 waves as 1 x 4, three ring stages (3 x 48 KiB), so two stages
+// of loads are in flight while one is multiplied. These serve few-row
+// batches, whose weights stream from HBM: a 256-row tile would mostly
+// multiply padding, and one stage in flight per CU does not cover HBM latency.
+// HL (BMT = 128): A is a [hi | lo] pair and the tile covers 64 token rows;
+// LDS rows 0..63 hold the hi halves and rows 64..127 the lo halves at the
+// same k, so each B tile is fetched once and serves both, and each wave adds
+// its lo accumulators to its hi ones. The k loop then runs over Kb only.
+// These are the decode tiles: the QKV epilogue takes their rows as sequences.
+template <int MODE, bool PART, int BMT, bool HL>
 __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G2Args p) {
   constexpr int NW = BMT / 32;          // waves
   constexpr int NT = NW * 64;           // threads
@@ -174,10 +192,14 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
   constexpr int LPT = CH / NT;          // direct loads per thread per stage
   constexpr int LPA = AC / NT;          // ... of which A
   constexpr int SB = CH * 16;           // stage bytes
+  constexpr int NS = BMT == 128 ? 3 : 2;  // ring stages
+  constexpr int kLds = NS * SB > kEpiBytes ? NS * SB : kEpiBytes;
   constexpr bool kDual = MODE == G2_SWIGLU;
+  constexpr int RT = HL ? BMT / 2 : BMT;  // token rows per tile
   static_assert(CH % NT == 0 && AC % NT == 0, "whole loads per thread");
-  static_assert(NSTAGE * SB <= kLdsBytes, "LDS ring");
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(!HL || BMT == 128, "hi/lo rows pair up inside one wave's row tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -205,8 +227,8 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
     const int in_group = pid % (kGroupM * p.tiles_n);
     const int tm = first_m + in_group % gsize;
     tn = in_group / gsize;
-    m0 = tm * BMT;
-    rows_valid = min(BMT, p.M - m0);
+    m0 = tm * RT;
+    rows_valid = min(RT, p.M - m0);
   }
   const int n0 = tn * (kDual ? BN / 2 : BN);  // first output column of the tile
 
@@ -238,8 +260,10 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
     const int row = Q / kRowChunks;
     const int c = (Q % kRowChunks) ^ swz(row);
     if (is_a) {
-      const int rr = min(row, rows_valid - 1);  // rows past the tile re-read a valid row
-      src[j] = p.A + (size_t)(m0 + rr) * p.lda + c * 8;
+      // rows past the tile re-read a valid row; HL: rows RT.. are the lo halves
+      const int rr = min(HL ? row % RT : row, rows_valid - 1);
+      const int kofs = HL && row >= RT ? p.Kb : 0;
+      src[j] = p.A + (size_t)(m0 + rr) * p.lda + kofs + c * 8;
     } else {
       const bf16* base;
       if constexpr (kDual) {
@@ -254,11 +278,11 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
   const int ks0 = split * p.ksteps_per_split;
   const int nk = min(p.ksteps_per_split, p.Ka / BK - ks0);
 
-  auto issue = [&](int kt) {  // stage kt of this split -> ring slot kt % NSTAGE
+  auto issue = [&](int kt) {  // stage kt of this split -> ring slot kt % NS
     const int ka = (ks0 + kt) * BK;
     int kb = ka;
     if (kb >= p.Kb) kb -= p.Kb;  // [hi | lo] A: B is read twice
-    char* slot = smem + (kt % NSTAGE) * SB;
+    char* slot = smem + (kt % NS) * SB;
 #pragma unroll
     for (int j = 0; j < LPT; ++j)
       load_lds16(src[j] + (j < LPA ? ka : kb), slot + (NW * j + wave) * 1024);
@@ -295,12 +319,17 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
   // One stage: the fragments of k steps (0, 1) are read, then those of (2, 3)
   // are requested before the MFMAs of (0, 1) run, so only the first reads of
   // a stage sit in front of its MFMAs.
+  // 4-wave tiles serve batches that may fill only part of the tile: 32-row
+  // MFMA tiles of padding rows are skipped (block-uniform branches)
+  bool act[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) act[i] = BMT == 256 || (HL ? (32 * i) % RT : 32 * i) < rows_valid;
   auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][4], bf16x8 (&bfr)[2][TJ]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+        if (act[i]) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
@@ -311,23 +340,32 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        if (act[i])
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
   };
   static_assert(KS == 4, "two halves of two k steps per stage");
 
-  // Two stages; stage kt+1 is requested right after the barrier that publishes
-  // stage kt and lands while stage kt is multiplied.
-  if (nk > 0) issue(0);
+  // Stage kt + NS - 1 is requested right after the barrier that publishes
+  // stage kt (and frees the slot stage kt - 1 used), and lands while stages
+  // kt .. kt + NS - 2 are multiplied.
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nk) issue(j);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();  // this wave's part of stage kt (the only stage in flight)
+    // this wave's part of stage kt has landed; vector loads complete in
+    // order, so with three stages the LPT loads of stage kt + 1 may remain
+    if (NS == 3 && kt + 1 < nk)
+      wait_vmcnt<LPT>();
+    else
+      wait_vmcnt<0>();
     // every wave's part of stage kt has landed and every wave is done with
-    // the other slot. A bare s_barrier: __syncthreads' release fence adds
-    // nothing here; the acquire fence keeps the LDS reads below it.
+    // the slot of stage kt - 1. A bare s_barrier: __syncthreads' release
+    // fence adds nothing here; the acquire fence keeps the LDS reads below it.
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (kt + 1 < nk) issue(kt + 1);
-    const char* st = smem + (kt % NSTAGE) * SB;
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    const char* st = smem + (kt % NS) * SB;
     bf16x8 a0[2][4], b0[2][TJ], a1[2][4], b1[2][TJ];
     read2(st, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
@@ -342,11 +380,23 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
 
   // ---- epilogue: 128 rows (one row of waves) at a time through LDS ----
   float* C = reinterpret_cast<float*>(smem);
+  // HL, BMT = 128: a wave's row tiles 0, 1 are hi rows and 2, 3 the matching
+  // lo rows; add them in registers and store two row tiles
+  constexpr bool kRegAdd = HL && BMT == 128;
+  constexpr int NI = kRegAdd ? 2 : 4;
+  if constexpr (kRegAdd) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += acc[i + 2][j][r];
+  }
 #pragma unroll
   for (int half = 0; half < WMW; ++half) {
     if (wm == half) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -356,12 +406,13 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
           }
     }
     __syncthreads();
+    constexpr int kEpiRows = RT < 128 ? RT : 128;
     const int rbase = half * 128;
     if constexpr (PART) {
       const int ldp = p.tiles_n * BN;
       float* dst = p.part + (size_t)split * p.M * ldp;
       const int seg = tid & 31;
-      for (int r = tid >> 5; r < 128; r += NT / 32) {
+      for (int r = tid >> 5; r < kEpiRows; r += NT / 32) {
         if (rbase + r >= rows_valid) break;
         const float* c = C + r * kPitch + seg * 8;
         float* o = dst + (size_t)(m0 + rbase + r) * ldp + tn * BN + seg * 8;
@@ -370,7 +421,7 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
       }
     } else if constexpr (kDual) {
       const int seg = tid & 15;
-      for (int r = tid >> 4; r < 128; r += NT / 16) {
+      for (int r = tid >> 4; r < kEpiRows; r += NT / 16) {
         if (rbase + r >= rows_valid) break;
         const float* g = C + r * kPitch + seg * 8;
         const float* u = g + BN / 2;
@@ -388,7 +439,7 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
       if constexpr (MODE == G2_BIAS) {
         if (bias) unpack8(load_bf16x8(bias + nb + seg * 8), badd);
       }
-      for (int r = tid >> 5; r < 128; r += NT / 32) {
+      for (int r = tid >> 5; r < kEpiRows; r += NT / 32) {
         if (rbase + r >= rows_valid) break;
         const float* c = C + r * kPitch + seg * 8;
         float v[8];
@@ -396,7 +447,7 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
         for (int e = 0; e < 8; ++e) v[e] = c[e] + badd[e];
         const size_t row = (size_t)(m0 + rbase + r);
         if constexpr (MODE == G2_BIAS) {
-          qkv_finish(p, row, col, v);
+          qkv_finish<HL>(p, row, col, v);  // the 128-row pair tiles serve decode
           continue;
         }
         if constexpr (MODE == G2_RESID_F32) {
@@ -483,7 +534,10 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] += b8[e];
       }
-      qkv_finish(p, (size_t)row, col, v);
+      if (p.cache_len)
+        qkv_finish<true>(p, (size_t)row, col, v);
+      else
+        qkv_finish<false>(p, (size_t)row, col, v);
       return;
     }
     if constexpr (MODE == G2_RESID_F32) {
@@ -505,23 +559,42 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
   }
 }
 
+// Tile shapes: 256 token rows (8 waves); 64 token rows from a [hi | lo]
+// pair (4 waves); 128 token rows from a plain bf16 A (4 waves).
+enum : int { T256 = 0, T64_HL, T128 };
+
+template <int MODE, int SHAPE>
+hipError_t launch(const G2Args& a, dim3 grid, hipStream_t s) {
+  constexpr int BMT = SHAPE == T256 ? 256 : 128;
+  constexpr bool HL = SHAPE == T64_HL;
+  // hi/lo inputs feed Q/K/V and O; plain bf16 inputs feed gate/up and down
+  constexpr bool kPairIn = MODE == G2_BIAS || MODE == G2_RESID_F32;
+  if constexpr (SHAPE != T256 && HL != kPairIn) {
+    return hipErrorInvalidValue;
+  } else {
+    if (a.splits == 1)
+      hipLaunchKernelGGL((gemm2_kernel<MODE, false, BMT, HL>), grid, dim3(BMT / 32 * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm2_kernel<MODE, true, BMT, HL>), grid, dim3(BMT / 32 * 64), 0, s, a);
+    return hipGetLastError();
+  }
+}
+
 template <int MODE>
-hipError_t run(G2Args a, hipStream_t s) {
+hipError_t run(G2Args a, int shape, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  a.tiles_m = (a.M + BM - 1) / BM;
+  const int rt = shape == T256 ? 256 : (shape == T64_HL ? 64 : 128);
+  a.tiles_m = (a.M + rt - 1) / rt;
   const int nks = a.Ka / BK;
   a.splits = a.splits < 1 ? 1 : (a.splits > nks ? nks : a.splits);
   a.ksteps_per_split = (nks + a.splits - 1) / a.splits;
   a.splits = (nks + a.ksteps_per_split - 1) / a.ksteps_per_split;
   const int total = a.tiles_m * a.tiles_n * a.splits;
   const dim3 grid(8 * ((total + 7) / 8));
-  if (a.splits == 1) {
-    hipLaunchKernelGGL((gemm2_kernel<MODE, false, 256>), grid, dim3(512), 0, s, a);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((gemm2_kernel<MODE, true, 256>), grid, dim3(512), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = shape == T256      ? launch<MODE, T256>(a, grid, s)
+                 : shape == T64_HL ? launch<MODE, T64_HL>(a, grid, s)
+                                    : launch<MODE, T128>(a, grid, s);
+  if (e != hipSuccess || a.splits == 1) return e;
   const int segs = (MODE == G2_SWIGLU ? a.tiles_n * BN / 2 : a.tiles_n * BN) / 8;
   const size_t threads = (size_t)a.M * segs;
   hipLaunchKernelGGL(gemm2_reduce_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
@@ -554,13 +627,18 @@ bool ql_gemm2_ok(int N, int Kb, bool dual) {
   return Kb % BK == 0 && (dual ? N % (BN / 2) == 0 : N % BN == 0);
 }
 
+int ql_gemm2_ksteps(int K) { return K / BK; }
+
 hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
-                        const QkvFinish& f, int splits, void* part, hipStream_t s) {
-  G2Args a = base(A2, M, 2 * K, Wq, K, splits, part);
+                        const QkvFinish& f, bool rows128, int splits, void* part, hipStream_t s) {
+  if (rows128 != (f.cache_len != nullptr)) return hipErrorInvalidValue;  // decode <=> 128 rows
+  G2Args a = base(A2, M, rows128 ? K : 2 * K, Wq, K, splits, part);
+  a.lda = 2 * K;
   a.S = f.S;
   a.pos_offset = f.pos_offset;
   a.T_max = f.T_max;
+  a.cache_len = f.cache_len;
   a.n_q_heads = q / 128;
   a.n_kv_heads = kv / 128;
   a.eps = f.eps;
@@ -579,23 +657,24 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
   a.bias3 = bv;
   a.ldo = q + 2 * kv;
   a.tiles_n = (q + 2 * kv) / BN;
-  return run<G2_BIAS>(a, s);
+  return run<G2_BIAS>(a, rows128 ? T64_HL : T256, s);
 }
 
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
-                              const bf16* resid, float* out, int splits, void* part,
+                              const bf16* resid, float* out, bool rows128, int splits, void* part,
                               hipStream_t s) {
-  G2Args a = base(A2, M, 2 * K, W, K, splits, part);
+  G2Args a = base(A2, M, rows128 ? K : 2 * K, W, K, splits, part);
+  a.lda = 2 * K;
   a.resid_bf16 = resid;
   a.ldr = N;
   a.out_f32 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_F32>(a, s);
+  return run<G2_RESID_F32>(a, rows128 ? T64_HL : T256, s);
 }
 
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
-                              const float* resid, bf16* out, int splits, void* part,
+                              const float* resid, bf16* out, bool rows128, int splits, void* part,
                               hipStream_t s) {
   G2Args a = base(A, M, K, W, K, splits, part);
   a.resid_f32 = resid;
@@ -603,16 +682,15 @@ hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
   a.out_bf16 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_OUT>(a, s);
+  return run<G2_RESID_OUT>(a, rows128 ? T128 : T256, s);
 }
 
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                           bf16* out, int splits, void* part, hipStream_t s) {
+                           bf16* out, bool rows128, int splits, void* part, hipStream_t s) {
   G2Args a = base(A, M, K, Wg, K, splits, part);
   a.B2 = Wu;
   a.out_bf16 = out;
   a.ldo = F;
   a.tiles_n = F / (BN / 2);
-  return run<G2_SWIGLU>(a, s);
+  return run<G2_SWIGLU>(a, rows128 ? T128 : T256, s);
 }
-

@@ -33,16 +33,23 @@ hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const 
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
                             int max_tiles, int bm, float* out, hipStream_t s);
 
-// ---- prefill GEMMs, 256 x 256 tiles (N % 256 == 0, or F % 128 for SwiGLU; K % 32) ----
-// A2 = [hi | lo] bf16 pair of an fp32 activation, [M, 2K]. splits > 1 runs split-K
-// through `part` (ql_gemm2_part_bytes(M, weight rows read per call, splits) bytes).
+// ---- GEMMs on 256-column tiles (N % 256 == 0, or F % 128 for SwiGLU; K % 64) ----
+// A2 = [hi | lo] bf16 pair of an fp32 activation, [M, 2K]. rows128 selects the
+// 4-wave decode tiles (three-stage ring): 64 token rows for a pair A, whose hi
+// and lo rows share each weight tile, 128 for a plain A.
+// splits > 1 runs split-K through `part` (ql_gemm2_part_bytes(M, weight rows
+// read per call, splits) bytes); the split count is clamped to the k steps.
 size_t ql_gemm2_part_bytes(int M, int b_rows, int splits);
 bool ql_gemm2_ok(int N, int Kb, bool dual);
-// QKV projection of [B*S] token rows with bias, per-head QK-norm, RoPE at
-// position (row % S) + pos_offset, q to q_out [M, q] and k, v to cache row
-// row % S of sequence row / S (q, kv multiples of 256; head_dim 128)
+int ql_gemm2_ksteps(int K);  // k steps of one pass over K
+// QKV projection with bias, per-head QK-norm, RoPE and the cache write. Prefill
+// (cache_len NULL): row = b * S + t, position t + pos_offset, cache row t.
+// Decode (cache_len set): row = b, position cache_len[b] + pos_offset, cache
+// row cache_len[b] (skipped when outside [0, T_max)). q goes to q_out [M, q].
+// (q, kv multiples of 256; head_dim 128)
 struct QkvFinish {
   int S, pos_offset, T_max;
+  const int* cache_len;  // decode: [M] device, or NULL
   float eps;
   const double* omega;   // [64]
   const bf16* q_norm_g;  // or NULL
@@ -53,34 +60,22 @@ struct QkvFinish {
 };
 hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
-                        const QkvFinish& f, int splits, void* part, hipStream_t s);
+                        const QkvFinish& f, bool rows128, int splits, void* part, hipStream_t s);
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
-                              const bf16* resid, float* out, int splits, void* part,
+                              const bf16* resid, float* out, bool rows128, int splits, void* part,
                               hipStream_t s);
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
-                              const float* resid, bf16* out, int splits, void* part,
+                              const float* resid, bf16* out, bool rows128, int splits, void* part,
                               hipStream_t s);
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                           bf16* out, int splits, void* part, hipStream_t s);
-
-// ---- decode GEMMs with M <= 128 rows (N % 16 == 0, K % 32 == 0) ----
-// out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x, gamma bf16;
-// RMSNorm's 1/rms and the QKV bias are applied by the consumer)
-hipError_t ql_skinny_qkv_raw(const bf16* x, const bf16* gamma, int M, const bf16* Wq,
-                             const bf16* Wk, const bf16* Wv, int q, int kv, int K, float* out,
-                             hipStream_t s);
-// out[M, N] fp32 = resid + X W^T (X fp32, used as a bf16 hi + lo pair)
-hipError_t ql_skinny_resid_f32(const float* X, int M, const bf16* W, int N, int K,
-                               const bf16* resid, float* out, hipStream_t s);
-// out[M, N] bf16 = resid + X W^T
-hipError_t ql_skinny_resid_out(const bf16* X, int M, const bf16* W, int N, int K,
-                               const float* resid, bf16* out, hipStream_t s);
-// out[M, F] = SiLU(X Wg^T) * (X Wu^T)
-hipError_t ql_skinny_swiglu(const bf16* X, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                            bf16* out, hipStream_t s);
+                           bf16* out, bool rows128, int splits, void* part, hipStream_t s);
 
 // ---- decode GEMVs for M <= kGemvMaxRows rows (N % 2 == 0, K % 8 == 0) ----
-// Same contracts as the skinny forms above; fp32 X is used unsplit.
+// qkv_raw: out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x,
+// gamma bf16; RMSNorm's 1/rms and the QKV bias are applied by the consumer).
+// resid_f32: out[M, N] fp32 = resid + X W^T (X fp32). resid_out: out[M, N]
+// bf16 = resid + X W^T. rmsnorm_swiglu: out[M, F] = SiLU(z Wg^T) * (z Wu^T)
+// with z = RMSNorm(R) formed on the fly.
 constexpr int kGemvMaxRows = 4;
 bool ql_gemv_ok(int M, int N, int K);
 // (the QKV form also writes RMSNorm's 1/rms of each x row to inv_rms[M] if non-NULL)
@@ -154,7 +149,11 @@ struct AttnDecodeArgs {
   float eps, theta;
   int pos_offset;
   bf16* q_out;           // [B, Hq*dh] rotated queries (optional copy)
+  const bf16* q_in;      // [B, Hq*dh] finished queries, row cache_len[b] already in
+                         // the cache: no prologue (or NULL)
   float* out;            // [B, ldo] fp32
+  bf16* out_hilo;        // or [B, ldo] bf16 hi at col, lo at col + lo_off
+  int lo_off;
   const float* qf;
   const float* kf;
   const float* vf;

@@ -171,7 +171,51 @@ int gemm2_splits(int M, int b_rows, int K) {
   int sp = std::max(1, kGemmTargetBlocks / std::max(tiles, 1));
   return std::max(1, std::min(sp, K / 512));
 }
-// Partial-tile bytes for the four dense prefill GEMMs at M rows (the largest).
+// Decode-sized GEMMs (64 token rows per tile for the hi/lo inputs of Q/K/V
+// and O, 128 for gate/up and down) stream their weights from HBM. The split count minimises an estimate of the call time: each wave of
+// at most one block per CU costs, per k step, the larger of its share of HBM
+// bandwidth (256 x 64 bf16 weights per block per step) and one CU's own fetch
+// rate, plus a start-up; split partials cost their write and read-back and a
+// reduce launch.
+constexpr double kHbmBytesPerUs = 6.0e6, kCuBytesPerUs = 4.5e4;
+constexpr double kBlockStartUs = 2.0, kReduceUs = 3.0;
+int decode_gemm_splits(int M, int tiles, int nks, int out_cols) {
+  constexpr double step_bytes = 256.0 * 64 * 2;
+  int best = 1;
+  double best_t = 1e30;
+  for (int sp = 1; sp <= std::min(nks, 64); ++sp) {
+    const int per = (nks + sp - 1) / sp;
+    const int s_eff = (nks + per - 1) / per;
+    if (s_eff != sp) continue;
+    const int blocks = tiles * s_eff;
+    double t = 0;
+    for (int left = blocks; left > 0; left -= kGemmTargetBlocks) {
+      const int a = std::min(left, kGemmTargetBlocks);
+      t += per * std::max(a * step_bytes / kHbmBytesPerUs, step_bytes / kCuBytesPerUs) +
+           kBlockStartUs;
+    }
+    if (s_eff > 1) t += 2.0 * s_eff * M * out_cols * 4 / kHbmBytesPerUs + kReduceUs;
+    if (t < best_t) {
+      best_t = t;
+      best = s_eff;
+    }
+  }
+  return best;
+}
+struct DecodeSplits {
+  int qkv, o, gu, dn;
+};
+DecodeSplits decode_gemm_plan(const ql_config& c, int q_dim, int qkv_dim, int M) {
+  DecodeSplits d;
+  const int tm = (M + 63) / 64;
+  d.qkv = decode_gemm_splits(M, tm * qkv_dim / 256, ql_gemm2_ksteps(c.d), qkv_dim);
+  d.o = decode_gemm_splits(M, tm * c.d / 256, ql_gemm2_ksteps(q_dim), c.d);
+  d.gu = decode_gemm_splits(M, c.ffn_dim / 128, ql_gemm2_ksteps(c.d), 2 * c.ffn_dim);
+  d.dn = decode_gemm_splits(M, c.d / 256, ql_gemm2_ksteps(c.ffn_dim), c.d);
+  return d;
+}
+// Partial-tile bytes: the four dense GEMMs at the largest prefill M, and at
+// every decode batch size that takes the MFMA tiles.
 size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
   size_t b = 0;
   b = std::max(b, ql_gemm2_part_bytes(M, qkv_dim, gemm2_splits(M, qkv_dim, 2 * c.d)));
@@ -180,12 +224,21 @@ size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
     b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, c.d)));
     b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, c.ffn_dim)));
   }
+  for (int B = kGemvMaxRows + 1; B <= c.max_batch; ++B) {
+    const DecodeSplits d = decode_gemm_plan(c, q_dim, qkv_dim, B);
+    b = std::max(b, ql_gemm2_part_bytes(B, qkv_dim, d.qkv));
+    b = std::max(b, ql_gemm2_part_bytes(B, c.d, d.o));
+    if (c.n_experts == 0) {
+      b = std::max(b, ql_gemm2_part_bytes(B, 2 * c.ffn_dim, d.gu));
+      b = std::max(b, ql_gemm2_part_bytes(B, c.d, d.dn));
+    }
+  }
   return b;
 }
 
 // Decode attention launch shape: about kDecodeTargetWaves waves over
 // (key split, KV head, sequence), at least one 16-key tile per split.
-constexpr int kDecodeTargetWaves = 2048;
+constexpr int kDecodeTargetWaves = 3072;
 int decode_splits(int groups, int T_max, int* chunk) {
   int ns = (kDecodeTargetWaves + groups - 1) / groups;
   ns = std::max(1, std::min({ns, kMaxDecodeSplits, (T_max + 15) / 16}));
@@ -220,7 +273,7 @@ size_t layout(ql_handle* h, char* base) {
   h->xhat = k.take<void>(N * c.d * 4);  // [hi | lo] bf16 pair of the fp32 RMSNorm1 output
   h->qkv = k.take<float>(N * h->qkv_dim * 4);
   h->q = k.take<void>(N * h->q_dim * es);
-  h->attn = k.take<void>(N * h->q_dim * 4);  // prefill: [hi | lo] bf16 pair; decode: fp32
+  h->attn = k.take<void>(N * h->q_dim * 4);  // [hi | lo] bf16 pair, or fp32 (GEMV decode)
   h->r = k.take<float>(N * c.d * 4);
   h->z = k.take<void>(N * c.d * es);
   const size_t B = (size_t)std::max(c.max_batch, 0);
@@ -355,41 +408,38 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
   const bf16* g2 = static_cast<const bf16*>(w.ln2_g);
   // few rows on the dense path: RMSNorm2 rides inside the gate/up projection
   // (z is then only formed when a tap asks for it)
-  const bool gemv = decode && c.n_experts == 0 && ql_gemv_ok(N, c.ffn_dim, c.d) &&
-                    ql_gemv_ok(N, c.d, c.ffn_dim);
+  const bool gemv = decode && c.n_experts == 0 && N <= kGemvMaxRows &&
+                    ql_gemv_ok(N, c.ffn_dim, c.d) && ql_gemv_ok(N, c.d, c.ffn_dim);
   if (!gemv || h->taps.z)
     QL_STAGE(h, QL_STAGE_RMSNORM2, s,
              QL_HIP(ql_rmsnorm_f32in_bf16(h->r, g2, z, c.n_experts > 0 ? h->zf : nullptr, N,
                                           c.d, c.rms_eps, s)));
   if (c.n_experts > 0) return moe_core(h, N, h->r, 1, y, s);
   bf16* hh = static_cast<bf16*>(h->h);
-  if (decode) {
-    const bf16* wg = static_cast<const bf16*>(w.w_gate);
-    const bf16* wu = static_cast<const bf16*>(w.w_up);
-    const bf16* wd = static_cast<const bf16*>(w.w_down);
-    if (gemv) {
-      QL_STAGE(h, QL_STAGE_GATE_UP, s,
-               QL_HIP(ql_gemv_rmsnorm_swiglu(h->r, g2, c.rms_eps, N, wg, wu, c.ffn_dim, c.d, hh,
-                                             s)));
-      QL_STAGE(h, QL_STAGE_DOWN, s,
-               QL_HIP(ql_gemv_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
-    } else {
-      QL_STAGE(h, QL_STAGE_GATE_UP, s,
-               QL_HIP(ql_skinny_swiglu(z, N, wg, wu, c.ffn_dim, c.d, hh, s)));
-      QL_STAGE(h, QL_STAGE_DOWN, s,
-               QL_HIP(ql_skinny_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
-    }
-  } else {
-    const int sgu = gemm2_splits(N, 2 * c.ffn_dim, c.d);
-    const int sdn = gemm2_splits(N, c.d, c.ffn_dim);
+  const bf16* wg = static_cast<const bf16*>(w.w_gate);
+  const bf16* wu = static_cast<const bf16*>(w.w_up);
+  const bf16* wd = static_cast<const bf16*>(w.w_down);
+  if (gemv) {
     QL_STAGE(h, QL_STAGE_GATE_UP, s,
-             QL_HIP(ql_gemm2_swiglu(z, N, static_cast<const bf16*>(w.w_gate),
-                                    static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, sgu,
-                                    h->g2part, s)));
+             QL_HIP(ql_gemv_rmsnorm_swiglu(h->r, g2, c.rms_eps, N, wg, wu, c.ffn_dim, c.d, hh, s)));
     QL_STAGE(h, QL_STAGE_DOWN, s,
-             QL_HIP(ql_gemm2_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d,
-                                       c.ffn_dim, h->r, y, sdn, h->g2part, s)));
+             QL_HIP(ql_gemv_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
+    return QL_OK;
   }
+  int sgu, sdn;
+  if (decode) {
+    const DecodeSplits d = decode_gemm_plan(c, h->q_dim, h->qkv_dim, N);
+    sgu = d.gu;
+    sdn = d.dn;
+  } else {
+    sgu = gemm2_splits(N, 2 * c.ffn_dim, c.d);
+    sdn = gemm2_splits(N, c.d, c.ffn_dim);
+  }
+  QL_STAGE(h, QL_STAGE_GATE_UP, s,
+           QL_HIP(ql_gemm2_swiglu(z, N, wg, wu, c.ffn_dim, c.d, hh, decode, sgu, h->g2part, s)));
+  QL_STAGE(h, QL_STAGE_DOWN, s,
+           QL_HIP(ql_gemm2_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, decode, sdn, h->g2part,
+                                     s)));
   return QL_OK;
 }
 
@@ -422,7 +472,7 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   QL_STAGE(h, QL_STAGE_QKV, s,
            QL_HIP(ql_gemm2_qkv(xhat, N, static_cast<const bf16*>(w.wq),
                                static_cast<const bf16*>(w.wk), static_cast<const bf16*>(w.wv),
-                               h->q_dim, h->kv_dim, c.d, bq, bk, bv, f,
+                               h->q_dim, h->kv_dim, c.d, bq, bk, bv, f, false,
                                gemm2_splits(N, h->qkv_dim, 2 * c.d), h->g2part, s)));
   AttnPrefillArgs pa{};
   pa.q = static_cast<const bf16*>(h->q);
@@ -444,41 +494,88 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   QL_STAGE(h, QL_STAGE_O_PROJ, s,
            QL_HIP(ql_gemm2_resid_f32(static_cast<const bf16*>(h->attn), N,
                                      static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
-                                     gemm2_splits(N, c.d, 2 * h->q_dim), h->g2part, s)));
+                                     false, gemm2_splits(N, c.d, 2 * h->q_dim), h->g2part, s)));
   return ffn_dense_or_moe(h, N, false, y, s);
 }
 
-// Decode: QKV projection of x * gamma1 (raw sums) -> attention with RMSNorm1
-// scale, QK-norm, RoPE and the cache append fused in -> O projection +
-// residual -> FFN half.
+// Decode, up to kGemvMaxRows sequences: QKV projection of x * gamma1 (raw
+// sums) -> attention with RMSNorm1 scale, QK-norm, RoPE and the cache append
+// fused in -> O projection + residual -> FFN half.
+// More sequences: RMSNorm1 -> QKV on MFMA tiles with QK-norm, RoPE and the
+// cache append in the epilogue -> attention -> O projection + residual ->
+// FFN half; the hi/lo activation pairs share each weight tile.
 ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, int pos_offset,
                       void* kc, void* vc, int T_max, bf16* y, hipStream_t s) {
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
-  const bool gemv = ql_gemv_ok(B, h->qkv_dim, c.d) && ql_gemv_ok(B, c.d, h->q_dim);
+  const bool gemv = B <= kGemvMaxRows && ql_gemv_ok(B, h->qkv_dim, c.d) &&
+                    ql_gemv_ok(B, c.d, h->q_dim);
   const bf16* g1 = static_cast<const bf16*>(w.ln1_g);
   const bf16* wq = static_cast<const bf16*>(w.wq);
   const bf16* wk = static_cast<const bf16*>(w.wk);
   const bf16* wv = static_cast<const bf16*>(w.wv);
-  QL_STAGE(h, QL_STAGE_QKV, s,
-           QL_HIP(gemv ? ql_gemv_qkv_raw(x, g1, B, wq, wk, wv, h->q_dim, h->kv_dim, c.d, h->qkv,
-                                         c.rms_eps, h->inv_rms, s)
-                       : ql_skinny_qkv_raw(x, g1, B, wq, wk, wv, h->q_dim, h->kv_dim, c.d,
-                                           h->qkv, s)));
+  const bf16* wo = static_cast<const bf16*>(w.wo);
+  const bf16* bq = c.qkv_bias ? static_cast<const bf16*>(w.bq) : nullptr;
+  const bf16* bk = c.qkv_bias ? static_cast<const bf16*>(w.bk) : nullptr;
+  const bf16* bv = c.qkv_bias ? static_cast<const bf16*>(w.bv) : nullptr;
   AttnDecodeArgs da{};
   da.k_cache = static_cast<const bf16*>(kc);
   da.v_cache = static_cast<const bf16*>(vc);
+  da.cache_len = cache_len;
+  da.B = B;
+  da.T_max = T_max;
+  da.n_q_heads = c.n_q_heads;
+  da.n_kv_heads = c.n_kv_heads;
+  da.head_dim = c.head_dim;
+  int chunk = 0;
+  da.nsplit = decode_splits(B * c.n_kv_heads, T_max, &chunk);
+  da.chunk = chunk;
+  da.part_o = h->part_o;
+  da.part_ml = h->part_ml;
+  da.scale_log2 = scale_log2(c.head_dim);
+  if (!gemv) {
+    const DecodeSplits sp = decode_gemm_plan(c, h->q_dim, h->qkv_dim, B);
+    bf16* xhat = static_cast<bf16*>(h->xhat);  // [B, 2d]: hi | lo
+    QL_STAGE(h, QL_STAGE_RMSNORM1, s,
+             QL_HIP(ql_rmsnorm_bf16_to_hilo(x, g1, xhat, B, c.d, c.rms_eps, s)));
+    QkvFinish f{};
+    f.S = 1;
+    f.pos_offset = pos_offset;
+    f.T_max = T_max;
+    f.cache_len = cache_len;
+    f.eps = c.rms_eps;
+    f.omega = h->rope_omega;
+    f.q_norm_g = c.qk_norm ? static_cast<const bf16*>(w.q_norm_g) : nullptr;
+    f.k_norm_g = c.qk_norm ? static_cast<const bf16*>(w.k_norm_g) : nullptr;
+    f.q_out = static_cast<bf16*>(h->q);
+    f.k_cache = static_cast<bf16*>(kc);
+    f.v_cache = static_cast<bf16*>(vc);
+    QL_STAGE(h, QL_STAGE_QKV, s,
+             QL_HIP(ql_gemm2_qkv(xhat, B, wq, wk, wv, h->q_dim, h->kv_dim, c.d, bq, bk, bv, f,
+                                 true, sp.qkv, h->g2part, s)));
+    da.q_in = static_cast<const bf16*>(h->q);
+    da.out_hilo = static_cast<bf16*>(h->attn);  // [B, 2q]: hi | lo
+    da.lo_off = h->q_dim;
+    da.ldo = 2 * h->q_dim;
+    QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
+    h->attn_hilo = true;
+    QL_STAGE(h, QL_STAGE_O_PROJ, s,
+             QL_HIP(ql_gemm2_resid_f32(static_cast<const bf16*>(h->attn), B, wo, c.d, h->q_dim,
+                                       x, h->r, true, sp.o, h->g2part, s)));
+    return ffn_dense_or_moe(h, B, true, y, s);
+  }
+  QL_STAGE(h, QL_STAGE_QKV, s,
+           QL_HIP(ql_gemv_qkv_raw(x, g1, B, wq, wk, wv, h->q_dim, h->kv_dim, c.d, h->qkv,
+                                  c.rms_eps, h->inv_rms, s)));
   da.k_cache_w = static_cast<bf16*>(kc);
   da.v_cache_w = static_cast<bf16*>(vc);
   da.qkv_raw = h->qkv;
   da.ld_raw = h->qkv_dim;
   da.x = x;
   da.d = c.d;
-  if (c.qkv_bias) {
-    da.bq = static_cast<const bf16*>(w.bq);
-    da.bk = static_cast<const bf16*>(w.bk);
-    da.bv = static_cast<const bf16*>(w.bv);
-  }
+  da.bq = bq;
+  da.bk = bk;
+  da.bv = bv;
   if (c.qk_norm) {
     da.q_norm_g = static_cast<const bf16*>(w.q_norm_g);
     da.k_norm_g = static_cast<const bf16*>(w.k_norm_g);
@@ -488,29 +585,14 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
   da.pos_offset = pos_offset;
   da.q_out = static_cast<bf16*>(h->q);
   da.out = static_cast<float*>(h->attn);
-  da.cache_len = cache_len;
   da.ldo = h->q_dim;
-  da.B = B;
-  da.T_max = T_max;
-  da.n_q_heads = c.n_q_heads;
-  da.n_kv_heads = c.n_kv_heads;
-  da.head_dim = c.head_dim;
-  int chunk = 0;
-  const int nsplit = decode_splits(B * c.n_kv_heads, T_max, &chunk);
-  da.chunk = chunk;
-  da.nsplit = nsplit;
-  da.part_o = h->part_o;
-  da.part_ml = h->part_ml;
   da.rope_omega = h->rope_omega;
-  da.inv_rms = gemv ? h->inv_rms : nullptr;
-  da.scale_log2 = scale_log2(c.head_dim);
+  da.inv_rms = h->inv_rms;
   QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_decode_bf16(da, s)));
   h->attn_hilo = false;
-  const float* attn = static_cast<const float*>(h->attn);
-  const bf16* wo = static_cast<const bf16*>(w.wo);
   QL_STAGE(h, QL_STAGE_O_PROJ, s,
-           QL_HIP(gemv ? ql_gemv_resid_f32(attn, B, wo, c.d, h->q_dim, x, h->r, s)
-                       : ql_skinny_resid_f32(attn, B, wo, c.d, h->q_dim, x, h->r, s)));
+           QL_HIP(ql_gemv_resid_f32(static_cast<const float*>(h->attn), B, wo, c.d, h->q_dim, x,
+                                    h->r, s)));
   return ffn_dense_or_moe(h, B, true, y, s);
 }
 
