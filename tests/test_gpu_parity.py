@@ -149,14 +149,23 @@ def test_small_bf16_prefill_stages():
             assert v <= 1.0, (k, v)
 
 
-# up to 4 sequences take the VALU GEMV path, more the MFMA tiles; lengths
-# include an empty cache (0) and a full one (T_max - 1)
-@pytest.mark.parametrize("lens", [[5, 100, 257], [0, 5, 100, 257, 31, 128, 299]],
-                         ids=["gemv_B3", "mfma_B7"])
-def test_small_bf16_decode_ragged_lengths(lens):
+# up to 4 sequences take the VALU GEMV path, more the MFMA tiles (whose A
+# tile holds 32, 64 or 128 rows, hi/lo pairs counted twice); lengths include
+# an empty cache (0) and a full one (T_max - 1)
+RAGGED = {
+    "gemv_B3": [5, 100, 257],
+    "mfma_B7": [0, 5, 100, 257, 31, 128, 299],
+    "mfma_B40": [int(v) for v in np.random.default_rng(7).integers(0, 300, 40)],
+    "mfma_B70": [int(v) for v in np.random.default_rng(8).integers(0, 300, 70)] + [299],
+}
+
+
+@pytest.mark.parametrize("case", list(RAGGED))
+def test_small_bf16_decode_ragged_lengths(case):
+    lens = RAGGED[case]
     cfg = small_cfg()
     Bn, T_max = len(lens), 300
-    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=8)
+    layer, w32 = make_layer(cfg, max_tokens=8, max_batch=max(8, Bn))
     q_t = torch.empty(Bn, cfg.q_dim, dtype=torch.bfloat16, device="cuda")
     a_t = torch.empty(Bn, cfg.q_dim, dtype=torch.float32, device="cuda")
     r_t = torch.empty(Bn, cfg.d, dtype=torch.float32, device="cuda")

@@ -15,6 +15,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 #define QL_DEV __device__ __forceinline__
+#define QL_HD __host__ __device__ __forceinline__
 
 constexpr int kWave = 64;
 

@@ -67,6 +67,10 @@ struct G2Args {
   const float* resid_f32;
   int ldr;
   float* part;  // [splits][M][tiles_n * BN]
+  // stream-K (decode tiles): the tile-major (tile, k step) units are cut into
+  // sk_grid contiguous runs, one per block; partial index = ordinal of the
+  // block among those touching the tile
+  int streamk, sk_grid, rows_per_tile;
   // BIAS (the QKV projection): per-head QK-norm, RoPE and the cache write
   // fused into the epilogue
   int S, pos_offset, T_max, n_q_heads, n_kv_heads;
@@ -144,6 +148,10 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
   }
 }
 
+// Block that owns unit u when U units are cut into G contiguous runs
+// [floor(b U / G), floor((b + 1) U / G)).
+QL_HD int sk_owner(long long u, long long U, int G) { return (int)(((u + 1) * G - 1) / U); }
+
 // LDS slot of chunk c of row r is c ^ swz(r). A 16-byte read by the lanes of
 // one MFMA fragment touches 16 consecutive rows (from a multiple of 16) at one
 // chunk; with 128-byte rows this puts them on 16 distinct 16-byte positions of
@@ -166,21 +174,13 @@ QL_DEV void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// PART: write this split's fp32 partial tile instead of MODE's epilogue.
-// BMT = 256: 8 waves as 2 (rows) x 4 (columns), a wave owns 128 x 64; two
-// waves share each SIMD, so one wave's MFMAs run while the other waits. Two
-// ring stages (2 x 64 KiB).
-// BMT = 128: 4 waves as 1 x 4, three ring stages (3 x 48 KiB), so two stages
-// of loads are in flight while one is multiplied. These serve few-row
-// batches, whose weights stream from HBM: a 256-row tile would mostly
-// multiply padding, and one stage in flight per CU does not cover HBM latency.
-// HL (BMT = 128): A is a [hi | lo] pair and the tile covers 64 token rows;
-// LDS rows 0..63 hold the hi halves and rows 64..127 the lo halves at the
-// same k, so each B tile is fetched once and serves both, and each wave adds
-// its lo accumulators to its hi ones. The k loop then runs over Kb only.
-// These are the decode tiles: the QKV epilogue takes their rows as sequences.
-template <int MODE, bool PART, int BMT, bool HL>
-__global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G2Args p) {
+// Prefill tiles. PART: write this split's fp32 partial tile instead of
+// MODE's epilogue. 8 waves as 2 (rows) x 4 (columns), a wave owns 128 x 64;
+// two waves share each SIMD, so one wave's MFMAs run while the other waits.
+// Two ring stages (2 x 64 KiB).
+template <int MODE, bool PART>
+__global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
+  constexpr int BMT = 256;
   constexpr int NW = BMT / 32;          // waves
   constexpr int NT = NW * 64;           // threads
   constexpr int WMW = BMT / 128;        // waves along M
@@ -192,20 +192,20 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
   constexpr int LPT = CH / NT;          // direct loads per thread per stage
   constexpr int LPA = AC / NT;          // ... of which A
   constexpr int SB = CH * 16;           // stage bytes
-  constexpr int NS = BMT == 128 ? 3 : 2;  // ring stages
+  constexpr int NS = 2;                 // ring stages
   constexpr int kLds = NS * SB > kEpiBytes ? NS * SB : kEpiBytes;
   constexpr bool kDual = MODE == G2_SWIGLU;
-  constexpr int RT = HL ? BMT / 2 : BMT;  // token rows per tile
+  constexpr int RT = BMT;               // token rows per tile
   static_assert(CH % NT == 0 && AC % NT == 0, "whole loads per thread");
   static_assert(kLds <= 160 * 1024, "LDS");
-  static_assert(!HL || BMT == 128, "hi/lo rows pair up inside one wave's row tiles");
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
 
-  int split = 0, tn, m0, rows_valid;
+  const int nks_all = p.Ka / BK;
+  int split = 0, tm = 0, tn = 0, ks0 = 0, nk = 0;
   {
     // XCD-aware tile order. Consecutive block ids go to the 8 XCDs
     // round-robin, each XCD with its own L2; so block b works on item
@@ -225,11 +225,13 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
     const int first_m = group * kGroupM;
     const int gsize = min(p.tiles_m - first_m, kGroupM);
     const int in_group = pid % (kGroupM * p.tiles_n);
-    const int tm = first_m + in_group % gsize;
+    tm = first_m + in_group % gsize;
     tn = in_group / gsize;
-    m0 = tm * RT;
-    rows_valid = min(RT, p.M - m0);
+    ks0 = split * p.ksteps_per_split;
+    nk = min(p.ksteps_per_split, nks_all - ks0);
   }
+  const int m0 = tm * RT;
+  const int rows_valid = min(RT, p.M - m0);
   const int n0 = tn * (kDual ? BN / 2 : BN);  // first output column of the tile
 
   // QKV: a 256-column tile lies inside one of the three weight matrices
@@ -260,10 +262,8 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
     const int row = Q / kRowChunks;
     const int c = (Q % kRowChunks) ^ swz(row);
     if (is_a) {
-      // rows past the tile re-read a valid row; HL: rows RT.. are the lo halves
-      const int rr = min(HL ? row % RT : row, rows_valid - 1);
-      const int kofs = HL && row >= RT ? p.Kb : 0;
-      src[j] = p.A + (size_t)(m0 + rr) * p.lda + kofs + c * 8;
+      const int rr = min(row, rows_valid - 1);  // rows past the tile re-read a valid row
+      src[j] = p.A + (size_t)(m0 + rr) * p.lda + c * 8;
     } else {
       const bf16* base;
       if constexpr (kDual) {
@@ -275,8 +275,6 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
       src[j] = base + c * 8;
     }
   }
-  const int ks0 = split * p.ksteps_per_split;
-  const int nk = min(p.ksteps_per_split, p.Ka / BK - ks0);
 
   auto issue = [&](int kt) {  // stage kt of this split -> ring slot kt % NS
     const int ka = (ks0 + kt) * BK;
@@ -319,17 +317,12 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
   // One stage: the fragments of k steps (0, 1) are read, then those of (2, 3)
   // are requested before the MFMAs of (0, 1) run, so only the first reads of
   // a stage sit in front of its MFMAs.
-  // 4-wave tiles serve batches that may fill only part of the tile: 32-row
-  // MFMA tiles of padding rows are skipped (block-uniform branches)
-  bool act[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) act[i] = BMT == 256 || (HL ? (32 * i) % RT : 32 * i) < rows_valid;
   auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][4], bf16x8 (&bfr)[2][TJ]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (act[i]) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+        af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
@@ -340,31 +333,22 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (act[i])
 #pragma unroll
-          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
   };
   static_assert(KS == 4, "two halves of two k steps per stage");
 
-  // Stage kt + NS - 1 is requested right after the barrier that publishes
-  // stage kt (and frees the slot stage kt - 1 used), and lands while stages
-  // kt .. kt + NS - 2 are multiplied.
-#pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < nk) issue(j);
+  // Two stages; stage kt+1 is requested right after the barrier that publishes
+  // stage kt and lands while stage kt is multiplied.
+  if (nk > 0) issue(0);
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's part of stage kt has landed; vector loads complete in
-    // order, so with three stages the LPT loads of stage kt + 1 may remain
-    if (NS == 3 && kt + 1 < nk)
-      wait_vmcnt<LPT>();
-    else
-      wait_vmcnt<0>();
+    wait_vmcnt<0>();  // this wave's part of stage kt (the only stage in flight)
     // every wave's part of stage kt has landed and every wave is done with
-    // the slot of stage kt - 1. A bare s_barrier: __syncthreads' release
-    // fence adds nothing here; the acquire fence keeps the LDS reads below it.
+    // the other slot. A bare s_barrier: __syncthreads' release fence adds
+    // nothing here; the acquire fence keeps the LDS reads below it.
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    if (kt + 1 < nk) issue(kt + 1);
     const char* st = smem + (kt % NS) * SB;
     bf16x8 a0[2][4], b0[2][TJ], a1[2][4], b1[2][TJ];
     read2(st, 0, a0, b0);
@@ -380,23 +364,11 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
 
   // ---- epilogue: 128 rows (one row of waves) at a time through LDS ----
   float* C = reinterpret_cast<float*>(smem);
-  // HL, BMT = 128: a wave's row tiles 0, 1 are hi rows and 2, 3 the matching
-  // lo rows; add them in registers and store two row tiles
-  constexpr bool kRegAdd = HL && BMT == 128;
-  constexpr int NI = kRegAdd ? 2 : 4;
-  if constexpr (kRegAdd) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += acc[i + 2][j][r];
-  }
 #pragma unroll
   for (int half = 0; half < WMW; ++half) {
     if (wm == half) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -406,7 +378,7 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
           }
     }
     __syncthreads();
-    constexpr int kEpiRows = RT < 128 ? RT : 128;
+    constexpr int kEpiRows = 128;
     const int rbase = half * 128;
     if constexpr (PART) {
       const int ldp = p.tiles_n * BN;
@@ -447,7 +419,7 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
         for (int e = 0; e < 8; ++e) v[e] = c[e] + badd[e];
         const size_t row = (size_t)(m0 + rbase + r);
         if constexpr (MODE == G2_BIAS) {
-          qkv_finish<HL>(p, row, col, v);  // the 128-row pair tiles serve decode
+          qkv_finish<false>(p, row, col, v);
           continue;
         }
         if constexpr (MODE == G2_RESID_F32) {
@@ -477,47 +449,333 @@ __global__ __launch_bounds__(BMT / 32 * 64, BMT / 128) void gemm2_kernel(const G
   }
 }
 
-// Sum of the split-K partials + the epilogue of MODE; one thread per 8 output
-// columns of one row.
+// Decode tiles: 4 waves as 1 x 4, each owning all RA LDS rows of A x 64
+// columns. Few-row batches stream their weights from HBM, and covering HBM
+// latency at full bandwidth takes about three 32 KiB weight stages in flight
+// per CU; so the A tile holds only RA rows (the batch rounded up to 32, 64 or
+// 128, [hi | lo] pairs counted twice) and the ring has four slots when RA <=
+// 64 (three stages in flight while one is multiplied), three otherwise.
+// HL: A is a [hi | lo] pair and the tile covers RA / 2 token rows; LDS rows
+// below RA / 2 hold the hi halves and the rest the lo halves at the same k,
+// so each B tile is fetched once and serves both, and each wave adds its lo
+// accumulators to its hi ones. The k loop then runs over Kb only; the QKV
+// epilogue takes the rows as sequences. 32-row MFMA tiles made only of
+// padding rows are skipped.
+// Work is cut stream-K: the tile-major (tile, k step) units are split into
+// gridDim.x contiguous runs, one per block. The ring runs on across the
+// tiles of a run; each tile's fp32 partial goes out straight from the
+// accumulators, at partial index = the block's ordinal among the blocks
+// touching the tile, and the reduce kernel sums them. Stores count in the
+// same vector-memory counter as the ring's loads, so a store in mid-run
+// would hold up the next stage's wait: for a plain A with RA <= 64 (long
+// gate/up and down runs) the first tile's accumulators are parked in a
+// second register set and every partial is stored after the last stage (a
+// run crossing more than one tile boundary stores the middle tiles as it
+// leaves them); otherwise (short Q/K/V and O runs, or no room for two sets)
+// each tile is stored as the run leaves it.
+template <int MODE, bool HL, int RA>
+__global__ __launch_bounds__(256, 1) void gemm2_dec_kernel(const G2Args p) {
+  constexpr int NT = 256, WCOLS = 64, TJ = 2;
+  constexpr int NI = RA / 32;           // 32-row MFMA tiles of A
+  constexpr int AC = RA * kRowChunks;   // A chunks per stage
+  constexpr int CH = AC + BN * kRowChunks;
+  constexpr int LPT = CH / NT;          // direct loads per thread per stage
+  constexpr int LPA = AC / NT;          // ... of which A
+  constexpr int SB = CH * 16;           // stage bytes
+  constexpr int NS = RA <= 64 ? 4 : 3;  // ring slots
+  constexpr bool kDual = MODE == G2_SWIGLU;
+  constexpr int RT = HL ? RA / 2 : RA;  // token rows per tile
+  constexpr int NO = HL ? NI / 2 : NI;  // 32-row tiles stored
+  static_assert(CH % NT == 0 && AC % NT == 0, "whole loads per thread");
+  static_assert(NS * SB <= 160 * 1024, "LDS");
+  static_assert(NS * LPT <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * SB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wn = tid >> 6;
+  const int nks = p.Ka / BK;
+  const int U = p.tiles_m * p.tiles_n * nks;
+  const int u0 = __builtin_amdgcn_readfirstlane((int)((long long)blockIdx.x * U / p.sk_grid));
+  const int total = __builtin_amdgcn_readfirstlane(
+      (int)((long long)(blockIdx.x + 1) * U / p.sk_grid) - u0);
+  const int ldp = p.tiles_n * BN;
+
+  // issue side: load plan of the tile whose stages are being requested
+  int itile = -1;
+  const bf16* src[LPT];
+  auto plan = [&](int t) {
+    const int m0 = (t % p.tiles_m) * RT;
+    const int rows_valid = min(RT, p.M - m0);
+    const int n0 = (t / p.tiles_m) * (kDual ? BN / 2 : BN);
+    const bf16* Bw = p.B;
+    int nb = n0;
+    if constexpr (MODE == G2_BIAS) {  // a 256-column tile lies inside one of Wq, Wk, Wv
+      if (n0 >= p.seg2) {
+        Bw = p.B3;
+        nb = n0 - p.seg2;
+      } else if (n0 >= p.seg1) {
+        Bw = p.B2;
+        nb = n0 - p.seg1;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int P = (4 * j + wn) * 64 + lane;
+      const bool is_a = j < LPA;
+      const int Q = is_a ? P : P - AC;
+      const int row = Q / kRowChunks;
+      const int c = (Q % kRowChunks) ^ swz(row);
+      if (is_a) {
+        // rows past the tile re-read a valid row; HL: rows RT.. are the lo halves
+        const int rr = min(HL ? row % RT : row, rows_valid - 1);
+        const int kofs = HL && row >= RT ? p.Kb : 0;
+        src[j] = p.A + (size_t)(m0 + rr) * p.lda + kofs + c * 8;
+      } else {
+        const bf16* base;
+        if constexpr (kDual) {
+          base = row < BN / 2 ? p.B + (size_t)(n0 + row) * p.ldb
+                              : p.B2 + (size_t)(n0 + row - BN / 2) * p.ldb;
+        } else {
+          base = Bw + (size_t)(nb + row) * p.ldb;
+        }
+        src[j] = base + c * 8;
+      }
+    }
+  };
+  // (integer division runs on the vector ALU; readfirstlane keeps the
+  // block-uniform tile index scalar, so branches on it stay scalar)
+  auto tile_of = [&](int uu) { return __builtin_amdgcn_readfirstlane(uu / nks); };
+  auto issue = [&](int g) {  // stage g of the run -> ring slot g % NS
+    const int uu = u0 + g;
+    const int t = tile_of(uu);
+    if (t != itile) {
+      plan(t);
+      itile = t;
+    }
+    const int ka = (uu - t * nks) * BK;
+    char* slot = smem + (g % NS) * SB;
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) load_lds16(src[j] + ka, slot + (4 * j + wn) * 1024);
+  };
+
+  f32x16 acc[NI][TJ], park[NI][TJ];
+  auto zero = [&]() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  zero();
+  // fp32 partial of tile t from accumulator set a
+  auto store_part = [&](f32x16 (&a)[NI][TJ], int t) {
+    const int m0 = __builtin_amdgcn_readfirstlane((t % p.tiles_m) * RT);
+    const int rows_valid = min(RT, p.M - m0);
+    if constexpr (HL) {
+#pragma unroll
+      for (int i = 0; i < NO; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a[i][j][r] += a[i + NO][j][r];
+    }
+    // element offsets (partials stay far below 2^32 elements): the uniform
+    // part per store, the lane's column and row parity
+    const int ord = __builtin_amdgcn_readfirstlane(
+        (int)blockIdx.x - sk_owner((long long)t * nks, U, p.sk_grid));
+    const uint32_t tile_off = (uint32_t)(((uint32_t)ord * p.M + m0) * ldp) +
+                              (uint32_t)((t / p.tiles_m) * BN + wn * WCOLS);
+    const uint32_t lane_off = (uint32_t)(4 * (lane >> 5) * ldp + (lane & 31));
+    const int lrow = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < NO; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rowc = 32 * i + 8 * (r >> 2) + (r & 3);
+        if (rowc + lrow < rows_valid) {
+          const uint32_t o = tile_off + (uint32_t)(rowc * ldp) + lane_off;
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) p.part[o + 32 * j] = a[i][j][r];
+        }
+      }
+  };
+  int t_park = -1;  // the run's first tile once its accumulators are parked
+
+  const int fr = lane & 31;
+  const int fk = lane >> 5;
+  constexpr int KS = BK / 16;
+  int aoff[KS][NI], boff[KS][TJ];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = 2 * ks + fk;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int ra = 32 * i + fr;
+      aoff[ks][i] = (ra * kRowChunks + (c ^ swz(ra))) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int rb = wn * WCOLS + 32 * j + fr;
+      boff[ks][j] = AC * 16 + (rb * kRowChunks + (c ^ swz(rb))) * 16;
+    }
+  }
+
+  bool act[NI];
+  auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][NI], bf16x8 (&bfr)[2][TJ]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (act[i]) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
+    }
+  };
+  auto mma2 = [&](const bf16x8 (&af)[2][NI], const bf16x8 (&bfr)[2][TJ]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (act[i])
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+  };
+  static_assert(KS == 4, "two halves of two k steps per stage");
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < total) issue(j);
+  for (int g = 0; g < total; ++g) {
+    // this wave's part of stage g has landed: loads complete in order, so the
+    // loads of the (up to NS - 2) later stages already requested may remain
+    // (stores of partials only make the wait longer)
+    const int later = min(NS - 2, total - 1 - g);
+    if (NS == 4 && later == 2)
+      wait_vmcnt<2 * LPT>();
+    else if (later >= 1)
+      wait_vmcnt<LPT>();
+    else
+      wait_vmcnt<0>();
+    // every wave's part of stage g has landed and every wave is done with
+    // the slot of stage g - 1
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (g + NS - 1 < total) issue(g + NS - 1);
+    const int uu = u0 + g;
+    const int t = tile_of(uu);
+    const int m0 = __builtin_amdgcn_readfirstlane((t % p.tiles_m) * RT);
+    const int rows_valid = min(RT, p.M - m0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) act[i] = (HL ? (32 * i) % RT : 32 * i) < rows_valid;
+    const char* st = smem + (g % NS) * SB;
+    bf16x8 a0[2][NI], b0[2][TJ], a1[2][NI], b1[2][TJ];
+    read2(st, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    read2(st, 2, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma2(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma2(a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (uu - t * nks == nks - 1 && g + 1 < total) {  // the run moves on to the next tile
+      if (!HL && RA <= 64 && t_park < 0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) park[i][j] = acc[i][j];
+        t_park = t;
+      } else {
+        store_part(acc, t);
+      }
+      zero();
+    }
+  }
+  if (total > 0) {
+    store_part(acc, tile_of(u0 + total - 1));
+    if (t_park >= 0) store_part(park, t_park);
+  }
+}
+
+// Sum of the split-K / stream-K partials + the epilogue of MODE. A block
+// takes one row and 64 groups of 8 output columns; its 4 waves sum every
+// 4th partial (lane = column group, up to four partials' loads in flight),
+// meet in LDS, and wave 0 applies the epilogue (16 lanes = one head of 128
+// columns for the QKV epilogue).
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
   constexpr bool kDual = MODE == G2_SWIGLU;
+  constexpr int NV = kDual ? 16 : 8;  // values summed per lane (gate and up for SwiGLU)
+  __shared__ float red[3][64][NV + 1];
   const int ldp = p.tiles_n * BN;
   const int segs = (kDual ? p.tiles_n * BN / 2 : p.tiles_n * BN) / 8;  // per row
-  const size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  if (idx >= (size_t)p.M * segs) return;
-  const int row = (int)(idx / segs);
-  const int seg = (int)(idx % segs);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.y;
+  const int seg = blockIdx.x * 64 + lane;
+  const bool live = seg < segs;
+  const int sg = live ? seg : segs - 1;
   const size_t pstride = (size_t)p.M * ldp;
-  if constexpr (kDual) {
-    const int tn = seg / (BN / 16), c = (seg % (BN / 16)) * 8;
-    const float* pg = p.part + (size_t)row * ldp + tn * BN + c;
-    float g[8] = {}, u[8] = {};
-    for (int s = 0; s < p.splits; ++s) {
-      const float* q = pg + s * pstride;
+  const int tn = kDual ? sg / (BN / 16) : sg / (BN / 8);
+  int cnt = p.splits;
+  if (p.streamk) {  // blocks whose runs touched this tile
+    const int nks = p.Ka / BK;
+    const long long U = (long long)p.tiles_m * p.tiles_n * nks;
+    const long long t = (long long)tn * p.tiles_m + row / p.rows_per_tile;
+    cnt = sk_owner(t * nks + nks - 1, U, p.sk_grid) - sk_owner(t * nks, U, p.sk_grid) + 1;
+  }
+  // partial columns of this lane: [c0, c0 + 8) (and the up half at + BN / 2)
+  const int c0 = kDual ? tn * BN + (sg % (BN / 16)) * 8 : sg * 8;
+  const float* q0 = p.part + (size_t)row * ldp + c0;
+  float v[NV];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        g[e] += q[e];
-        u[e] += q[e + BN / 2];
-      }
+  for (int e = 0; e < NV; ++e) v[e] = 0.f;
+  auto add = [&](const f32x4 (&x)[NV / 4]) {
+#pragma unroll
+    for (int h = 0; h < NV / 4; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * h + e] += x[h][e];
+  };
+  auto load = [&](int s, f32x4 (&x)[NV / 4]) {
+    const float* q = q0 + s * pstride;
+    x[0] = *reinterpret_cast<const f32x4*>(q);
+    x[1] = *reinterpret_cast<const f32x4*>(q + 4);
+    if constexpr (kDual) {
+      x[2] = *reinterpret_cast<const f32x4*>(q + BN / 2);
+      x[3] = *reinterpret_cast<const f32x4*>(q + BN / 2 + 4);
     }
+  };
+  int s = wave;
+  for (; s + 12 < cnt; s += 16) {
+    f32x4 x[4][NV / 4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load(s + 4 * i, x[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) add(x[i]);
+  }
+  for (; s < cnt; s += 4) {
+    f32x4 x[NV / 4];
+    load(s, x);
+    add(x);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e) red[wave - 1][lane][e] = v[e];
+  }
+  __syncthreads();
+  if (wave > 0 || !live) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int e = 0; e < NV; ++e) v[e] += red[w][lane][e];
+  if constexpr (kDual) {
     float h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = silu_f32(g[e]) * u[e];
+    for (int e = 0; e < 8; ++e) h[e] = silu_f32(v[e]) * v[e + 8];
     store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + seg * 8, pack8(h));
   } else {
     const int col = seg * 8;
-    const float* pc = p.part + (size_t)row * ldp + col;
-    float v[8] = {};
-    for (int s = 0; s < p.splits; ++s) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(pc + s * pstride);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(pc + s * pstride + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] += a[e];
-        v[e + 4] += b[e];
-      }
-    }
+    float (&w8)[8] = *reinterpret_cast<float (*)[8]>(v);
     if constexpr (MODE == G2_BIAS) {
       const bf16* bias = p.bias;
       int nb = col;
@@ -532,73 +790,114 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
         float b8[8];
         unpack8(load_bf16x8(bias + nb), b8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] += b8[e];
+        for (int e = 0; e < 8; ++e) w8[e] += b8[e];
       }
       if (p.cache_len)
-        qkv_finish<true>(p, (size_t)row, col, v);
+        qkv_finish<true>(p, (size_t)row, col, w8);
       else
-        qkv_finish<false>(p, (size_t)row, col, v);
+        qkv_finish<false>(p, (size_t)row, col, w8);
       return;
     }
     if constexpr (MODE == G2_RESID_F32) {
       float x[8];
       unpack8(load_bf16x8(p.resid_bf16 + (size_t)row * p.ldr + col), x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += x[e];
+      for (int e = 0; e < 8; ++e) w8[e] += x[e];
     }
     if constexpr (MODE == G2_RESID_OUT) {
       const float* rr = p.resid_f32 + (size_t)row * p.ldr + col;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += rr[e];
-      store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + col, pack8(v));
+      for (int e = 0; e < 8; ++e) w8[e] += rr[e];
+      store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + col, pack8(w8));
     } else {
       float* o = p.out_f32 + (size_t)row * p.ldo + col;
-      *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      *reinterpret_cast<f32x4*>(o) = f32x4{w8[0], w8[1], w8[2], w8[3]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{w8[4], w8[5], w8[6], w8[7]};
     }
   }
 }
 
-// Tile shapes: 256 token rows (8 waves); 64 token rows from a [hi | lo]
-// pair (4 waves); 128 token rows from a plain bf16 A (4 waves).
-enum : int { T256 = 0, T64_HL, T128 };
+// Tile shapes: 256 token rows (8 waves); the 4-wave decode tiles with an A
+// tile of 32, 64 or 128 LDS rows, from a plain bf16 A or from a [hi | lo]
+// pair (16, 32 or 64 token rows).
+enum : int { T256 = 0, D32, D64, D128, D32_HL, D64_HL, D128_HL };
+constexpr int shape_ra(int sh) { return sh == D32 || sh == D32_HL ? 32 : (sh == D64 || sh == D64_HL ? 64 : 128); }
+constexpr bool shape_hl(int sh) { return sh >= D32_HL; }
+// (a pair needs its hi and lo rows in different 32-row MFMA tiles: RA >= 64)
+int decode_shape(int M, bool pair) {
+  if (pair) return M <= 32 ? D64_HL : D128_HL;
+  return M <= 32 ? D32 : (M <= 64 ? D64 : D128);
+}
 
 template <int MODE, int SHAPE>
 hipError_t launch(const G2Args& a, dim3 grid, hipStream_t s) {
-  constexpr int BMT = SHAPE == T256 ? 256 : 128;
-  constexpr bool HL = SHAPE == T64_HL;
+  constexpr bool HL = shape_hl(SHAPE);
   // hi/lo inputs feed Q/K/V and O; plain bf16 inputs feed gate/up and down
   constexpr bool kPairIn = MODE == G2_BIAS || MODE == G2_RESID_F32;
-  if constexpr (SHAPE != T256 && HL != kPairIn) {
+  if constexpr (SHAPE != T256 && (HL != kPairIn || SHAPE == D32_HL)) {
     return hipErrorInvalidValue;
+  } else if constexpr (SHAPE != T256) {  // decode tiles: stream-K partials
+    hipLaunchKernelGGL((gemm2_dec_kernel<MODE, HL, shape_ra(SHAPE)>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
   } else {
     if (a.splits == 1)
-      hipLaunchKernelGGL((gemm2_kernel<MODE, false, BMT, HL>), grid, dim3(BMT / 32 * 64), 0, s, a);
+      hipLaunchKernelGGL((gemm2_kernel<MODE, false>), grid, dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm2_kernel<MODE, true, BMT, HL>), grid, dim3(BMT / 32 * 64), 0, s, a);
+      hipLaunchKernelGGL((gemm2_kernel<MODE, true>), grid, dim3(512), 0, s, a);
     return hipGetLastError();
   }
+}
+
+int rows_per_tile(int shape) {
+  return shape == T256 ? 256 : (shape_hl(shape) ? shape_ra(shape) / 2 : shape_ra(shape));
+}
+
+// stream-K cut of the (tile, k step) units over at most kSkBlocks blocks
+constexpr int kSkBlocks = 256;
+int sk_grid(long long units) { return (int)std::min<long long>(kSkBlocks, units); }
+int sk_max_count(int tiles, int nks, int G) {
+  const long long U = (long long)tiles * nks;
+  int mx = 1;
+  for (int t = 0; t < tiles; ++t)
+    mx = std::max(mx, sk_owner((long long)t * nks + nks - 1, U, G) -
+                          sk_owner((long long)t * nks, U, G) + 1);
+  return mx;
 }
 
 template <int MODE>
 hipError_t run(G2Args a, int shape, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  const int rt = shape == T256 ? 256 : (shape == T64_HL ? 64 : 128);
+  const int rt = rows_per_tile(shape);
+  a.rows_per_tile = rt;
   a.tiles_m = (a.M + rt - 1) / rt;
   const int nks = a.Ka / BK;
-  a.splits = a.splits < 1 ? 1 : (a.splits > nks ? nks : a.splits);
-  a.ksteps_per_split = (nks + a.splits - 1) / a.splits;
-  a.splits = (nks + a.ksteps_per_split - 1) / a.ksteps_per_split;
-  const int total = a.tiles_m * a.tiles_n * a.splits;
-  const dim3 grid(8 * ((total + 7) / 8));
-  hipError_t e = shape == T256      ? launch<MODE, T256>(a, grid, s)
-                 : shape == T64_HL ? launch<MODE, T64_HL>(a, grid, s)
-                                    : launch<MODE, T128>(a, grid, s);
-  if (e != hipSuccess || a.splits == 1) return e;
+  dim3 grid;
+  if (shape != T256) {  // decode tiles: stream-K, always through the partials
+    a.streamk = 1;
+    a.sk_grid = sk_grid((long long)a.tiles_m * a.tiles_n * nks);
+    a.splits = 1;
+    grid = dim3(a.sk_grid);
+  } else {
+    a.splits = a.splits < 1 ? 1 : (a.splits > nks ? nks : a.splits);
+    a.ksteps_per_split = (nks + a.splits - 1) / a.splits;
+    a.splits = (nks + a.ksteps_per_split - 1) / a.ksteps_per_split;
+    const int total = a.tiles_m * a.tiles_n * a.splits;
+    grid = dim3(8 * ((total + 7) / 8));
+  }
+  hipError_t e;
+  switch (shape) {
+    case T256: e = launch<MODE, T256>(a, grid, s); break;
+    case D32: e = launch<MODE, D32>(a, grid, s); break;
+    case D64: e = launch<MODE, D64>(a, grid, s); break;
+    case D128: e = launch<MODE, D128>(a, grid, s); break;
+    case D64_HL: e = launch<MODE, D64_HL>(a, grid, s); break;
+    case D128_HL: e = launch<MODE, D128_HL>(a, grid, s); break;
+    default: e = hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || (!a.streamk && a.splits == 1)) return e;
   const int segs = (MODE == G2_SWIGLU ? a.tiles_n * BN / 2 : a.tiles_n * BN) / 8;
-  const size_t threads = (size_t)a.M * segs;
-  hipLaunchKernelGGL(gemm2_reduce_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                     0, s, a);
+  hipLaunchKernelGGL(gemm2_reduce_kernel<MODE>, dim3((unsigned)((segs + 63) / 64), (unsigned)a.M),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -627,7 +926,15 @@ bool ql_gemm2_ok(int N, int Kb, bool dual) {
   return Kb % BK == 0 && (dual ? N % (BN / 2) == 0 : N % BN == 0);
 }
 
-int ql_gemm2_ksteps(int K) { return K / BK; }
+size_t ql_gemm2_decode_part_bytes(int M, int b_rows, int K, bool pair) {
+  if (M <= 0) return 0;
+  const int shape = decode_shape(M, pair);
+  const int rt = rows_per_tile(shape);
+  const int tiles = ((M + rt - 1) / rt) * ((b_rows + BN - 1) / BN);
+  const int nks = K / BK;
+  const int G = sk_grid((long long)tiles * nks);
+  return (size_t)sk_max_count(tiles, nks, G) * M * ((b_rows + BN - 1) / BN) * BN * 4;
+}
 
 hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
@@ -657,7 +964,7 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
   a.bias3 = bv;
   a.ldo = q + 2 * kv;
   a.tiles_n = (q + 2 * kv) / BN;
-  return run<G2_BIAS>(a, rows128 ? T64_HL : T256, s);
+  return run<G2_BIAS>(a, rows128 ? decode_shape(M, true) : T256, s);
 }
 
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
@@ -670,7 +977,7 @@ hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K
   a.out_f32 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_F32>(a, rows128 ? T64_HL : T256, s);
+  return run<G2_RESID_F32>(a, rows128 ? decode_shape(M, true) : T256, s);
 }
 
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
@@ -682,7 +989,7 @@ hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
   a.out_bf16 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_OUT>(a, rows128 ? T128 : T256, s);
+  return run<G2_RESID_OUT>(a, rows128 ? decode_shape(M, false) : T256, s);
 }
 
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
@@ -692,5 +999,5 @@ hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu,
   a.out_bf16 = out;
   a.ldo = F;
   a.tiles_n = F / (BN / 2);
-  return run<G2_SWIGLU>(a, rows128 ? T128 : T256, s);
+  return run<G2_SWIGLU>(a, rows128 ? decode_shape(M, false) : T256, s);
 }

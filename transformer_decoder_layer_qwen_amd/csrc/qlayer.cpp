@@ -171,49 +171,6 @@ int gemm2_splits(int M, int b_rows, int K) {
   int sp = std::max(1, kGemmTargetBlocks / std::max(tiles, 1));
   return std::max(1, std::min(sp, K / 512));
 }
-// Decode-sized GEMMs (64 token rows per tile for the hi/lo inputs of Q/K/V
-// and O, 128 for gate/up and down) stream their weights from HBM. The split count minimises an estimate of the call time: each wave of
-// at most one block per CU costs, per k step, the larger of its share of HBM
-// bandwidth (256 x 64 bf16 weights per block per step) and one CU's own fetch
-// rate, plus a start-up; split partials cost their write and read-back and a
-// reduce launch.
-constexpr double kHbmBytesPerUs = 6.0e6, kCuBytesPerUs = 4.5e4;
-constexpr double kBlockStartUs = 2.0, kReduceUs = 3.0;
-int decode_gemm_splits(int M, int tiles, int nks, int out_cols) {
-  constexpr double step_bytes = 256.0 * 64 * 2;
-  int best = 1;
-  double best_t = 1e30;
-  for (int sp = 1; sp <= std::min(nks, 64); ++sp) {
-    const int per = (nks + sp - 1) / sp;
-    const int s_eff = (nks + per - 1) / per;
-    if (s_eff != sp) continue;
-    const int blocks = tiles * s_eff;
-    double t = 0;
-    for (int left = blocks; left > 0; left -= kGemmTargetBlocks) {
-      const int a = std::min(left, kGemmTargetBlocks);
-      t += per * std::max(a * step_bytes / kHbmBytesPerUs, step_bytes / kCuBytesPerUs) +
-           kBlockStartUs;
-    }
-    if (s_eff > 1) t += 2.0 * s_eff * M * out_cols * 4 / kHbmBytesPerUs + kReduceUs;
-    if (t < best_t) {
-      best_t = t;
-      best = s_eff;
-    }
-  }
-  return best;
-}
-struct DecodeSplits {
-  int qkv, o, gu, dn;
-};
-DecodeSplits decode_gemm_plan(const ql_config& c, int q_dim, int qkv_dim, int M) {
-  DecodeSplits d;
-  const int tm = (M + 63) / 64;
-  d.qkv = decode_gemm_splits(M, tm * qkv_dim / 256, ql_gemm2_ksteps(c.d), qkv_dim);
-  d.o = decode_gemm_splits(M, tm * c.d / 256, ql_gemm2_ksteps(q_dim), c.d);
-  d.gu = decode_gemm_splits(M, c.ffn_dim / 128, ql_gemm2_ksteps(c.d), 2 * c.ffn_dim);
-  d.dn = decode_gemm_splits(M, c.d / 256, ql_gemm2_ksteps(c.ffn_dim), c.d);
-  return d;
-}
 // Partial-tile bytes: the four dense GEMMs at the largest prefill M, and at
 // every decode batch size that takes the MFMA tiles.
 size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
@@ -225,12 +182,11 @@ size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
     b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, c.ffn_dim)));
   }
   for (int B = kGemvMaxRows + 1; B <= c.max_batch; ++B) {
-    const DecodeSplits d = decode_gemm_plan(c, q_dim, qkv_dim, B);
-    b = std::max(b, ql_gemm2_part_bytes(B, qkv_dim, d.qkv));
-    b = std::max(b, ql_gemm2_part_bytes(B, c.d, d.o));
+    b = std::max(b, ql_gemm2_decode_part_bytes(B, qkv_dim, c.d, true));
+    b = std::max(b, ql_gemm2_decode_part_bytes(B, c.d, q_dim, true));
     if (c.n_experts == 0) {
-      b = std::max(b, ql_gemm2_part_bytes(B, 2 * c.ffn_dim, d.gu));
-      b = std::max(b, ql_gemm2_part_bytes(B, c.d, d.dn));
+      b = std::max(b, ql_gemm2_decode_part_bytes(B, 2 * c.ffn_dim, c.d, false));
+      b = std::max(b, ql_gemm2_decode_part_bytes(B, c.d, c.ffn_dim, false));
     }
   }
   return b;
@@ -426,15 +382,9 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
              QL_HIP(ql_gemv_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
     return QL_OK;
   }
-  int sgu, sdn;
-  if (decode) {
-    const DecodeSplits d = decode_gemm_plan(c, h->q_dim, h->qkv_dim, N);
-    sgu = d.gu;
-    sdn = d.dn;
-  } else {
-    sgu = gemm2_splits(N, 2 * c.ffn_dim, c.d);
-    sdn = gemm2_splits(N, c.d, c.ffn_dim);
-  }
+  // (decode tiles cut their work evenly over the CUs themselves)
+  const int sgu = decode ? 1 : gemm2_splits(N, 2 * c.ffn_dim, c.d);
+  const int sdn = decode ? 1 : gemm2_splits(N, c.d, c.ffn_dim);
   QL_STAGE(h, QL_STAGE_GATE_UP, s,
            QL_HIP(ql_gemm2_swiglu(z, N, wg, wu, c.ffn_dim, c.d, hh, decode, sgu, h->g2part, s)));
   QL_STAGE(h, QL_STAGE_DOWN, s,
@@ -534,7 +484,6 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
   da.part_ml = h->part_ml;
   da.scale_log2 = scale_log2(c.head_dim);
   if (!gemv) {
-    const DecodeSplits sp = decode_gemm_plan(c, h->q_dim, h->qkv_dim, B);
     bf16* xhat = static_cast<bf16*>(h->xhat);  // [B, 2d]: hi | lo
     QL_STAGE(h, QL_STAGE_RMSNORM1, s,
              QL_HIP(ql_rmsnorm_bf16_to_hilo(x, g1, xhat, B, c.d, c.rms_eps, s)));
@@ -552,7 +501,7 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
     f.v_cache = static_cast<bf16*>(vc);
     QL_STAGE(h, QL_STAGE_QKV, s,
              QL_HIP(ql_gemm2_qkv(xhat, B, wq, wk, wv, h->q_dim, h->kv_dim, c.d, bq, bk, bv, f,
-                                 true, sp.qkv, h->g2part, s)));
+                                 true, 1, h->g2part, s)));
     da.q_in = static_cast<const bf16*>(h->q);
     da.out_hilo = static_cast<bf16*>(h->attn);  // [B, 2q]: hi | lo
     da.lo_off = h->q_dim;
@@ -561,7 +510,7 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
     h->attn_hilo = true;
     QL_STAGE(h, QL_STAGE_O_PROJ, s,
              QL_HIP(ql_gemm2_resid_f32(static_cast<const bf16*>(h->attn), B, wo, c.d, h->q_dim,
-                                       x, h->r, true, sp.o, h->g2part, s)));
+                                       x, h->r, true, 1, h->g2part, s)));
     return ffn_dense_or_moe(h, B, true, y, s);
   }
   QL_STAGE(h, QL_STAGE_QKV, s,
