@@ -339,8 +339,8 @@ GemmArgs base_args(const bf16* A, int lda, int M, const bf16* B, int ldb, int K)
 
 hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
                           int mf, int d, const int* tile_expert, const int* tile_row0,
-                          const int* tile_rows, const int* num_tiles, int max_tiles, int bm,
-                          bf16* H, hipStream_t s) {
+                          const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                          hipStream_t s) {
   GemmArgs a = base_args(Z, d, 0, Wg, d, d);
   a.B2 = Wu;
   a.b_expert_stride = (size_t)mf * d;
@@ -352,13 +352,12 @@ hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, 
   a.out_bf16 = H;
   a.ldo = mf;
   a.tiles_n = mf / 64;
-  if (bm == 128) return launch<128, 128, 64, 64, GM_MOE_GU>(a, max_tiles, s);
   return launch<32, 128, 32, 32, GM_MOE_GU>(a, max_tiles, s);
 }
 
 hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                            int max_tiles, int bm, float* out, hipStream_t s) {
+                            int max_tiles, float* out, hipStream_t s) {
   GemmArgs a = base_args(H, mf, 0, Wd, mf, mf);
   a.b_expert_stride = (size_t)d * mf;
   a.tile_expert = tile_expert;
@@ -368,6 +367,5 @@ hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const 
   a.out_f32 = out;
   a.ldo = d;
   a.tiles_n = d / 128;
-  if (bm == 128) return launch<128, 128, 64, 64, GM_MOE_DOWN>(a, max_tiles, s);
   return launch<32, 128, 32, 32, GM_MOE_DOWN>(a, max_tiles, s);
 }

@@ -32,6 +32,8 @@
 //   RESID_F32 out_f32 = resid_bf16 + acc        R = X + O W_O^T
 //   RESID_OUT out     = bf16(resid_f32 + acc)   Y = R + H W_down^T
 //   SWIGLU    out     = bf16(SiLU(g) * u)       B tile = [128 W_gate rows | 128 W_up rows]
+//   MOE_GU    SWIGLU on gathered token rows with one expert's weights per tile
+//   MOE_DOWN  out_f32 = acc for one expert's slot rows
 // With split-K each split stores its fp32 partial tile and the reduce kernel
 // applies the epilogue.
 // ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §4, §9, §10.)
@@ -40,7 +42,7 @@
 
 namespace {
 
-enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU };
+enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU, G2_MOE_GU, G2_MOE_DOWN };
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kGroupM = 4;  // tile rows per L2 group
@@ -82,6 +84,15 @@ struct G2Args {
   bf16* q_out;          // [M, Hq*128]
   bf16* k_cache;        // [B, T_max, Hkv, 128]
   bf16* v_cache;
+  // MoE expert tiles: tile i covers slot rows [tile_row0[i], + tile_rows[i])
+  // of expert tile_expert[i]; *num_tiles tiles exist. MOE_GU gathers A row
+  // row_index[slot]; expert e's weights start e * b_expert_stride elements in.
+  const int* row_index;
+  const int* tile_expert;
+  const int* tile_row0;
+  const int* tile_rows;
+  const int* num_tiles;
+  size_t b_expert_stride;
 };
 
 // QKV epilogue for 8 columns [col, col + 8) of token row `row`, bias added.
@@ -194,10 +205,12 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   constexpr int SB = CH * 16;           // stage bytes
   constexpr int NS = 2;                 // ring stages
   constexpr int kLds = NS * SB > kEpiBytes ? NS * SB : kEpiBytes;
-  constexpr bool kDual = MODE == G2_SWIGLU;
+  constexpr bool kDual = MODE == G2_SWIGLU || MODE == G2_MOE_GU;
+  constexpr bool kMoe = MODE == G2_MOE_GU || MODE == G2_MOE_DOWN;
   constexpr int RT = BMT;               // token rows per tile
   static_assert(CH % NT == 0 && AC % NT == 0, "whole loads per thread");
   static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(!kMoe || !PART, "expert tiles run whole");
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -206,7 +219,26 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
 
   const int nks_all = p.Ka / BK;
   int split = 0, tm = 0, tn = 0, ks0 = 0, nk = 0;
-  {
+  int m0, rows_valid;
+  size_t eoff = 0;  // expert weight offset
+  if constexpr (kMoe) {
+    // The grid covers the most tiles routing can produce; the tile count is
+    // known on the device only. Work item w = tile * tiles_n + tn, split into
+    // 8 contiguous stretches by XCD as below, so the column tiles of an
+    // expert tile, and the tiles of one expert, run close together on one
+    // XCD and share A and B through its L2.
+    const int total = *p.num_tiles * p.tiles_n;
+    const int chunk = (total + 7) / 8;
+    if ((int)(blockIdx.x / 8) >= chunk) return;
+    const int w = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
+    if (w >= total) return;
+    const int ti = w / p.tiles_n;
+    tn = w % p.tiles_n;
+    m0 = p.tile_row0[ti];
+    rows_valid = p.tile_rows[ti];
+    eoff = (size_t)p.tile_expert[ti] * p.b_expert_stride;
+    nk = nks_all;
+  } else {
     // XCD-aware tile order. Consecutive block ids go to the 8 XCDs
     // round-robin, each XCD with its own L2; so block b works on item
     // (b % 8) * chunk + b / 8 of the work list, and every XCD walks a
@@ -229,13 +261,13 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     tn = in_group / gsize;
     ks0 = split * p.ksteps_per_split;
     nk = min(p.ksteps_per_split, nks_all - ks0);
+    m0 = tm * RT;
+    rows_valid = min(RT, p.M - m0);
   }
-  const int m0 = tm * RT;
-  const int rows_valid = min(RT, p.M - m0);
   const int n0 = tn * (kDual ? BN / 2 : BN);  // first output column of the tile
 
   // QKV: a 256-column tile lies inside one of the three weight matrices
-  const bf16* Bw = p.B;
+  const bf16* Bw = p.B + eoff;
   const bf16* bias = p.bias;
   int nb = n0;
   if constexpr (MODE == G2_BIAS) {
@@ -263,12 +295,13 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     const int c = (Q % kRowChunks) ^ swz(row);
     if (is_a) {
       const int rr = min(row, rows_valid - 1);  // rows past the tile re-read a valid row
-      src[j] = p.A + (size_t)(m0 + rr) * p.lda + c * 8;
+      const size_t ar = MODE == G2_MOE_GU ? (size_t)p.row_index[m0 + rr] : (size_t)(m0 + rr);
+      src[j] = p.A + ar * p.lda + c * 8;
     } else {
       const bf16* base;
       if constexpr (kDual) {
-        base = row < BN / 2 ? p.B + (size_t)(n0 + row) * p.ldb
-                            : p.B2 + (size_t)(n0 + row - BN / 2) * p.ldb;
+        base = row < BN / 2 ? Bw + (size_t)(n0 + row) * p.ldb
+                            : p.B2 + eoff + (size_t)(n0 + row - BN / 2) * p.ldb;
       } else {
         base = Bw + (size_t)(nb + row) * p.ldb;
       }
@@ -316,13 +349,20 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
 
   // One stage: the fragments of k steps (0, 1) are read, then those of (2, 3)
   // are requested before the MFMAs of (0, 1) run, so only the first reads of
-  // a stage sit in front of its MFMAs.
+  // a stage sit in front of its MFMAs. Expert tiles are often part-filled:
+  // their 32-row MFMA tiles made only of padding rows are skipped.
+  bool act[4];
+  {
+    const int wmu = __builtin_amdgcn_readfirstlane(wm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) act[i] = !kMoe || wmu * 128 + 32 * i < rows_valid;
+  }
   auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][4], bf16x8 (&bfr)[2][TJ]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+        if (act[i]) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
@@ -333,8 +373,9 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
+        if (act[i])
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
   };
   static_assert(KS == 4, "two halves of two k steps per stage");
 
@@ -1000,4 +1041,45 @@ hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu,
   a.ldo = F;
   a.tiles_n = F / (BN / 2);
   return run<G2_SWIGLU>(a, rows128 ? decode_shape(M, false) : T256, s);
+}
+
+hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
+                           int mf, int d, const int* tile_expert, const int* tile_row0,
+                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                           hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  G2Args a = base(Z, 0, d, Wg, d, 1, nullptr);
+  a.B2 = Wu;
+  a.b_expert_stride = (size_t)mf * d;
+  a.row_index = slot_token;
+  a.tile_expert = tile_expert;
+  a.tile_row0 = tile_row0;
+  a.tile_rows = tile_rows;
+  a.num_tiles = num_tiles;
+  a.out_bf16 = H;
+  a.ldo = mf;
+  a.tiles_n = mf / (BN / 2);
+  const int total = max_tiles * a.tiles_n;
+  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false>), dim3(8 * ((total + 7) / 8)), dim3(512), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
+                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
+                             int max_tiles, float* out, hipStream_t s) {
+  if (max_tiles <= 0) return hipSuccess;
+  G2Args a = base(H, 0, mf, Wd, mf, 1, nullptr);
+  a.b_expert_stride = (size_t)d * mf;
+  a.tile_expert = tile_expert;
+  a.tile_row0 = tile_row0;
+  a.tile_rows = tile_rows;
+  a.num_tiles = num_tiles;
+  a.out_f32 = out;
+  a.ldo = d;
+  a.tiles_n = d / BN;
+  const int total = max_tiles * a.tiles_n;
+  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false>), dim3(8 * ((total + 7) / 8)), dim3(512),
+                     0, s, a);
+  return hipGetLastError();
 }

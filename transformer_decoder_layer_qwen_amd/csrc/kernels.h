@@ -24,14 +24,15 @@ hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, f
 hipError_t ql_rmsnorm_f32(const float* x, const float* gamma, float* out, int rows, int d,
                           float eps, hipStream_t s);
 
-// ---- MoE expert GEMMs over routed row tiles (mf % 64 == 0, d % 128 == 0) ----
+// ---- MoE expert GEMMs over routed 32-row tiles (decode-sized batches;
+// mf % 64 == 0, d % 128 == 0) ----
 hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
                           int mf, int d, const int* tile_expert, const int* tile_row0,
-                          const int* tile_rows, const int* num_tiles, int max_tiles, int bm,
-                          bf16* H, hipStream_t s);
+                          const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                          hipStream_t s);
 hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                            int max_tiles, int bm, float* out, hipStream_t s);
+                            int max_tiles, float* out, hipStream_t s);
 
 // ---- GEMMs on 256-column tiles (N % 256 == 0, or F % 128 for SwiGLU; K % 64) ----
 // A2 = [hi | lo] bf16 pair of an fp32 activation, [M, 2K].
@@ -73,6 +74,15 @@ hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
                               hipStream_t s);
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
                            bf16* out, bool rows128, int splits, void* part, hipStream_t s);
+// MoE expert GEMMs on 256-row expert tiles (the permute's tile table built
+// with bm = 256; max_tiles bounds *num_tiles; mf % 128 == 0, d % 256 == 0)
+hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
+                           int mf, int d, const int* tile_expert, const int* tile_row0,
+                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                           hipStream_t s);
+hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
+                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
+                             int max_tiles, float* out, hipStream_t s);
 
 // ---- decode GEMVs for M <= kGemvMaxRows rows (N % 2 == 0, K % 8 == 0) ----
 // qkv_raw: out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x,

@@ -312,8 +312,11 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
   ra.w = h->topw;
   QL_STAGE(h, QL_STAGE_ROUTER, s, QL_HIP(ql_router_topk(ra, s)));
 
-  // rows per expert tile: 128 when experts see many rows, 32 for decode-sized batches
-  const int bm = ((long long)N * c.top_k >= 64LL * c.n_experts) ? 128 : kMinMoeTile;
+  // Expert tiles: 256 rows on the 8-wave MFMA tiles when experts see many
+  // rows (the prefill), 32 rows on the small-tile kernel for decode-sized
+  // batches.
+  const bool big = (long long)N * c.top_k >= 64LL * c.n_experts;
+  const int bm = big ? 256 : kMinMoeTile;
   const int max_tiles = (int)(((long long)N * c.top_k + bm - 1) / bm + c.n_experts);
   PermuteArgs pa{};
   pa.idx = h->idx;
@@ -332,17 +335,26 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
   pa.pos_of = h->pos_of;
   QL_STAGE(h, QL_STAGE_PERMUTE, s, QL_HIP(ql_moe_permute(pa, s)));
 
-  QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
-           QL_HIP(ql_gemm_moe_gu(static_cast<const bf16*>(h->z), h->slot_token,
-                                 static_cast<const bf16*>(w.we_gate),
-                                 static_cast<const bf16*>(w.we_up), c.ffn_dim, c.d,
-                                 h->tile_expert, h->tile_row0, h->tile_rows, h->num_tiles,
-                                 max_tiles, bm, static_cast<bf16*>(h->hm), s)));
-  QL_STAGE(h, QL_STAGE_EXPERT_DOWN, s,
-           QL_HIP(ql_gemm_moe_down(static_cast<const bf16*>(h->hm),
-                                   static_cast<const bf16*>(w.we_down), c.ffn_dim, c.d,
-                                   h->tile_expert, h->tile_row0, h->tile_rows, h->num_tiles,
-                                   max_tiles, bm, h->out_slot, s)));
+  const bf16* z = static_cast<const bf16*>(h->z);
+  const bf16* wg = static_cast<const bf16*>(w.we_gate);
+  const bf16* wu = static_cast<const bf16*>(w.we_up);
+  const bf16* wd = static_cast<const bf16*>(w.we_down);
+  bf16* hm = static_cast<bf16*>(h->hm);
+  if (big) {
+    QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
+             QL_HIP(ql_gemm2_moe_gu(z, h->slot_token, wg, wu, c.ffn_dim, c.d, h->tile_expert,
+                                    h->tile_row0, h->tile_rows, h->num_tiles, max_tiles, hm, s)));
+    QL_STAGE(h, QL_STAGE_EXPERT_DOWN, s,
+             QL_HIP(ql_gemm2_moe_down(hm, wd, c.ffn_dim, c.d, h->tile_expert, h->tile_row0,
+                                      h->tile_rows, h->num_tiles, max_tiles, h->out_slot, s)));
+  } else {
+    QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
+             QL_HIP(ql_gemm_moe_gu(z, h->slot_token, wg, wu, c.ffn_dim, c.d, h->tile_expert,
+                                   h->tile_row0, h->tile_rows, h->num_tiles, max_tiles, hm, s)));
+    QL_STAGE(h, QL_STAGE_EXPERT_DOWN, s,
+             QL_HIP(ql_gemm_moe_down(hm, wd, c.ffn_dim, c.d, h->tile_expert, h->tile_row0,
+                                     h->tile_rows, h->num_tiles, max_tiles, h->out_slot, s)));
+  }
   CombineArgs ca{};
   ca.out_slot = h->out_slot;
   ca.pos_of = h->pos_of;
