@@ -189,7 +189,13 @@ QL_DEV void wait_vmcnt() {
 // MODE's epilogue. 8 waves as 2 (rows) x 4 (columns), a wave owns 128 x 64;
 // two waves share each SIMD, so one wave's MFMAs run while the other waits.
 // Two ring stages (2 x 64 KiB).
-template <int MODE, bool PART>
+// HL: A is a [hi | lo] pair and a tile covers 128 token rows: LDS rows
+// 0..127 hold the hi halves, 128..255 the lo halves at the same k, so each B
+// tile serves both and the k loop runs over Kb only; the lo accumulators
+// (waves wm = 1) are added to the hi ones through LDS in the epilogue. Same
+// MFMA work as the doubled K, twice the tiles at half the k steps, which
+// evens out the last wave of tiles on some shapes.
+template <int MODE, bool PART, bool HL>
 __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   constexpr int BMT = 256;
   constexpr int NW = BMT / 32;          // waves
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   constexpr int kLds = NS * SB > kEpiBytes ? NS * SB : kEpiBytes;
   constexpr bool kDual = MODE == G2_SWIGLU || MODE == G2_MOE_GU;
   constexpr bool kMoe = MODE == G2_MOE_GU || MODE == G2_MOE_DOWN;
-  constexpr int RT = BMT;               // token rows per tile
+  constexpr int RT = HL ? BMT / 2 : BMT;  // token rows per tile
   static_assert(CH % NT == 0 && AC % NT == 0, "whole loads per thread");
   static_assert(kLds <= 160 * 1024, "LDS");
   static_assert(!kMoe || !PART, "expert tiles run whole");
@@ -294,9 +300,10 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     const int row = Q / kRowChunks;
     const int c = (Q % kRowChunks) ^ swz(row);
     if (is_a) {
-      const int rr = min(row, rows_valid - 1);  // rows past the tile re-read a valid row
+      // rows past the tile re-read a valid row; HL: rows RT.. are the lo halves
+      const int rr = min(HL ? row % RT : row, rows_valid - 1);
       const size_t ar = MODE == G2_MOE_GU ? (size_t)p.row_index[m0 + rr] : (size_t)(m0 + rr);
-      src[j] = p.A + ar * p.lda + c * 8;
+      src[j] = p.A + ar * p.lda + (HL && row >= RT ? p.Kb : 0) + c * 8;
     } else {
       const bf16* base;
       if constexpr (kDual) {
@@ -356,6 +363,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     const int wmu = __builtin_amdgcn_readfirstlane(wm);
 #pragma unroll
     for (int i = 0; i < 4; ++i) act[i] = !kMoe || wmu * 128 + 32 * i < rows_valid;
+    (void)wmu;
   }
   auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][4], bf16x8 (&bfr)[2][TJ]) {
 #pragma unroll
@@ -405,18 +413,25 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
 
   // ---- epilogue: 128 rows (one row of waves) at a time through LDS ----
   float* C = reinterpret_cast<float*>(smem);
+  constexpr int NH = HL ? 1 : WMW;  // 128-row halves written out
 #pragma unroll
-  for (int half = 0; half < WMW; ++half) {
-    if (wm == half) {
+  for (int half = 0; half < NH; ++half) {
+    // HL: the hi rows (wm 0) are stored, then the lo rows (wm 1) added on top
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int pass = 0; pass < (HL ? 2 : 1); ++pass) {
+      if (wm == (HL ? pass : half)) {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            C[row * kPitch + wn * WCOLS + 32 * j + (lane & 31)] = acc[i][j][r];
-          }
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              float* dst = C + row * kPitch + wn * WCOLS + 32 * j + (lane & 31);
+              *dst = (HL && pass == 1) ? *dst + acc[i][j][r] : acc[i][j][r];
+            }
+      }
+      if (HL && pass == 0) __syncthreads();
     }
     __syncthreads();
     constexpr int kEpiRows = 128;
@@ -858,12 +873,12 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
   }
 }
 
-// Tile shapes: 256 token rows (8 waves); the 4-wave decode tiles with an A
-// tile of 32, 64 or 128 LDS rows, from a plain bf16 A or from a [hi | lo]
-// pair (16, 32 or 64 token rows).
-enum : int { T256 = 0, D32, D64, D128, D32_HL, D64_HL, D128_HL };
+// Tile shapes: 256 token rows (8 waves); 128 token rows from a [hi | lo] pair
+// (8 waves); the 4-wave decode tiles with an A tile of 32, 64 or 128 LDS
+// rows, from a plain bf16 A or from a [hi | lo] pair (16, 32 or 64 token rows).
+enum : int { T256 = 0, P128_HL, D32, D64, D128, D32_HL, D64_HL, D128_HL };
 constexpr int shape_ra(int sh) { return sh == D32 || sh == D32_HL ? 32 : (sh == D64 || sh == D64_HL ? 64 : 128); }
-constexpr bool shape_hl(int sh) { return sh >= D32_HL; }
+constexpr bool shape_hl(int sh) { return sh >= D32_HL || sh == P128_HL; }
 // (a pair needs its hi and lo rows in different 32-row MFMA tiles: RA >= 64)
 int decode_shape(int M, bool pair) {
   if (pair) return M <= 32 ? D64_HL : D128_HL;
@@ -875,22 +890,25 @@ hipError_t launch(const G2Args& a, dim3 grid, hipStream_t s) {
   constexpr bool HL = shape_hl(SHAPE);
   // hi/lo inputs feed Q/K/V and O; plain bf16 inputs feed gate/up and down
   constexpr bool kPairIn = MODE == G2_BIAS || MODE == G2_RESID_F32;
+  constexpr bool kDec = SHAPE != T256 && SHAPE != P128_HL;
   if constexpr (SHAPE != T256 && (HL != kPairIn || SHAPE == D32_HL)) {
     return hipErrorInvalidValue;
-  } else if constexpr (SHAPE != T256) {  // decode tiles: stream-K partials
+  } else if constexpr (kDec) {  // decode tiles: stream-K partials
     hipLaunchKernelGGL((gemm2_dec_kernel<MODE, HL, shape_ra(SHAPE)>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
     if (a.splits == 1)
-      hipLaunchKernelGGL((gemm2_kernel<MODE, false>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gemm2_kernel<MODE, false, HL>), grid, dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm2_kernel<MODE, true>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gemm2_kernel<MODE, true, HL>), grid, dim3(512), 0, s, a);
     return hipGetLastError();
   }
 }
 
 int rows_per_tile(int shape) {
-  return shape == T256 ? 256 : (shape_hl(shape) ? shape_ra(shape) / 2 : shape_ra(shape));
+  if (shape == T256) return 256;
+  if (shape == P128_HL) return 128;
+  return shape_hl(shape) ? shape_ra(shape) / 2 : shape_ra(shape);
 }
 
 // stream-K cut of the (tile, k step) units over at most kSkBlocks blocks
@@ -913,7 +931,7 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
   a.tiles_m = (a.M + rt - 1) / rt;
   const int nks = a.Ka / BK;
   dim3 grid;
-  if (shape != T256) {  // decode tiles: stream-K, always through the partials
+  if (shape != T256 && shape != P128_HL) {  // decode tiles: stream-K, always through the partials
     a.streamk = 1;
     a.sk_grid = sk_grid((long long)a.tiles_m * a.tiles_n * nks);
     a.splits = 1;
@@ -928,6 +946,7 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
   hipError_t e;
   switch (shape) {
     case T256: e = launch<MODE, T256>(a, grid, s); break;
+    case P128_HL: e = launch<MODE, P128_HL>(a, grid, s); break;
     case D32: e = launch<MODE, D32>(a, grid, s); break;
     case D64: e = launch<MODE, D64>(a, grid, s); break;
     case D128: e = launch<MODE, D128>(a, grid, s); break;
@@ -940,6 +959,37 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
   hipLaunchKernelGGL(gemm2_reduce_kernel<MODE>, dim3((unsigned)((segs + 63) / 64), (unsigned)a.M),
                      dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// Prefill GEMMs of a [hi | lo] pair A: 256-row tiles over the doubled K, or
+// 128-row tiles holding hi and lo rows over K (same MFMA work, twice the
+// tiles, half the k steps). Shape and split count minimise an estimate in
+// units of one 256 x 256 x 64 k step of a block (about 1.9 us measured):
+// waves of up to 256 blocks times k steps per block, plus, with split-K, a
+// reduce launch and the partials' write and read back at ~5 TB/s.
+struct PairPlan {
+  int shape, splits;
+};
+PairPlan pair_plan(int M, int N, int K) {
+  PairPlan best{T256, 1};
+  double best_c = 1e30;
+  for (int shape : {T256, P128_HL}) {
+    const int rows = shape == T256 ? 256 : 128;
+    const int ks = (shape == T256 ? 2 * K : K) / BK;
+    const int tiles = ((M + rows - 1) / rows) * (N / BN);
+    for (int sp = 1; sp <= 8 && sp * 8 <= ks; ++sp) {
+      const int per = (ks + sp - 1) / sp;
+      if ((ks + per - 1) / per != sp) continue;
+      const long long blocks = (long long)tiles * sp;
+      double c = (double)((blocks + 255) / 256) * per;
+      if (sp > 1) c += (5.0 + 2.0 * sp * M * (double)N * 4 / 5e6) / 1.9;
+      if (c < best_c - 1e-9) {
+        best_c = c;
+        best = {shape, sp};
+      }
+    }
+  }
+  return best;
 }
 
 G2Args base(const bf16* A, int M, int Ka, const bf16* B, int Kb, int splits, void* part) {
@@ -967,6 +1017,12 @@ bool ql_gemm2_ok(int N, int Kb, bool dual) {
   return Kb % BK == 0 && (dual ? N % (BN / 2) == 0 : N % BN == 0);
 }
 
+size_t ql_gemm2_pair_part_bytes(int M, int N, int K) {
+  if (M <= 0) return 0;
+  const PairPlan pl = pair_plan(M, N, K);
+  return ql_gemm2_part_bytes(M, N, pl.splits);
+}
+
 size_t ql_gemm2_decode_part_bytes(int M, int b_rows, int K, bool pair) {
   if (M <= 0) return 0;
   const int shape = decode_shape(M, pair);
@@ -981,7 +1037,9 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
                         const QkvFinish& f, bool rows128, int splits, void* part, hipStream_t s) {
   if (rows128 != (f.cache_len != nullptr)) return hipErrorInvalidValue;  // decode <=> 128 rows
-  G2Args a = base(A2, M, rows128 ? K : 2 * K, Wq, K, splits, part);
+  const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1} : pair_plan(M, q + 2 * kv, K);
+  (void)splits;
+  G2Args a = base(A2, M, pl.shape == T256 ? 2 * K : K, Wq, K, pl.splits, part);
   a.lda = 2 * K;
   a.S = f.S;
   a.pos_offset = f.pos_offset;
@@ -1005,20 +1063,22 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
   a.bias3 = bv;
   a.ldo = q + 2 * kv;
   a.tiles_n = (q + 2 * kv) / BN;
-  return run<G2_BIAS>(a, rows128 ? decode_shape(M, true) : T256, s);
+  return run<G2_BIAS>(a, pl.shape, s);
 }
 
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
                               const bf16* resid, float* out, bool rows128, int splits, void* part,
                               hipStream_t s) {
-  G2Args a = base(A2, M, rows128 ? K : 2 * K, W, K, splits, part);
+  const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1} : pair_plan(M, N, K);
+  (void)splits;
+  G2Args a = base(A2, M, pl.shape == T256 ? 2 * K : K, W, K, pl.splits, part);
   a.lda = 2 * K;
   a.resid_bf16 = resid;
   a.ldr = N;
   a.out_f32 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_F32>(a, rows128 ? decode_shape(M, true) : T256, s);
+  return run<G2_RESID_F32>(a, pl.shape, s);
 }
 
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
@@ -1060,7 +1120,7 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg,
   a.ldo = mf;
   a.tiles_n = mf / (BN / 2);
   const int total = max_tiles * a.tiles_n;
-  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false>), dim3(8 * ((total + 7) / 8)), dim3(512), 0,
+  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, false>), dim3(8 * ((total + 7) / 8)), dim3(512), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -1079,7 +1139,7 @@ hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const
   a.ldo = d;
   a.tiles_n = d / BN;
   const int total = max_tiles * a.tiles_n;
-  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false>), dim3(8 * ((total + 7) / 8)), dim3(512),
+  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, false>), dim3(8 * ((total + 7) / 8)), dim3(512),
                      0, s, a);
   return hipGetLastError();
 }

@@ -36,15 +36,18 @@ hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const 
 
 // ---- GEMMs on 256-column tiles (N % 256 == 0, or F % 128 for SwiGLU; K % 64) ----
 // A2 = [hi | lo] bf16 pair of an fp32 activation, [M, 2K].
-// rows128 = false: 256-row tiles; splits > 1 runs split-K through `part`
+// rows128 = false: prefill tiles; splits > 1 runs split-K through `part`
 // (ql_gemm2_part_bytes(M, weight rows read per call, splits) bytes); the
-// split count is clamped to the k steps.
+// split count is clamped to the k steps. The pair-input forms (QKV, O) pick
+// their own tile shape and split count (ql_gemm2_pair_part_bytes bytes of
+// `part`) and ignore `splits`.
 // rows128 = true: the 4-wave decode tiles (three-stage ring), 64 token rows
 // for a pair A, whose hi and lo rows share each weight tile, 128 for a plain
 // A; the (tile, k step) units are cut evenly over up to 256 blocks (stream-K)
 // whose partials go through `part` (ql_gemm2_decode_part_bytes bytes);
 // `splits` is ignored.
 size_t ql_gemm2_part_bytes(int M, int b_rows, int splits);
+size_t ql_gemm2_pair_part_bytes(int M, int N, int K);
 size_t ql_gemm2_decode_part_bytes(int M, int b_rows, int K, bool pair);
 bool ql_gemm2_ok(int N, int Kb, bool dual);
 // QKV projection with bias, per-head QK-norm, RoPE and the cache write. Prefill

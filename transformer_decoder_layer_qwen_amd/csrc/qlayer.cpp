@@ -175,8 +175,8 @@ int gemm2_splits(int M, int b_rows, int K) {
 // every decode batch size that takes the MFMA tiles.
 size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
   size_t b = 0;
-  b = std::max(b, ql_gemm2_part_bytes(M, qkv_dim, gemm2_splits(M, qkv_dim, 2 * c.d)));
-  b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, 2 * q_dim)));
+  b = std::max(b, ql_gemm2_pair_part_bytes(M, qkv_dim, c.d));
+  b = std::max(b, ql_gemm2_pair_part_bytes(M, c.d, q_dim));
   if (c.n_experts == 0) {
     b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, c.d)));
     b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, c.ffn_dim)));
@@ -434,8 +434,8 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   QL_STAGE(h, QL_STAGE_QKV, s,
            QL_HIP(ql_gemm2_qkv(xhat, N, static_cast<const bf16*>(w.wq),
                                static_cast<const bf16*>(w.wk), static_cast<const bf16*>(w.wv),
-                               h->q_dim, h->kv_dim, c.d, bq, bk, bv, f, false,
-                               gemm2_splits(N, h->qkv_dim, 2 * c.d), h->g2part, s)));
+                               h->q_dim, h->kv_dim, c.d, bq, bk, bv, f, false, 0, h->g2part,
+                               s)));
   AttnPrefillArgs pa{};
   pa.q = static_cast<const bf16*>(h->q);
   pa.k_cache = static_cast<const bf16*>(kc);
@@ -456,7 +456,7 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   QL_STAGE(h, QL_STAGE_O_PROJ, s,
            QL_HIP(ql_gemm2_resid_f32(static_cast<const bf16*>(h->attn), N,
                                      static_cast<const bf16*>(w.wo), c.d, h->q_dim, x, h->r,
-                                     false, gemm2_splits(N, c.d, 2 * h->q_dim), h->g2part, s)));
+                                     false, 0, h->g2part, s)));
   return ffn_dense_or_moe(h, N, false, y, s);
 }
 
