@@ -29,9 +29,12 @@ constexpr int kKElems = kBK * kDh;
 constexpr int kVElems = kDh * kVtPitch;
 constexpr int kStage = kKElems + kVElems;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
-constexpr int kPairMinBlocks = 256;  // the CU count
+constexpr int kCUs = 256;
 
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs p) {
+// Two blocks per CU (the LDS ring is 68 KiB): the register budget of two
+// waves per SIMD keeps every accumulator in VGPRs, and one wave's MFMAs run
+// while the other works through its softmax.
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillArgs p) {
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -257,10 +260,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const AttnPrefillArgs
 hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   const int nqt = (a.S + kBQ - 1) / kBQ;
-  // pair query tiles when the unpaired grid would still give every CU at
-  // least two blocks
+  // pair query tiles when the paired grid still gives every CU two blocks
+  // (the occupancy the kernel is built for)
   AttnPrefillArgs b = a;
-  b.pair = (long)nqt * a.n_q_heads * a.B >= 2L * kPairMinBlocks;
+  b.pair = (long)((nqt + 1) / 2) * a.n_q_heads * a.B >= 2L * kCUs;
   const int gx = b.pair ? (nqt + 1) / 2 : nqt;
   hipLaunchKernelGGL(attn_prefill_kernel, dim3(gx, a.n_q_heads, a.B), dim3(256), 0, s, b);
   return hipGetLastError();
