@@ -13,8 +13,10 @@
 // is the MFMA column, so a lane owns one query and its running max / sum
 // need only one cross-lane exchange per tile. P^T stays in registers and is
 // the B operand of O^T += V^T P^T; V is stored transposed in LDS (pitch 68
-// elements, which spreads the 16 rows read together over distinct banks).
-// K rows keep 16-byte chunks XOR-swizzled by (key & 7). The fp32 output is
+// elements, which spreads the rows read together over distinct banks; the
+// 16 lanes of a store cover 64 keys of one row). K rows are padded to 136
+// elements, so the 16 lanes of a fragment read fall on distinct banks and a
+// lane's fragments sit at fixed offsets from one base. The fp32 output is
 // stored as a bf16 pair hi + lo, the form in which the O projection reads it.
 #include "common.h"
 #include "kernels.h"
@@ -25,7 +27,8 @@ constexpr int kDh = 128;
 constexpr int kBQ = 128;      // queries per block
 constexpr int kBK = 64;       // keys per tile
 constexpr int kVtPitch = 68;  // bf16 elements per transposed-V row
-constexpr int kKElems = kBK * kDh;
+constexpr int kKPitch = kDh + 8;  // bf16 elements per K row
+constexpr int kKElems = kBK * kKPitch;
 constexpr int kVElems = kDh * kVtPitch;
 constexpr int kStage = kKElems + kVElems;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
@@ -74,9 +77,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
 
   // tile-load assignment
   //   K: chunk = tid + 256*i, key = chunk >> 4, 16-byte piece c = chunk & 15
-  //   V: 8-wide dh piece c = tid & 15, keys 4*(tid>>4) .. +3
-  const int vc = tid & 15;
-  const int vk = (tid >> 4) * 4;
+  //   V: keys 4*(tid & 15) .. +3, 8-wide dh piece c = tid >> 4
+  const int vk = (tid & 15) * 4;
+  const int vc = tid >> 4;
   u32x4 rk[4], rv[4];
   auto gload = [&](int kt) {
     const int k0 = kt * kBK;
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
     for (int i = 0; i < 4; ++i) {
       const int ch = tid + 256 * i;
       const int key = ch >> 4, c = ch & 15;
-      *reinterpret_cast<u32x4*>(Ks + key * kDh + ((c ^ (key & 7)) * 8)) = rk[i];
+      *reinterpret_cast<u32x4*>(Ks + key * kKPitch + c * 8) = rk[i];
     }
     const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&rv[0]);
     const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&rv[1]);
@@ -157,12 +160,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
-        const int key = 32 * t + col;
+        const bf16* kr = Ks + (32 * t + col) * kKPitch + 8 * hi;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const int c = 2 * s + hi;
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(Ks + key * kDh + ((c ^ (key & 7)) * 8));
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
           sc[t] = mfma_32x32x16(kf, qf[s], sc[t]);
         }
       }
