@@ -30,7 +30,7 @@
 //   RESID_OUT  out     = bf16(resid_f32 + acc)   Y = R + H W_down^T
 //   SWIGLU     out     = bf16(SiLU(g) * u)       B tile = [W_gate rows | W_up rows]
 //   MOE_GU     SWIGLU on gathered token rows with one expert's weights
-//   MOE_DOWN   out_f32 = acc for one expert's slot rows
+//   MOE_DOWN   out     = bf16(acc) for one expert's slot rows
 // ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §4, §9, §10; "MoE 初步"
 // Expert 的 FFN 结构.)
 #include "common.h"
@@ -305,6 +305,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
           v[i + 4] += r1[i];
         }
         store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
+      } else if constexpr (MODE == GM_MOE_DOWN) {
+        store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
       } else {
         float* o = p.out_f32 + row * p.ldo + col;
         *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
@@ -357,14 +359,14 @@ hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, 
 
 hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                            int max_tiles, float* out, hipStream_t s) {
+                            int max_tiles, bf16* out, hipStream_t s) {
   GemmArgs a = base_args(H, mf, 0, Wd, mf, mf);
   a.b_expert_stride = (size_t)d * mf;
   a.tile_expert = tile_expert;
   a.tile_row0 = tile_row0;
   a.tile_rows = tile_rows;
   a.num_tiles = num_tiles;
-  a.out_f32 = out;
+  a.out_bf16 = out;
   a.ldo = d;
   a.tiles_n = d / 128;
   return launch<32, 128, 32, 32, GM_MOE_DOWN>(a, max_tiles, s);

@@ -33,7 +33,7 @@
 //   RESID_OUT out     = bf16(resid_f32 + acc)   Y = R + H W_down^T
 //   SWIGLU    out     = bf16(SiLU(g) * u)       B tile = [128 W_gate rows | 128 W_up rows]
 //   MOE_GU    SWIGLU on gathered token rows with one expert's weights per tile
-//   MOE_DOWN  out_f32 = acc for one expert's slot rows
+//   MOE_DOWN  out     = bf16(acc) for one expert's slot rows
 // With split-K each split stores its fp32 partial tile and the reduce kernel
 // applies the epilogue.
 // ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §4, §9, §10.)
@@ -493,6 +493,8 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
             v[e] += r0[e];
             v[e + 4] += r1[e];
           }
+          store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
+        } else if constexpr (MODE == G2_MOE_DOWN) {
           store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
         } else {  // RESID_F32: fp32 rows
           float* o = p.out_f32 + row * p.ldo + col;
@@ -1127,7 +1129,7 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg,
 
 hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                              const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                             int max_tiles, float* out, hipStream_t s) {
+                             int max_tiles, bf16* out, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   G2Args a = base(H, 0, mf, Wd, mf, 1, nullptr);
   a.b_expert_stride = (size_t)d * mf;
@@ -1135,7 +1137,7 @@ hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const
   a.tile_row0 = tile_row0;
   a.tile_rows = tile_rows;
   a.num_tiles = num_tiles;
-  a.out_f32 = out;
+  a.out_bf16 = out;
   a.ldo = d;
   a.tiles_n = d / BN;
   const int total = max_tiles * a.tiles_n;

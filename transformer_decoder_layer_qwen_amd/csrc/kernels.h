@@ -32,7 +32,7 @@ hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, 
                           hipStream_t s);
 hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                            int max_tiles, float* out, hipStream_t s);
+                            int max_tiles, bf16* out, hipStream_t s);
 
 // ---- GEMMs on 256-column tiles (N % 256 == 0, or F % 128 for SwiGLU; K % 64) ----
 // A2 = [hi | lo] bf16 pair of an fp32 activation, [M, 2K].
@@ -85,7 +85,7 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg,
                            hipStream_t s);
 hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                              const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                             int max_tiles, float* out, hipStream_t s);
+                             int max_tiles, bf16* out, hipStream_t s);
 
 // ---- decode GEMVs for M <= kGemvMaxRows rows (N % 2 == 0, K % 8 == 0) ----
 // qkv_raw: out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x,
@@ -223,7 +223,7 @@ struct PermuteArgs {
 hipError_t ql_moe_permute(const PermuteArgs& a, hipStream_t s);
 
 struct CombineArgs {
-  const float* out_slot;  // [N*k, d]
+  const bf16* out_slot;   // [N*k, d] expert outputs in slot order
   const int* pos_of;      // [N, k]
   const float* w;         // [N, k]
   int N, k, d;

@@ -260,26 +260,55 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const PermuteArgs p) {
 }
 
 template <class TR>
+QL_DEV void load8(const TR* p, float (&f)[8]);
+template <>
+QL_DEV void load8<float>(const float* p, float (&f)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = a[j];
+    f[j + 4] = b[j];
+  }
+}
+template <>
+QL_DEV void load8<bf16>(const bf16* p, float (&f)[8]) {
+  unpack8(load_bf16x8(p), f);
+}
+
+// One wave per token, 8 consecutive columns per lane; the expert rows are
+// read 8 at a time with their loads issued together and summed in rank
+// order in fp32, then added to the residual.
+template <class TR>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const CombineArgs p, const TR* resid) {
+  constexpr int kGroup = 8;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.N) return;
-  int pos[kMaxTopK];
-  float w[kMaxTopK];
-  for (int i = 0; i < p.k; ++i) {
-    pos[i] = p.pos_of[(size_t)t * p.k + i];
-    w[i] = p.w[(size_t)t * p.k + i];
-  }
-  for (int c = lane * 4; c < p.d; c += 256) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < p.k; ++i) {
-      const f32x4 o = *reinterpret_cast<const f32x4*>(p.out_slot + (size_t)pos[i] * p.d + c);
+  for (int c = lane * 8; c < p.d; c += 512) {
+    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < p.k; i0 += kGroup) {
+      bf16x8 o[kGroup];
+      float w[kGroup];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += w[i] * o[j];
+      for (int i = 0; i < kGroup; ++i) {
+        const int r = min(i0 + i, p.k - 1);
+        o[i] = load_bf16x8(p.out_slot + (size_t)p.pos_of[(size_t)t * p.k + r] * p.d + c);
+        w[i] = i0 + i < p.k ? p.w[(size_t)t * p.k + r] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        float f[8];
+        unpack8(o[i], f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[j] += w[i] * f[j];
+      }
     }
+    float acc[8];
+    load8<TR>(resid + (size_t)t * p.d + c, acc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      p.y[(size_t)t * p.d + c + j] = (bf16)(to_f32(resid[(size_t)t * p.d + c + j]) + acc[j]);
+    for (int j = 0; j < 8; ++j) acc[j] += sum[j];
+    store_bf16x8(p.y + (size_t)t * p.d + c, pack8(acc));
   }
 }
 

@@ -81,7 +81,7 @@ struct ql_handle {
   int* slot_token;
   int* pos_of;
   void* hm;
-  float* out_slot;
+  bf16* out_slot;
   int max_tiles;
   ql_taps taps;
   int ev_stage;
@@ -259,7 +259,7 @@ size_t layout(ql_handle* h, char* base) {
     h->slot_token = k.take<int>(NK * 4);
     h->pos_of = k.take<int>(NK * 4);
     h->hm = k.take<void>(NK * c.ffn_dim * 2);
-    h->out_slot = k.take<float>(NK * c.d * 4);
+    h->out_slot = k.take<bf16>(NK * c.d * 2);
   } else {
     h->h = k.take<void>(N * c.ffn_dim * es);
   }
