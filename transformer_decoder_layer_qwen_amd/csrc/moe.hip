@@ -26,31 +26,41 @@ namespace {
 
 constexpr int kTok = 16;  // tokens per router block (the MFMA's N)
 constexpr int kRW = 8;    // waves per router block; they split K
+constexpr int kEP = kTok + 4;  // LDS pitch (floats) of one expert's token row
 
 // logits[t][e] = z_t . w_e with z fp32 (a bf16 hi + lo pair on the MFMA) and
-// w bf16; wave w sums K range [w d/8, (w+1) d/8) for every expert tile, KU
-// 32-deep k steps per round with all of the round's loads in flight; the
-// waves' partial logits meet in LDS. Then one wave per token picks the top k
-// (descending logit, ties to the lower expert index) and forms the weights.
-// MT: expert tiles held per wave (E <= 16 MT); KU: k steps per round.
+// w bf16. A block takes 16 tokens x 16 MT experts; wave w sums K range
+// [w d/8, (w+1) d/8), KU 32-deep k steps per round with all of the round's
+// loads in flight (no branches inside a round); the waves' partial logits
+// meet in LDS (expert rows padded to 20 floats so the 16 token lanes and the
+// 4 expert groups of a write land on distinct banks) and the block writes
+// its logits to `logits` [N, E]. Blocks go to the XCDs in contiguous
+// stretches of (token block, expert group) with the expert group fastest,
+// so the groups of a token block share its z rows through one L2.
 template <int MT, int KU>
-__global__ __launch_bounds__(kRW * 64) void router_topk_kernel(const RouterArgs p) {
-  extern __shared__ float part[];  // [kRW / 2][kTok][E]
+__global__ __launch_bounds__(kRW * 64) void router_logits_kernel(const RouterArgs p, int ngroups) {
+  constexpr int EB = 16 * MT;  // experts per block
+  __shared__ float part[kRW / 2][EB * kEP];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const int t0 = blockIdx.x * kTok;
-  const int E = p.E;
-  const int etiles = E / 16;
+  const int ntb = (p.N + kTok - 1) / kTok;
+  const int total = ntb * ngroups;
+  const int chunk = (total + 7) / 8;
+  if ((int)(blockIdx.x / 8) >= chunk) return;
+  const int wk = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
+  if (wk >= total) return;
+  const int t0 = (wk / ngroups) * kTok;
+  const int e0 = (wk % ngroups) * EB;
 
   // B operand: z^T; lane (token col, k group grp)
   const int tok = t0 + col;
   const bool tv = tok < p.N;
-  const int kw = p.d / kRW;  // K per wave (a multiple of 32: d % 256 == 0)
+  const int kw = p.d / kRW;  // K per wave (a multiple of 32 KU)
   const float* zr = p.zf + (size_t)(tv ? tok : 0) * p.d + wave * kw + 8 * grp;
-  const bf16* wr = p.wr + (size_t)col * p.d + wave * kw + 8 * grp;
+  const bf16* wr = p.wr + (size_t)(e0 + col) * p.d + wave * kw + 8 * grp;
 
   f32x4 acc[MT];
 #pragma unroll
@@ -60,16 +70,13 @@ __global__ __launch_bounds__(kRW * 64) void router_topk_kernel(const RouterArgs 
     bf16x8 wf[KU][MT];
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      if (k + 32 * u >= kw) break;  // the wave's K range ends inside the round
       z[u][0] = *reinterpret_cast<const f32x4*>(zr + k + 32 * u);
       z[u][1] = *reinterpret_cast<const f32x4*>(zr + k + 32 * u + 4);
 #pragma unroll
-      for (int et = 0; et < MT; ++et)
-        if (et < etiles) wf[u][et] = load_bf16x8(wr + (size_t)et * 16 * p.d + k + 32 * u);
+      for (int et = 0; et < MT; ++et) wf[u][et] = load_bf16x8(wr + (size_t)et * 16 * p.d + k + 32 * u);
     }
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      if (k + 32 * u >= kw) break;
       bf16x8 zh, zl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -81,10 +88,8 @@ __global__ __launch_bounds__(kRW * 64) void router_topk_kernel(const RouterArgs 
       }
 #pragma unroll
       for (int et = 0; et < MT; ++et) {
-        if (et < etiles) {
-          acc[et] = mfma_16x16x32(wf[u][et], zh, acc[et]);
-          acc[et] = mfma_16x16x32(wf[u][et], zl, acc[et]);
-        }
+        acc[et] = mfma_16x16x32(wf[u][et], zh, acc[et]);
+        acc[et] = mfma_16x16x32(wf[u][et], zl, acc[et]);
       }
     }
   }
@@ -94,97 +99,100 @@ __global__ __launch_bounds__(kRW * 64) void router_topk_kernel(const RouterArgs 
   if (wave >= kHalf) {
 #pragma unroll
     for (int et = 0; et < MT; ++et)
-      if (et < etiles)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          part[((wave - kHalf) * kTok + col) * E + et * 16 + 4 * grp + r] = acc[et][r];
+      for (int r = 0; r < 4; ++r) part[wave - kHalf][(et * 16 + 4 * grp + r) * kEP + col] = acc[et][r];
   }
   __syncthreads();
   if (wave < kHalf) {
 #pragma unroll
     for (int et = 0; et < MT; ++et)
-      if (et < etiles)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          part[(wave * kTok + col) * E + et * 16 + 4 * grp + r] += acc[et][r];
+      for (int r = 0; r < 4; ++r) part[wave][(et * 16 + 4 * grp + r) * kEP + col] += acc[et][r];
   }
   __syncthreads();
-  for (int i = tid; i < kTok * E; i += kRW * 64) {
+  for (int i = tid; i < kTok * EB; i += kRW * 64) {
+    const int tl = i / EB, e = i % EB;  // expert fastest: coalesced stores
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kHalf; ++w) v += part[w * kTok * E + i];
-    part[i] = v;  // slot 0 now holds the logits; each i is read and written by one thread
+    for (int w = 0; w < kHalf; ++w) v += part[w][e * kEP + tl];
+    if (t0 + tl < p.N) p.logits[(size_t)(t0 + tl) * p.E + e0 + e] = v;
   }
-  __syncthreads();
+}
 
-  // top-k: one wave per token; lane holds experts lane, lane + 64, ...
-  const int per = (E + 63) / 64;
-  for (int tl = wave; tl < kTok; tl += kRW) {
-    const int t = t0 + tl;
-    if (t >= p.N) break;
-    float v[4];
+// Top-k and gate weights, one wave per token. Expert i's rank is the number
+// of experts j with logit_j > logit_i, plus those with an equal logit and
+// j < i (descending logit, ties to the lower index; a NaN logit counts as
+// -inf); the k experts of rank < k are the selection, in rank order. Each
+// lane ranks its PER experts against the token's whole row, read from LDS as
+// broadcasts: one compare and one add per pair for "greater", the same for
+// "equal", and only a lane that sees a tie counts the lower-index equals.
+// Weights: a softmax over the selected logits (norm_topk_prob), else the
+// selected probabilities of a softmax over all E.
+template <int PER>
+__global__ __launch_bounds__(256) void router_topk_kernel(const RouterArgs p) {
+  __shared__ __attribute__((aligned(16))) float row[4][kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= p.N) return;  // wave-uniform: the other waves use only their own rows
+  const int E = p.E;
+  float v[PER];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = (j < per && e < E) ? part[tl * E + e] : -INFINITY;
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    float x = -INFINITY;
+    if (e < E) {
+      x = p.logits[(size_t)t * E + e];
+      x = x == x ? x : -INFINITY;
+      row[wave][e] = x;
     }
-    if (p.logits) {
+    v[j] = x;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  int gt[PER], eq[PER];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < per && lane + 64 * j < E) p.logits[(size_t)t * E + lane + 64 * j] = v[j];
+  for (int j = 0; j < PER; ++j) gt[j] = eq[j] = 0;
+  for (int j0 = 0; j0 < E; j0 += 4) {
+    const f32x4 o = *reinterpret_cast<const f32x4*>(&row[wave][j0]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        gt[j] += o[q] > v[j] ? 1 : 0;
+        eq[j] += o[q] == v[j] ? 1 : 0;
+      }
+  }
+  int rank[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    rank[j] = gt[j];
+    if (eq[j] > 1 && e < E) {  // a tie: the equal experts below e come first
+      for (int jj = 0; jj < e; ++jj) rank[j] += row[wave][jj] == v[j] ? 1 : 0;
     }
-    // full-softmax statistics (used when norm_topk_prob == 0)
-    float mx = -INFINITY;
+  }
+  float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mx = fmaxf(mx, v[j]);
-    mx = wave_max(mx);
-    float den_all = 0.f;
+  for (int j = 0; j < PER; ++j) mx = fmaxf(mx, v[j]);
+  mx = wave_max(mx);
+  float den_sel = 0.f, den_all = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) den_all += (v[j] == -INFINITY) ? 0.f : __expf(v[j] - mx);
-    den_all = wave_sum(den_all);
-
-    // selection i lands in lane i (k <= 32 < 64 lanes)
-    float my_v = -INFINITY, top = -INFINITY;
-    int my_i = 0;
-    for (int i = 0; i < p.k; ++i) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+  for (int j = 0; j < PER; ++j) {
+    const bool live = lane + 64 * j < E;
+    const float ex = (live && v[j] != -INFINITY) ? __expf(v[j] - mx) : 0.f;
+    den_all += ex;
+    if (live && rank[j] < p.k) den_sel += ex;
+  }
+  den_sel = wave_sum(den_sel);
+  den_all = wave_sum(den_all);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        if (v[j] > bv || (v[j] == bv && e < bi && v[j] != -INFINITY)) {
-          bv = v[j];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, kWave);
-        const int oi = __shfl_xor(bi, m, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      // NaN logits compare false everywhere: keep the index in range so the
-      // permutation never addresses outside its tables
-      if (bi < 0 || bi >= E) bi = i % E;
-      if (i == 0) top = bv;
-      if (lane == i) {
-        my_v = bv;
-        my_i = bi;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (lane + 64 * j == bi) v[j] = -INFINITY;
-    }
-    const bool mine = lane < p.k;
-    const float ew = mine ? __expf(my_v - top) : 0.f;
-    const float den = wave_sum(ew);
-    if (mine) {
-      const float w = p.norm_topk ? ew / den : __expf(my_v - mx) / den_all;
-      p.idx[(size_t)t * p.k + lane] = my_i;
-      p.w[(size_t)t * p.k + lane] = w;
+  for (int j = 0; j < PER; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E && rank[j] < p.k) {
+      const float ex = v[j] != -INFINITY ? __expf(v[j] - mx) : 0.f;
+      p.idx[(size_t)t * p.k + rank[j]] = e;
+      p.w[(size_t)t * p.k + rank[j]] = ex / (p.norm_topk ? den_sel : den_all);
     }
   }
 }
@@ -316,13 +324,40 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const CombineArgs p, c
 
 hipError_t ql_router_topk(const RouterArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  const int blocks = (a.N + kTok - 1) / kTok;
-  const size_t lds = (size_t)(kRW / 2) * kTok * a.E * sizeof(float);
+  if (!a.logits || a.E % 16 || a.E > kMaxExperts || a.d % (32 * kRW)) return hipErrorInvalidValue;
+  const int ntb = (a.N + kTok - 1) / kTok;
   const int et = a.E / 16;
-  if (et <= 2) hipLaunchKernelGGL((router_topk_kernel<2, 4>), dim3(blocks), dim3(kRW * 64), lds, s, a);
-  else if (et <= 4) hipLaunchKernelGGL((router_topk_kernel<4, 4>), dim3(blocks), dim3(kRW * 64), lds, s, a);
-  else if (et <= 8) hipLaunchKernelGGL((router_topk_kernel<8, 2>), dim3(blocks), dim3(kRW * 64), lds, s, a);
-  else hipLaunchKernelGGL((router_topk_kernel<16, 1>), dim3(blocks), dim3(kRW * 64), lds, s, a);
+  // expert tiles per block: all of them when token blocks alone fill the
+  // chip (z rows read once), else one (more blocks, one round of loads each;
+  // the expert groups of a token block share its z rows through one L2)
+  const int mt = ntb >= 128 ? et : 1;
+  const int ngroups = et / mt;
+  const int kw = a.d / kRW;
+  const int ku = (kw % 256 == 0 && mt == 1) ? 8 : (kw % 128 == 0 && mt <= 4) ? 4 : (kw % 64 == 0 && mt <= 8) ? 2 : 1;
+  const int total = ntb * ngroups;
+  const dim3 grid(8 * ((total + 7) / 8)), block(kRW * 64);
+  switch (mt * 16 + ku) {
+#define QL_R(MT, KU)                                                                        \
+  case MT * 16 + KU:                                                                        \
+    hipLaunchKernelGGL((router_logits_kernel<MT, KU>), grid, block, 0, s, a, ngroups);      \
+    break;
+    QL_R(1, 1) QL_R(1, 2) QL_R(1, 4) QL_R(1, 8)
+    QL_R(2, 1) QL_R(2, 2) QL_R(2, 4) QL_R(3, 1) QL_R(3, 2) QL_R(3, 4) QL_R(4, 1) QL_R(4, 2) QL_R(4, 4)
+    QL_R(5, 1) QL_R(5, 2) QL_R(6, 1) QL_R(6, 2) QL_R(7, 1) QL_R(7, 2) QL_R(8, 1) QL_R(8, 2)
+    QL_R(9, 1) QL_R(10, 1) QL_R(11, 1) QL_R(12, 1) QL_R(13, 1) QL_R(14, 1) QL_R(15, 1) QL_R(16, 1)
+#undef QL_R
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 tgrid((a.N + 3) / 4);
+  switch ((a.E + 63) / 64) {
+    case 1: hipLaunchKernelGGL(router_topk_kernel<1>, tgrid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(router_topk_kernel<2>, tgrid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(router_topk_kernel<3>, tgrid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(router_topk_kernel<4>, tgrid, dim3(256), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
