@@ -32,11 +32,13 @@
 // them to the cache and uses them from LDS ("Qwen2.5-7B 结构拆解" §09.1;
 // "推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §5, §6, §12). All cache,
 // projection, bias and norm loads are issued before any is waited on.
-// QR: the projection already finished q and appended the new row (larger
-// batches, where the projection runs on MFMA tiles); the wave only attends.
+// Larger batches, where the projection runs on MFMA tiles and already
+// finished q and appended the new row, use attn_decode_mfma_kernel below.
 //
 // Output: fp32, or (out_hilo) the bf16 pair hi = RNE(o), lo = RNE(o - hi)
 // that the O projection takes as its A operand.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -58,7 +60,7 @@ QL_DEV void store_out8(const AttnDecodeArgs& p, size_t idx, const float (&v)[8])
   }
 }
 
-template <int G, bool QR>
+template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attn_decode_kernel(const AttnDecodeArgs p) {
   constexpr int HPL = (G + 3) / 4;  // heads per lane in P V
   __shared__ float p_lds[16 * 16];  // P[key 16][head 16]
@@ -80,8 +82,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   // projection / bias / norm loads are unconditional (absent biases and norms
   // read a harmless valid address and are masked to 0 / 1).
   const int L = p.cache_len[b];
+  // splits of `chunk` keys; the last one also takes the remainder
   const int kbeg = split * p.chunk;
-  const int kcap = min(kbeg + p.chunk, p.T_max);
+  const int kcap = split == p.nsplit - 1 ? p.T_max : min(kbeg + p.chunk, p.T_max);
   const size_t row_stride = (size_t)p.n_kv_heads * kDh;
   const bf16* kb_ = p.k_cache + (size_t)b * p.T_max * row_stride + g * kDh;
   const bf16* vb_ = p.v_cache + (size_t)b * p.T_max * row_stride + g * kDh;
@@ -109,19 +112,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   const int kvd = p.n_kv_heads * kDh;
   // Q^T fragments: lane (head col, group grp) holds dh [32s + 8grp, +8)
   bf16x8 qf[4];
-  if constexpr (QR) {  // finished queries; columns >= G are zero padding
-    const bf16* qrow = p.q_in + (size_t)b * qd + (size_t)(g * G + min(col, G - 1)) * kDh;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) qf[s] = load_bf16x8(qrow + 32 * s + 8 * grp);
-    if (col >= G) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) qf[s] = bf16x8{};
-    }
-  }
   const bool valid = L >= 0 && L < p.T_max;
   const int nkeys = valid ? L + 1 : 0;
-  const int kend = min(kbeg + p.chunk, nkeys);
-  const bool has_new = !QR && valid && kbeg <= L && L < kend;
+  const int kend = min(kcap, nkeys);
+  const bool has_new = valid && kbeg <= L && L < kend;
   // first-tile rows past the live keys may hold anything (a NaN would survive
   // a zero softmax weight in P V): zero their V, once every load is out
   auto zero_dead_v = [&]() {
@@ -129,9 +123,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
     for (int j = 0; j < 4; ++j)
       if (kbeg + 4 * grp + j >= kend) vcur[j] = zero4;
   };
-  if constexpr (QR) zero_dead_v();
-
-  if constexpr (!QR) {
+  {
     const float* raw = p.qkv_raw + (size_t)b * p.ld_raw;
     // slots 0 .. G-1: the group's query heads; G, G+1: the new K and V row
     float hv[G + 2][2], hb[G + 2][2];
@@ -361,95 +353,281 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   }
 }
 
-// Merge the splits of one (sequence, head). 512 threads: thread t owns output
-// element t % 128 and the splits s = t / 128 (mod 4). The partial outputs of
-// the first 128 splits and all split maxima / sums are requested together, so
-// the merge waits on memory once; weights go through LDS.
-constexpr int kCombineThreads = 512;
-constexpr int kCombineBatch = 32;  // partial outputs in flight per thread
-__global__ __launch_bounds__(kCombineThreads) void attn_decode_combine_kernel(const AttnDecodeArgs p) {
-  constexpr int kQ = kCombineThreads / kDh;  // split residues per element
-  constexpr int kW = kCombineThreads / 64;
-  __shared__ float s_m[kMaxDecodeSplits], s_l[kMaxDecodeSplits];
-  __shared__ float red[kW];
-  __shared__ float qsum[kQ][kDh];
-  const int bh = blockIdx.x;  // b * Hq + head
-  const int b = bh / p.n_q_heads;
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int d = t & (kDh - 1);
-  const int q = t / kDh;
-  const int ns = p.nsplit;
-  const size_t base = (size_t)bh * ns;
-  float ov[kCombineBatch];
+// Batched decode: the Q/K/V projection already finished the queries (scale,
+// bias, QK-norm, RoPE) and appended the new row to the cache, so the wave only
+// attends ("Qwen2.5-7B 结构拆解" §09.1; §05.2 for the shared K/V bytes of a
+// group). One wave per (key split, KV head, sequence), 32 keys per step, both
+// products on 16x16x32 MFMAs with the group's G <= 16 heads padded to 16:
+//   * S^T = K Q^T: K rows straight from the cache as the A operand (two
+//     16-key halves), Q^T fragments in registers;
+//   * online softmax per head: lane (col, grp) holds keys 4 grp + r and
+//     16 + 4 grp + r of head col, so the eight P values a lane owns are exactly
+//     its B-operand slots of O^T += V^T P^T (k slot j < 4: key 4 grp + j,
+//     j >= 4: key 16 + 4 grp + j - 4); P never leaves the registers;
+//   * V^T: the tile's V rows are written transposed to LDS (four keys of one
+//     dh value per 8-byte store) and read back as A fragments in that slot
+//     order; the running output O^T (128 x 16) lives in eight accumulators,
+//     rescaled only when some head's running maximum moved.
+// The next tile's 16 KB are in flight while the current one is processed.
+constexpr int kVtP = 36;  // bf16 per transposed-V row: 32 keys + 4 (bank spread)
+
+QL_DEV void store_out4(const AttnDecodeArgs& p, size_t idx, const f32x4& v) {
+  if (p.out_hilo) {
+    bf16x4 h, l;
 #pragma unroll
-  for (int u = 0; u < kCombineBatch; ++u) {
-    const int s = q + kQ * u;
-    ov[u] = s < ns ? p.part_o[(base + s) * kDh + d] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      h[e] = (bf16)v[e];
+      l[e] = (bf16)(v[e] - (float)h[e]);
+    }
+    *reinterpret_cast<bf16x4*>(p.out_hilo + idx) = h;
+    *reinterpret_cast<bf16x4*>(p.out_hilo + idx + p.lo_off) = l;
+  } else {
+    *reinterpret_cast<f32x4*>(p.out + idx) = v;
   }
-  float mx = -INFINITY;
-  for (int s = t; s < ns; s += kCombineThreads) {
-    const float m = p.part_ml[(base + s) * 2];
-    s_m[s] = m;
-    s_l[s] = p.part_ml[(base + s) * 2 + 1];
-    mx = fmaxf(mx, m);
+}
+
+template <int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_mfma_kernel(const AttnDecodeArgs p) {
+  static_assert(G >= 1 && G <= 16, "query heads per KV head");
+  __shared__ __attribute__((aligned(16))) bf16 vt_lds[kDh * kVtP];
+
+  const int lane = threadIdx.x;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  // KV heads fastest: the Hkv waves of one key range read neighbouring bytes
+  const int g = blockIdx.x;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;
+
+  // splits of `chunk` keys; the last one also takes the remainder
+  const int kbeg = split * p.chunk;
+  const int kcap = split == p.nsplit - 1 ? p.T_max : min(kbeg + p.chunk, p.T_max);
+  const size_t rs = (size_t)p.n_kv_heads * kDh;
+  const bf16* kb_ = p.k_cache + (size_t)b * p.T_max * rs + g * kDh;
+  const bf16* vb_ = p.v_cache + (size_t)b * p.T_max * rs + g * kDh;
+  // K lane (key col of half h, k-group grp): dh [32 s + 8 grp, +8) of key
+  // k0 + 16 h + col. V lane: keys k0 + vkey + j (j < 4), dh pieces vpc + 8 i.
+  // Loads are unconditional (a guarded load becomes a branch whose join waits
+  // for it): rows at or past `lim` read row lim - 1 instead; such K rows are
+  // masked in the scores and such V rows meet a zero weight.
+  const int vkey = 4 * (lane & 7);
+  const int vpc = lane >> 3;
+  auto load_k = [&](int k0, int lim, u32x4 (&kt)[2][4]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16* kr = kb_ + (size_t)min(k0 + 16 * h + col, lim - 1) * rs + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kt[h][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s);
+    }
+  };
+  auto load_v = [&](int k0, int lim, u32x4 (&vv)[2][4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16* vr = vb_ + (size_t)min(k0 + vkey + j, lim - 1) * rs + 8 * vpc;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vv[i][j] = *reinterpret_cast<const u32x4*>(vr + 64 * i);
+    }
+  };
+
+  const int qd = p.n_q_heads * kDh;
+  bf16x8 qf[4];  // Q^T fragments: lane (head col, grp) holds dh [32 s + 8 grp, +8)
+  {
+    const bf16* qrow = p.q_in + (size_t)b * qd + (size_t)(g * G + min(col, G - 1)) * kDh + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[s] = load_bf16x8(qrow + 32 * s);
+  }
+  // Two tiles in registers (A, B). The first two do not wait for cache_len:
+  // they are read up to the split's end within T_max; their rows past the
+  // live keys may hold anything (a NaN would survive a zero softmax weight),
+  // so the first two steps zero those V rows.
+  u32x4 kA[2][4], vA[2][4], kB[2][4], vB[2][4];
+  load_k(kbeg, kcap, kA);
+  load_v(kbeg, kcap, vA);
+  load_k(kbeg + 32, kcap, kB);
+  load_v(kbeg + 32, kcap, vB);
+  if (col >= G) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[s] = bf16x8{};
   }
   const int L = p.cache_len[b];
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float M = red[0];
+  const bool valid = L >= 0 && L < p.T_max;
+  const int kend = min(kcap, valid ? L + 1 : 0);
+
+  f32x4 acc[8];  // lane: O^T[dh 16 blk + 4 grp + r][head col]
 #pragma unroll
-  for (int w = 1; w < kW; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
-  // split weights (in place of the maxima) and the total l
-  float lsum = 0.f;
-  for (int s = t; s < ns; s += kCombineThreads) {
-    const float m = s_m[s];
-    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-    s_m[s] = w;
-    lsum += w * s_l[s];
-  }
-  lsum = wave_sum(lsum);
-  if (lane == 0) red[wave] = lsum;
-  __syncthreads();
-  float l = 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // head col
+  float l_run = 0.f;        // head col, this lane's keys only
+
+  // One 32-key step on the tile held in (kt, vv); the other buffer holds the
+  // next tile. Each register set is refilled with the tile after next as soon
+  // as it is consumed (V after its LDS transpose, K after the scores), so
+  // about two tiles stay in flight during the arithmetic.
+  auto step = [&](int k0, u32x4 (&kt)[2][4], u32x4 (&vv)[2][4], auto first) {
+    // V^T rows: dh 8 (vpc + 8 i) + e, keys vkey .. vkey + 3
 #pragma unroll
-  for (int w = 0; w < kW; ++w) l += red[w];
-  float o = 0.f;
+    for (int i = 0; i < 2; ++i) {
+      bf16x8 v[4];
 #pragma unroll
-  for (int u = 0; u < kCombineBatch; ++u) {
-    const int s = q + kQ * u;
-    if (s < ns) o += ov[u] * s_m[s];
-  }
-  for (int s0 = q + kQ * kCombineBatch; s0 < ns; s0 += kQ * kCombineBatch) {
+      for (int j = 0; j < 4; ++j) {
+        v[j] = *reinterpret_cast<const bf16x8*>(&vv[i][j]);
+        if constexpr (decltype(first)::value)
+          if (k0 + vkey + j >= kend) v[j] = bf16x8{};
+      }
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
-      const int s = s0 + kQ * u;
-      ov[u] = s < ns ? p.part_o[(base + s) * kDh + d] : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const bf16x4 t = {v[0][e], v[1][e], v[2][e], v[3][e]};
+        *reinterpret_cast<bf16x4*>(&vt_lds[(8 * (vpc + 8 * i) + e) * kVtP + vkey]) = t;
+      }
     }
+    load_v(k0 + 64, kend, vv);  // the tile after next
+    f32x4 sc[2];
 #pragma unroll
-    for (int u = 0; u < kCombineBatch; ++u) {
-      const int s = s0 + kQ * u;
-      if (s < ns) o += ov[u] * s_m[s];
+    for (int h = 0; h < 2; ++h) {
+      sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sc[h] = mfma_16x16x32(*reinterpret_cast<const bf16x8*>(&kt[h][s]), qf[s], sc[h]);
+    }
+    load_k(k0 + 64, kend, kt);
+    // sc[h][r]: S^T[key k0 + 16 h + 4 grp + r][head col]
+    float mt = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = sc[h][r] * p.scale_log2;
+        if (k0 + 16 * h + 4 * grp + r >= kend) x = -INFINITY;
+        sc[h][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float m_new = fmaxf(m_run, mt);  // finite: key k0 < kend is live
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    bf16x8 pf;
+    float ps = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = exp2f(sc[h][r] - m_new);
+        ps += pv;
+        pf[4 * h + r] = (bf16)pv;
+      }
+    l_run = l_run * alpha + ps;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][r] *= alpha;
+    }
+    // LDS traffic of one wave is processed in order; the barrier only keeps
+    // the compiler from moving LDS accesses across it
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16* vr = &vt_lds[(16 * i + col) * kVtP + 4 * grp];
+      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+      const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[i] = mfma_16x16x32(vf, pf, acc[i]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  };
+  using First = std::integral_constant<bool, true>;
+  using Rest = std::integral_constant<bool, false>;
+  // steps go in pairs; a second step past kend has every key masked and
+  // changes nothing (its refill loads stay inside the live rows)
+  if (kbeg < kend) {
+    step(kbeg, kA, vA, First{});
+    step(kbeg + 32, kB, vB, First{});
+    for (int k0 = kbeg + 64; k0 < kend; k0 += 64) {
+      step(k0, kA, vA, Rest{});
+      step(k0 + 32, kB, vB, Rest{});
     }
   }
-  qsum[q][d] = o;
-  __syncthreads();
-  if (q == 0) {
-    float tot = 0.f;
+
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (col >= G) return;
+  const int hq = g * G + col;
+  if (p.nsplit == 1) {  // the only split: normalise here
+    const float rl = valid ? 1.0f / l_run : __builtin_nanf("");
+    const size_t base = (size_t)b * p.ldo + (size_t)hq * kDh + 4 * grp;
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) tot += qsum[i][d];
-    const bool valid = L >= 0 && L < p.T_max;
-    const float v = valid ? tot / l : __builtin_nanf("");
-    const size_t idx = (size_t)b * p.ldo + (size_t)(bh % p.n_q_heads) * kDh + d;
-    if (p.out_hilo) {
-      const bf16 hi = (bf16)v;
-      p.out_hilo[idx] = hi;
-      p.out_hilo[idx + p.lo_off] = (bf16)(v - (float)hi);
-    } else {
-      p.out[idx] = v;
+    for (int i = 0; i < 8; ++i) {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = acc[i][r] * rl;
+      store_out4(p, base + 16 * i, o);
     }
+  } else {
+    const size_t slot = ((size_t)b * p.n_q_heads + hq) * p.nsplit + split;
+    float* o = p.part_o + slot * kDh + 4 * grp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4*>(o + 16 * i) = acc[i];
+    if (grp == 0) {
+      p.part_ml[slot * 2 + 0] = m_run;
+      p.part_ml[slot * 2 + 1] = l_run;
+    }
+  }
+}
+
+// Merge the splits of one (sequence, head): one wave per head, lane owns
+// output elements 2 lane and 2 lane + 1. Lane s reads split s's (m, l); the
+// split weights w_s = 2^(m_s - max m) go to every lane by lane reads, and the
+// partial outputs are requested eight splits at a time.
+constexpr int kCombineWaves = 4;
+__global__ __launch_bounds__(64 * kCombineWaves) void attn_decode_combine_kernel(const AttnDecodeArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * kCombineWaves + (threadIdx.x >> 6);  // b * Hq + head
+  if (bh >= p.B * p.n_q_heads) return;
+  const int b = bh / p.n_q_heads;
+  const int ns = p.nsplit;
+  const size_t base = (size_t)bh * ns;
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, p.part_ml[(base + s) * 2]);
+  M = wave_max(M);
+  float o0 = 0.f, o1 = 0.f, l = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float w = 0.f;
+    if (s0 + lane < ns) {
+      const float m = p.part_ml[(base + s0 + lane) * 2];
+      w = m == -INFINITY ? 0.f : exp2f(m - M);
+      l += w * p.part_ml[(base + s0 + lane) * 2 + 1];
+    }
+    const int n = min(64, ns - s0);
+    for (int j = 0; j < n; j += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = j + u < n ? *reinterpret_cast<const float2*>(p.part_o + (base + s0 + j + u) * kDh + 2 * lane)
+                         : float2{0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
+        o0 += wu * v[u].x;
+        o1 += wu * v[u].y;
+      }
+    }
+  }
+  l = wave_sum(l);
+  const int L = p.cache_len[b];
+  const bool valid = L >= 0 && L < p.T_max;
+  const float rl = valid ? 1.0f / l : __builtin_nanf("");
+  const float v0 = o0 * rl, v1 = o1 * rl;
+  const size_t idx = (size_t)b * p.ldo + (size_t)(bh % p.n_q_heads) * kDh + 2 * lane;
+  if (p.out_hilo) {
+    const bf16 h0 = (bf16)v0, h1 = (bf16)v1;
+    *reinterpret_cast<bf16x2*>(p.out_hilo + idx) = bf16x2{h0, h1};
+    *reinterpret_cast<bf16x2*>(p.out_hilo + idx + p.lo_off) =
+        bf16x2{(bf16)(v0 - (float)h0), (bf16)(v1 - (float)h1)};
+  } else {
+    *reinterpret_cast<float2*>(p.out + idx) = float2{v0, v1};
   }
 }
 
@@ -459,13 +637,14 @@ hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
   if (a.nsplit < 1 || a.nsplit > kMaxDecodeSplits) return hipErrorInvalidValue;
   const dim3 grid(a.nsplit, a.n_kv_heads, a.B);
+  const dim3 grid_kv(a.n_kv_heads, a.nsplit, a.B);
   switch (a.n_q_heads / a.n_kv_heads) {
-#define QL_G(V)                                                                      \
-  case V:                                                                            \
-    if (a.q_in)                                                                      \
-      hipLaunchKernelGGL((attn_decode_kernel<V, true>), grid, dim3(64), 0, s, a);   \
-    else                                                                             \
-      hipLaunchKernelGGL((attn_decode_kernel<V, false>), grid, dim3(64), 0, s, a);  \
+#define QL_G(V)                                                                          \
+  case V:                                                                                \
+    if (a.q_in)                                                                          \
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<V>), grid_kv, dim3(64), 0, s, a);      \
+    else                                                                                 \
+      hipLaunchKernelGGL((attn_decode_kernel<V>), grid, dim3(64), 0, s, a);              \
     break;
     QL_G(1) QL_G(2) QL_G(3) QL_G(4) QL_G(5) QL_G(6) QL_G(7) QL_G(8)
     QL_G(9) QL_G(10) QL_G(11) QL_G(12) QL_G(13) QL_G(14) QL_G(15) QL_G(16)
@@ -475,7 +654,8 @@ hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(a.B * a.n_q_heads), dim3(kCombineThreads),
-                     0, s, a);
+  const int heads = a.B * a.n_q_heads;
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((heads + kCombineWaves - 1) / kCombineWaves),
+                     dim3(64 * kCombineWaves), 0, s, a);
   return hipGetLastError();
 }

@@ -192,21 +192,29 @@ size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
   return b;
 }
 
-// Decode attention launch shape: about kDecodeTargetWaves waves over
-// (key split, KV head, sequence), at least one 16-key tile per split.
-constexpr int kDecodeTargetWaves = 3072;
-int decode_splits(int groups, int T_max, int* chunk) {
-  int ns = (kDecodeTargetWaves + groups - 1) / groups;
-  ns = std::max(1, std::min({ns, kMaxDecodeSplits, (T_max + 15) / 16}));
-  int ch = (T_max + ns - 1) / ns;
-  ch = (ch + 15) / 16 * 16;
+// Decode attention launch shape: about `target` waves over (key split, KV
+// head, sequence); splits of `chunk` keys (a whole number of `tile`-key
+// steps), the last split running to T_max (fewer than 2 chunks), so the
+// longest split is about as short as the step size allows.
+constexpr int kDecodeTargetWaves = 3072;      // fused-prologue kernel, 16-key steps
+constexpr int kDecodeMfmaTargetWaves = 2048;  // MFMA kernel, 32-key steps
+int decode_splits(int groups, int T_max, int tile, int target, int* chunk) {
+  int ns = (target + groups - 1) / groups;
+  ns = std::max(1, std::min({ns, kMaxDecodeSplits, T_max / tile}));
+  int ch = std::max(tile, T_max / ns / tile * tile);
+  int n = std::max(1, T_max / ch);
+  if (n > ns) {  // rounding the chunk down would add splits: round it up
+    ch = ((T_max + ns - 1) / ns + tile - 1) / tile * tile;
+    n = (T_max + ch - 1) / ch;
+  }
   *chunk = ch;
-  return (T_max + ch - 1) / ch;
+  return n;
 }
 // Upper bound of B * nsplit over every batch size (sizes the split partials).
 size_t decode_split_slots(const ql_config& c) {
   const int hkv = std::max(c.n_kv_heads, 1);
-  return (size_t)std::max(c.max_batch, 0) + (kDecodeTargetWaves + hkv - 1) / hkv;
+  const int target = std::max(kDecodeTargetWaves, kDecodeMfmaTargetWaves);
+  return (size_t)std::max(c.max_batch, 0) + (target + hkv - 1) / hkv;
 }
 
 struct Carve {
@@ -490,7 +498,8 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
   da.n_kv_heads = c.n_kv_heads;
   da.head_dim = c.head_dim;
   int chunk = 0;
-  da.nsplit = decode_splits(B * c.n_kv_heads, T_max, &chunk);
+  da.nsplit = gemv ? decode_splits(B * c.n_kv_heads, T_max, 16, kDecodeTargetWaves, &chunk)
+                   : decode_splits(B * c.n_kv_heads, T_max, 32, kDecodeMfmaTargetWaves, &chunk);
   da.chunk = chunk;
   da.part_o = h->part_o;
   da.part_ml = h->part_ml;
