@@ -578,9 +578,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 }
 
 // Merge the splits of one (sequence, head): one wave per head, lane owns
-// output elements 2 lane and 2 lane + 1. Lane s reads split s's (m, l); the
-// split weights w_s = 2^(m_s - max m) go to every lane by lane reads, and the
-// partial outputs are requested eight splits at a time.
+// output elements 2 lane and 2 lane + 1; lane s holds split s's (m, l). Up
+// to 64 splits take one round trip: every split's (m, l) and partial output
+// are requested before any is used (the loads are unconditional, since a
+// guarded load becomes a branch whose join waits for it: rows past the last
+// split re-read it and get weight 0); the split weights w_s = 2^(m_s - max m)
+// then reach every lane by lane reads. More splits take one such round per
+// 64 after a first pass for the maximum.
+template <int U>
+QL_DEV void combine_round(const AttnDecodeArgs& p, size_t base, int s0, int n, int lane, float M_in,
+                          bool have_max, float& M_out, float& o0, float& o1, float& l) {
+  const int sl = s0 + min(lane, n - 1);
+  const float m = p.part_ml[(base + sl) * 2];
+  const float ls = p.part_ml[(base + sl) * 2 + 1];
+  float2 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    v[u] = *reinterpret_cast<const float2*>(p.part_o + (base + s0 + min(u, n - 1)) * kDh + 2 * lane);
+  const float M = have_max ? M_in : wave_max(lane < n ? m : -INFINITY);
+  M_out = M;
+  const float w = lane < n && m != -INFINITY ? exp2f(m - M) : 0.f;
+  l += w * ls;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+    o0 += wu * v[u].x;
+    o1 += wu * v[u].y;
+  }
+}
+
 constexpr int kCombineWaves = 4;
 __global__ __launch_bounds__(64 * kCombineWaves) void attn_decode_combine_kernel(const AttnDecodeArgs p) {
   const int lane = threadIdx.x & 63;
@@ -589,31 +615,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_decode_combine_kernel
   const int b = bh / p.n_q_heads;
   const int ns = p.nsplit;
   const size_t base = (size_t)bh * ns;
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, p.part_ml[(base + s) * 2]);
-  M = wave_max(M);
-  float o0 = 0.f, o1 = 0.f, l = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    float w = 0.f;
-    if (s0 + lane < ns) {
-      const float m = p.part_ml[(base + s0 + lane) * 2];
-      w = m == -INFINITY ? 0.f : exp2f(m - M);
-      l += w * p.part_ml[(base + s0 + lane) * 2 + 1];
-    }
-    const int n = min(64, ns - s0);
-    for (int j = 0; j < n; j += 8) {
-      float2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = j + u < n ? *reinterpret_cast<const float2*>(p.part_o + (base + s0 + j + u) * kDh + 2 * lane)
-                         : float2{0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
-        o0 += wu * v[u].x;
-        o1 += wu * v[u].y;
-      }
-    }
+  float M = -INFINITY, o0 = 0.f, o1 = 0.f, l = 0.f;
+  if (ns <= 8) {
+    combine_round<8>(p, base, 0, ns, lane, 0.f, false, M, o0, o1, l);
+  } else if (ns <= 64) {
+    combine_round<64>(p, base, 0, ns, lane, 0.f, false, M, o0, o1, l);
+  } else {
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, p.part_ml[(base + s) * 2]);
+    M = wave_max(M);
+    for (int s0 = 0; s0 < ns; s0 += 64)
+      combine_round<64>(p, base, s0, min(64, ns - s0), lane, M, true, M, o0, o1, l);
   }
   l = wave_sum(l);
   const int L = p.cache_len[b];
