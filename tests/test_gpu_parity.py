@@ -226,9 +226,12 @@ def test_decode_out_of_range_length_is_contained(lens):
 
 # --------------------------------------------------------- small MoE ----
 
-@pytest.mark.parametrize("N", [37, 300, 700])
-def test_small_moe_ffn(N):
-    cfg = small_moe_cfg()
+# expert GEMM paths by routed rows N k (E = 32, k = 4): 148 and 1200 take the
+# 32-row tiles, 2800 (>= 64 E) the 256-row tiles; with E = 64, 2800 rows stay
+# on the 32-row tiles with some experts holding several tiles
+@pytest.mark.parametrize("N,E", [(37, 32), (300, 32), (700, 32), (700, 64)])
+def test_small_moe_ffn(N, E):
+    cfg = small_moe_cfg(n_experts=E)
     layer, w32 = make_layer(cfg, max_tokens=max(N, 8), max_batch=4)
     r = synth.make_moe_input(cfg, 1006, N)
     idx_t = torch.empty(N, cfg.top_k, dtype=torch.int32, device="cuda")

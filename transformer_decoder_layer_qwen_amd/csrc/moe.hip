@@ -13,8 +13,9 @@
 //
 // Permutation: a histogram of expert ids per 256-token block, one scan that
 // turns counts into expert segments and a tile table for the grouped GEMM,
-// and a stable scatter that lists each expert's tokens in token order. Every
-// step is integer work, so the permutation is exactly reproducible.
+// and a stable scatter that lists each expert's tokens in token order (up to
+// 256 tokens, all three steps run in one block). Every step is integer work,
+// so the permutation is exactly reproducible.
 //
 // Combine ("Qwen2.5-7B 结构拆解" §10.2: the k outputs are added elementwise
 // with their gate weights, no further normalisation): y = r + sum_i w_i out_i
@@ -267,6 +268,61 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const PermuteArgs p) {
   }
 }
 
+// Up to 256 tokens: the histogram, the scan with the tile table and the
+// scatter in one block (the same slots as the three kernels: experts in
+// order, tokens ascending within an expert). Per expert a 256-bit token mask
+// in LDS gives both the expert's count and each token's rank.
+__global__ __launch_bounds__(256) void moe_permute_small_kernel(const PermuteArgs p) {
+  __shared__ uint32_t bits[kMaxExperts][8];
+  __shared__ int tot[kMaxExperts];
+  __shared__ int ntile[kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  const int tl = threadIdx.x;
+  for (int i = tl; i < p.E * 8; i += 256) bits[i / 8][i % 8] = 0u;
+  __syncthreads();
+  const bool tv = tl < p.N;
+  if (tv)
+    for (int i = 0; i < p.k; ++i) atomicOr(&bits[p.idx[(size_t)tl * p.k + i]][tl >> 5], 1u << (tl & 31));
+  __syncthreads();
+  const int e = tl;
+  if (e < p.E) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c += __popc(bits[e][w]);
+    tot[e] = c;
+    ntile[e] = (c + p.bm - 1) / p.bm;
+  }
+  __syncthreads();
+  if (e < p.E) {
+    int off = 0, toff = 0;
+    for (int j = 0; j < e; ++j) {  // E <= 256: a plain prefix is cheap enough
+      off += tot[j];
+      toff += ntile[j];
+    }
+    base[e] = off;
+    p.offsets[e] = off;
+    for (int j = 0; j < ntile[e]; ++j) {
+      p.tile_expert[toff + j] = e;
+      p.tile_row0[toff + j] = off + j * p.bm;
+      p.tile_rows[toff + j] = min(p.bm, tot[e] - j * p.bm);
+    }
+    if (e == p.E - 1) {
+      p.offsets[p.E] = off + tot[e];
+      *p.num_tiles = toff + ntile[e];
+    }
+  }
+  __syncthreads();
+  if (!tv) return;
+  for (int i = 0; i < p.k; ++i) {
+    const int x = p.idx[(size_t)tl * p.k + i];
+    int rank = __popc(bits[x][tl >> 5] & ((1u << (tl & 31)) - 1u));
+    for (int w = 0; w < (tl >> 5); ++w) rank += __popc(bits[x][w]);
+    const int pos = base[x] + rank;
+    p.slot_token[pos] = tl;
+    p.pos_of[(size_t)tl * p.k + i] = pos;
+  }
+}
+
 template <class TR>
 QL_DEV void load8(const TR* p, float (&f)[8]);
 template <>
@@ -284,40 +340,44 @@ QL_DEV void load8<bf16>(const bf16* p, float (&f)[8]) {
   unpack8(load_bf16x8(p), f);
 }
 
-// One wave per token, 8 consecutive columns per lane; the expert rows are
-// read 8 at a time with their loads issued together and summed in rank
-// order in fp32, then added to the residual.
+// One wave per (token, 512-column chunk), 8 consecutive columns per lane:
+// small batches still spread over many waves, and a wave waits on memory
+// twice (slot indices, weights and residual, then the expert rows). The
+// expert rows are read 8 at a time with their loads issued together and
+// summed in rank order in fp32, then added to the residual.
 template <class TR>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const CombineArgs p, const TR* resid) {
   constexpr int kGroup = 8;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= p.N) return;
-  for (int c = lane * 8; c < p.d; c += 512) {
-    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < p.k; i0 += kGroup) {
-      bf16x8 o[kGroup];
-      float w[kGroup];
+  const int nchunk = (p.d + 511) / 512;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= p.N * nchunk) return;
+  const int t = gw / nchunk;
+  const int c = (gw - t * nchunk) * 512 + lane * 8;
+  if (c >= p.d) return;  // d % 256 == 0: the upper half of a last, half chunk
+  float acc[8];
+  load8<TR>(resid + (size_t)t * p.d + c, acc);
+  float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < p.k; i0 += kGroup) {
+    bf16x8 o[kGroup];
+    float w[kGroup];
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const int r = min(i0 + i, p.k - 1);
-        o[i] = load_bf16x8(p.out_slot + (size_t)p.pos_of[(size_t)t * p.k + r] * p.d + c);
-        w[i] = i0 + i < p.k ? p.w[(size_t)t * p.k + r] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        float f[8];
-        unpack8(o[i], f);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sum[j] += w[i] * f[j];
-      }
+    for (int i = 0; i < kGroup; ++i) {
+      const int r = min(i0 + i, p.k - 1);
+      o[i] = load_bf16x8(p.out_slot + (size_t)p.pos_of[(size_t)t * p.k + r] * p.d + c);
+      w[i] = i0 + i < p.k ? p.w[(size_t)t * p.k + r] : 0.f;
     }
-    float acc[8];
-    load8<TR>(resid + (size_t)t * p.d + c, acc);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] += sum[j];
-    store_bf16x8(p.y + (size_t)t * p.d + c, pack8(acc));
+    for (int i = 0; i < kGroup; ++i) {
+      float f[8];
+      unpack8(o[i], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum[j] += w[i] * f[j];
+    }
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] += sum[j];
+  store_bf16x8(p.y + (size_t)t * p.d + c, pack8(acc));
 }
 
 }  // namespace
@@ -363,6 +423,10 @@ hipError_t ql_router_topk(const RouterArgs& a, hipStream_t s) {
 
 hipError_t ql_moe_permute(const PermuteArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
+  if (a.N <= 256) {
+    hipLaunchKernelGGL(moe_permute_small_kernel, dim3(1), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int nblk = (a.N + 255) / 256;
   hipLaunchKernelGGL(moe_hist_kernel, dim3(nblk), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -377,7 +441,8 @@ hipError_t ql_moe_permute(const PermuteArgs& a, hipStream_t s) {
 hipError_t ql_moe_combine(const CombineArgs& a, const void* resid, int resid_is_f32,
                           hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  const int blocks = (a.N + 3) / 4;
+  if (a.d % 8) return hipErrorInvalidValue;
+  const int blocks = (a.N * ((a.d + 511) / 512) + 3) / 4;
   if (resid_is_f32)
     hipLaunchKernelGGL(moe_combine_kernel<float>, dim3(blocks), dim3(256), 0, s, a,
                        static_cast<const float*>(resid));
