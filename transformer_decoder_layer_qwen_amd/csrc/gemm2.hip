@@ -37,6 +37,8 @@
 // With split-K each split stores its fp32 partial tile and the reduce kernel
 // applies the epilogue.
 // ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §4, §9, §10.)
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -756,44 +758,38 @@ __global__ __launch_bounds__(256, 1) void gemm2_dec_kernel(const G2Args p) {
   }
 }
 
-// Sum of the split-K / stream-K partials + the epilogue of MODE. A block
-// takes one row and 64 groups of 8 output columns; its 4 waves sum every
-// 4th partial (lane = column group, up to four partials' loads in flight),
-// meet in LDS, and wave 0 applies the epilogue (16 lanes = one head of 128
-// columns for the QKV epilogue).
+// Sum of the split-K / stream-K partials + the epilogue of MODE. A block is
+// one 256-column weight tile by 4 waves of rows; in a wave, each group of S
+// lanes (32, or 16 for SwiGLU's gate/up pairs) is one row and a lane owns 8
+// output columns (and the up columns BN/2 further for SwiGLU). Every row of
+// a wave lies in one GEMM tile, so all its lanes sum the same number of
+// partials; a lane requests up to four of them at once, and the residual or
+// bias with the first, so the wave waits on memory about once. The 16 lanes
+// of an aligned group hold one head of 128 columns for the QKV epilogue.
 template <int MODE>
 __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
   constexpr bool kDual = MODE == G2_SWIGLU;
-  constexpr int NV = kDual ? 16 : 8;  // values summed per lane (gate and up for SwiGLU)
-  __shared__ float red[3][64][NV + 1];
+  constexpr int NV = kDual ? 16 : 8;        // values summed per lane (gate and up for SwiGLU)
+  constexpr int S = kDual ? BN / 16 : BN / 8;  // lanes per row
+  constexpr int RW = 64 / S;                // rows per wave
   const int ldp = p.tiles_n * BN;
-  const int segs = (kDual ? p.tiles_n * BN / 2 : p.tiles_n * BN) / 8;  // per row
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.y;
-  const int seg = blockIdx.x * 64 + lane;
-  const bool live = seg < segs;
-  const int sg = live ? seg : segs - 1;
+  const int tn = blockIdx.x;
+  const int row = (blockIdx.y * 4 + wave) * RW + lane / S;
+  if (row >= p.M) return;  // whole groups of S lanes
+  const int j = lane % S;
   const size_t pstride = (size_t)p.M * ldp;
-  const int tn = kDual ? sg / (BN / 16) : sg / (BN / 8);
   int cnt = p.splits;
-  if (p.streamk) {  // blocks whose runs touched this tile
+  if (p.streamk) {  // blocks whose runs touched this tile (the same for every row of the wave)
     const int nks = p.Ka / BK;
     const long long U = (long long)p.tiles_m * p.tiles_n * nks;
     const long long t = (long long)tn * p.tiles_m + row / p.rows_per_tile;
     cnt = sk_owner(t * nks + nks - 1, U, p.sk_grid) - sk_owner(t * nks, U, p.sk_grid) + 1;
   }
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
   // partial columns of this lane: [c0, c0 + 8) (and the up half at + BN / 2)
-  const int c0 = kDual ? tn * BN + (sg % (BN / 16)) * 8 : sg * 8;
+  const int c0 = tn * BN + j * 8;
   const float* q0 = p.part + (size_t)row * ldp + c0;
-  float v[NV];
-#pragma unroll
-  for (int e = 0; e < NV; ++e) v[e] = 0.f;
-  auto add = [&](const f32x4 (&x)[NV / 4]) {
-#pragma unroll
-    for (int h = 0; h < NV / 4; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * h + e] += x[h][e];
-  };
   auto load = [&](int s, f32x4 (&x)[NV / 4]) {
     const float* q = q0 + s * pstride;
     x[0] = *reinterpret_cast<const f32x4*>(q);
@@ -803,36 +799,50 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
       x[3] = *reinterpret_cast<const f32x4*>(q + BN / 2 + 4);
     }
   };
-  int s = wave;
-  for (; s + 12 < cnt; s += 16) {
-    f32x4 x[4][NV / 4];
+  float v[NV];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load(s + 4 * i, x[i]);
+  for (int e = 0; e < NV; ++e) v[e] = 0.f;
+  auto sum = [&](int s0, auto n_c) {  // n_c partials from s0, all requested first
+    constexpr int n = decltype(n_c)::value;
+    f32x4 x[n][NV / 4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) add(x[i]);
+    for (int i = 0; i < n; ++i) load(s0 + i, x[i]);
+#pragma unroll
+    for (int i = 0; i < n; ++i)
+#pragma unroll
+      for (int h = 0; h < NV / 4; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * h + e] += x[i][h][e];
+  };
+  // epilogue inputs requested alongside the partials
+  const int col = kDual ? tn * (BN / 2) + j * 8 : c0;
+  float extra[8];
+  if constexpr (MODE == G2_RESID_F32) {
+    unpack8(load_bf16x8(p.resid_bf16 + (size_t)row * p.ldr + col), extra);
+  } else if constexpr (MODE == G2_RESID_OUT) {
+    const float* rr = p.resid_f32 + (size_t)row * p.ldr + col;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(rr);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(rr + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      extra[e] = a0[e];
+      extra[e + 4] = a1[e];
+    }
   }
-  for (; s < cnt; s += 4) {
-    f32x4 x[NV / 4];
-    load(s, x);
-    add(x);
+  int s = 0;
+  for (; s + 4 <= cnt; s += 4) sum(s, std::integral_constant<int, 4>{});
+  switch (cnt - s) {
+    case 3: sum(s, std::integral_constant<int, 3>{}); break;
+    case 2: sum(s, std::integral_constant<int, 2>{}); break;
+    case 1: sum(s, std::integral_constant<int, 1>{}); break;
+    default: break;
   }
-  if (wave > 0) {
-#pragma unroll
-    for (int e = 0; e < NV; ++e) red[wave - 1][lane][e] = v[e];
-  }
-  __syncthreads();
-  if (wave > 0 || !live) return;
-#pragma unroll
-  for (int w = 0; w < 3; ++w)
-#pragma unroll
-    for (int e = 0; e < NV; ++e) v[e] += red[w][lane][e];
   if constexpr (kDual) {
     float h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = silu_f32(v[e]) * v[e + 8];
-    store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + seg * 8, pack8(h));
+    store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + col, pack8(h));
   } else {
-    const int col = seg * 8;
     float (&w8)[8] = *reinterpret_cast<float (*)[8]>(v);
     if constexpr (MODE == G2_BIAS) {
       const bf16* bias = p.bias;
@@ -856,16 +866,11 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
         qkv_finish<false>(p, (size_t)row, col, w8);
       return;
     }
-    if constexpr (MODE == G2_RESID_F32) {
-      float x[8];
-      unpack8(load_bf16x8(p.resid_bf16 + (size_t)row * p.ldr + col), x);
+    if constexpr (MODE == G2_RESID_F32 || MODE == G2_RESID_OUT) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w8[e] += x[e];
+      for (int e = 0; e < 8; ++e) w8[e] += extra[e];
     }
     if constexpr (MODE == G2_RESID_OUT) {
-      const float* rr = p.resid_f32 + (size_t)row * p.ldr + col;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w8[e] += rr[e];
       store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + col, pack8(w8));
     } else {
       float* o = p.out_f32 + (size_t)row * p.ldo + col;
@@ -957,8 +962,8 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
     default: e = hipErrorInvalidValue;
   }
   if (e != hipSuccess || (!a.streamk && a.splits == 1)) return e;
-  const int segs = (MODE == G2_SWIGLU ? a.tiles_n * BN / 2 : a.tiles_n * BN) / 8;
-  hipLaunchKernelGGL(gemm2_reduce_kernel<MODE>, dim3((unsigned)((segs + 63) / 64), (unsigned)a.M),
+  constexpr int kRowsPerBlock = 4 * (MODE == G2_SWIGLU ? 4 : 2);  // 4 waves x rows per wave
+  hipLaunchKernelGGL(gemm2_reduce_kernel<MODE>, dim3((unsigned)a.tiles_n, (unsigned)((a.M + kRowsPerBlock - 1) / kRowsPerBlock)),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
