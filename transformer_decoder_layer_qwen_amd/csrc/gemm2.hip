@@ -61,6 +61,7 @@ struct G2Args {
   int seg1, seg2;
   int ldb, Kb;
   int tiles_m, tiles_n, splits, ksteps_per_split;
+  int tn_base;  // first weight column tile of this launch (its tiles_n tiles follow)
   float* out_f32;
   bf16* out_bf16;
   int ldo;
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     m0 = tm * RT;
     rows_valid = min(RT, p.M - m0);
   }
-  const int n0 = tn * (kDual ? BN / 2 : BN);  // first output column of the tile
+  const int n0 = (tn + p.tn_base) * (kDual ? BN / 2 : BN);  // first output column of the tile
 
   // QKV: a 256-column tile lies inside one of the three weight matrices
   const bf16* Bw = p.B + eoff;
@@ -789,6 +790,7 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
   cnt = __builtin_amdgcn_readfirstlane(cnt);
   // partial columns of this lane: [c0, c0 + 8) (and the up half at + BN / 2)
   const int c0 = tn * BN + j * 8;
+  const int tg = tn + p.tn_base;  // the tile's place among the weight's columns
   const float* q0 = p.part + (size_t)row * ldp + c0;
   auto load = [&](int s, f32x4 (&x)[NV / 4]) {
     const float* q = q0 + s * pstride;
@@ -815,7 +817,7 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
         for (int e = 0; e < 4; ++e) v[4 * h + e] += x[i][h][e];
   };
   // epilogue inputs requested alongside the partials
-  const int col = kDual ? tn * (BN / 2) + j * 8 : c0;
+  const int col = tg * (kDual ? BN / 2 : BN) + j * 8;
   float extra[8];
   if constexpr (MODE == G2_RESID_F32) {
     unpack8(load_bf16x8(p.resid_bf16 + (size_t)row * p.ldr + col), extra);
@@ -973,28 +975,47 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
 // tiles, half the k steps). Shape and split count minimise an estimate in
 // units of one 256 x 256 x 64 k step of a block (about 1.9 us measured):
 // waves of up to 256 blocks times k steps per block, plus, with split-K, a
-// reduce launch and the partials' write and read back at ~5 TB/s.
+// reduce launch and the partials' write and read back at ~5 TB/s. A tile
+// count just past a whole number of waves leaves most CUs idle in the last
+// one; then the first columns can run as whole tiles and the last
+// `tail_cols` column tiles as a second launch split `tail_splits` ways
+// (Qwen2.5-7B 4 x 512 QKV: 288 tiles, 190 -> 157 us).
 struct PairPlan {
-  int shape, splits;
+  int shape, splits, tail_cols, tail_splits;
 };
 PairPlan pair_plan(int M, int N, int K) {
-  PairPlan best{T256, 1};
+  PairPlan best{T256, 1, 0, 1};
   double best_c = 1e30;
+  auto waves = [](long long blocks) { return (double)((blocks + 255) / 256); };
+  auto part_cost = [&](int sp, int cols) { return (5.0 + 2.0 * sp * M * (double)cols * 4 / 5e6) / 1.9; };
   for (int shape : {T256, P128_HL}) {
     const int rows = shape == T256 ? 256 : 128;
     const int ks = (shape == T256 ? 2 * K : K) / BK;
-    const int tiles = ((M + rows - 1) / rows) * (N / BN);
+    const int tiles_m = (M + rows - 1) / rows, tiles_n = N / BN;
+    auto consider = [&](double c, PairPlan pl) {
+      if (c < best_c - 1e-9) {
+        best_c = c;
+        best = pl;
+      }
+    };
     for (int sp = 1; sp <= 8 && sp * 8 <= ks; ++sp) {
       const int per = (ks + sp - 1) / sp;
       if ((ks + per - 1) / per != sp) continue;
-      const long long blocks = (long long)tiles * sp;
-      double c = (double)((blocks + 255) / 256) * per;
-      if (sp > 1) c += (5.0 + 2.0 * sp * M * (double)N * 4 / 5e6) / 1.9;
-      if (c < best_c - 1e-9) {
-        best_c = c;
-        best = {shape, sp};
-      }
+      double c = waves((long long)tiles_m * tiles_n * sp) * per;
+      if (sp > 1) c += part_cost(sp, N);
+      consider(c, {shape, sp, 0, 1});
     }
+    for (int tc = 1; tc < tiles_n; ++tc)
+      for (int st = 2; st <= 8 && st * 8 <= ks; ++st) {
+        const int per = (ks + st - 1) / st;
+        if ((ks + per - 1) / per != st) continue;
+        // + the second GEMM launch and its partial epilogue, ~20 units as
+        // measured (a half-empty last wave is better left alone; a nearly
+        // empty one is worth the split)
+        const double c = waves((long long)tiles_m * (tiles_n - tc)) * ks +
+                         waves((long long)tiles_m * tc * st) * per + part_cost(st, tc * BN) + 20.0;
+        consider(c, {shape, 1, tc, st});
+      }
   }
   return best;
 }
@@ -1027,7 +1048,8 @@ bool ql_gemm2_ok(int N, int Kb, bool dual) {
 size_t ql_gemm2_pair_part_bytes(int M, int N, int K) {
   if (M <= 0) return 0;
   const PairPlan pl = pair_plan(M, N, K);
-  return ql_gemm2_part_bytes(M, N, pl.splits);
+  return pl.tail_cols > 0 ? ql_gemm2_part_bytes(M, pl.tail_cols * BN, pl.tail_splits)
+                          : ql_gemm2_part_bytes(M, N, pl.splits);
 }
 
 size_t ql_gemm2_decode_part_bytes(int M, int b_rows, int K, bool pair) {
@@ -1040,11 +1062,28 @@ size_t ql_gemm2_decode_part_bytes(int M, int b_rows, int K, bool pair) {
   return (size_t)sk_max_count(tiles, nks, G) * M * ((b_rows + BN - 1) / BN) * BN * 4;
 }
 
+namespace {
+// a prefill pair plan: one launch over every column tile, or whole tiles
+// for the first columns and a split-K launch for the last tail_cols
+template <int MODE>
+hipError_t run_pair(const G2Args& a, const PairPlan& pl, hipStream_t s) {
+  if (pl.tail_cols <= 0) return run<MODE>(a, pl.shape, s);
+  G2Args m = a, t = a;
+  m.tiles_n = a.tiles_n - pl.tail_cols;
+  m.splits = 1;
+  t.tn_base = m.tiles_n;
+  t.tiles_n = pl.tail_cols;
+  t.splits = pl.tail_splits;
+  hipError_t e = run<MODE>(m, pl.shape, s);
+  return e != hipSuccess ? e : run<MODE>(t, pl.shape, s);
+}
+}  // namespace
+
 hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, const bf16* Wv,
                         int q, int kv, int K, const bf16* bq, const bf16* bk, const bf16* bv,
                         const QkvFinish& f, bool rows128, int splits, void* part, hipStream_t s) {
   if (rows128 != (f.cache_len != nullptr)) return hipErrorInvalidValue;  // decode <=> 128 rows
-  const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1} : pair_plan(M, q + 2 * kv, K);
+  const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1, 0, 1} : pair_plan(M, q + 2 * kv, K);
   (void)splits;
   G2Args a = base(A2, M, pl.shape == T256 ? 2 * K : K, Wq, K, pl.splits, part);
   a.lda = 2 * K;
@@ -1070,13 +1109,13 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
   a.bias3 = bv;
   a.ldo = q + 2 * kv;
   a.tiles_n = (q + 2 * kv) / BN;
-  return run<G2_BIAS>(a, pl.shape, s);
+  return run_pair<G2_BIAS>(a, pl, s);
 }
 
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
                               const bf16* resid, float* out, bool rows128, int splits, void* part,
                               hipStream_t s) {
-  const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1} : pair_plan(M, N, K);
+  const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1, 0, 1} : pair_plan(M, N, K);
   (void)splits;
   G2Args a = base(A2, M, pl.shape == T256 ? 2 * K : K, W, K, pl.splits, part);
   a.lda = 2 * K;
@@ -1085,7 +1124,7 @@ hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K
   a.out_f32 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_F32>(a, pl.shape, s);
+  return run_pair<G2_RESID_F32>(a, pl, s);
 }
 
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
