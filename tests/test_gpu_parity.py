@@ -158,13 +158,22 @@ RAGGED = {
     "mfma_B40": [int(v) for v in np.random.default_rng(7).integers(0, 300, 40)],
     "mfma_B70": [int(v) for v in np.random.default_rng(8).integers(0, 300, 70)] + [299],
 }
+# (lengths, T_max) with 2, 3, 6 and 8 key splits of 32-key steps: the splits
+# run as the waves of one block (2, 4 or 8 waves, some idle) and merge there
+SPLIT_MERGE = {
+    "wg2_B5": ([0, 33, 69, 12, 40], 70),
+    "wg4_B6": ([99, 0, 31, 64, 65, 7], 100),
+    "wg8_B7": ([199, 0, 150, 33, 96, 191, 5], 200),
+    "wg8_B5": ([259, 0, 224, 255, 100], 260),
+}
+RAGGED_CASES = {**{k: (v, 300) for k, v in RAGGED.items()}, **SPLIT_MERGE}
 
 
-@pytest.mark.parametrize("case", list(RAGGED))
+@pytest.mark.parametrize("case", list(RAGGED_CASES))
 def test_small_bf16_decode_ragged_lengths(case):
-    lens = RAGGED[case]
+    lens, T_max = RAGGED_CASES[case]
     cfg = small_cfg()
-    Bn, T_max = len(lens), 300
+    Bn = len(lens)
     layer, w32 = make_layer(cfg, max_tokens=8, max_batch=max(8, Bn))
     q_t = torch.empty(Bn, cfg.q_dim, dtype=torch.bfloat16, device="cuda")
     a_t = torch.empty(Bn, cfg.q_dim, dtype=torch.float32, device="cuda")

@@ -386,22 +386,30 @@ QL_DEV void store_out4(const AttnDecodeArgs& p, size_t idx, const f32x4& v) {
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_mfma_kernel(const AttnDecodeArgs p) {
+// W > 1: the block's W waves are the splits of one (KV head, sequence) and
+// merge in LDS at the end (waves past nsplit have no keys), so no combine
+// kernel runs; W = 1: one wave per split, merged by the combine kernel.
+template <int G, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_mfma_kernel(const AttnDecodeArgs p) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head");
-  __shared__ __attribute__((aligned(16))) bf16 vt_lds[kDh * kVtP];
+  static_assert(16 * kDh * sizeof(float) <= kDh * kVtP * sizeof(bf16), "merge rows fit a V^T slot");
+  __shared__ __attribute__((aligned(16))) bf16 vt_all[W][kDh * kVtP];
 
-  const int lane = threadIdx.x;
+  const int wave = W == 1 ? 0 : (int)(threadIdx.x >> 6);
+  bf16* vt_lds = vt_all[wave];
+  const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
   // KV heads fastest: the Hkv waves of one key range read neighbouring bytes
   const int g = blockIdx.x;
-  const int split = blockIdx.y;
+  const int split = W == 1 ? (int)blockIdx.y : wave;
   const int b = blockIdx.z;
+  const bool idle = split >= p.nsplit;  // W > 1 only
 
   // splits of `chunk` keys; the last one also takes the remainder
-  const int kbeg = split * p.chunk;
-  const int kcap = split == p.nsplit - 1 ? p.T_max : min(kbeg + p.chunk, p.T_max);
+  const int kbeg = idle ? 0 : split * p.chunk;
+  const int kcap = idle ? min(p.chunk, p.T_max)
+                        : (split == p.nsplit - 1 ? p.T_max : min(kbeg + p.chunk, p.T_max));
   const size_t rs = (size_t)p.n_kv_heads * kDh;
   const bf16* kb_ = p.k_cache + (size_t)b * p.T_max * rs + g * kDh;
   const bf16* vb_ = p.v_cache + (size_t)b * p.T_max * rs + g * kDh;
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
   }
   const int L = p.cache_len[b];
   const bool valid = L >= 0 && L < p.T_max;
-  const int kend = min(kcap, valid ? L + 1 : 0);
+  const int kend = idle ? 0 : min(kcap, valid ? L + 1 : 0);
 
   f32x4 acc[8];  // lane: O^T[dh 16 blk + 4 grp + r][head col]
 #pragma unroll
@@ -553,6 +561,46 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void at
 
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
+  if constexpr (W > 1) {
+    // each wave's partial (m, l, O) to LDS (O in its own V^T slot, which only
+    // this wave has used), then the block merges: thread t takes elements
+    // t, t + 64 W, ... of the G x 128 outputs
+    __shared__ float mb[W][16], lb[W][16];
+    float* ob = reinterpret_cast<float*>(vt_lds);  // [16][128]
+    if (col < G) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4*>(ob + col * kDh + 16 * i + 4 * grp) = acc[i];
+      if (grp == 0) {
+        mb[wave][col] = m_run;
+        lb[wave][col] = l_run;
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < G * kDh; e += 64 * W) {
+      const int h = e / kDh, d = e % kDh;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < W; ++w) M = fmaxf(M, mb[w][h]);
+      float l = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float m = mb[w][h];
+        const float wt = m == -INFINITY ? 0.f : exp2f(m - M);
+        l += wt * lb[w][h];
+        o += wt * reinterpret_cast<const float*>(vt_all[w])[h * kDh + d];
+      }
+      const float v = valid ? o / l : __builtin_nanf("");
+      const size_t idx = (size_t)b * p.ldo + (size_t)(g * G + h) * kDh + d;
+      if (p.out_hilo) {
+        const bf16 hi = (bf16)v;
+        p.out_hilo[idx] = hi;
+        p.out_hilo[idx + p.lo_off] = (bf16)(v - (float)hi);
+      } else {
+        p.out[idx] = v;
+      }
+    }
+    return;
+  }
   if (col >= G) return;
   const int hq = g * G + col;
   if (p.nsplit == 1) {  // the only split: normalise here
@@ -649,13 +697,23 @@ hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.nsplit < 1 || a.nsplit > kMaxDecodeSplits) return hipErrorInvalidValue;
   const dim3 grid(a.nsplit, a.n_kv_heads, a.B);
   const dim3 grid_kv(a.n_kv_heads, a.nsplit, a.B);
+  // finished queries with up to 8 splits: the splits are the waves of one
+  // block and merge there
+  const int wm = !a.q_in || a.nsplit == 1 || a.nsplit > 8 ? 1 : (a.nsplit <= 2 ? 2 : a.nsplit <= 4 ? 4 : 8);
+  const dim3 grid_wg(a.n_kv_heads, 1, a.B);
   switch (a.n_q_heads / a.n_kv_heads) {
-#define QL_G(V)                                                                          \
-  case V:                                                                                \
-    if (a.q_in)                                                                          \
-      hipLaunchKernelGGL((attn_decode_mfma_kernel<V>), grid_kv, dim3(64), 0, s, a);      \
-    else                                                                                 \
-      hipLaunchKernelGGL((attn_decode_kernel<V>), grid, dim3(64), 0, s, a);              \
+#define QL_G(V)                                                                                 \
+  case V:                                                                                       \
+    if (!a.q_in)                                                                                \
+      hipLaunchKernelGGL((attn_decode_kernel<V>), grid, dim3(64), 0, s, a);                     \
+    else if (wm == 1)                                                                           \
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<V, 1>), grid_kv, dim3(64), 0, s, a);          \
+    else if (wm == 2)                                                                           \
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<V, 2>), grid_wg, dim3(128), 0, s, a);         \
+    else if (wm == 4)                                                                           \
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<V, 4>), grid_wg, dim3(256), 0, s, a);         \
+    else                                                                                        \
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<V, 8>), grid_wg, dim3(512), 0, s, a);         \
     break;
     QL_G(1) QL_G(2) QL_G(3) QL_G(4) QL_G(5) QL_G(6) QL_G(7) QL_G(8)
     QL_G(9) QL_G(10) QL_G(11) QL_G(12) QL_G(13) QL_G(14) QL_G(15) QL_G(16)
@@ -664,7 +722,7 @@ hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
       return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  if (e != hipSuccess || a.nsplit == 1 || wm > 1) return e;
   const int heads = a.B * a.n_q_heads;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((heads + kCombineWaves - 1) / kCombineWaves),
                      dim3(64 * kCombineWaves), 0, s, a);
