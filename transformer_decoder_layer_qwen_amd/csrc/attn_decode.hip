@@ -19,10 +19,11 @@
 //     no cross-lane reduction is needed at the end.
 // With one split the wave writes the normalised output; otherwise it writes an
 // unnormalised partial (m, l, o[128]) per head and the combine kernel merges
-// the splits. (A merge inside the kernel would need device-scope fences,
-// which write back and invalidate the whole L2 of the XCD on this GPU and cost
-// far more than a second launch.) Short caches get one tile per wave, so every
-// K/V byte a wave needs is requested when the wave starts.
+// the splits. (Merging across blocks would need device-scope fences, which
+// write back and invalidate the whole L2 of the XCD on this GPU and cost far
+// more than a second launch; the batched kernel below merges splits that
+// share a block.) Short caches get one tile per wave, so every K/V byte a
+// wave needs is requested when the wave starts.
 //
 // Prologue (fused QK-norm / RoPE / cache append): the Q/K/V projection hands
 // over raw sums of (x * gamma1) W^T, and 1/rms of x (or the wave computes it
@@ -368,7 +369,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
 //     dh value per 8-byte store) and read back as A fragments in that slot
 //     order; the running output O^T (128 x 16) lives in eight accumulators,
 //     rescaled only when some head's running maximum moved.
-// The next tile's 16 KB are in flight while the current one is processed.
+// Two register sets of 16 KB each are refilled with the tile after next as
+// soon as they are consumed, so about two tiles stay in flight.
 constexpr int kVtP = 36;  // bf16 per transposed-V row: 32 keys + 4 (bank spread)
 
 QL_DEV void store_out4(const AttnDecodeArgs& p, size_t idx, const f32x4& v) {
