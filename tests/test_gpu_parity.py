@@ -210,6 +210,47 @@ def test_small_bf16_decode_ragged_lengths(case):
                         noise=1e-4) <= 1.0
 
 
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    """Argument errors on a live handle return their status and write nothing: sizes beyond
+    the handle's workspace, S > T_max, empty batches, y aliasing x, and the MoE entry point
+    on a dense layer."""
+    cfg = small_cfg()
+    layer, _ = make_layer(cfg, max_tokens=16, max_batch=4)
+    h, dt = layer.handle, tdt(cfg)
+    x = torch.zeros(4, 8, cfg.d, dtype=dt, device="cuda")
+    y = torch.full_like(x, float("nan"))
+    kc = torch.zeros(4, 8, cfg.n_kv_heads, cfg.head_dim, dtype=dt, device="cuda")
+    vc = torch.zeros_like(kc)
+    lens = torch.zeros(8, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    X, Y, K, V, L = x.data_ptr(), y.data_ptr(), kc.data_ptr(), vc.data_ptr(), lens.data_ptr()
+    cases = {
+        "prefill B*S > max_tokens": (lambda: B.qlayer_prefill(h, X, 4, 8, 0, K, V, 8, Y, s),
+                                     B.QL_EINVAL),
+        "prefill S > T_max": (lambda: B.qlayer_prefill(h, X, 1, 8, 0, K, V, 4, Y, s), B.QL_EINVAL),
+        "prefill B = 0": (lambda: B.qlayer_prefill(h, X, 0, 8, 0, K, V, 8, Y, s), B.QL_EINVAL),
+        "prefill S = 0": (lambda: B.qlayer_prefill(h, X, 1, 0, 0, K, V, 8, Y, s), B.QL_EINVAL),
+        "prefill y aliases x": (lambda: B.qlayer_prefill(h, X, 1, 8, 0, K, V, 8, X, s),
+                                B.QL_EINVAL),
+        "decode B > max_batch": (lambda: B.qlayer_decode(h, X, 5, L, None, 0, K, V, 8, Y, s),
+                                 B.QL_EINVAL),
+        "decode B = 0": (lambda: B.qlayer_decode(h, X, 0, L, None, 0, K, V, 8, Y, s), B.QL_EINVAL),
+        "decode T_max = 0": (lambda: B.qlayer_decode(h, X, 2, L, None, 0, K, V, 0, Y, s),
+                             B.QL_EINVAL),
+        "decode NULL cache_len": (lambda: B.qlayer_decode(h, X, 2, None, None, 0, K, V, 8, Y, s),
+                                  B.QL_EINVAL),
+        "moe_ffn on a dense layer": (lambda: B.qlayer_moe_ffn(h, X, 8, Y, None, None, s),
+                                     B.QL_EUNSUPPORTED),
+    }
+    for name, (call, status) in cases.items():
+        with pytest.raises(B.QLayerError) as e:
+            call()
+        assert e.value.status == status, name
+    torch.cuda.synchronize()
+    assert torch.isnan(y.float()).all()
+    assert not kc.any() and not vc.any()
+
+
 @pytest.mark.parametrize("lens", [[8, 16], [8, 16, 3, 0, 5, 7]], ids=["gemv_B2", "mfma_B6"])
 def test_decode_out_of_range_length_is_contained(lens):
     cfg = small_cfg()
