@@ -46,7 +46,7 @@ namespace {
 
 enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU, G2_MOE_GU, G2_MOE_DOWN };
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BN = 256, BK = 64;  // weight-tile columns, k depth of a stage
 constexpr int kGroupM = 4;  // tile rows per L2 group
 constexpr int kRowChunks = BK / 8;                     // 16-byte chunks per LDS row
 constexpr int kPitch = BN + 4;                         // fp32 epilogue tile pitch

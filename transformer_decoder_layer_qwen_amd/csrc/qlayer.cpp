@@ -240,7 +240,6 @@ size_t layout(ql_handle* h, char* base) {
   h->attn = k.take<void>(N * h->q_dim * 4);  // [hi | lo] bf16 pair, or fp32 (GEMV decode)
   h->r = k.take<float>(N * c.d * 4);
   h->z = k.take<void>(N * c.d * es);
-  const size_t B = (size_t)std::max(c.max_batch, 0);
   const size_t slots = decode_split_slots(c);
   h->part_o = k.take<float>(slots * c.n_q_heads * c.head_dim * 4);
   h->part_ml = k.take<float>(slots * c.n_q_heads * 2 * 4);
@@ -691,7 +690,7 @@ ql_status qlayer_create(const ql_config* cfg, const ql_weights* w, ql_handle** o
       om[i] = std::pow((double)cfg->rope_theta, -2.0 * i / (double)cfg->head_dim);
     e = hipMemcpy(h->rope_omega, om.data(), om.size() * sizeof(double), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
-      hipFree(h->ws);
+      (void)hipFree(h->ws);  // the upload's error is the one reported
       delete h;
       return fail(QL_EHIP, "RoPE table upload: %s", hipGetErrorString(e));
     }
