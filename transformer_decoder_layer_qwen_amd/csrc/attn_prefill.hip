@@ -7,8 +7,13 @@
 // diagonal are skipped in both products). The [S, S] probability matrix is
 // never written to memory ("推理系统 03" §12).
 //
-// Block = 4 waves = 128 query rows of one (sequence, head); a wave owns 32
-// rows. Key tiles of 64 rows stream through LDS, double-buffered.
+// Block = 4 waves on 128 query rows of one (sequence, head); a wave owns 32
+// rows. With KSPLIT the block has two such groups of 4 waves: group 0 takes
+// the first half of the query tile's key tiles and group 1 the rest, and the
+// two partial softmax states are merged through LDS at the end. That halves
+// the longest tiles' time when the causal work would otherwise leave most
+// CUs idle behind them (grids of at most one block per CU).
+// Key tiles of 64 rows stream through LDS, double-buffered per group.
 // Scores are formed transposed, S^T = K Q^T, with 32x32x16 MFMAs: the query
 // is the MFMA column, so a lane owns one query and its running max / sum
 // need only one cross-lane exchange per tile. P^T stays in registers and is
@@ -34,14 +39,19 @@ constexpr int kStage = kKElems + kVElems;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
 constexpr int kCUs = 256;
 
-// Two blocks per CU (the LDS ring is 68 KiB): the register budget of two
-// waves per SIMD keeps every accumulator in VGPRs, and one wave's MFMAs run
-// while the other works through its softmax.
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * kStage];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// Two 4-wave blocks per CU (one 68 KiB ring each), or one KSPLIT block with
+// two rings: the register budget of two waves per SIMD keeps every
+// accumulator in VGPRs, and one wave's MFMAs run while the other works
+// through its softmax.
+template <bool KSPLIT>
+__global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefill_kernel(
+    const AttnPrefillArgs p) {
+  constexpr int NG = KSPLIT ? 2 : 1;  // wave groups
+  __shared__ __attribute__((aligned(16))) bf16 lds[NG * 2 * kStage];  // [group][stage]
+  const int lane = threadIdx.x & 63;
+  const int grp = KSPLIT ? (int)(threadIdx.x >> 8) : 0;  // key half
+  const int tid = threadIdx.x & 255;                     // thread within the group
+  const int wave = tid >> 6;          // query rows 32 wave .. +31 of the tile
   const int col = lane & 31;
   const int hi = lane >> 5;
   const int h = blockIdx.y;
@@ -74,6 +84,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
   const bf16* vbase = p.v_cache + ((size_t)b * p.T_max) * kv_row_stride + g * kDh;
   const int kend = min(q0 + kBQ, S);  // keys needed by this block
   const int ntiles = (kend + kBK - 1) / kBK;
+  // this group's key tiles [kt_lo, kt_hi); both groups step niter times
+  const int kt_lo = !KSPLIT ? 0 : grp == 0 ? 0 : ntiles / 2;
+  const int kt_hi = !KSPLIT ? ntiles : grp == 0 ? ntiles / 2 : ntiles;
+  const int niter = !KSPLIT ? ntiles : ntiles - ntiles / 2;
+  bf16* ring = lds + grp * 2 * kStage;
 
   // tile-load assignment
   //   K: chunk = tid + 256*i, key = chunk >> 4, 16-byte piece c = chunk & 15
@@ -115,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
     }
   };
   auto lstore = [&](int st) {
-    bf16* Ks = lds + st * kStage;
+    bf16* Ks = ring + st * kStage;
     bf16* Vt = Ks + kKElems;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -142,18 +157,22 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  gload(0);
-  lstore(0);
+  if (kt_lo < kt_hi) {
+    gload(kt_lo);
+    lstore(0);
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int st = kt & 1;
-    const bool more = kt + 1 < ntiles;
+  for (int it = 0; it < niter; ++it) {
+    const int kt = kt_lo + it;
+    const int st = it & 1;
+    const bool more = kt + 1 < kt_hi;
     if (more) gload(kt + 1);
     const int k0 = kt * kBK;
-    // skip tiles whose every key is in this wave's future (wave-uniform)
-    if (__builtin_amdgcn_readfirstlane(k0 <= wave_qmax)) {
-      const bf16* Ks = lds + st * kStage;
+    // skip tiles past the group's range (its last step when it has one tile
+    // fewer) and tiles whose every key is in this wave's future (wave-uniform)
+    if (__builtin_amdgcn_readfirstlane(kt < kt_hi && k0 <= wave_qmax)) {
+      const bf16* Ks = ring + st * kStage;
       const bf16* Vt = Ks + kKElems;
       f32x16 sc[2];
 #pragma unroll
@@ -233,8 +252,34 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
     __syncthreads();
   }
 
+  // merge: group 1 hands its state to group 0 through LDS (the rings are
+  // free: every tile read ended before the loop's last barrier). A lane's
+  // state is relative to its own reference maximum m_run; a group that saw
+  // no key of this query has m_run = -inf and contributes nothing.
+  static_assert(4 * 66 * 64 * 4 <= 2 * kStage * 2, "merge state fits group 0's ring");
+  float* mst = reinterpret_cast<float*>(lds) + wave * (66 * 64) + lane;
+  if (KSPLIT && grp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mst[(16 * dt + r) * 64] = acc_o[dt][r];
+    mst[64 * 64] = m_run;
+    mst[65 * 64] = l_run;
+  }
+  if (KSPLIT) __syncthreads();
+  if (grp == 1 || my_q >= S) continue;  // (the next pass starts with a barrier)
+  if (KSPLIT) {
+    const float m1 = mst[64 * 64], l1 = mst[65 * 64];
+    const float m = fmaxf(m_run, m1);  // finite: every query sees key 0
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    l_run = a0 * l_run + a1 * l1;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[dt][r] = a0 * acc_o[dt][r] + a1 * mst[(16 * dt + r) * 64];
+  }
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  if (my_q >= S) continue;
   const float inv = 1.0f / l_tot;
   // the fp32 output as a bf16 pair: hi = RNE(o) at column c, lo = RNE(o - hi)
   // at column c + lo_off (the O projection multiplies both)
@@ -261,11 +306,25 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnPrefillA
 hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
   const int nqt = (a.S + kBQ - 1) / kBQ;
-  // pair query tiles when the paired grid still gives every CU two blocks
-  // (the occupancy the kernel is built for)
+  const long pairs = (long)((nqt + 1) / 2) * a.n_q_heads * a.B;
+  const long tiles = (long)nqt * a.n_q_heads * a.B;
   AttnPrefillArgs b = a;
-  b.pair = (long)((nqt + 1) / 2) * a.n_q_heads * a.B >= 2L * kCUs;
-  const int gx = b.pair ? (nqt + 1) / 2 : nqt;
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3(gx, a.n_q_heads, a.B), dim3(256), 0, s, b);
+  if (pairs >= 2L * kCUs) {
+    // enough tile pairs (equal work each) for two 4-wave blocks per CU
+    b.pair = true;
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3((nqt + 1) / 2, a.n_q_heads, a.B),
+                       dim3(256), 0, s, b);
+  } else if (pairs >= kCUs || tiles <= kCUs) {
+    // one 8-wave block per CU, each tile's keys split between its two groups:
+    // tile pairs when they fill the CUs, else single tiles
+    b.pair = pairs >= kCUs;
+    hipLaunchKernelGGL(attn_prefill_kernel<true>,
+                       dim3(b.pair ? (nqt + 1) / 2 : nqt, a.n_q_heads, a.B), dim3(512), 0, s, b);
+  } else {
+    // single tiles, longest first, two 4-wave blocks per CU
+    b.pair = false;
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nqt, a.n_q_heads, a.B), dim3(256), 0, s,
+                       b);
+  }
   return hipGetLastError();
 }
