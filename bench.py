@@ -19,6 +19,11 @@ per-stage breakdown taken from the library's stage events (eager calls, each
 queued behind a short spin kernel so that host launch latency stays outside
 the measured windows).
 
+Beside the published peaks, "measured_peaks" gives reference rates taken on
+the same GPU through torch (a plain device copy, the vendor library's bf16
+matrix-vector and matrix products). MoE workloads also report the rows routed
+to each expert in one call ("expert_rows": mean, sd, min, max).
+
 One JSON line is printed on stdout.
 """
 from __future__ import annotations
@@ -370,8 +375,70 @@ def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_g
         gemms = [s for s in ("qkv", "o_proj", "gate_up", "down", "expert_gate_up",
                              "expert_down") if s in st]
         out["stage_roofline"] = {s: roofline_entry(cfg, wl, s, st[s]) for s in gemms + ["attention"]}
+    if cfg.is_moe:
+        out["expert_rows"] = expert_rows(setup)
     setup.close()
     return out, setup
+
+
+def expert_rows(setup):
+    """Rows routed to each expert in one call: the router logits are tapped
+    from the library (fp32, as the top-k reads them) and the top-k taken here.
+    Returns mean, standard deviation, min and max over the experts."""
+    import torch
+    cfg, wl = setup.cfg, setup.wl
+    lg = torch.empty(wl.tokens, cfg.n_experts, dtype=torch.float32, device="cuda")
+    layer = setup.layers[0]
+    layer.set_taps(logits=lg)
+    setup.step(0)
+    torch.cuda.synchronize()
+    layer.set_taps()
+    l = lg.cpu().numpy()
+    top = np.argpartition(-l, cfg.top_k - 1, axis=1)[:, :cfg.top_k]
+    cnt = np.bincount(top.ravel(), minlength=cfg.n_experts)
+    return {"mean": round(float(cnt.mean()), 2), "sd": round(float(cnt.std()), 2),
+            "min": int(cnt.min()), "max": int(cnt.max()), "experts": int(cfg.n_experts)}
+
+
+def measured_peaks():
+    """Reference rates measured on this GPU, beside the published peaks: a
+    plain 1 GiB device copy (read + write bytes), the vendor library's bf16
+    matrix-vector product on the headline gate/up weight shape (37888 x 3584,
+    read bytes), and its bf16 8192^3 matrix product, all through torch. Best
+    of 5, events on the current stream."""
+    import torch
+    def best_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        return min(t)
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = best_ms(lambda: dst.copy_(src))
+    del src, dst
+    rows, cols = 2 * 18944, 3584
+    wmat = torch.randn(rows, cols, dtype=torch.bfloat16, device="cuda")
+    xv = torch.randn(cols, dtype=torch.bfloat16, device="cuda")
+    mv_ms = best_ms(lambda: torch.mv(wmat, xv))
+    del wmat, xv
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    mm_ms = best_ms(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBs": round(2 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "vendor_gemv_GBs": round(2 * rows * cols / (mv_ms * 1e-3) / 1e9, 1),
+            "bf16_matmul_TFLOPs": round(2 * m ** 3 / (mm_ms * 1e-3) / 1e12, 1),
+            "method": "torch: 1 GiB copy_; mv bf16 37888x3584; matmul bf16 8192^3; best of 5"}
 
 
 # ------------------------------------------------------------ CPU oracle ----
@@ -475,6 +542,8 @@ def main():
     roof = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dom["stage"]
     roof["kernel_ms"] = dom["kernel_ms"]
+    peaks = measured_peaks()
+    log(f"[bench] measured peaks: {peaks}")
     line = {
         "metric": METRIC,
         "value": head["tokens_per_s"],
@@ -496,6 +565,7 @@ def main():
         "layer_frac_hbm": head.get("layer_frac_hbm"),
         "stage_ms": head.get("stage_ms"),
         "secondary": secondary,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

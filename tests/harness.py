@@ -110,6 +110,24 @@ def weights_for(cfg: configs.LayerConfig, seed: int):
     return w, widen(w)
 
 
+def flip_report(logits_gpu, logits_ref, k, edges=(1e-3, 1e-2)):
+    """Tokens whose top-k expert set from the GPU's router logits differs from
+    the oracle's, binned by the oracle's k-th/(k+1)-th logit gap: a dict
+    "lo..hi" -> (flipped, tokens)."""
+    lr = np.asarray(logits_ref, np.float64)
+    srt = -np.sort(-lr, axis=-1)
+    gap = srt[:, k - 1] - srt[:, k]
+    want = np.sort(ref.topk_select(lr, k), axis=-1)
+    got = np.sort(ref.topk_select(np.asarray(logits_gpu, np.float64), k), axis=-1)
+    diff = np.any(want != got, axis=-1)
+    bounds = (0.0,) + tuple(edges) + (np.inf,)
+    out = {}
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        sel = (gap >= lo) & (gap < hi)
+        out[f"{lo:g}..{hi:g}"] = (int(diff[sel].sum()), int(sel.sum()))
+    return out
+
+
 def routing_mismatch(idx_gpu, logits_ref, k, gap_min=GAP_MIN):
     """Tokens whose selected set differs from the oracle's where its
     k-th/(k+1)-th logit gap exceeds gap_min. Returns (bad tokens, checked)."""

@@ -12,7 +12,8 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from harness import (ATT_BRANCH_TOL, BF16_TOL, F32_TOL, FFN_BRANCH_TOL, attention_err,  # noqa: E402
-                     branch_err, log, rel_err, rounding_err, routing_mismatch, small_cfg, small_moe_cfg,
+                     branch_err, flip_report, log, rel_err, rounding_err, routing_mismatch, small_cfg,
+                     small_moe_cfg,
                      spec_of, weights_for)
 from oracle import qlayer_ref as ref  # noqa: E402
 from transformer_decoder_layer_qwen_amd import binding as B  # noqa: E402
@@ -379,12 +380,31 @@ def test_full_size(cid, wl):
         layer, w32 = make_layer(cfg, seed=configs.weight_seed(cid), max_tokens=wl.tokens,
                                 max_batch=1)
         r_t = torch.empty(wl.tokens, cfg.d, dtype=torch.float32, device="cuda")
-        layer.set_taps(r=r_t)
+        lg_t = (torch.empty(wl.tokens, cfg.n_experts, dtype=torch.float32, device="cuda")
+                if cfg.is_moe else None)
+        layer.set_taps(r=r_t, logits=lg_t)
         x = synth.make_prefill_input(cfg, wl.seed, wl.batch, wl.seq)
         y, kc, vc = run_prefill(layer, cfg, x, T_max=wl.seq)
-        rows = sorted({0, 1, 127, 128, wl.seq // 2 + 3, wl.seq - 2, wl.seq - 1})
+        checked = sorted({0, 1, 127, 128, wl.seq // 2 + 3, wl.seq - 2, wl.seq - 1})
+        rows = set(checked)
+        if cfg.is_moe:  # more rows for the routing report of the whole layer
+            rows |= set(np.linspace(0, wl.seq - 1, 192).astype(int).tolist())
+        rows = sorted(rows)
         x32 = synth.to_f32(x).astype(np.float64)
-        o = ref.layer_prefill(x32, w32, spec, rows=rows)
+        o_all = ref.layer_prefill(x32, w32, spec, rows=rows)
+        if cfg.is_moe:
+            # whole-layer routing: R differs from the oracle's by the bf16 roundings
+            # upstream, so near-ties may flip; reported by gap, not asserted (the
+            # routing criterion is graded on qlayer_moe_ffn with identical R)
+            lg = host(lg_t).reshape(wl.batch, wl.seq, -1)[:, rows]
+            flips = flip_report(lg.reshape(-1, cfg.n_experts),
+                                o_all["logits"].reshape(-1, cfg.n_experts), cfg.top_k)
+            log(f"[gpu] {wl.label}: routing flips vs the oracle over {len(rows)} rows, by the "
+                f"oracle's k-th/(k+1)-th logit gap (flipped, tokens): {flips}")
+        # the parity checks below: the fixed sample of rows
+        sel = [rows.index(r) for r in checked]
+        o = {k: (v[:, sel] if k not in ("k", "v", "xhat") else v) for k, v in o_all.items()}
+        rows = checked
         got = host(y)[:, rows]
         rg = host(r_t).reshape(wl.batch, wl.seq, -1)[:, rows]
         e = rel_err(got, o["y"])
