@@ -520,8 +520,11 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
 // below RA / 2 hold the hi halves and the rest the lo halves at the same k,
 // so each B tile is fetched once and serves both, and each wave adds its lo
 // accumulators to its hi ones. The k loop then runs over Kb only; the QKV
-// epilogue takes the rows as sequences. 32-row MFMA tiles made only of
-// padding rows are skipped.
+// epilogue takes the rows as sequences. In plain tiles, 32-row MFMA tiles
+// made only of padding rows are multiplied too and never stored: the matrix
+// cores are far from busy here, and a branch around them made the compiler
+// move the accumulators between register files at every step (gate/up and
+// down at 64 rows ran 13 % slower); hi/lo tiles skip them.
 // Work is cut stream-K: the tile-major (tile, k step) units are split into
 // gridDim.x contiguous runs, one per block. The ring runs on across the
 // tiles of a run; each tile's fp32 partial goes out straight from the
@@ -682,13 +685,17 @@ __global__ __launch_bounds__(256, 1) void gemm2_dec_kernel(const G2Args p) {
     }
   }
 
+  // hi/lo tiles skip their padding-only 32-row MFMA tiles (wave-uniform
+  // branches); plain tiles multiply them (see above)
   bool act[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) act[i] = true;
   auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][NI], bf16x8 (&bfr)[2][TJ]) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        if (act[i]) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+        if (!HL || act[i]) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
@@ -699,7 +706,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_dec_kernel(const G2Args p) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        if (act[i])
+        if (!HL || act[i])
 #pragma unroll
           for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
   };
@@ -726,10 +733,12 @@ __global__ __launch_bounds__(256, 1) void gemm2_dec_kernel(const G2Args p) {
     if (g + NS - 1 < total) issue(g + NS - 1);
     const int uu = u0 + g;
     const int t = tile_of(uu);
-    const int m0 = __builtin_amdgcn_readfirstlane((t % p.tiles_m) * RT);
-    const int rows_valid = min(RT, p.M - m0);
+    if constexpr (HL) {
+      const int m0 = __builtin_amdgcn_readfirstlane((t % p.tiles_m) * RT);
+      const int rows_valid = min(RT, p.M - m0);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) act[i] = (HL ? (32 * i) % RT : 32 * i) < rows_valid;
+      for (int i = 0; i < NI; ++i) act[i] = (32 * i) % RT < rows_valid;
+    }
     const char* st = smem + (g % NS) * SB;
     bf16x8 a0[2][NI], b0[2][TJ], a1[2][NI], b1[2][TJ];
     read2(st, 0, a0, b0);
