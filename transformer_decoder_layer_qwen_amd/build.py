@@ -27,6 +27,10 @@ DEVICE_FLAGS = [
     "-Wno-unused-result",
 ]
 HOST_FLAGS = [f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-fPIC"]
+# Per-file device flags. gemm2.hip: MFMA results in the ordinary vector
+# registers, so the decode tiles' accumulators, which also feed stores and
+# selects, are not copied between register files at every k step.
+FILE_FLAGS = {"gemm2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -49,7 +53,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         obj = os.path.join(BUILD, f + ".o")
         objs.append(obj)
         if f.endswith(".hip"):
-            cmds.append([HIPCC, *DEVICE_FLAGS, f"-I{INCLUDE}", "-c", src, "-o", obj])
+            cmds.append([HIPCC, *DEVICE_FLAGS, *FILE_FLAGS.get(f, []), f"-I{INCLUDE}", "-c", src,
+                         "-o", obj])
         else:
             cmds.append([HIPCC, *HOST_FLAGS, f"-I{INCLUDE}", "-c", src, "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
