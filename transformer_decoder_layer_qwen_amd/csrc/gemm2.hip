@@ -360,7 +360,10 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   // One stage: the fragments of k steps (0, 1) are read, then those of (2, 3)
   // are requested before the MFMAs of (0, 1) run, so only the first reads of
   // a stage sit in front of its MFMAs. Expert tiles are often part-filled:
-  // their 32-row MFMA tiles made only of padding rows are skipped.
+  // their 32-row MFMA tiles made only of padding rows are skipped, the MFMAs
+  // only (the fragment reads stay unconditional: reads inside the branches
+  // made the compiler wait for them before every pair of MFMAs; the padding
+  // rows hold copies of a valid row).
   bool act[4];
   {
     const int wmu = __builtin_amdgcn_readfirstlane(wm);
@@ -372,8 +375,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (act[i]) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+      for (int i = 0; i < 4; ++i) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
