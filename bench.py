@@ -323,6 +323,9 @@ PMC_WRITE_SCALE = 262144.0 / 262144.0
 PMC_TRAFFIC_KIB = {
     # profiles/gemv_gate_up_qwen25_7b_decode_b1_hbm_counters.md (csrc/gemv.hip as of e72cee5)
     ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132731.3, 296.2),
+    # profiles/decode_b32_b64_hbm_counters.md (library at a5f47d2); a stage's kernels summed
+    ("qwen3-8b decode B=64 cache=4096", "attention"): (526717.1, 4608.0),
+    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (136845.9 + 6382.7, 12672.0 + 1184.0),
 }
 
 
