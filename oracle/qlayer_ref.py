@@ -379,30 +379,29 @@ def layer_decode(x, k_cache, v_cache, cache_len, w, spec: LayerSpec,
     the new token is cache row cache_len[b] at position cache_len[b] +
     pos_offset and attends to all cache_len[b]+1 rows.
 
+    The projections and the FFN take the B rows as one matrix (rows never
+    interact, [P1 §03.2]); only attention is per sequence.
+
     Returns y [B, d], k_new/v_new [B, Hkv, dh] (the row written to the cache),
     r, attn, q, z and FFN intermediates.
     """
     x = f64(x)
     B, d = x.shape
     Hq, dh = spec.n_q_heads, spec.head_dim
-    out = {k: [] for k in ("y", "r", "xhat", "q", "k_new", "v_new", "attn", "z", "f",
-                           "h", "idx", "w", "logits")}
+    lens = np.asarray(cache_len, dtype=np.int64).reshape(B)
+    xhat = rmsnorm(x, w["ln1_g"], spec.eps)
+    q, k, v = _project_qkv(xhat, w, spec, lens.astype(np.float64) + pos_offset)
+    attn = np.empty((B, Hq * dh))
     for b in range(B):
-        L = int(cache_len[b])
-        xhat = rmsnorm(x[b:b + 1], w["ln1_g"], spec.eps)
-        q, k, v = _project_qkv(xhat, w, spec, np.array([L + pos_offset], np.float64))
-        K = np.concatenate([f64(k_cache[b, :L]), k], axis=0)
-        V = np.concatenate([f64(v_cache[b, :L]), v], axis=0)
-        o = attention(q, K, V, np.array([L]), np.arange(L + 1), spec.n_kv_heads)
-        attn = o.reshape(1, Hq * dh)
-        r = x[b:b + 1] + linear(attn, w["wo"])
-        z = rmsnorm(r, w["ln2_g"], spec.eps)
-        F, extra = _ffn(z, w, spec)
-        y = r + F
-        for name, val in (("y", y[0]), ("r", r[0]), ("xhat", xhat[0]), ("q", q[0]),
-                          ("k_new", k[0]), ("v_new", v[0]), ("attn", attn[0]),
-                          ("z", z[0]), ("f", F[0])):
-            out[name].append(val)
-        for name, val in extra.items():
-            out[name].append(val[0])
-    return {k: np.stack(v) for k, v in out.items() if v}
+        L = int(lens[b])
+        K = np.concatenate([f64(k_cache[b, :L]), k[b:b + 1]], axis=0)
+        V = np.concatenate([f64(v_cache[b, :L]), v[b:b + 1]], axis=0)
+        o = attention(q[b:b + 1], K, V, np.array([L]), np.arange(L + 1), spec.n_kv_heads)
+        attn[b] = o.reshape(Hq * dh)                                  # concat heads [P3 §9]
+    r = x + linear(attn, w["wo"])
+    z = rmsnorm(r, w["ln2_g"], spec.eps)
+    F, extra = _ffn(z, w, spec)
+    out = {"y": r + F, "r": r, "xhat": xhat, "q": q, "k_new": k, "v_new": v, "attn": attn,
+           "z": z, "f": F}
+    out.update(extra)
+    return out

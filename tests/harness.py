@@ -11,12 +11,17 @@ from oracle import qlayer_ref as ref
 from transformer_decoder_layer_qwen_amd import configs, synth
 
 BF16_TOL = 2e-2     # max|err| <= 2e-2 * RMS(output) for bf16 paths (the layer output Y)
-# Branch self-checks (R - X and Y - R on their own scale). The attention branch
-# inherits the bf16 rounding of q, k, v (K and V live in the bf16 cache); a
-# bf16-rounding emulation of the oracle puts that floor at ~2.8% on the small
-# test layer, so its bound is 4e-2. The FFN branch is measured through Y after
-# removing Y's own rounding (branch_err) and keeps the 2e-2 bound.
-ATT_BRANCH_TOL = 4e-2
+# Branch self-checks, so the residual cannot hide an error in a branch. The
+# FFN branch Y - R is measured through Y after removing Y's own rounding
+# (branch_err) against its RMS over all rows, with the 2e-2 bar. The
+# attention branch R - X is measured row by row: row t's largest error over
+# row t's own branch RMS (rowwise_err), so the bound does not depend on which
+# rows are compared. Its floor is the bf16 storage of q, k and v that the
+# cache format imposes: the oracle fed bf16-rounded q, k, v (nothing else
+# rounded) reads 1.2e-2 (d=256 test layer), 1.9e-2 (Qwen2.5-7B, 512 rows)
+# and 1.4e-2 (Qwen3-8B, 512 rows) at the worst row, medians 0.7-1.3e-2; the
+# bound is twice the largest of them.
+ATT_ROW_TOL = 4e-2
 FFN_BRANCH_TOL = 2e-2
 F32_TOL = 1e-5      # relative, fp32 toy
 GAP_MIN = 1e-3      # routing sets must match where the k-th/(k+1)-th gap exceeds this
@@ -37,7 +42,9 @@ def spec_of(cfg: configs.LayerConfig, **kw) -> ref.LayerSpec:
 
 
 def widen(w_np):
-    return {k: synth.to_f32(v) for k, v in w_np.items()}
+    """Stored weights -> float64, once (the oracle would otherwise widen every
+    matrix at every call)."""
+    return {k: synth.to_f32(v).astype(np.float64) for k, v in w_np.items()}
 
 
 def rel_err(got, want) -> float:
@@ -62,15 +69,28 @@ def rounding_err(got, want, rel=2.0 ** -8, noise=1e-3) -> float:
 
 def attention_err(got, want, v) -> float:
     """Attention output against the oracle fed the same q, k, v, in units of
-    its rounding bound. The kernel rounds each probability p to bf16 before
-    the P*V product (relative error <= 2^-9) and divides by the unrounded sum,
-    so |o - o_ref| <= 2^-9 * sum_u p_u |v_u| / sum_u p_u <= 2^-9 * max|v|; the
-    allowance is twice that plus fp32 noise. <= 1 passes."""
+    its rounding bound. The kernels round each probability p to bf16 (relative
+    error <= 2^-9) and normalise by the sum of the rounded values, so the
+    weights w~ = p~ / sum p~ differ from w = p / sum p by at most 2 * 2^-9 * w
+    and |o - o_ref| = |sum (w~ - w) v| <= 2^-8 * max|v|; the allowance is twice
+    that plus fp32 noise. <= 1 passes."""
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
     rms = float(np.sqrt(np.mean(want * want)))
-    allow = 2.0 ** -8 * float(np.max(np.abs(v))) + 1e-4 * rms
+    allow = 2.0 ** -7 * float(np.max(np.abs(v))) + 1e-4 * rms
     return float(np.max(np.abs(got - want))) / allow
+
+
+def rowwise_err(got, want) -> float:
+    """Largest over rows (leading axes flattened) of max|got - want| in the row
+    over RMS(want) of the same row."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    d = got.shape[-1]
+    g = got.reshape(-1, d)
+    w = want.reshape(-1, d)
+    rms = np.sqrt(np.mean(w * w, axis=1))
+    return float(np.max(np.max(np.abs(g - w), axis=1) / np.maximum(rms, 1e-30)))
 
 
 def branch_err(y_bf16, r, f_ref) -> float:
@@ -105,7 +125,7 @@ def small_moe_cfg(**kw) -> configs.LayerConfig:
 
 @functools.lru_cache(maxsize=4)
 def weights_for(cfg: configs.LayerConfig, seed: int):
-    """(stored numpy weights, widened fp32 weights)."""
+    """(stored numpy weights, weights widened to float64)."""
     w = synth.make_weights(cfg, seed)
     return w, widen(w)
 
@@ -139,3 +159,39 @@ def routing_mismatch(idx_gpu, logits_ref, k, gap_min=GAP_MIN):
     check = gap > gap_min
     bad = np.nonzero(check & np.any(want != got, axis=-1))[0]
     return bad, int(check.sum())
+
+
+def oracle_gaps(logits_ref, k) -> np.ndarray:
+    """The oracle's k-th minus (k+1)-th largest logit per token."""
+    l = np.asarray(logits_ref, np.float64)
+    if l.shape[-1] <= k:
+        return np.full(l.shape[0], np.inf)
+    srt = -np.sort(-l, axis=-1)
+    return srt[:, k - 1] - srt[:, k]
+
+
+def moe_rerouted(o, logits_gpu, w, spec):
+    """Whole-layer MoE rows: the bf16 roundings upstream of the router move
+    the GPU's logits by ~1e-3 from the oracle's, so a token whose k-th/(k+1)-th
+    gap is that small may select another expert set; its FFN output is then a
+    different (equally valid) sum. For every such token this returns the
+    oracle's own FFN output for the GPU's selection (the oracle's z, its gate
+    weights over the oracle's logits at those experts), so every row can be
+    compared. o: the oracle's layer outputs flattened to [N, ...] ("z", "f",
+    "logits", "idx"). Returns (f [N, d], flipped [N] bool)."""
+    k = spec.top_k
+    lg = np.asarray(logits_gpu, np.float64).reshape(-1, spec.n_experts)
+    idx_g = ref.topk_select(lg, k)
+    flipped = np.any(np.sort(idx_g, -1) != np.sort(np.asarray(o["idx"]).reshape(-1, k), -1), -1)
+    f = np.array(o["f"], np.float64).reshape(lg.shape[0], -1)
+    z = np.asarray(o["z"], np.float64).reshape(lg.shape[0], -1)
+    lr = np.asarray(o["logits"], np.float64).reshape(lg.shape[0], -1)
+    for t in np.nonzero(flipped)[0]:
+        wts = ref.gate_weights(lr[t:t + 1], idx_g[t:t + 1], spec.norm_topk_prob)[0]
+        acc = np.zeros(f.shape[1])
+        for i in range(k):
+            e = int(idx_g[t, i])
+            acc = acc + wts[i] * ref.swiglu_ffn(z[t:t + 1], w["we_gate"][e], w["we_up"][e],
+                                                w["we_down"][e])[0]
+        f[t] = acc
+    return f, flipped

@@ -78,7 +78,8 @@ def test_create_rejects_bad_configs_on_host(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(n_experts=20, top_k=2), b.QL_EUNSUPPORTED),
+    (dict(n_experts=-1, top_k=0), b.QL_EINVAL),
+    (dict(n_experts=8, top_k=9), b.QL_EINVAL),
     (dict(n_experts=16, top_k=0), b.QL_EINVAL),
     (dict(n_experts=16, top_k=17), b.QL_EINVAL),
     (dict(n_experts=512, top_k=8), b.QL_EUNSUPPORTED),

@@ -522,9 +522,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pv = exp2f(sc[h][r] - m_new);
-        ps += pv;
-        pf[4 * h + r] = (bf16)pv;
+        // the sum takes the rounded weights P*V is formed with, so the
+        // normalised weights sum to one
+        const bf16 pb = (bf16)exp2f(sc[h][r] - m_new);
+        ps += (float)pb;
+        pf[4 * h + r] = pb;
       }
     l_run = l_run * alpha + ps;
     if (__any(alpha != 1.f)) {

@@ -228,9 +228,10 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[t][r], p.scale_log2, -m_run));
-          lsum += pv;
-          pf[2 * t + (r >> 3)][r & 7] = (bf16)pv;
+          // the sum takes the rounded weights P*V is formed with
+          const bf16 pb = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][r], p.scale_log2, -m_run));
+          lsum += (float)pb;
+          pf[2 * t + (r >> 3)][r & 7] = pb;
         }
       l_run += lsum;
       // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]; k-step u covers keys

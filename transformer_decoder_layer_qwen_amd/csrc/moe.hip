@@ -61,7 +61,12 @@ __global__ __launch_bounds__(kRW * 64) void router_logits_kernel(const RouterArg
   const bool tv = tok < p.N;
   const int kw = p.d / kRW;  // K per wave (a multiple of 32 KU)
   const float* zr = p.zf + (size_t)(tv ? tok : 0) * p.d + wave * kw + 8 * grp;
-  const bf16* wr = p.wr + (size_t)(e0 + col) * p.d + wave * kw + 8 * grp;
+  // expert rows past E (a last, part-filled expert tile) re-read row E - 1
+  // and are never stored
+  const bf16* wr[MT];
+#pragma unroll
+  for (int et = 0; et < MT; ++et)
+    wr[et] = p.wr + (size_t)min(e0 + 16 * et + col, p.E - 1) * p.d + wave * kw + 8 * grp;
 
   f32x4 acc[MT];
 #pragma unroll
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(kRW * 64) void router_logits_kernel(const RouterArg
       z[u][0] = *reinterpret_cast<const f32x4*>(zr + k + 32 * u);
       z[u][1] = *reinterpret_cast<const f32x4*>(zr + k + 32 * u + 4);
 #pragma unroll
-      for (int et = 0; et < MT; ++et) wf[u][et] = load_bf16x8(wr + (size_t)et * 16 * p.d + k + 32 * u);
+      for (int et = 0; et < MT; ++et) wf[u][et] = load_bf16x8(wr[et] + k + 32 * u);
     }
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(kRW * 64) void router_logits_kernel(const RouterArg
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kHalf; ++w) v += part[w][e * kEP + tl];
-    if (t0 + tl < p.N) p.logits[(size_t)(t0 + tl) * p.E + e0 + e] = v;
+    if (t0 + tl < p.N && e0 + e < p.E) p.logits[(size_t)(t0 + tl) * p.E + e0 + e] = v;
   }
 }
 
@@ -145,8 +150,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const RouterArgs p) {
     if (e < E) {
       x = p.logits[(size_t)t * E + e];
       x = x == x ? x : -INFINITY;
-      row[wave][e] = x;
     }
+    // entries up to the next multiple of 4 are read by the rank loop below:
+    // -inf there never counts as a greater logit
+    if (e < ((E + 3) & ~3)) row[wave][e] = x;
     v[j] = x;
   }
   __builtin_amdgcn_wave_barrier();
@@ -384,9 +391,9 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const CombineArgs p, c
 
 hipError_t ql_router_topk(const RouterArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  if (!a.logits || a.E % 16 || a.E > kMaxExperts || a.d % (32 * kRW)) return hipErrorInvalidValue;
+  if (!a.logits || a.E < 1 || a.E > kMaxExperts || a.d % (32 * kRW)) return hipErrorInvalidValue;
   const int ntb = (a.N + kTok - 1) / kTok;
-  const int et = a.E / 16;
+  const int et = (a.E + 15) / 16;
   // expert tiles per block: all of them when token blocks alone fill the
   // chip (z rows read once), else one (more blocks, one round of loads each;
   // the expert groups of a token block share its z rows through one L2)

@@ -65,7 +65,8 @@ struct ql_handle {
   float* part_o;
   float* part_ml;
   float* inv_rms;   // [rows] RMSNorm1 1/rms handed from the QKV GEMV to attention
-  void* g2part;     // split-K partial tiles of the prefill GEMMs
+  void* g2part;     // split-K / stream-K partial tiles of the MFMA GEMMs
+  size_t g2part_bytes;
   bool attn_hilo;   // the attention buffer holds a [hi | lo] bf16 pair (prefill)
   double* rope_omega;  // [head_dim / 2] RoPE frequencies
   float* logits;
@@ -137,8 +138,8 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
   const int G = c->n_q_heads / c->n_kv_heads;
   if (c->n_experts > 0) {
     if (c->dtype != QL_BF16) return fail(QL_EUNSUPPORTED, "MoE layers need dtype QL_BF16");
-    if (c->n_experts % 16 || c->n_experts > kMaxExperts)
-      return fail(QL_EUNSUPPORTED, "n_experts must be a multiple of 16 and <= %d", kMaxExperts);
+    if (c->n_experts > kMaxExperts)
+      return fail(QL_EUNSUPPORTED, "n_experts must be <= %d", kMaxExperts);
     if (c->top_k < 1 || c->top_k > std::min(c->n_experts, kMaxTopK))
       return fail(QL_EINVAL, "top_k must be in [1, min(n_experts, %d)]", kMaxTopK);
     if (!w->w_router || !w->we_gate || !w->we_up || !w->we_down)
@@ -171,24 +172,42 @@ int gemm2_splits(int M, int b_rows, int K) {
   int sp = std::max(1, kGemmTargetBlocks / std::max(tiles, 1));
   return std::max(1, std::min(sp, K / 512));
 }
-// Partial-tile bytes: the four dense GEMMs at the largest prefill M, and at
-// every decode batch size that takes the MFMA tiles.
-size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M) {
+// Partial-tile bytes one call of M rows needs: the pair-input QKV and O
+// GEMMs and the two dense FFN GEMMs (prefill: the split-K plans; decode with
+// rows past the VALU GEMV: the stream-K cut). The bytes are not monotone in M
+// (fewer row tiles can mean more splits), so the workspace takes the maximum
+// over every M a handle accepts.
+size_t gemm2_call_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M, bool decode) {
+  if (M <= 0) return 0;
   size_t b = 0;
-  b = std::max(b, ql_gemm2_pair_part_bytes(M, qkv_dim, c.d));
-  b = std::max(b, ql_gemm2_pair_part_bytes(M, c.d, q_dim));
-  if (c.n_experts == 0) {
-    b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, c.d)));
-    b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, c.ffn_dim)));
-  }
-  for (int B = kGemvMaxRows + 1; B <= c.max_batch; ++B) {
-    b = std::max(b, ql_gemm2_decode_part_bytes(B, qkv_dim, c.d, true));
-    b = std::max(b, ql_gemm2_decode_part_bytes(B, c.d, q_dim, true));
+  if (!decode) {
+    b = std::max(b, ql_gemm2_pair_part_bytes(M, qkv_dim, c.d));
+    b = std::max(b, ql_gemm2_pair_part_bytes(M, c.d, q_dim));
     if (c.n_experts == 0) {
-      b = std::max(b, ql_gemm2_decode_part_bytes(B, 2 * c.ffn_dim, c.d, false));
-      b = std::max(b, ql_gemm2_decode_part_bytes(B, c.d, c.ffn_dim, false));
+      b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, c.d)));
+      b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, c.ffn_dim)));
     }
+    return b;
   }
+  const bool gemv_attn = M <= kGemvMaxRows && ql_gemv_ok(M, qkv_dim, c.d) && ql_gemv_ok(M, c.d, q_dim);
+  if (!gemv_attn) {
+    b = std::max(b, ql_gemm2_decode_part_bytes(M, qkv_dim, c.d, true));
+    b = std::max(b, ql_gemm2_decode_part_bytes(M, c.d, q_dim, true));
+  }
+  const bool gemv_ffn = M <= kGemvMaxRows && ql_gemv_ok(M, c.ffn_dim, c.d) &&
+                        ql_gemv_ok(M, c.d, c.ffn_dim);
+  if (c.n_experts == 0 && !gemv_ffn) {
+    b = std::max(b, ql_gemm2_decode_part_bytes(M, 2 * c.ffn_dim, c.d, false));
+    b = std::max(b, ql_gemm2_decode_part_bytes(M, c.d, c.ffn_dim, false));
+  }
+  return b;
+}
+size_t gemm2_part_bytes(const ql_config& c, int q_dim, int qkv_dim) {
+  size_t b = 0;
+  for (int M = 1; M <= c.max_tokens; ++M)
+    b = std::max(b, gemm2_call_part_bytes(c, q_dim, qkv_dim, M, false));
+  for (int M = 1; M <= c.max_batch; ++M)
+    b = std::max(b, gemm2_call_part_bytes(c, q_dim, qkv_dim, M, true));
   return b;
 }
 
@@ -245,9 +264,8 @@ size_t layout(ql_handle* h, char* base) {
   h->part_ml = k.take<float>(slots * c.n_q_heads * 2 * 4);
   h->rope_omega = k.take<double>((size_t)std::max(c.head_dim / 2, 1) * 8);
   h->inv_rms = k.take<float>(N * 4);
-  h->g2part = c.dtype == QL_BF16 ? k.take<void>(gemm2_part_bytes(c, h->q_dim, h->qkv_dim,
-                                                                 std::max(c.max_tokens, 0)))
-                                 : nullptr;
+  if (c.dtype == QL_BF16 && !base) h->g2part_bytes = gemm2_part_bytes(c, h->q_dim, h->qkv_dim);
+  h->g2part = c.dtype == QL_BF16 ? k.take<void>(h->g2part_bytes) : nullptr;
   if (c.n_experts > 0) {
     const size_t E = c.n_experts, K = c.top_k, NK = N * K;
     const size_t nblk = (N + 255) / 256;
@@ -419,6 +437,9 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
   const int N = B * S;
+  if (gemm2_call_part_bytes(c, h->q_dim, h->qkv_dim, N, false) > h->g2part_bytes)
+    return fail(QL_EUNSUPPORTED, "prefill: %d rows need more GEMM partial space than the handle holds",
+                N);
   bf16* xhat = static_cast<bf16*>(h->xhat);  // [N, 2d]: hi | lo
   QL_STAGE(h, QL_STAGE_RMSNORM1, s,
            QL_HIP(ql_rmsnorm_bf16_to_hilo(x, static_cast<const bf16*>(w.ln1_g), xhat, N, c.d,
@@ -479,6 +500,9 @@ ql_status decode_bf16(ql_handle* h, const bf16* x, int B, const int* cache_len, 
   const ql_weights& w = h->w;
   const bool gemv = B <= kGemvMaxRows && ql_gemv_ok(B, h->qkv_dim, c.d) &&
                     ql_gemv_ok(B, c.d, h->q_dim);
+  if (gemm2_call_part_bytes(c, h->q_dim, h->qkv_dim, B, true) > h->g2part_bytes)
+    return fail(QL_EUNSUPPORTED, "decode: %d rows need more GEMM partial space than the handle holds",
+                B);
   const bf16* g1 = static_cast<const bf16*>(w.ln1_g);
   const bf16* wq = static_cast<const bf16*>(w.wq);
   const bf16* wk = static_cast<const bf16*>(w.wk);
