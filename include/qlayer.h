@@ -29,8 +29,9 @@
  *   fp32 arithmetic, one round-to-nearest-even rounding when a bf16 tensor is
  *   stored; the residual stream between the two halves, the RMSNorm1 output
  *   and the attention output are kept in fp32 (the last two enter their bf16
- *   MFMA projections as a bf16 hi + lo pair). QL_F32 -> fp32 storage and
- *   arithmetic (small shapes only, generic kernels).
+ *   MFMA projections as a bf16 hi + lo pair), and so are, in a dense
+ *   prefill, the RMSNorm2 output and the SwiGLU hidden. QL_F32 -> fp32
+ *   storage and arithmetic (small shapes only, generic kernels).
  * - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) with
  *   no host synchronisation and no device-to-host copy. Argument errors
  *   return before anything is enqueued. A failed launch returns QL_EHIP;
@@ -184,8 +185,10 @@ ql_status qlayer_moe_ffn(ql_handle* h, const void* r, int N, void* y, int* topk_
  *   q      [N, Hq*dh]  dtype   queries after QK-norm and RoPE
  *   attn   [N, Hq*dh]  fp32    attention output, heads concatenated (before W_O)
  *   r      [N, d]      fp32    residual stream after the attention half
- *   z      [N, d]      dtype   RMSNorm2(r)
- *   h      [N, f]      dtype   dense SwiGLU hidden SiLU(gate)*up (dense only)
+ *   z      [N, d]      fp32    RMSNorm2(r) as the FFN's GEMMs see it (the
+ *                              hi + lo of a pair, or the stored value widened)
+ *   h      [N, f]      fp32    dense SwiGLU hidden SiLU(gate)*up, likewise
+ *                              (dense only)
  *   logits [N, E]      fp32    router logits (MoE only)
  * qlayer_moe_ffn fills the z and logits taps for its N rows.
  * Passing NULL (or a struct of NULLs) turns taps off. */

@@ -23,6 +23,12 @@ BF16_TOL = 2e-2     # max|err| <= 2e-2 * RMS(output) for bf16 paths (the layer o
 # bound is twice the largest of them.
 ATT_ROW_TOL = 4e-2
 FFN_BRANCH_TOL = 2e-2
+# The MoE FFN branch is small beside the residual (RMS 0.14 against RMS(Y)
+# 1.0 at Qwen3-30B-A3B) and passes three bf16 stores of its own: z (the
+# experts' input), h and each expert's output (kept in slot order before the
+# weighted sum). The oracle with exactly those roundings and nothing else, on
+# identical R, reads 2.6e-2 over 4096 tokens; the bound is about twice that.
+MOE_BRANCH_TOL = 5e-2
 F32_TOL = 1e-5      # relative, fp32 toy
 GAP_MIN = 1e-3      # routing sets must match where the k-th/(k+1)-th gap exceeds this
 

@@ -65,6 +65,7 @@ struct G2Args {
   float* out_f32;
   bf16* out_bf16;
   int ldo;
+  int out_lo;  // SWIGLU: > 0 stores h as a [hi | lo] pair, lo at + out_lo elements
   const bf16* bias;
   const bf16* bias2;
   const bf16* bias3;
@@ -159,6 +160,21 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
   } else if (!DEC || (t >= 0 && t < p.T_max)) {
     bf16* cache = part == 1 ? p.k_cache : p.v_cache;
     store_bf16x8(cache + (((size_t)b * p.T_max + t) * p.n_kv_heads + head) * 128 + d0, pack8(v));
+  }
+}
+
+// SwiGLU hidden values of columns [col, col + 8) of `row`: bf16, or the
+// [hi | lo] pair (hi = RNE(h), lo = RNE(h - hi)) that keeps h to about 16
+// significant bits for the down projection.
+QL_DEV void store_h(const G2Args& p, size_t row, int col, const float (&h)[8]) {
+  bf16* o = p.out_bf16 + row * p.ldo + col;
+  const bf16x8 hi = pack8(h);
+  store_bf16x8(o, hi);
+  if (p.out_lo > 0) {
+    float lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lo[e] = h[e] - (float)hi[e];
+    store_bf16x8(o + p.out_lo, pack8(lo));
   }
 }
 
@@ -461,7 +477,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
         float hv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) hv[e] = silu_f32(g[e]) * u[e];
-        store_bf16x8(p.out_bf16 + (size_t)(m0 + rbase + r) * p.ldo + n0 + seg * 8, pack8(hv));
+        store_h(p, (size_t)(m0 + rbase + r), n0 + seg * 8, hv);
       }
     } else {
       const int seg = tid & 31;
@@ -854,7 +870,7 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
     float h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = silu_f32(v[e]) * v[e + 8];
-    store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + col, pack8(h));
+    store_h(p, (size_t)row, col, h);
   } else {
     float (&w8)[8] = *reinterpret_cast<float (*)[8]>(v);
     if constexpr (MODE == G2_BIAS) {
@@ -1140,8 +1156,9 @@ hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K
 
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
                               const float* resid, bf16* out, bool rows128, int splits, void* part,
-                              hipStream_t s) {
-  G2Args a = base(A, M, K, W, K, splits, part);
+                              hipStream_t s, bool pair_in) {
+  if (pair_in && rows128) return hipErrorInvalidValue;
+  G2Args a = base(A, M, pair_in ? 2 * K : K, W, K, splits, part);
   a.resid_f32 = resid;
   a.ldr = N;
   a.out_bf16 = out;
@@ -1151,11 +1168,14 @@ hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
 }
 
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                           bf16* out, bool rows128, int splits, void* part, hipStream_t s) {
-  G2Args a = base(A, M, K, Wg, K, splits, part);
+                           bf16* out, bool rows128, int splits, void* part, hipStream_t s,
+                           bool pair) {
+  if (pair && rows128) return hipErrorInvalidValue;
+  G2Args a = base(A, M, pair ? 2 * K : K, Wg, K, splits, part);
   a.B2 = Wu;
   a.out_bf16 = out;
-  a.ldo = F;
+  a.ldo = pair ? 2 * F : F;
+  a.out_lo = pair ? F : 0;
   a.tiles_n = F / (BN / 2);
   return run<G2_SWIGLU>(a, rows128 ? decode_shape(M, false) : T256, s);
 }

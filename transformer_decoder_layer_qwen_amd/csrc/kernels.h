@@ -21,6 +21,11 @@ hipError_t ql_rmsnorm_bf16_to_hilo(const bf16* x, const bf16* gamma, bf16* out, 
 hipError_t ql_hilo_to_f32(const bf16* hl, int rows, int cols, float* out, hipStream_t s);
 hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, float* out_f32,
                                  int rows, int d, float eps, hipStream_t s);
+// fp32 rows -> normalised rows as a bf16 pair per row: [hi (d) | lo (d)]
+hipError_t ql_rmsnorm_f32_to_hilo(const float* x, const bf16* gamma, bf16* out, int rows, int d,
+                                  float eps, hipStream_t s);
+// bf16 -> fp32, n elements
+hipError_t ql_bf16_to_f32(const bf16* x, size_t n, float* out, hipStream_t s);
 hipError_t ql_rmsnorm_f32(const float* x, const float* gamma, float* out, int rows, int d,
                           float eps, hipStream_t s);
 
@@ -72,11 +77,14 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
                               const bf16* resid, float* out, bool rows128, int splits, void* part,
                               hipStream_t s);
+// pair_in / pair (prefill tiles only): A is a [hi | lo] pair [M, 2K] read
+// over a doubled K; SwiGLU also stores h as a pair [M, 2F] (hi | lo).
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
                               const float* resid, bf16* out, bool rows128, int splits, void* part,
-                              hipStream_t s);
+                              hipStream_t s, bool pair_in = false);
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
-                           bf16* out, bool rows128, int splits, void* part, hipStream_t s);
+                           bf16* out, bool rows128, int splits, void* part, hipStream_t s,
+                           bool pair = false);
 // MoE expert GEMMs on 256-row expert tiles (the permute's tile table built
 // with bm = 256; max_tiles bounds *num_tiles; mf % 128 == 0, d % 256 == 0)
 hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,

@@ -68,6 +68,7 @@ struct ql_handle {
   void* g2part;     // split-K / stream-K partial tiles of the MFMA GEMMs
   size_t g2part_bytes;
   bool attn_hilo;   // the attention buffer holds a [hi | lo] bf16 pair (prefill)
+  bool ffn_pair;    // the last call kept RMSNorm2's output (in xhat) and h as [hi | lo] pairs
   double* rope_omega;  // [head_dim / 2] RoPE frequencies
   float* logits;
   int* idx;
@@ -183,9 +184,9 @@ size_t gemm2_call_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M, 
   if (!decode) {
     b = std::max(b, ql_gemm2_pair_part_bytes(M, qkv_dim, c.d));
     b = std::max(b, ql_gemm2_pair_part_bytes(M, c.d, q_dim));
-    if (c.n_experts == 0) {
-      b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, c.d)));
-      b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, c.ffn_dim)));
+    if (c.n_experts == 0) {  // [hi | lo] pair inputs: doubled K
+      b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, 2 * c.d)));
+      b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, 2 * c.ffn_dim)));
     }
     return b;
   }
@@ -286,7 +287,7 @@ size_t layout(ql_handle* h, char* base) {
     h->hm = k.take<void>(NK * c.ffn_dim * 2);
     h->out_slot = k.take<bf16>(NK * c.d * 2);
   } else {
-    h->h = k.take<void>(N * c.ffn_dim * es);
+    h->h = k.take<void>(N * c.ffn_dim * es * (c.dtype == QL_BF16 ? 2 : 1));  // bf16: [hi | lo]
   }
   return k.off;
 }
@@ -296,6 +297,7 @@ float scale_log2(int dh) { return 1.4426950408889634f / std::sqrt((float)dh); }
 ql_status copy_taps(ql_handle* h, int N, hipStream_t s) {
   const ql_config& c = h->cfg;
   const size_t es = h->es;
+  const bool f32 = c.dtype == QL_F32;
   if (h->taps.q)
     QL_HIP(hipMemcpyAsync(h->taps.q, h->q, (size_t)N * h->q_dim * es, hipMemcpyDeviceToDevice, s));
   if (h->taps.attn) {
@@ -308,11 +310,27 @@ ql_status copy_taps(ql_handle* h, int N, hipStream_t s) {
   }
   if (h->taps.r)
     QL_HIP(hipMemcpyAsync(h->taps.r, h->r, (size_t)N * c.d * 4, hipMemcpyDeviceToDevice, s));
-  if (h->taps.z)
-    QL_HIP(hipMemcpyAsync(h->taps.z, h->z, (size_t)N * c.d * es, hipMemcpyDeviceToDevice, s));
-  if (h->taps.h && c.n_experts == 0)
-    QL_HIP(hipMemcpyAsync(h->taps.h, h->h, (size_t)N * c.ffn_dim * es, hipMemcpyDeviceToDevice,
-                          s));
+  // z and h taps are fp32: the pair's hi + lo, or the stored value widened
+  if (h->taps.z) {
+    float* tz = static_cast<float*>(h->taps.z);
+    if (h->ffn_pair)
+      QL_HIP(ql_hilo_to_f32(static_cast<const bf16*>(h->xhat), N, c.d, tz, s));
+    else if (c.n_experts > 0)
+      QL_HIP(hipMemcpyAsync(tz, h->zf, (size_t)N * c.d * 4, hipMemcpyDeviceToDevice, s));
+    else if (f32)
+      QL_HIP(hipMemcpyAsync(tz, h->z, (size_t)N * c.d * 4, hipMemcpyDeviceToDevice, s));
+    else
+      QL_HIP(ql_bf16_to_f32(static_cast<const bf16*>(h->z), (size_t)N * c.d, tz, s));
+  }
+  if (h->taps.h && c.n_experts == 0) {
+    float* th = static_cast<float*>(h->taps.h);
+    if (h->ffn_pair)
+      QL_HIP(ql_hilo_to_f32(static_cast<const bf16*>(h->h), N, c.ffn_dim, th, s));
+    else if (f32)
+      QL_HIP(hipMemcpyAsync(th, h->h, (size_t)N * c.ffn_dim * 4, hipMemcpyDeviceToDevice, s));
+    else
+      QL_HIP(ql_bf16_to_f32(static_cast<const bf16*>(h->h), (size_t)N * c.ffn_dim, th, s));
+  }
   if (h->taps.logits && c.n_experts > 0)
     QL_HIP(hipMemcpyAsync(h->taps.logits, h->logits, (size_t)N * c.n_experts * 4,
                           hipMemcpyDeviceToDevice, s));
@@ -399,6 +417,27 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
   const ql_weights& w = h->w;
   bf16* z = static_cast<bf16*>(h->z);
   const bf16* g2 = static_cast<const bf16*>(w.ln2_g);
+  h->ffn_pair = false;
+  if (!decode && c.n_experts == 0) {
+    // Prefill, dense: RMSNorm2's output and the SwiGLU hidden stay fp32 as
+    // [hi | lo] bf16 pairs (the x-hat buffer is free once Q/K/V exist) and
+    // enter gate/up and down over a doubled K.
+    bf16* z2 = static_cast<bf16*>(h->xhat);
+    bf16* hh = static_cast<bf16*>(h->h);
+    QL_STAGE(h, QL_STAGE_RMSNORM2, s,
+             QL_HIP(ql_rmsnorm_f32_to_hilo(h->r, g2, z2, N, c.d, c.rms_eps, s)));
+    const int sgu = gemm2_splits(N, 2 * c.ffn_dim, 2 * c.d);
+    const int sdn = gemm2_splits(N, c.d, 2 * c.ffn_dim);
+    QL_STAGE(h, QL_STAGE_GATE_UP, s,
+             QL_HIP(ql_gemm2_swiglu(z2, N, static_cast<const bf16*>(w.w_gate),
+                                    static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, false,
+                                    sgu, h->g2part, s, true)));
+    QL_STAGE(h, QL_STAGE_DOWN, s,
+             QL_HIP(ql_gemm2_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d, c.ffn_dim,
+                                       h->r, y, false, sdn, h->g2part, s, true)));
+    h->ffn_pair = true;
+    return QL_OK;
+  }
   // few rows on the dense path: RMSNorm2 rides inside the gate/up projection
   // (z is then only formed when a tap asks for it)
   const bool gemv = decode && c.n_experts == 0 && N <= kGemvMaxRows &&
@@ -419,14 +458,12 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
              QL_HIP(ql_gemv_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
     return QL_OK;
   }
-  // (decode tiles cut their work evenly over the CUs themselves)
-  const int sgu = decode ? 1 : gemm2_splits(N, 2 * c.ffn_dim, c.d);
-  const int sdn = decode ? 1 : gemm2_splits(N, c.d, c.ffn_dim);
+  // decode tiles (more rows than the GEMV takes) cut their work evenly over
+  // the CUs themselves
   QL_STAGE(h, QL_STAGE_GATE_UP, s,
-           QL_HIP(ql_gemm2_swiglu(z, N, wg, wu, c.ffn_dim, c.d, hh, decode, sgu, h->g2part, s)));
+           QL_HIP(ql_gemm2_swiglu(z, N, wg, wu, c.ffn_dim, c.d, hh, true, 1, h->g2part, s)));
   QL_STAGE(h, QL_STAGE_DOWN, s,
-           QL_HIP(ql_gemm2_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, decode, sdn, h->g2part,
-                                     s)));
+           QL_HIP(ql_gemm2_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, true, 1, h->g2part, s)));
   return QL_OK;
 }
 
@@ -595,6 +632,7 @@ ql_status layer_f32(ql_handle* h, const float* x, int N, bool decode, int B, int
                     const int* cache_len, int pos_offset, void* kc, void* vc, int T_max, float* y,
                     hipStream_t s) {
   h->attn_hilo = false;
+  h->ffn_pair = false;
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
   float* xhat = static_cast<float*>(h->xhat);
@@ -830,7 +868,7 @@ ql_status qlayer_moe_ffn(ql_handle* h, const void* r, int N, void* y, int* topk_
     QL_HIP(hipMemcpyAsync(h->taps.logits, h->logits, (size_t)N * c.n_experts * 4,
                           hipMemcpyDeviceToDevice, s));
   if (h->taps.z)
-    QL_HIP(hipMemcpyAsync(h->taps.z, h->z, (size_t)N * c.d * 2, hipMemcpyDeviceToDevice, s));
+    QL_HIP(hipMemcpyAsync(h->taps.z, h->zf, (size_t)N * c.d * 4, hipMemcpyDeviceToDevice, s));
   return QL_OK;
 }
 

@@ -180,6 +180,25 @@ hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, f
                                  int rows, int d, float eps, hipStream_t s) {
   return launch<float, bf16, bf16>(x, gamma, out, out_f32, rows, d, eps, s);
 }
+hipError_t ql_rmsnorm_f32_to_hilo(const float* x, const bf16* gamma, bf16* out, int rows, int d,
+                                  float eps, hipStream_t s) {
+  return launch<float, bf16, bf16, true>(x, gamma, out, nullptr, rows, d, eps, s);
+}
+
+namespace {
+__global__ __launch_bounds__(256) void bf16_to_f32_kernel(const bf16* __restrict__ x, size_t n,
+                                                          float* __restrict__ out) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (float)x[i];
+}
+}  // namespace
+
+hipError_t ql_bf16_to_f32(const bf16* x, size_t n, float* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, n,
+                     out);
+  return hipGetLastError();
+}
 hipError_t ql_rmsnorm_f32(const float* x, const float* gamma, float* out, int rows, int d,
                           float eps, hipStream_t s) {
   return launch<float, float, float>(x, gamma, out, nullptr, rows, d, eps, s);
