@@ -167,6 +167,26 @@ ql_status qlayer_decode(ql_handle* h, const void* x, int B, const int* cache_len
                         const int* cache_len_host, int pos_offset, void* k_cache,
                         void* v_cache, int T_max, void* y, void* stream);
 
+/* Largest workspace, in bytes, of a qlayer_decode_noalloc call. */
+#define QLAYER_NOALLOC_MAX_WORKSPACE (64u << 20)
+
+/* Decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and errors as qlayer_decode, with the config and
+ * weights passed directly instead of a handle. The workspace is a
+ * file-scope device array of QLAYER_NOALLOC_MAX_WORKSPACE bytes that every
+ * GPU the library runs on holds from module load until the process ends;
+ * no hipMalloc / hipFree or other allocating call is made. The array is
+ * laid out afresh for each call (cfg->max_tokens and cfg->max_batch are
+ * ignored; B is the call's size) and keeps the last call's contents.
+ * Calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (two streams, two threads) race and must be serialised by the
+ * caller. Errors: as qlayer_decode; QL_EUNSUPPORTED also when the call's
+ * workspace would exceed the array (the message gives the bytes needed). */
+ql_status qlayer_decode_noalloc(const ql_config* cfg, const ql_weights* w, const void* x, int B,
+                                const int* cache_len, const int* cache_len_host, int pos_offset,
+                                void* k_cache, void* v_cache, int T_max, void* y, void* stream);
+
 /* The sparse-MoE FFN half of a layer on N residual rows ("Qwen2.5-7B 结构拆解"
  * §10.2; "MoE 初步" Sparse MoE 架构详解):
  *     y = r + sum_{i<k} w_i * Expert_{idx_i}(RMSNorm2(r))

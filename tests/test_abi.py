@@ -113,3 +113,27 @@ def test_config_table_fits_the_bf16_limits():
         for wl in configs.WORKLOADS[cid]:
             if wl.kind == "decode":
                 assert wl.batch <= 128
+
+
+def test_noalloc_decode_rejects_on_the_host():
+    """Argument errors and a workspace beyond the static array return before
+    any HIP call (pointers are never dereferenced on these paths)."""
+    lib = b.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    lens_host = (ctypes.c_int * 2)(3, 3)
+    cfg = _cfg()
+    w = _weights()
+    out = ctypes.c_void_p(0x2000)
+    call = lambda c, B, lh=None, T=8, y=out: lib.qlayer_decode_noalloc(  # noqa: E731
+        ctypes.byref(c), ctypes.byref(w), fake, B, fake, lh, 0, fake, fake, T, y, None)
+    assert lib.qlayer_decode_noalloc(None, None, fake, 1, fake, None, 0, fake, fake, 8, fake,
+                                     None) == b.QL_EINVAL
+    assert call(cfg, 0) == b.QL_EINVAL
+    assert call(cfg, 2, T=0) == b.QL_EINVAL
+    assert call(cfg, 2, y=None) == b.QL_EINVAL
+    assert call(cfg, 2, y=fake) == b.QL_EINVAL               # y aliases x
+    assert call(cfg, 2, lh=ctypes.cast(lens_host, ctypes.c_void_p), T=3) == b.QL_ECACHE_FULL
+    assert call(_cfg(head_dim=64), 2) == b.QL_EUNSUPPORTED
+    big = _cfg(d=8192, n_q_heads=64, n_kv_heads=8, ffn_dim=65536)
+    assert call(big, 128) == b.QL_EUNSUPPORTED
+    assert "static" in b.qlayer_last_error()

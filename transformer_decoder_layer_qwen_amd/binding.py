@@ -26,8 +26,9 @@ STATUS_NAMES = {0: "QL_OK", -1: "QL_EINVAL", -2: "QL_EUNSUPPORTED", -3: "QL_ENOM
 
 # every function include/qlayer.h declares
 EXPORTS = ("qlayer_create", "qlayer_destroy", "qlayer_workspace_bytes", "qlayer_prefill",
-           "qlayer_decode", "qlayer_moe_ffn", "qlayer_set_taps", "qlayer_set_stage_events",
-           "qlayer_last_error", "qlayer_abi_version")
+           "qlayer_decode", "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
+           "qlayer_set_stage_events", "qlayer_last_error", "qlayer_abi_version")
+NOALLOC_MAX_WORKSPACE = 64 << 20
 
 # ql_stage
 STAGES = {"rmsnorm1": 1, "qkv": 2, "qkv_post": 3, "attention": 4, "o_proj": 5, "rmsnorm2": 6,
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qlayer_workspace_bytes.restype = ctypes.c_size_t
     lib.qlayer_prefill.argtypes = [vp, vp, ci, ci, ci, vp, vp, ci, vp, vp]
     lib.qlayer_decode.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, ci, vp, vp]
+    lib.qlayer_decode_noalloc.argtypes = [ctypes.POINTER(QlConfig), ctypes.POINTER(QlWeights), vp,
+                                          ci, vp, vp, ci, vp, vp, ci, vp, vp]
     lib.qlayer_moe_ffn.argtypes = [vp, vp, ci, vp, vp, vp, vp]
     lib.qlayer_set_taps.argtypes = [vp, ctypes.POINTER(QlTaps)]
     lib.qlayer_set_stage_events.argtypes = [vp, ci, vp, vp]
@@ -97,7 +100,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qlayer_last_error.argtypes = []
     lib.qlayer_abi_version.restype = ci
     for name in ("qlayer_create", "qlayer_destroy", "qlayer_prefill", "qlayer_decode",
-                 "qlayer_moe_ffn", "qlayer_set_taps", "qlayer_set_stage_events"):
+                 "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
+                 "qlayer_set_stage_events"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -142,6 +146,13 @@ def qlayer_decode(h, x, B, cache_len, cache_len_host, pos_offset, k_cache, v_cac
                   stream) -> None:
     _check(load_library().qlayer_decode(h, x, B, cache_len, cache_len_host, pos_offset, k_cache,
                                         v_cache, T_max, y, stream))
+
+
+def qlayer_decode_noalloc(cfg: QlConfig, w: QlWeights, x, B, cache_len, cache_len_host,
+                          pos_offset, k_cache, v_cache, T_max, y, stream) -> None:
+    _check(load_library().qlayer_decode_noalloc(ctypes.byref(cfg), ctypes.byref(w), x, B,
+                                                cache_len, cache_len_host, pos_offset, k_cache,
+                                                v_cache, T_max, y, stream))
 
 
 def qlayer_moe_ffn(h, r, N, y, topk_idx, topk_w, stream) -> None:
@@ -210,6 +221,7 @@ class QLayer:
                      dtype=QL_BF16 if cfg.dtype == "bf16" else QL_F32,
                      max_tokens=max_tokens, max_batch=max_batch)
         w = QlWeights(**{n: _ptr(weights.get(n)) for n in WEIGHT_FIELDS})
+        self.c_config, self.c_weights = c, w
         self.handle = qlayer_create(c, w)
         self.max_tokens, self.max_batch = max_tokens, max_batch
         self._taps = None

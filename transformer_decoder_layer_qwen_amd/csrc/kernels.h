@@ -239,3 +239,10 @@ struct CombineArgs {
 };
 hipError_t ql_moe_combine(const CombineArgs& a, const void* resid, int resid_is_f32,
                           hipStream_t s);
+
+// ---- allocation-free decode (noalloc.hip) ----
+// Device address of this device's file-scope workspace array
+// (QLAYER_NOALLOC_MAX_WORKSPACE bytes), looked up once per device.
+hipError_t ql_noalloc_scratch(void** ptr);
+// dst[0..n) = w[0..n) (n <= 64) by a kernel on `s`
+hipError_t ql_fill_rope_table(const double* w, int n, double* dst, hipStream_t s);

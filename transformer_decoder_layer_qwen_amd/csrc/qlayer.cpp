@@ -248,8 +248,11 @@ struct Carve {
   }
 };
 
-// Lays the workspace out (base == nullptr only measures it).
-size_t layout(ql_handle* h, char* base) {
+// Lays the workspace out (base == nullptr only measures it). exact_rows > 0
+// sizes the GEMM partials for a decode of exactly that many rows (the
+// allocation-free entry point lays its array out per call) instead of every
+// row count the handle accepts.
+size_t layout(ql_handle* h, char* base, int exact_rows = 0) {
   const ql_config& c = h->cfg;
   const size_t N = (size_t)h->rows;
   const size_t es = (size_t)h->es;
@@ -265,7 +268,10 @@ size_t layout(ql_handle* h, char* base) {
   h->part_ml = k.take<float>(slots * c.n_q_heads * 2 * 4);
   h->rope_omega = k.take<double>((size_t)std::max(c.head_dim / 2, 1) * 8);
   h->inv_rms = k.take<float>(N * 4);
-  if (c.dtype == QL_BF16 && !base) h->g2part_bytes = gemm2_part_bytes(c, h->q_dim, h->qkv_dim);
+  if (c.dtype == QL_BF16 && !base)
+    h->g2part_bytes = exact_rows > 0
+                          ? gemm2_call_part_bytes(c, h->q_dim, h->qkv_dim, exact_rows, true)
+                          : gemm2_part_bytes(c, h->q_dim, h->qkv_dim);
   h->g2part = c.dtype == QL_BF16 ? k.take<void>(h->g2part_bytes) : nullptr;
   if (c.n_experts > 0) {
     const size_t E = c.n_experts, K = c.top_k, NK = N * K;
@@ -712,6 +718,54 @@ ql_status layer_f32(ql_handle* h, const float* x, int N, bool decode, int B, int
   return QL_OK;
 }
 
+void init_dims(ql_handle* h, const ql_config* cfg, const ql_weights* w) {
+  h->cfg = *cfg;
+  h->w = *w;
+  h->es = cfg->dtype == QL_BF16 ? 2 : 4;
+  h->q_dim = cfg->n_q_heads * cfg->head_dim;
+  h->kv_dim = cfg->n_kv_heads * cfg->head_dim;
+  h->qkv_dim = h->q_dim + 2 * h->kv_dim;
+  h->G = cfg->n_q_heads / cfg->n_kv_heads;
+  h->rows = std::max(std::max(cfg->max_tokens, cfg->max_batch), 1);
+}
+
+// omega_i = theta^(-2i/dh), i < dh/2 ("推理系统 03" §6), in fp64 on the host
+std::vector<double> rope_table(const ql_config& c) {
+  std::vector<double> om(c.head_dim / 2);
+  for (int i = 0; i < c.head_dim / 2; ++i)
+    om[i] = std::pow((double)c.rope_theta, -2.0 * i / (double)c.head_dim);
+  return om;
+}
+
+ql_status check_decode_args(const void* x, int B, const int* cache_len, const int* cache_len_host,
+                            const void* k_cache, const void* v_cache, int T_max, const void* y) {
+  if (!x || !cache_len || !k_cache || !v_cache || !y)
+    return fail(QL_EINVAL, "decode: NULL argument");
+  if (B <= 0) return fail(QL_EINVAL, "decode: B must be positive");
+  if (T_max <= 0) return fail(QL_EINVAL, "decode: T_max must be positive");
+  if (x == y) return fail(QL_EINVAL, "decode: y must not alias x");
+  if (cache_len_host)
+    for (int b = 0; b < B; ++b)
+      if (cache_len_host[b] < 0 || cache_len_host[b] + 1 > T_max)
+        return fail(QL_ECACHE_FULL, "decode: cache_len[%d] = %d does not fit T_max = %d", b,
+                    cache_len_host[b], T_max);
+  return QL_OK;
+}
+
+ql_status run_decode(ql_handle* h, const void* x, int B, const int* cache_len, int pos_offset,
+                     void* k_cache, void* v_cache, int T_max, void* y, hipStream_t s) {
+  ql_status st;
+  if (h->cfg.dtype == QL_F32) {
+    st = layer_f32(h, static_cast<const float*>(x), B, true, B, 1, cache_len, pos_offset, k_cache,
+                   v_cache, T_max, static_cast<float*>(y), s);
+  } else {
+    st = decode_bf16(h, static_cast<const bf16*>(x), B, cache_len, pos_offset, k_cache, v_cache,
+                     T_max, static_cast<bf16*>(y), s);
+  }
+  if (st == QL_OK) st = copy_taps(h, B, s);
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -726,14 +780,7 @@ ql_status qlayer_create(const ql_config* cfg, const ql_weights* w, ql_handle** o
   ql_status st = validate(cfg, w);
   if (st != QL_OK) return st;
   ql_handle* h = new ql_handle();
-  h->cfg = *cfg;
-  h->w = *w;
-  h->es = cfg->dtype == QL_BF16 ? 2 : 4;
-  h->q_dim = cfg->n_q_heads * cfg->head_dim;
-  h->kv_dim = cfg->n_kv_heads * cfg->head_dim;
-  h->qkv_dim = h->q_dim + 2 * h->kv_dim;
-  h->G = cfg->n_q_heads / cfg->n_kv_heads;
-  h->rows = std::max(std::max(cfg->max_tokens, cfg->max_batch), 1);
+  init_dims(h, cfg, w);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) {
     delete h;
@@ -747,9 +794,7 @@ ql_status qlayer_create(const ql_config* cfg, const ql_weights* w, ql_handle** o
   }
   layout(h, h->ws);
   if (cfg->dtype == QL_BF16) {
-    std::vector<double> om(cfg->head_dim / 2);
-    for (int i = 0; i < cfg->head_dim / 2; ++i)
-      om[i] = std::pow((double)cfg->rope_theta, -2.0 * i / (double)cfg->head_dim);
+    const std::vector<double> om = rope_table(*cfg);
     e = hipMemcpy(h->rope_omega, om.data(), om.size() * sizeof(double), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(h->ws);  // the upload's error is the one reported
@@ -822,29 +867,46 @@ ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offs
 ql_status qlayer_decode(ql_handle* h, const void* x, int B, const int* cache_len,
                         const int* cache_len_host, int pos_offset, void* k_cache, void* v_cache,
                         int T_max, void* y, void* stream) {
-  if (!h || !x || !cache_len || !k_cache || !v_cache || !y)
-    return fail(QL_EINVAL, "decode: NULL argument");
-  if (B <= 0) return fail(QL_EINVAL, "decode: B must be positive");
+  if (!h) return fail(QL_EINVAL, "decode: NULL argument");
+  ql_status st = check_decode_args(x, B, cache_len, cache_len_host, k_cache, v_cache, T_max, y);
+  if (st != QL_OK) return st;
   if (B > h->cfg.max_batch)
     return fail(QL_EINVAL, "decode: B = %d exceeds max_batch %d", B, h->cfg.max_batch);
-  if (T_max <= 0) return fail(QL_EINVAL, "decode: T_max must be positive");
-  if (x == y) return fail(QL_EINVAL, "decode: y must not alias x");
-  if (cache_len_host)
-    for (int b = 0; b < B; ++b)
-      if (cache_len_host[b] < 0 || cache_len_host[b] + 1 > T_max)
-        return fail(QL_ECACHE_FULL, "decode: cache_len[%d] = %d does not fit T_max = %d", b,
-                    cache_len_host[b], T_max);
+  return run_decode(h, x, B, cache_len, pos_offset, k_cache, v_cache, T_max, y,
+                    static_cast<hipStream_t>(stream));
+}
+
+ql_status qlayer_decode_noalloc(const ql_config* cfg, const ql_weights* w, const void* x, int B,
+                                const int* cache_len, const int* cache_len_host, int pos_offset,
+                                void* k_cache, void* v_cache, int T_max, void* y, void* stream) {
+  if (!cfg || !w) return fail(QL_EINVAL, "decode_noalloc: config and weights must not be NULL");
+  ql_status st = check_decode_args(x, B, cache_len, cache_len_host, k_cache, v_cache, T_max, y);
+  if (st != QL_OK) return st;
+  ql_config c = *cfg;
+  c.max_tokens = 0;
+  c.max_batch = B;
+  st = validate(&c, w);
+  if (st != QL_OK) return st;
+  ql_handle h{};  // a handle on the stack over the file-scope array: nothing is allocated
+  init_dims(&h, &c, w);
+  const size_t need = layout(&h, nullptr, B);
+  if (need > (size_t)QLAYER_NOALLOC_MAX_WORKSPACE)
+    return fail(QL_EUNSUPPORTED,
+                "decode_noalloc: B = %d of this layer needs %zu bytes of workspace; the static "
+                "array holds %zu",
+                B, need, (size_t)QLAYER_NOALLOC_MAX_WORKSPACE);
+  void* base = nullptr;
+  QL_HIP(ql_noalloc_scratch(&base));
+  QL_HIP(hipGetDevice(&h.device));
+  h.ws = static_cast<char*>(base);
+  h.ws_bytes = need;
+  layout(&h, h.ws, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  ql_status st;
-  if (h->cfg.dtype == QL_F32) {
-    st = layer_f32(h, static_cast<const float*>(x), B, true, B, 1, cache_len, pos_offset, k_cache,
-                   v_cache, T_max, static_cast<float*>(y), s);
-  } else {
-    st = decode_bf16(h, static_cast<const bf16*>(x), B, cache_len, pos_offset, k_cache, v_cache,
-                     T_max, static_cast<bf16*>(y), s);
+  if (c.dtype == QL_BF16) {
+    const std::vector<double> om = rope_table(c);
+    QL_HIP(ql_fill_rope_table(om.data(), (int)om.size(), h.rope_omega, s));
   }
-  if (st == QL_OK) st = copy_taps(h, B, s);
-  return st;
+  return run_decode(&h, x, B, cache_len, pos_offset, k_cache, v_cache, T_max, y, s);
 }
 
 ql_status qlayer_moe_ffn(ql_handle* h, const void* r, int N, void* y, int* topk_idx,
