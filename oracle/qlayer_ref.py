@@ -33,6 +33,9 @@ Readings where the pages are silent or disagree:
   the selected logits; ``gate_weights_via_full_softmax`` is the [P1] route,
   kept to pin the two equal.
 * Top-k ties (not on the pages): descending logit, ties to the lower index.
+* The shared expert's gate row W_sg ([P1 §10.1]) is stored [1, d] like every
+  [out, in] weight; its sigmoid scales the shared SwiGLU's output, which is
+  added to the routed sum with no further normalisation ([P1 §10.2]).
 * epsilon = 1e-6 everywhere, QK-norm included (the only value printed, [P3 §1]).
 * QKV bias only (Qwen2.5, [P1 §11]); no O-projection bias.
 * Decode-cache rows are stored after QK-norm and RoPE ([P3 §12]) and are
@@ -62,6 +65,7 @@ class LayerSpec:
     n_experts: int = 0
     top_k: int = 0
     norm_topk_prob: bool = True
+    shared_ffn_dim: int = 0
     qkv_bias: bool = False
     qk_norm: bool = False
     eps: float = 1e-6
@@ -214,6 +218,14 @@ def silu(z) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
+def sigmoid(z) -> np.ndarray:
+    """sigmoid(z) = 1 / (1 + e^-z), the (0, 1) squashing that [P1 §07.1]
+    uses inside SiLU and [P1 §10.1] applies to the shared expert's gate."""
+    z = f64(z)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
 def swiglu_ffn(z, w_gate, w_up, w_down) -> np.ndarray:
     """F = (SiLU(z W_gate^T) * (z W_up^T)) W_down^T, no bias ([P3 §10];
     [P1 §07.1])."""
@@ -266,10 +278,21 @@ def gate_weights_via_full_softmax(logits, idx) -> np.ndarray:
     return p / np.sum(p, axis=-1, keepdims=True)
 
 
-def moe_ffn_output(z, w, top_k: int, norm_topk_prob: bool = True):
+def shared_expert(z, w):
+    """Qwen2's shared expert ([P1 §10.1]): an ordinary SwiGLU of width sf run
+    on every token, its whole output vector scaled by the token's own gate
+    g = sigmoid(z W_sg^T), W_sg a single row [1, d] without bias.
+    Returns (g * SwiGLU_shared(z) [N, d], g [N, 1])."""
+    g = sigmoid(linear(z, w["w_shared_gate"]))
+    return g * swiglu_ffn(z, w["ws_gate"], w["ws_up"], w["ws_down"]), g
+
+
+def moe_ffn_output(z, w, top_k: int, norm_topk_prob: bool = True, shared: bool = False):
     """MoE(z) = sum_i w_i Expert_{idx_i}(z), i over the k selected experts in
     rank order, a plain elementwise weighted sum ([P1 §10.2]; [P2 "MoE 的最终
-    输出"]). Each expert is a SwiGLU with its own gate/up/down.
+    输出"]). Each expert is a SwiGLU with its own gate/up/down. With
+    ``shared`` (Qwen2, [P1 §10.1-§10.2]) the gated shared expert is added
+    elementwise as the ninth term.
 
     z: [N, d]. Returns (F [N, d], idx [N, k], weights [N, k], logits [N, E]).
     """
@@ -290,6 +313,8 @@ def moe_ffn_output(z, w, top_k: int, norm_topk_prob: bool = True):
     F = np.zeros((N, d))
     for i in range(top_k):
         F = F + wts[:, i:i + 1] * per_rank[:, i, :]
+    if shared:
+        F = F + shared_expert(z, w)[0]
     return F, idx, wts, logits
 
 
@@ -297,7 +322,8 @@ def moe_ffn(r, w, spec: LayerSpec) -> Dict[str, np.ndarray]:
     """The MoE half of a layer: Y = R + MoE(RMSNorm2(R)) ([P1 §10, §10.2])."""
     r = f64(r)
     z = rmsnorm(r, w["ln2_g"], spec.eps)
-    F, idx, wts, logits = moe_ffn_output(z, w, spec.top_k, spec.norm_topk_prob)
+    F, idx, wts, logits = moe_ffn_output(z, w, spec.top_k, spec.norm_topk_prob,
+                                         spec.shared_ffn_dim > 0)
     return {"y": r + F, "z": z, "f": F, "idx": idx, "w": wts, "logits": logits}
 
 
@@ -307,7 +333,8 @@ def moe_ffn(r, w, spec: LayerSpec) -> Dict[str, np.ndarray]:
 
 def _ffn(z, w, spec: LayerSpec):
     if spec.n_experts:
-        F, idx, wts, logits = moe_ffn_output(z, w, spec.top_k, spec.norm_topk_prob)
+        F, idx, wts, logits = moe_ffn_output(z, w, spec.top_k, spec.norm_topk_prob,
+                                             spec.shared_ffn_dim > 0)
         return F, {"idx": idx, "w": wts, "logits": logits}
     h = swiglu_hidden(z, w["w_gate"], w["w_up"])
     return linear(h, w["w_down"]), {"h": h}

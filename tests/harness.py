@@ -41,7 +41,8 @@ def log(msg: str) -> None:
 def spec_of(cfg: configs.LayerConfig, **kw) -> ref.LayerSpec:
     s = dict(d=cfg.d, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
              head_dim=cfg.head_dim, ffn_dim=cfg.ffn_dim, n_experts=cfg.n_experts,
-             top_k=cfg.top_k, norm_topk_prob=cfg.norm_topk_prob, qkv_bias=cfg.qkv_bias,
+             top_k=cfg.top_k, norm_topk_prob=cfg.norm_topk_prob,
+             shared_ffn_dim=cfg.shared_ffn_dim, qkv_bias=cfg.qkv_bias,
              qk_norm=cfg.qk_norm, eps=cfg.rms_eps, theta=cfg.rope_theta)
     s.update(kw)
     return ref.LayerSpec(**s)

@@ -309,6 +309,68 @@ def test_moe_topk_matches_bruteforce_per_token():
         assert np.allclose(F[t], acc_, atol=1e-13)
 
 
+def test_sigmoid_closed_form_points():
+    # 1 / (1 + e^-z): 0 -> 1/2; ln 3 -> 3/4; symmetric about 1/2
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 40.0, -40.0])
+    got = ref.sigmoid(z)
+    assert np.allclose(got, [0.5, 0.75, 0.25, 1.0, 0.0], atol=1e-15)
+    t = np.linspace(-6, 6, 25)
+    assert np.allclose(ref.sigmoid(t) + ref.sigmoid(-t), 1.0, atol=1e-15)
+    assert np.allclose(ref.silu(t), t * ref.sigmoid(t), atol=1e-15)   # SiLU = z sigmoid(z)
+
+
+def _shared_weights(rng, w, sf, d, gate_scale):
+    w = dict(w)
+    w.update(ws_gate=rng.standard_normal((sf, d)) * 0.3, ws_up=rng.standard_normal((sf, d)) * 0.3,
+             ws_down=rng.standard_normal((d, sf)) * 0.3,
+             w_shared_gate=np.full((1, d), gate_scale))
+    return w
+
+
+def test_shared_expert_gate_limits():
+    """"Qwen2.5-7B 结构拆解" §10.1: the gate scales the whole shared output by
+    sigmoid(x W_sg). A gate pushed to +inf gives routed + the plain SwiGLU of
+    width sf; pushed to -inf, the routed sum alone; at 0, half the SwiGLU."""
+    rng = np.random.default_rng(31)
+    E, k, mf, sf, d = 8, 2, 6, 10, 8
+    base = _moe_weights(rng, E, mf, d)
+    z = np.abs(rng.standard_normal((5, d))) + 0.1      # z . W_sg has the sign of the scale
+    routed, idx, wts, _ = ref.moe_ffn_output(z, base, k)
+    for scale, coeff in ((1e3, 1.0), (-1e3, 0.0), (0.0, 0.5)):
+        w = _shared_weights(rng, base, sf, d, scale)
+        F, idx2, wts2, _ = ref.moe_ffn_output(z, w, k, shared=True)
+        dense = ref.swiglu_ffn(z, w["ws_gate"], w["ws_up"], w["ws_down"])
+        assert np.array_equal(idx2, idx) and np.allclose(wts2, wts)
+        assert np.allclose(F, routed + coeff * dense, atol=1e-12)
+        assert np.allclose(ref.shared_expert(z, w)[1], coeff, atol=1e-12)
+
+
+def test_raw_probabilities_with_every_expert_selected_are_the_full_softmax():
+    """norm_topk_prob = false keeps the raw top-k probabilities ("Qwen2.5-7B
+    结构拆解" §10.2); selecting all E experts they are the whole softmax and
+    sum to one, and they then equal the renormalised weights."""
+    rng = np.random.default_rng(32)
+    logits = rng.standard_normal((9, 6)) * 2.0
+    idx = ref.topk_select(logits, 6)
+    raw = ref.gate_weights(logits, idx, False)
+    assert np.allclose(raw.sum(-1), 1.0, atol=1e-15)
+    assert np.allclose(raw, ref.gate_weights(logits, idx, True), atol=1e-15)
+
+
+def test_qwen2_57b_fixture_shapes_give_the_printed_counts():
+    """The synthetic Qwen2-57B-A14B layer allocates exactly the shared expert
+    (with its gate), router and active FFN of "Qwen2.5-7B 结构拆解" §10.1."""
+    g = gold("param_counts.json")["qwen2-57b-a14b-moe"]
+    cfg = configs.QWEN2_57B_A14B
+    sh = {n: int(np.prod(v)) for n, v in synth.weight_shapes(cfg).items()}
+    shared = sh["ws_gate"] + sh["ws_up"] + sh["ws_down"] + sh["w_shared_gate"]
+    assert shared == g["shared_expert_with_gate"]
+    assert sh["w_router"] == g["router"]
+    per_expert = (sh["we_gate"] + sh["we_up"] + sh["we_down"]) // cfg.n_experts
+    assert cfg.top_k * per_expert == g["routed_active_8"]
+    assert cfg.top_k * per_expert + shared + sh["w_router"] == g["ffn_active_per_layer"]
+
+
 # ---------------------------------------------------- full layer / toy ----
 
 def _toy_lists(w):

@@ -14,6 +14,16 @@ the pages print for each model:
   norm_topk_prob true).
 * The toy layer -- same Qwen3 page, §1 (3 positions, d=4, 2 query heads,
   1 KV head, head_dim 2, MLP width 6, gamma=1, eps=1e-6).
+* Qwen3-32B -- "MoE 初步" configuration table (d=5120, 64 query heads,
+  8 KV groups, head_dim 128, FFN 25600; QK-norm as every Qwen3 layer).
+* Qwen2-57B-A14B -- "Qwen2.5-7B 结构拆解" §10-§10.2: the Qwen2.5-7B attention
+  unchanged (d=3584, 28/4 heads, QKV bias), the MLP replaced by 64 SwiGLU
+  experts of width 2560, top-8 with raw (not renormalised) probabilities,
+  plus one shared SwiGLU expert of width 20480 scaled by sigmoid(x W_sg).
+* A Mixtral-like layer -- "第七章 模型容量与参数量推导" §3 gives only the
+  routing (8 FFN experts per layer, 2 chosen per token); the other sizes are
+  Qwen3-8B's attention (d=4096, 32/8 heads, no QK-norm) and experts of width
+  4096.
 """
 from __future__ import annotations
 
@@ -32,6 +42,7 @@ class LayerConfig:
     n_experts: int = 0           # 0 -> dense SwiGLU FFN
     top_k: int = 0
     norm_topk_prob: bool = True
+    shared_ffn_dim: int = 0      # width of an always-on shared SwiGLU expert (0: none)
     qkv_bias: bool = False
     qk_norm: bool = False
     rms_eps: float = 1e-6
@@ -98,7 +109,24 @@ QWEN3_30B_A3B = LayerConfig(
     ffn_dim=768, n_experts=128, top_k=8, norm_topk_prob=True, qk_norm=True,
 )
 
-CONFIGS = {1: TOY, 2: QWEN25_7B, 3: QWEN25_7B, 4: QWEN3_8B, 5: QWEN3_30B_A3B}
+QWEN3_32B = LayerConfig(
+    name="qwen3-32b", d=5120, n_q_heads=64, n_kv_heads=8, head_dim=128,
+    ffn_dim=25600, qk_norm=True,
+)
+
+QWEN2_57B_A14B = LayerConfig(
+    name="qwen2-57b-a14b", d=3584, n_q_heads=28, n_kv_heads=4, head_dim=128,
+    ffn_dim=2560, n_experts=64, top_k=8, norm_topk_prob=False, shared_ffn_dim=20480,
+    qkv_bias=True,
+)
+
+MIXTRAL_LIKE = LayerConfig(
+    name="mixtral-like", d=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+    ffn_dim=4096, n_experts=8, top_k=2, norm_topk_prob=True,
+)
+
+CONFIGS = {1: TOY, 2: QWEN25_7B, 3: QWEN25_7B, 4: QWEN3_8B, 5: QWEN3_30B_A3B,
+           6: QWEN3_32B, 7: MIXTRAL_LIKE, 8: QWEN2_57B_A14B}
 
 WORKLOADS = {
     1: [Workload(1, 1, "prefill", 1, 3, "toy prefill T=3")],
@@ -111,6 +139,13 @@ WORKLOADS = {
     5: [Workload(5, 1, "prefill", 1, 4096, "qwen3-30b-a3b prefill 4096 tokens"),
         Workload(5, 2, "decode", 128, 4096, "qwen3-30b-a3b decode B=128 cache=4096"),
         Workload(5, 3, "decode", 128, 1024, "qwen3-30b-a3b decode B=128 cache=1024")],
+    # shape variants beyond the graded configs
+    6: [Workload(6, 1, "prefill", 1, 2048, "qwen3-32b prefill B=1 S=2048"),
+        Workload(6, 2, "decode", 32, 4096, "qwen3-32b decode B=32 cache=4096")],
+    7: [Workload(7, 1, "prefill", 1, 2048, "mixtral-like prefill 2048 tokens"),
+        Workload(7, 2, "decode", 64, 2048, "mixtral-like decode B=64 cache=2048")],
+    8: [Workload(8, 1, "prefill", 1, 2048, "qwen2-57b-a14b prefill 2048 tokens"),
+        Workload(8, 2, "decode", 64, 1024, "qwen2-57b-a14b decode B=64 cache=1024")],
 }
 
 

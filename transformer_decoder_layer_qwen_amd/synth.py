@@ -17,6 +17,8 @@ as ``mean + std*z``:
     MoE:   w_router[E,d]                       N(0, router_std)
            we_gate[E,mf,d], we_up[E,mf,d], we_down[E,d,mf]  (expert by expert,
            gate then up then down inside an expert)         N(0, w_std)
+           shared expert (shared_ffn_dim sf > 0): ws_gate[sf,d], ws_up[sf,d],
+           ws_down[d,sf], w_shared_gate[1,d]                N(0, w_std)
 
 A tensor whose std is 0 is filled with its mean and consumes no draws.  All
 weights follow the ``[out, in]`` storage convention.
@@ -89,6 +91,9 @@ def weight_shapes(cfg: LayerConfig) -> Dict[str, tuple]:
     if cfg.is_moe:
         E = cfg.n_experts
         s.update(w_router=(E, d), we_gate=(E, f, d), we_up=(E, f, d), we_down=(E, d, f))
+        if cfg.shared_ffn_dim:
+            sf = cfg.shared_ffn_dim
+            s.update(ws_gate=(sf, d), ws_up=(sf, d), ws_down=(d, sf), w_shared_gate=(1, d))
     else:
         s.update(w_gate=(f, d), w_up=(f, d), w_down=(d, f))
     return s
@@ -121,6 +126,9 @@ def make_weights(cfg: LayerConfig, seed: int) -> Dict[str, np.ndarray]:
             u[e] = _draw(rng, (mf, d), 0.0, cfg.w_std, dt)
             dn[e] = _draw(rng, (d, mf), 0.0, cfg.w_std, dt)
         w.update(we_gate=g, we_up=u, we_down=dn)
+        if cfg.shared_ffn_dim:
+            for name in ("ws_gate", "ws_up", "ws_down", "w_shared_gate"):
+                w[name] = _draw(rng, shapes[name], 0.0, cfg.w_std, dt)
     else:
         for name in ("w_gate", "w_up", "w_down"):
             w[name] = _draw(rng, shapes[name], 0.0, cfg.w_std, dt)
