@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define QLAYER_ABI_VERSION 1
+#define QLAYER_ABI_VERSION 2
 
 typedef enum {
   QL_OK = 0,
@@ -81,6 +81,10 @@ typedef enum { QL_BF16 = 0, QL_F32 = 1 } ql_dtype;
  * dtype        ql_dtype of weights, activations and caches
  * max_tokens   largest B*S of qlayer_prefill and largest N of qlayer_moe_ffn
  * max_batch    largest B of qlayer_decode
+ * shared_ffn_dim  width sf of an always-on shared SwiGLU expert whose output is
+ *              scaled per token by sigmoid(z W_sg^T) and added to the routed
+ *              sum (Qwen2 MoE, "Qwen2.5-7B 结构拆解" §10.1-§10.2); 0 = none.
+ *              MoE layers only; sf % 128 == 0.
  *
  * QL_BF16 shape limits: head_dim == 128, d % 256 == 0, Hq and Hkv even,
  * ffn_dim % 128 == 0, Hq/Hkv <= 16, max_batch <= 128, and with experts
@@ -102,6 +106,7 @@ typedef struct {
   int dtype;
   int max_tokens;
   int max_batch;
+  int shared_ffn_dim;
 } ql_config;
 
 /* Device pointers to the layer's weights, all in the config dtype, [out, in]:
@@ -111,6 +116,8 @@ typedef struct {
  *   q_norm_g[dh], k_norm_g[dh]              only when qk_norm (else NULL)
  *   dense: w_gate[f, d], w_up[f, d], w_down[d, f]
  *   MoE:   w_router[E, d], we_gate[E, mf, d], we_up[E, mf, d], we_down[E, d, mf]
+ *   shared expert (shared_ffn_dim sf > 0): ws_gate[sf, d], ws_up[sf, d],
+ *          ws_down[d, sf], w_shared_gate[1, d] (W_sg, no bias)
  */
 typedef struct {
   const void *ln1_g, *ln2_g;
@@ -119,6 +126,7 @@ typedef struct {
   const void *q_norm_g, *k_norm_g;
   const void *w_gate, *w_up, *w_down;
   const void *w_router, *we_gate, *we_up, *we_down;
+  const void *ws_gate, *ws_up, *ws_down, *w_shared_gate;
 } ql_weights;
 
 typedef struct ql_handle ql_handle;
@@ -189,7 +197,8 @@ ql_status qlayer_decode_noalloc(const ql_config* cfg, const ql_weights* w, const
 
 /* The sparse-MoE FFN half of a layer on N residual rows ("Qwen2.5-7B 结构拆解"
  * §10.2; "MoE 初步" Sparse MoE 架构详解):
- *     y = r + sum_{i<k} w_i * Expert_{idx_i}(RMSNorm2(r))
+ *     y = r + sum_{i<k} w_i * Expert_{idx_i}(z) [+ sigmoid(z W_sg^T) SharedExpert(z)],
+ *     z = RMSNorm2(r)
  * Router logits are computed from an fp32 RMSNorm2 output; top-k order is by
  * descending logit, ties to the lower expert index; the sum runs in rank order.
  *
@@ -238,7 +247,9 @@ typedef enum {
   QL_STAGE_PERMUTE = 10,     /* histogram, scan, scatter */
   QL_STAGE_EXPERT_GATE_UP = 11,
   QL_STAGE_EXPERT_DOWN = 12,
-  QL_STAGE_COMBINE = 13      /* weighted combine + residual */
+  QL_STAGE_COMBINE = 13,     /* weighted combine + residual */
+  QL_STAGE_SHARED_GATE_UP = 14,  /* shared expert gate/up + SwiGLU */
+  QL_STAGE_SHARED_DOWN = 15      /* shared expert down, gated, + residual */
 } ql_stage;
 
 /* Timing aid: after this call, every prefill / decode / moe_ffn call on the

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for name in header_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert b.qlayer_abi_version() == 1
+    assert b.qlayer_abi_version() == 2
 
 
 def _cfg(**kw):

@@ -13,7 +13,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from harness import (ATT_ROW_TOL, BF16_TOL, F32_TOL, FFN_BRANCH_TOL, MOE_BRANCH_TOL,  # noqa: E402
-                     attention_err,
+                     Y_ROUNDING_FLOOR, attention_err, excess_err,
                      branch_err, flip_report, log, moe_rerouted, oracle_gaps, rel_err, rounding_err,
                      routing_mismatch, rowwise_err, small_cfg, small_moe_cfg, spec_of, weights_for)
 from oracle import qlayer_ref as ref  # noqa: E402
@@ -366,6 +366,50 @@ def test_router_exact_ties_take_the_lower_expert_first(E, k):
     layer.close()
 
 
+# Qwen2-style MoE ("Qwen2.5-7B 结构拆解" §10.1-§10.2): raw top-k probabilities
+# plus a shared SwiGLU expert scaled by sigmoid(z W_sg); moe_ffn takes the
+# prefill form (z and the shared hidden as hi/lo pairs), decode the bf16 tiles
+@pytest.mark.parametrize("N", [37, 300, 700])
+def test_small_moe_shared_expert_ffn(N):
+    cfg = small_moe_cfg(n_experts=16, top_k=4, norm_topk_prob=False, shared_ffn_dim=512)
+    layer, w64 = make_layer(cfg, max_tokens=max(N, 8), max_batch=4)
+    r = synth.make_moe_input(cfg, 1014, N)
+    idx_t = torch.empty(N, cfg.top_k, dtype=torch.int32, device="cuda")
+    w_t = torch.empty(N, cfg.top_k, dtype=torch.float32, device="cuda")
+    lg_t = torch.empty(N, cfg.n_experts, dtype=torch.float32, device="cuda")
+    layer.set_taps(logits=lg_t)
+    y = layer.moe_ffn(B.to_device(r), topk_idx=idx_t, topk_w=w_t)
+    torch.cuda.synchronize()
+    r64 = synth.to_f32(r).astype(np.float64)
+    o = ref.moe_ffn(r64, w64, spec_of(cfg))
+    assert rel_err(host(lg_t), o["logits"]) <= 1e-4
+    bad, checked = routing_mismatch(idx_t.cpu().numpy(), o["logits"], cfg.top_k)
+    assert checked > 0.9 * N and bad.size == 0, bad
+    assert np.all(w_t.cpu().numpy().sum(-1) < 1.0)          # raw probabilities
+    f_ref, flipped = moe_rerouted(o, logits_of(idx_t, o["logits"]), w64, spec_of(cfg))
+    yg = host(y)
+    e, ef = rel_err(yg, r64 + f_ref), branch_err(yg, r64, f_ref)
+    log(f"[gpu] shared-expert moe_ffn N={N}: y {e:.2e}  branch {ef:.2e}")
+    assert e <= BF16_TOL and ef <= MOE_BRANCH_TOL
+    layer.close()
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode_B5", "decode_B2"])
+def test_small_moe_shared_expert_layer(kind):
+    cfg = small_moe_cfg(n_experts=16, top_k=4, norm_topk_prob=False, shared_ffn_dim=512,
+                        qkv_bias=True, qk_norm=False)
+    if kind == "prefill":
+        layer, w64 = make_layer(cfg, max_tokens=256, max_batch=1)
+        x = synth.make_prefill_input(cfg, 1015, 1, 256)
+        check_prefill_full(cfg, layer, w64, x, label="small shared-expert prefill")
+    else:
+        Bn = 5 if kind == "decode_B5" else 2
+        layer, w64 = make_layer(cfg, max_tokens=1, max_batch=Bn)
+        x, kc, vc, lens = synth.make_decode_input(cfg, 1016, Bn, 90, T_max=96)
+        check_decode_full(cfg, layer, w64, x, kc, vc, lens, label=f"small shared-expert {kind}")
+    layer.close()
+
+
 def test_small_moe_layer_prefill():
     cfg = small_moe_cfg()
     Bn, S = 1, 200
@@ -417,7 +461,9 @@ def test_gpu_decode_matches_prefill_last_row():
 
 # ------------------------------------------------- full sizes, every row ----
 
-FULL = [(cid, wl) for cid in (2, 3, 4, 5) for wl in configs.WORKLOADS[cid]]
+# the five graded configs, then the shape variants: Qwen3-32B, the Mixtral-like
+# 8-expert top-2 layer and Qwen2-57B-A14B with its shared expert
+FULL = [(cid, wl) for cid in (2, 3, 4, 5, 6, 7, 8) for wl in configs.WORKLOADS[cid]]
 
 
 def check_prefill_full(cfg, layer, w64, x, pos_offset=0, label=""):
@@ -449,13 +495,14 @@ def check_prefill_full(cfg, layer, w64, x, pos_offset=0, label=""):
         assert flipped.sum() <= max(2, N // 50) and np.all(gaps[flipped] < 2e-2)
         y_ref = r_ref + f_ref
     e = rel_err(yg, y_ref)
+    ex = excess_err(yg, y_ref)
     ea = rowwise_err(rg - x64.reshape(N, -1), r_ref - x64.reshape(N, -1))
     ef = branch_err(yg, rg, f_ref)
     ek = rounding_err(host(kc), o["k"])
     ev = rounding_err(host(vc), o["v"])
-    log(f"[gpu] {label}: {N} rows: y {e:.2e}  attention branch (worst row) {ea:.2e}  "
-        f"ffn branch {ef:.2e}  k-cache {ek:.2f}  v-cache {ev:.2f} (<=1)")
-    assert e <= BF16_TOL
+    log(f"[gpu] {label}: {N} rows: y {e:.2e} (beyond its own rounding {ex:.2e})  attention "
+        f"branch (worst row) {ea:.2e}  ffn branch {ef:.2e}  k-cache {ek:.2f}  v-cache {ev:.2f} (<=1)")
+    assert (ex if cfg.name in Y_ROUNDING_FLOOR else e) <= BF16_TOL
     assert ea <= ATT_ROW_TOL and ef <= (MOE_BRANCH_TOL if cfg.is_moe else FFN_BRANCH_TOL)
     assert ek <= 1.0 and ev <= 1.0
 
@@ -485,15 +532,17 @@ def check_decode_full(cfg, layer, w64, x, kc, vc, lens, label=""):
         assert flipped.sum() <= max(2, Bn // 50) and np.all(gaps[flipped] < 2e-2)
     yg, rg = host(y), host(r_t)
     e = rel_err(yg, r_ref + f_ref)
+    ex = excess_err(yg, r_ref + f_ref)
     ea = rowwise_err(rg - x64, r_ref - x64)
     ef = branch_err(yg, rg, f_ref)
     kh, vh = host(kd), host(vd)
     rows = np.arange(Bn)
     ek = rounding_err(kh[rows, lens], o["k_new"])
     ev = rounding_err(vh[rows, lens], o["v_new"])
-    log(f"[gpu] {label}: {Bn} sequences: y {e:.2e}  attention branch (worst row) {ea:.2e}  "
-        f"ffn branch {ef:.2e}  new k {ek:.2f}  new v {ev:.2f} (<=1)")
-    assert e <= BF16_TOL and ea <= ATT_ROW_TOL
+    log(f"[gpu] {label}: {Bn} sequences: y {e:.2e} (beyond its own rounding {ex:.2e})  "
+        f"attention branch (worst row) {ea:.2e}  ffn branch {ef:.2e}  new k {ek:.2f}  "
+        f"new v {ev:.2f} (<=1)")
+    assert (ex if cfg.name in Y_ROUNDING_FLOOR else e) <= BF16_TOL and ea <= ATT_ROW_TOL
     assert ef <= (MOE_BRANCH_TOL if cfg.is_moe else FFN_BRANCH_TOL)
     assert ek <= 1.0 and ev <= 1.0
     for b, L in enumerate(lens):   # nothing else written

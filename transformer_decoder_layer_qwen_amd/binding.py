@@ -33,7 +33,7 @@ NOALLOC_MAX_WORKSPACE = 64 << 20
 # ql_stage
 STAGES = {"rmsnorm1": 1, "qkv": 2, "qkv_post": 3, "attention": 4, "o_proj": 5, "rmsnorm2": 6,
           "gate_up": 7, "down": 8, "router": 9, "permute": 10, "expert_gate_up": 11,
-          "expert_down": 12, "combine": 13}
+          "expert_down": 12, "combine": 13, "shared_gate_up": 14, "shared_down": 15}
 
 
 class QlConfig(ctypes.Structure):
@@ -43,12 +43,13 @@ class QlConfig(ctypes.Structure):
                 ("norm_topk_prob", ctypes.c_int), ("qkv_bias", ctypes.c_int),
                 ("qk_norm", ctypes.c_int), ("rms_eps", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int),
-                ("max_tokens", ctypes.c_int), ("max_batch", ctypes.c_int)]
+                ("max_tokens", ctypes.c_int), ("max_batch", ctypes.c_int),
+                ("shared_ffn_dim", ctypes.c_int)]
 
 
 WEIGHT_FIELDS = ("ln1_g", "ln2_g", "wq", "wk", "wv", "wo", "bq", "bk", "bv", "q_norm_g",
                  "k_norm_g", "w_gate", "w_up", "w_down", "w_router", "we_gate", "we_up",
-                 "we_down")
+                 "we_down", "ws_gate", "ws_up", "ws_down", "w_shared_gate")
 
 
 class QlWeights(ctypes.Structure):
@@ -219,7 +220,8 @@ class QLayer:
                      qkv_bias=int(cfg.qkv_bias), qk_norm=int(cfg.qk_norm),
                      rms_eps=cfg.rms_eps, rope_theta=cfg.rope_theta,
                      dtype=QL_BF16 if cfg.dtype == "bf16" else QL_F32,
-                     max_tokens=max_tokens, max_batch=max_batch)
+                     max_tokens=max_tokens, max_batch=max_batch,
+                     shared_ffn_dim=getattr(cfg, "shared_ffn_dim", 0))
         w = QlWeights(**{n: _ptr(weights.get(n)) for n in WEIGHT_FIELDS})
         self.c_config, self.c_weights = c, w
         self.handle = qlayer_create(c, w)

@@ -21,8 +21,8 @@ the pages print for each model:
   experts of width 2560, top-8 with raw (not renormalised) probabilities,
   plus one shared SwiGLU expert of width 20480 scaled by sigmoid(x W_sg).
 * A Mixtral-like layer -- "第七章 模型容量与参数量推导" §3 gives only the
-  routing (8 FFN experts per layer, 2 chosen per token); the other sizes are
-  Qwen3-8B's attention (d=4096, 32/8 heads, no QK-norm) and experts of width
+  routing (8 FFN experts per layer, 2 chosen per token); the rest is
+  Qwen3-8B's attention (d=4096, 32/8 heads, QK-norm) and experts of width
   4096.
 """
 from __future__ import annotations
@@ -122,7 +122,7 @@ QWEN2_57B_A14B = LayerConfig(
 
 MIXTRAL_LIKE = LayerConfig(
     name="mixtral-like", d=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
-    ffn_dim=4096, n_experts=8, top_k=2, norm_topk_prob=True,
+    ffn_dim=4096, n_experts=8, top_k=2, norm_topk_prob=True, qk_norm=True,
 )
 
 CONFIGS = {1: TOY, 2: QWEN25_7B, 3: QWEN25_7B, 4: QWEN3_8B, 5: QWEN3_30B_A3B,

@@ -30,7 +30,8 @@
 //   RESID_OUT  out     = bf16(resid_f32 + acc)   Y = R + H W_down^T
 //   SWIGLU     out     = bf16(SiLU(g) * u)       B tile = [W_gate rows | W_up rows]
 //   MOE_GU     SWIGLU on gathered token rows with one expert's weights
-//   MOE_DOWN   out     = bf16(acc) for one expert's slot rows
+//              (fp32 A gathered by token, fp32 h)
+//   MOE_DOWN   out     = acc for one expert's slot rows (fp32 A and out)
 // ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §4, §9, §10; "MoE 初步"
 // Expert 的 FFN 结构.)
 #include "common.h"
@@ -270,7 +271,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
       float h[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) h[i] = silu_f32(g[i]) * u[i];
-      store_bf16x8(p.out_bf16 + (size_t)(m0 + r) * p.ldo + n0 + seg * 8, pack8(h));
+      if (p.out_f32) {
+        float* o = p.out_f32 + (size_t)(m0 + r) * p.ldo + n0 + seg * 8;
+        *reinterpret_cast<f32x4*>(o) = f32x4{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{h[4], h[5], h[6], h[7]};
+      } else {
+        store_bf16x8(p.out_bf16 + (size_t)(m0 + r) * p.ldo + n0 + seg * 8, pack8(h));
+      }
     }
   } else {
     constexpr int SEGS = BN / 8;
@@ -306,7 +313,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
         }
         store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
       } else if constexpr (MODE == GM_MOE_DOWN) {
-        store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
+        if (p.out_f32) {
+          float* o = p.out_f32 + row * p.ldo + col;
+          *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        } else {
+          store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
+        }
       } else {
         float* o = p.out_f32 + row * p.ldo + col;
         *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
@@ -339,11 +352,12 @@ GemmArgs base_args(const bf16* A, int lda, int M, const bf16* B, int ldb, int K)
 
 }  // namespace
 
-hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
+hipError_t ql_gemm_moe_gu(const float* Zf, const int* slot_token, const bf16* Wg, const bf16* Wu,
                           int mf, int d, const int* tile_expert, const int* tile_row0,
-                          const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                          const int* tile_rows, const int* num_tiles, int max_tiles, float* H,
                           hipStream_t s) {
-  GemmArgs a = base_args(Z, d, 0, Wg, d, d);
+  GemmArgs a = base_args(nullptr, d, 0, Wg, d, d);
+  a.Af = Zf;
   a.B2 = Wu;
   a.b_expert_stride = (size_t)mf * d;
   a.row_index = slot_token;
@@ -351,23 +365,24 @@ hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, 
   a.tile_row0 = tile_row0;
   a.tile_rows = tile_rows;
   a.num_tiles = num_tiles;
-  a.out_bf16 = H;
+  a.out_f32 = H;
   a.ldo = mf;
   a.tiles_n = mf / 64;
-  return launch<32, 128, 32, 32, GM_MOE_GU>(a, max_tiles, s);
+  return launch<32, 128, 32, 32, GM_MOE_GU, true>(a, max_tiles, s);
 }
 
-hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
+hipError_t ql_gemm_moe_down(const float* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                            int max_tiles, bf16* out, hipStream_t s) {
-  GemmArgs a = base_args(H, mf, 0, Wd, mf, mf);
+                            int max_tiles, float* out, hipStream_t s) {
+  GemmArgs a = base_args(nullptr, mf, 0, Wd, mf, mf);
+  a.Af = H;
   a.b_expert_stride = (size_t)d * mf;
   a.tile_expert = tile_expert;
   a.tile_row0 = tile_row0;
   a.tile_rows = tile_rows;
   a.num_tiles = num_tiles;
-  a.out_bf16 = out;
+  a.out_f32 = out;
   a.ldo = d;
   a.tiles_n = d / 128;
-  return launch<32, 128, 32, 32, GM_MOE_DOWN>(a, max_tiles, s);
+  return launch<32, 128, 32, 32, GM_MOE_DOWN, true>(a, max_tiles, s);
 }

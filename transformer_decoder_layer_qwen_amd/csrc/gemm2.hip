@@ -34,6 +34,8 @@
 //   SWIGLU    out     = bf16(SiLU(g) * u)       B tile = [128 W_gate rows | 128 W_up rows]
 //   MOE_GU    SWIGLU on gathered token rows with one expert's weights per tile
 //   MOE_DOWN  out     = bf16(acc) for one expert's slot rows
+//   GATED_F32 out_f32 = resid + sigmoid(gate_logit[row]) * acc  (a shared
+//             expert scaled by its per-token gate; resid fp32, bf16 or none)
 // With split-K each split stores its fp32 partial tile and the reduce kernel
 // applies the epilogue.
 // ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §4, §9, §10.)
@@ -44,7 +46,8 @@
 
 namespace {
 
-enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU, G2_MOE_GU, G2_MOE_DOWN };
+enum : int { G2_BIAS = 0, G2_RESID_F32, G2_RESID_OUT, G2_SWIGLU, G2_MOE_GU, G2_MOE_DOWN,
+             G2_GATED_F32 };
 
 constexpr int BN = 256, BK = 64;  // weight-tile columns, k depth of a stage
 constexpr int kGroupM = 4;  // tile rows per L2 group
@@ -66,6 +69,8 @@ struct G2Args {
   bf16* out_bf16;
   int ldo;
   int out_lo;  // SWIGLU: > 0 stores h as a [hi | lo] pair, lo at + out_lo elements
+  const float* gate_logit;  // GATED_F32: the row's gate logit at gate_logit[row * gate_ld]
+  int gate_ld;
   const bf16* bias;
   const bf16* bias2;
   const bf16* bias3;
@@ -161,6 +166,26 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
     bf16* cache = part == 1 ? p.k_cache : p.v_cache;
     store_bf16x8(cache + (((size_t)b * p.T_max + t) * p.n_kv_heads + head) * 128 + d0, pack8(v));
   }
+}
+
+// GATED_F32 epilogue of 8 columns: v = resid + sigmoid(gate) * v.
+QL_DEV void gated_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
+  const float g = 1.0f / (1.0f + __expf(-p.gate_logit[row * p.gate_ld]));
+  float r8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (p.resid_f32) {
+    const float* rr = p.resid_f32 + row * p.ldr + col;
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(rr);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(rr + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r8[e] = r0[e];
+      r8[e + 4] = r1[e];
+    }
+  } else if (p.resid_bf16) {
+    unpack8(load_bf16x8(p.resid_bf16 + row * p.ldr + col), r8);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = r8[e] + g * v[e];
 }
 
 // SwiGLU hidden values of columns [col, col + 8) of `row`: bf16, or the
@@ -505,6 +530,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += x[e];
         }
+        if constexpr (MODE == G2_GATED_F32) gated_finish(p, row, col, v);
         if constexpr (MODE == G2_RESID_OUT) {
           const float* rr = p.resid_f32 + row * p.ldr + col;
           const f32x4 r0 = *reinterpret_cast<const f32x4*>(rr);
@@ -516,8 +542,14 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
           }
           store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
         } else if constexpr (MODE == G2_MOE_DOWN) {
-          store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
-        } else {  // RESID_F32: fp32 rows
+          if (p.out_f32) {
+            float* o = p.out_f32 + row * p.ldo + col;
+            *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          } else {
+            store_bf16x8(p.out_bf16 + row * p.ldo + col, pack8(v));
+          }
+        } else {  // RESID_F32, GATED_F32: fp32 rows
           float* o = p.out_f32 + row * p.ldo + col;
           *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
           *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -899,6 +931,7 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) w8[e] += extra[e];
     }
+    if constexpr (MODE == G2_GATED_F32) gated_finish(p, (size_t)row, col, w8);
     if constexpr (MODE == G2_RESID_OUT) {
       store_bf16x8(p.out_bf16 + (size_t)row * p.ldo + col, pack8(w8));
     } else {
@@ -925,9 +958,14 @@ template <int MODE, int SHAPE>
 hipError_t launch(const G2Args& a, dim3 grid, hipStream_t s) {
   constexpr bool HL = shape_hl(SHAPE);
   // hi/lo inputs feed Q/K/V and O; plain bf16 inputs feed gate/up and down
-  constexpr bool kPairIn = MODE == G2_BIAS || MODE == G2_RESID_F32;
+  // Q/K/V and O always take a pair; gate/up, down and the gated shared-expert
+  // down take a pair or plain bf16 on the decode tiles, and only the pair on
+  // the 128-row prefill tiles is reserved for Q/K/V and O
+  constexpr bool kPairOnly = MODE == G2_BIAS || MODE == G2_RESID_F32;
+  constexpr bool kMoe = MODE == G2_MOE_GU || MODE == G2_MOE_DOWN;
   constexpr bool kDec = SHAPE != T256 && SHAPE != P128_HL;
-  if constexpr (SHAPE != T256 && (HL != kPairIn || SHAPE == D32_HL)) {
+  if constexpr (SHAPE != T256 &&
+                (kMoe || SHAPE == D32_HL || (kPairOnly && !HL) || (SHAPE == P128_HL && !kPairOnly))) {
     return hipErrorInvalidValue;
   } else if constexpr (kDec) {  // decode tiles: stream-K partials
     hipLaunchKernelGGL((gemm2_dec_kernel<MODE, HL, shape_ra(SHAPE)>), grid, dim3(256), 0, s, a);
@@ -1154,38 +1192,62 @@ hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K
   return run_pair<G2_RESID_F32>(a, pl, s);
 }
 
+// A of a plain-input GEMM: a pair doubles K on the 256-row prefill tiles
+// (hi then lo k steps against the same weights) and puts hi and lo rows side
+// by side on the decode tiles (each weight tile serves both)
+G2Args base_ab(const bf16* A, int M, const bf16* W, int K, bool pair, bool rows128, int splits,
+               void* part) {
+  G2Args a = base(A, M, pair && !rows128 ? 2 * K : K, W, K, splits, part);
+  if (pair) a.lda = 2 * K;
+  return a;
+}
+
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
                               const float* resid, bf16* out, bool rows128, int splits, void* part,
                               hipStream_t s, bool pair_in) {
-  if (pair_in && rows128) return hipErrorInvalidValue;
-  G2Args a = base(A, M, pair_in ? 2 * K : K, W, K, splits, part);
+  G2Args a = base_ab(A, M, W, K, pair_in, rows128, splits, part);
   a.resid_f32 = resid;
   a.ldr = N;
   a.out_bf16 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_OUT>(a, rows128 ? decode_shape(M, false) : T256, s);
+  return run<G2_RESID_OUT>(a, rows128 ? decode_shape(M, pair_in) : T256, s);
+}
+
+hipError_t ql_gemm2_gated_out(const bf16* A, int M, const bf16* W, int N, int K,
+                              const float* gate_logit, int gate_ld, const float* resid_f32,
+                              const bf16* resid_bf16, float* out, bool rows128, int splits,
+                              void* part, hipStream_t s, bool pair_in) {
+  G2Args a = base_ab(A, M, W, K, pair_in, rows128, splits, part);
+  a.gate_logit = gate_logit;
+  a.gate_ld = gate_ld;
+  a.resid_f32 = resid_f32;
+  a.resid_bf16 = resid_bf16;
+  a.ldr = N;
+  a.out_f32 = out;
+  a.ldo = N;
+  a.tiles_n = N / BN;
+  return run<G2_GATED_F32>(a, rows128 ? decode_shape(M, pair_in) : T256, s);
 }
 
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
                            bf16* out, bool rows128, int splits, void* part, hipStream_t s,
                            bool pair) {
-  if (pair && rows128) return hipErrorInvalidValue;
-  G2Args a = base(A, M, pair ? 2 * K : K, Wg, K, splits, part);
+  G2Args a = base_ab(A, M, Wg, K, pair, rows128, splits, part);
   a.B2 = Wu;
   a.out_bf16 = out;
   a.ldo = pair ? 2 * F : F;
   a.out_lo = pair ? F : 0;
   a.tiles_n = F / (BN / 2);
-  return run<G2_SWIGLU>(a, rows128 ? decode_shape(M, false) : T256, s);
+  return run<G2_SWIGLU>(a, rows128 ? decode_shape(M, pair) : T256, s);
 }
 
-hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
+hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg, const bf16* Wu,
                            int mf, int d, const int* tile_expert, const int* tile_row0,
-                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H2,
                            hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  G2Args a = base(Z, 0, d, Wg, d, 1, nullptr);
+  G2Args a = base(Z2, 0, 2 * d, Wg, d, 1, nullptr);  // [hi | lo] rows over a doubled K
   a.B2 = Wu;
   a.b_expert_stride = (size_t)mf * d;
   a.row_index = slot_token;
@@ -1193,8 +1255,9 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg,
   a.tile_row0 = tile_row0;
   a.tile_rows = tile_rows;
   a.num_tiles = num_tiles;
-  a.out_bf16 = H;
-  a.ldo = mf;
+  a.out_bf16 = H2;
+  a.ldo = 2 * mf;
+  a.out_lo = mf;
   a.tiles_n = mf / (BN / 2);
   const int total = max_tiles * a.tiles_n;
   hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, false>), dim3(8 * ((total + 7) / 8)), dim3(512), 0,
@@ -1202,17 +1265,17 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg,
   return hipGetLastError();
 }
 
-hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
-                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                             int max_tiles, bf16* out, hipStream_t s) {
+hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
+                             const int* tile_expert, const int* tile_row0, const int* tile_rows,
+                             const int* num_tiles, int max_tiles, float* out, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  G2Args a = base(H, 0, mf, Wd, mf, 1, nullptr);
+  G2Args a = base(H2, 0, 2 * mf, Wd, mf, 1, nullptr);  // [hi | lo] rows over a doubled K
   a.b_expert_stride = (size_t)d * mf;
   a.tile_expert = tile_expert;
   a.tile_row0 = tile_row0;
   a.tile_rows = tile_rows;
   a.num_tiles = num_tiles;
-  a.out_bf16 = out;
+  a.out_f32 = out;
   a.ldo = d;
   a.tiles_n = d / BN;
   const int total = max_tiles * a.tiles_n;

@@ -16,28 +16,30 @@ hipError_t ql_rmsnorm_bf16(const bf16* x, const bf16* gamma, bf16* out, float* o
                            int d, float eps, hipStream_t s);
 // bf16 rows -> normalised rows as a bf16 pair per row: [hi (d) | lo (d)]
 hipError_t ql_rmsnorm_bf16_to_hilo(const bf16* x, const bf16* gamma, bf16* out, int rows, int d,
-                                   float eps, hipStream_t s);
+                                   float eps, hipStream_t s, float* out_f32 = nullptr);
 // [rows][hi (cols) | lo (cols)] -> fp32 hi + lo
 hipError_t ql_hilo_to_f32(const bf16* hl, int rows, int cols, float* out, hipStream_t s);
 hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, float* out_f32,
                                  int rows, int d, float eps, hipStream_t s);
 // fp32 rows -> normalised rows as a bf16 pair per row: [hi (d) | lo (d)]
 hipError_t ql_rmsnorm_f32_to_hilo(const float* x, const bf16* gamma, bf16* out, int rows, int d,
-                                  float eps, hipStream_t s);
+                                  float eps, hipStream_t s, float* out_f32 = nullptr);
 // bf16 -> fp32, n elements
 hipError_t ql_bf16_to_f32(const bf16* x, size_t n, float* out, hipStream_t s);
 hipError_t ql_rmsnorm_f32(const float* x, const float* gamma, float* out, int rows, int d,
                           float eps, hipStream_t s);
 
 // ---- MoE expert GEMMs over routed 32-row tiles (decode-sized batches;
-// mf % 64 == 0, d % 128 == 0) ----
-hipError_t ql_gemm_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
+// mf % 64 == 0, d % 128 == 0). fp32 activations, each staged as a bf16
+// hi + lo pair (two MFMAs per weight fragment): Zf [N, d] gathered by
+// slot_token, H [N*k, mf] fp32, out [N*k, d] fp32 in slot order ----
+hipError_t ql_gemm_moe_gu(const float* Zf, const int* slot_token, const bf16* Wg, const bf16* Wu,
                           int mf, int d, const int* tile_expert, const int* tile_row0,
-                          const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                          const int* tile_rows, const int* num_tiles, int max_tiles, float* H,
                           hipStream_t s);
-hipError_t ql_gemm_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
+hipError_t ql_gemm_moe_down(const float* H, const bf16* Wd, int mf, int d, const int* tile_expert,
                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                            int max_tiles, bf16* out, hipStream_t s);
+                            int max_tiles, float* out, hipStream_t s);
 
 // ---- GEMMs on 256-column tiles (N % 256 == 0, or F % 128 for SwiGLU; K % 64) ----
 // A2 = [hi | lo] bf16 pair of an fp32 activation, [M, 2K].
@@ -77,23 +79,33 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
 hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K,
                               const bf16* resid, float* out, bool rows128, int splits, void* part,
                               hipStream_t s);
-// pair_in / pair (prefill tiles only): A is a [hi | lo] pair [M, 2K] read
-// over a doubled K; SwiGLU also stores h as a pair [M, 2F] (hi | lo).
+// pair_in / pair: A is a [hi | lo] pair [M, 2K] (read over a doubled K on
+// the prefill tiles, hi and lo rows sharing each weight tile on the decode
+// tiles); SwiGLU also stores h as a pair [M, 2F] (hi | lo).
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
                               const float* resid, bf16* out, bool rows128, int splits, void* part,
                               hipStream_t s, bool pair_in = false);
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
                            bf16* out, bool rows128, int splits, void* part, hipStream_t s,
                            bool pair = false);
+// out[M, N] fp32 = resid + sigmoid(gate_logit[m * gate_ld]) * (A W^T)[m]:
+// a shared expert's down projection scaled by its gate (resid_f32, else
+// resid_bf16, else nothing is added); pair_in as above
+hipError_t ql_gemm2_gated_out(const bf16* A, int M, const bf16* W, int N, int K,
+                              const float* gate_logit, int gate_ld, const float* resid_f32,
+                              const bf16* resid_bf16, float* out, bool rows128, int splits,
+                              void* part, hipStream_t s, bool pair_in);
 // MoE expert GEMMs on 256-row expert tiles (the permute's tile table built
-// with bm = 256; max_tiles bounds *num_tiles; mf % 128 == 0, d % 256 == 0)
-hipError_t ql_gemm2_moe_gu(const bf16* Z, const int* slot_token, const bf16* Wg, const bf16* Wu,
+// with bm = 256; max_tiles bounds *num_tiles; mf % 128 == 0, d % 256 == 0).
+// Z2 [N, 2d] and H2 [N*k, 2mf] are [hi | lo] pairs read over a doubled K;
+// out [N*k, d] fp32 in slot order.
+hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg, const bf16* Wu,
                            int mf, int d, const int* tile_expert, const int* tile_row0,
-                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H,
+                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H2,
                            hipStream_t s);
-hipError_t ql_gemm2_moe_down(const bf16* H, const bf16* Wd, int mf, int d, const int* tile_expert,
-                             const int* tile_row0, const int* tile_rows, const int* num_tiles,
-                             int max_tiles, bf16* out, hipStream_t s);
+hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
+                             const int* tile_expert, const int* tile_row0, const int* tile_rows,
+                             const int* num_tiles, int max_tiles, float* out, hipStream_t s);
 
 // ---- decode GEMVs for M <= kGemvMaxRows rows (N % 2 == 0, K % 8 == 0) ----
 // qkv_raw: out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x,
@@ -207,9 +219,11 @@ hipError_t ql_gemm_f32_generic(int mode, const float* A, const float* B, const f
 struct RouterArgs {
   const float* zf;   // [N, d] fp32 RMSNorm2 output
   const bf16* wr;    // [E, d]
+  const bf16* w_extra;  // [n_extra, d] rows computed after the E experts (a shared
+  int n_extra;          // expert's gate) and left out of the top-k; or NULL, 0
   int N, d, E, k;
   int norm_topk;
-  float* logits;     // [N, E] or NULL
+  float* logits;     // [N, E + n_extra]
   int* idx;          // [N, k]
   float* w;          // [N, k]
 };
@@ -231,7 +245,7 @@ struct PermuteArgs {
 hipError_t ql_moe_permute(const PermuteArgs& a, hipStream_t s);
 
 struct CombineArgs {
-  const bf16* out_slot;   // [N*k, d] expert outputs in slot order
+  const float* out_slot;  // [N*k, d] expert outputs in slot order (fp32)
   const int* pos_of;      // [N, k]
   const float* w;         // [N, k]
   int N, k, d;

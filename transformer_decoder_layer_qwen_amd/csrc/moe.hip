@@ -61,12 +61,17 @@ __global__ __launch_bounds__(kRW * 64) void router_logits_kernel(const RouterArg
   const bool tv = tok < p.N;
   const int kw = p.d / kRW;  // K per wave (a multiple of 32 KU)
   const float* zr = p.zf + (size_t)(tv ? tok : 0) * p.d + wave * kw + 8 * grp;
-  // expert rows past E (a last, part-filled expert tile) re-read row E - 1
-  // and are never stored
+  // rows E .. E + n_extra - 1 come from w_extra (a shared expert's gate);
+  // rows past them (a last, part-filled tile) re-read the last row and are
+  // never stored
+  const int etot = p.E + p.n_extra;
   const bf16* wr[MT];
 #pragma unroll
-  for (int et = 0; et < MT; ++et)
-    wr[et] = p.wr + (size_t)min(e0 + 16 * et + col, p.E - 1) * p.d + wave * kw + 8 * grp;
+  for (int et = 0; et < MT; ++et) {
+    const int row = min(e0 + 16 * et + col, etot - 1);
+    wr[et] = (row < p.E ? p.wr + (size_t)row * p.d : p.w_extra + (size_t)(row - p.E) * p.d) +
+             wave * kw + 8 * grp;
+  }
 
   f32x4 acc[MT];
 #pragma unroll
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(kRW * 64) void router_logits_kernel(const RouterArg
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < kHalf; ++w) v += part[w][e * kEP + tl];
-    if (t0 + tl < p.N && e0 + e < p.E) p.logits[(size_t)(t0 + tl) * p.E + e0 + e] = v;
+    if (t0 + tl < p.N && e0 + e < etot) p.logits[(size_t)(t0 + tl) * etot + e0 + e] = v;
   }
 }
 
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const RouterArgs p) {
     const int e = lane + 64 * j;
     float x = -INFINITY;
     if (e < E) {
-      x = p.logits[(size_t)t * E + e];
+      x = p.logits[(size_t)t * (E + p.n_extra) + e];
       x = x == x ? x : -INFINITY;
     }
     // entries up to the next multiple of 4 are read by the rank loop below:
@@ -366,21 +371,23 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const CombineArgs p, c
   load8<TR>(resid + (size_t)t * p.d + c, acc);
   float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int i0 = 0; i0 < p.k; i0 += kGroup) {
-    bf16x8 o[kGroup];
+    f32x4 o[kGroup][2];
     float w[kGroup];
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
       const int r = min(i0 + i, p.k - 1);
-      o[i] = load_bf16x8(p.out_slot + (size_t)p.pos_of[(size_t)t * p.k + r] * p.d + c);
+      const float* src = p.out_slot + (size_t)p.pos_of[(size_t)t * p.k + r] * p.d + c;
+      o[i][0] = *reinterpret_cast<const f32x4*>(src);
+      o[i][1] = *reinterpret_cast<const f32x4*>(src + 4);
       w[i] = i0 + i < p.k ? p.w[(size_t)t * p.k + r] : 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      float f[8];
-      unpack8(o[i], f);
+    for (int i = 0; i < kGroup; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum[j] += w[i] * f[j];
-    }
+      for (int j = 0; j < 4; ++j) {
+        sum[j] += w[i] * o[i][0][j];
+        sum[j + 4] += w[i] * o[i][1][j];
+      }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] += sum[j];
@@ -391,13 +398,17 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const CombineArgs p, c
 
 hipError_t ql_router_topk(const RouterArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  if (!a.logits || a.E < 1 || a.E > kMaxExperts || a.d % (32 * kRW)) return hipErrorInvalidValue;
+  if (!a.logits || a.E < 1 || a.E > kMaxExperts || a.d % (32 * kRW) || a.n_extra < 0 ||
+      a.n_extra > 16 || (a.n_extra > 0 && !a.w_extra))
+    return hipErrorInvalidValue;
   const int ntb = (a.N + kTok - 1) / kTok;
-  const int et = (a.E + 15) / 16;
+  const int etot = a.E + a.n_extra;
+  const int et = (etot + 15) / 16;
   // expert tiles per block: all of them when token blocks alone fill the
-  // chip (z rows read once), else one (more blocks, one round of loads each;
-  // the expert groups of a token block share its z rows through one L2)
-  const int mt = ntb >= 128 ? et : 1;
+  // chip (z rows read once) and the tiles are whole, else one (more blocks,
+  // one round of loads each; the expert groups of a token block share its z
+  // rows through one L2)
+  const int mt = (ntb >= 128 && etot % 16 == 0) ? et : 1;
   const int ngroups = et / mt;
   const int kw = a.d / kRW;
   const int ku = (kw % 256 == 0 && mt == 1) ? 8 : (kw % 128 == 0 && mt <= 4) ? 4 : (kw % 64 == 0 && mt <= 8) ? 2 : 1;

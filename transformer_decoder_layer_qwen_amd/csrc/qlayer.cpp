@@ -83,7 +83,9 @@ struct ql_handle {
   int* slot_token;
   int* pos_of;
   void* hm;
-  bf16* out_slot;
+  float* out_slot;  // [N*k, d] expert outputs in slot order
+  void* hs;         // shared expert hidden: [N, 2 sf] pair (prefill) or [N, sf]
+  float* rs;        // [N, d] residual + gated shared expert output (fp32)
   int max_tiles;
   ql_taps taps;
   int ev_stage;
@@ -145,8 +147,17 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
       return fail(QL_EINVAL, "top_k must be in [1, min(n_experts, %d)]", kMaxTopK);
     if (!w->w_router || !w->we_gate || !w->we_up || !w->we_down)
       return fail(QL_EINVAL, "MoE weights must not be NULL");
+    if (c->shared_ffn_dim < 0) return fail(QL_EINVAL, "shared_ffn_dim must be >= 0");
+    if (c->shared_ffn_dim > 0) {
+      if (c->shared_ffn_dim % 128)
+        return fail(QL_EUNSUPPORTED, "shared_ffn_dim %% 128 must be 0");
+      if (!w->ws_gate || !w->ws_up || !w->ws_down || !w->w_shared_gate)
+        return fail(QL_EINVAL, "shared expert weights must not be NULL");
+    }
   } else {
     if (c->n_experts < 0) return fail(QL_EINVAL, "n_experts must be >= 0");
+    if (c->shared_ffn_dim != 0)
+      return fail(QL_EINVAL, "shared_ffn_dim needs a MoE layer (n_experts > 0)");
     if (!w->w_gate || !w->w_up || !w->w_down)
       return fail(QL_EINVAL, "dense FFN weights must not be NULL");
   }
@@ -184,9 +195,11 @@ size_t gemm2_call_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M, 
   if (!decode) {
     b = std::max(b, ql_gemm2_pair_part_bytes(M, qkv_dim, c.d));
     b = std::max(b, ql_gemm2_pair_part_bytes(M, c.d, q_dim));
-    if (c.n_experts == 0) {  // [hi | lo] pair inputs: doubled K
-      b = std::max(b, ql_gemm2_part_bytes(M, 2 * c.ffn_dim, gemm2_splits(M, 2 * c.ffn_dim, 2 * c.d)));
-      b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, 2 * c.ffn_dim)));
+    // dense FFN or shared expert: [hi | lo] pair inputs, doubled K
+    const int f = c.n_experts == 0 ? c.ffn_dim : c.shared_ffn_dim;
+    if (f > 0) {
+      b = std::max(b, ql_gemm2_part_bytes(M, 2 * f, gemm2_splits(M, 2 * f, 2 * c.d)));
+      b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, 2 * f)));
     }
     return b;
   }
@@ -197,9 +210,11 @@ size_t gemm2_call_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M, 
   }
   const bool gemv_ffn = M <= kGemvMaxRows && ql_gemv_ok(M, c.ffn_dim, c.d) &&
                         ql_gemv_ok(M, c.d, c.ffn_dim);
-  if (c.n_experts == 0 && !gemv_ffn) {
-    b = std::max(b, ql_gemm2_decode_part_bytes(M, 2 * c.ffn_dim, c.d, false));
-    b = std::max(b, ql_gemm2_decode_part_bytes(M, c.d, c.ffn_dim, false));
+  // dense FFN past the GEMV, or the shared expert: [hi | lo] pair inputs
+  const int f = c.n_experts == 0 ? (gemv_ffn ? 0 : c.ffn_dim) : c.shared_ffn_dim;
+  if (f > 0) {
+    b = std::max(b, ql_gemm2_decode_part_bytes(M, 2 * f, c.d, true));
+    b = std::max(b, ql_gemm2_decode_part_bytes(M, c.d, f, true));
   }
   return b;
 }
@@ -278,7 +293,7 @@ size_t layout(ql_handle* h, char* base, int exact_rows = 0) {
     const size_t nblk = (N + 255) / 256;
     h->max_tiles = (int)((NK + kMinMoeTile - 1) / kMinMoeTile + E);
     h->zf = k.take<float>(N * c.d * 4);
-    h->logits = k.take<float>(N * E * 4);
+    h->logits = k.take<float>(N * (E + (c.shared_ffn_dim > 0 ? 1 : 0)) * 4);
     h->idx = k.take<int>(NK * 4);
     h->topw = k.take<float>(NK * 4);
     h->hist = k.take<int>(nblk * E * 4);
@@ -290,8 +305,12 @@ size_t layout(ql_handle* h, char* base, int exact_rows = 0) {
     h->num_tiles = k.take<int>(4);
     h->slot_token = k.take<int>(NK * 4);
     h->pos_of = k.take<int>(NK * 4);
-    h->hm = k.take<void>(NK * c.ffn_dim * 2);
-    h->out_slot = k.take<bf16>(NK * c.d * 2);
+    h->hm = k.take<void>(NK * c.ffn_dim * 4);  // [hi | lo] bf16 pair, or fp32
+    h->out_slot = k.take<float>(NK * c.d * 4);
+    if (c.shared_ffn_dim > 0) {
+      h->hs = k.take<void>(N * 2 * (size_t)c.shared_ffn_dim * 2);
+      h->rs = k.take<float>(N * c.d * 4);
+    }
   } else {
     h->h = k.take<void>(N * c.ffn_dim * es * (c.dtype == QL_BF16 ? 2 : 1));  // bf16: [hi | lo]
   }
@@ -299,6 +318,8 @@ size_t layout(ql_handle* h, char* base, int exact_rows = 0) {
 }
 
 float scale_log2(int dh) { return 1.4426950408889634f / std::sqrt((float)dh); }
+
+ql_status copy_logits(ql_handle* h, int N, float* dst, hipStream_t s);
 
 ql_status copy_taps(ql_handle* h, int N, hipStream_t s) {
   const ql_config& c = h->cfg;
@@ -337,20 +358,27 @@ ql_status copy_taps(ql_handle* h, int N, hipStream_t s) {
     else
       QL_HIP(ql_bf16_to_f32(static_cast<const bf16*>(h->h), (size_t)N * c.ffn_dim, th, s));
   }
-  if (h->taps.logits && c.n_experts > 0)
-    QL_HIP(hipMemcpyAsync(h->taps.logits, h->logits, (size_t)N * c.n_experts * 4,
-                          hipMemcpyDeviceToDevice, s));
+  if (h->taps.logits && c.n_experts > 0) {
+    ql_status st = copy_logits(h, N, h->taps.logits, s);
+    if (st != QL_OK) return st;
+  }
   return QL_OK;
 }
 
-// y = resid + MoE(z); z bf16 and zf fp32 hold RMSNorm2 of the residual rows.
+// y = resid + MoE(z). RMSNorm2 of the residual rows is in zf (fp32: the
+// router and the 32-row expert tiles) and in h->xhat as a [hi | lo] bf16
+// pair (the 256-row expert tiles and the shared expert). `decode`: the
+// shared expert runs on the decode tiles.
 ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf16* y,
-                   hipStream_t s) {
+                   bool decode, hipStream_t s) {
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
+  const int sf = c.shared_ffn_dim;
   RouterArgs ra{};
   ra.zf = h->zf;
   ra.wr = static_cast<const bf16*>(w.w_router);
+  ra.w_extra = sf > 0 ? static_cast<const bf16*>(w.w_shared_gate) : nullptr;  // logit column E
+  ra.n_extra = sf > 0 ? 1 : 0;
   ra.N = N;
   ra.d = c.d;
   ra.E = c.n_experts;
@@ -384,25 +412,52 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
   pa.pos_of = h->pos_of;
   QL_STAGE(h, QL_STAGE_PERMUTE, s, QL_HIP(ql_moe_permute(pa, s)));
 
-  const bf16* z = static_cast<const bf16*>(h->z);
+  // The experts see z at fp32 precision and keep h and their outputs so:
+  // 256-row tiles read the [hi | lo] pair of z (x-hat buffer) over a doubled
+  // K and store h as a pair; 32-row tiles stage fp32 z and h as pairs
+  // themselves. Outputs are fp32 in slot order.
+  const bf16* z2 = static_cast<const bf16*>(h->xhat);
   const bf16* wg = static_cast<const bf16*>(w.we_gate);
   const bf16* wu = static_cast<const bf16*>(w.we_up);
   const bf16* wd = static_cast<const bf16*>(w.we_down);
-  bf16* hm = static_cast<bf16*>(h->hm);
   if (big) {
+    bf16* hm = static_cast<bf16*>(h->hm);
     QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
-             QL_HIP(ql_gemm2_moe_gu(z, h->slot_token, wg, wu, c.ffn_dim, c.d, h->tile_expert,
+             QL_HIP(ql_gemm2_moe_gu(z2, h->slot_token, wg, wu, c.ffn_dim, c.d, h->tile_expert,
                                     h->tile_row0, h->tile_rows, h->num_tiles, max_tiles, hm, s)));
     QL_STAGE(h, QL_STAGE_EXPERT_DOWN, s,
              QL_HIP(ql_gemm2_moe_down(hm, wd, c.ffn_dim, c.d, h->tile_expert, h->tile_row0,
                                       h->tile_rows, h->num_tiles, max_tiles, h->out_slot, s)));
   } else {
+    float* hm = static_cast<float*>(h->hm);
     QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
-             QL_HIP(ql_gemm_moe_gu(z, h->slot_token, wg, wu, c.ffn_dim, c.d, h->tile_expert,
+             QL_HIP(ql_gemm_moe_gu(h->zf, h->slot_token, wg, wu, c.ffn_dim, c.d, h->tile_expert,
                                    h->tile_row0, h->tile_rows, h->num_tiles, max_tiles, hm, s)));
     QL_STAGE(h, QL_STAGE_EXPERT_DOWN, s,
              QL_HIP(ql_gemm_moe_down(hm, wd, c.ffn_dim, c.d, h->tile_expert, h->tile_row0,
                                      h->tile_rows, h->num_tiles, max_tiles, h->out_slot, s)));
+  }
+  if (sf > 0) {
+    // Shared expert ("Qwen2.5-7B 结构拆解" §10.1): SwiGLU of width sf on every
+    // row from the pair of z, h_s kept as a pair, then rs = resid +
+    // sigmoid(gate logit) * (h_s W_sd^T); the gate logit is the router's
+    // column E. Prefill tiles with split-K plans, or the decode tiles.
+    bf16* hs = static_cast<bf16*>(h->hs);
+    const bf16* sg = static_cast<const bf16*>(w.ws_gate);
+    const bf16* su = static_cast<const bf16*>(w.ws_up);
+    const bf16* sd = static_cast<const bf16*>(w.ws_down);
+    const int sgu = decode ? 1 : gemm2_splits(N, 2 * sf, 2 * c.d);
+    const int sdn = decode ? 1 : gemm2_splits(N, c.d, 2 * sf);
+    QL_STAGE(h, QL_STAGE_SHARED_GATE_UP, s,
+             QL_HIP(ql_gemm2_swiglu(z2, N, sg, su, sf, c.d, hs, decode, sgu, h->g2part, s, true)));
+    QL_STAGE(h, QL_STAGE_SHARED_DOWN, s,
+             QL_HIP(ql_gemm2_gated_out(
+                 hs, N, sd, c.d, sf, h->logits + c.n_experts, c.n_experts + 1,
+                 resid_is_f32 ? static_cast<const float*>(resid) : nullptr,
+                 resid_is_f32 ? nullptr : static_cast<const bf16*>(resid), h->rs, decode, sdn,
+                 h->g2part, s, true)));
+    resid = h->rs;
+    resid_is_f32 = 1;
   }
   CombineArgs ca{};
   ca.out_slot = h->out_slot;
@@ -416,60 +471,63 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
   return QL_OK;
 }
 
+// router logits [N, E] of the last MoE call -> dst (the handle keeps a gate
+// column E beside them when the layer has a shared expert)
+ql_status copy_logits(ql_handle* h, int N, float* dst, hipStream_t s) {
+  const ql_config& c = h->cfg;
+  const size_t E = c.n_experts, ld = E + (c.shared_ffn_dim > 0 ? 1 : 0);
+  if (ld == E)
+    QL_HIP(hipMemcpyAsync(dst, h->logits, (size_t)N * E * 4, hipMemcpyDeviceToDevice, s));
+  else
+    QL_HIP(hipMemcpy2DAsync(dst, E * 4, h->logits, ld * 4, E * 4, (size_t)N,
+                            hipMemcpyDeviceToDevice, s));
+  return QL_OK;
+}
+
 // ---- bf16 layer -------------------------------------------------------------
 
 ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_t s) {
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
-  bf16* z = static_cast<bf16*>(h->z);
   const bf16* g2 = static_cast<const bf16*>(w.ln2_g);
-  h->ffn_pair = false;
-  if (!decode && c.n_experts == 0) {
-    // Prefill, dense: RMSNorm2's output and the SwiGLU hidden stay fp32 as
-    // [hi | lo] bf16 pairs (the x-hat buffer is free once Q/K/V exist) and
-    // enter gate/up and down over a doubled K.
-    bf16* z2 = static_cast<bf16*>(h->xhat);
-    bf16* hh = static_cast<bf16*>(h->h);
-    QL_STAGE(h, QL_STAGE_RMSNORM2, s,
-             QL_HIP(ql_rmsnorm_f32_to_hilo(h->r, g2, z2, N, c.d, c.rms_eps, s)));
-    const int sgu = gemm2_splits(N, 2 * c.ffn_dim, 2 * c.d);
-    const int sdn = gemm2_splits(N, c.d, 2 * c.ffn_dim);
-    QL_STAGE(h, QL_STAGE_GATE_UP, s,
-             QL_HIP(ql_gemm2_swiglu(z2, N, static_cast<const bf16*>(w.w_gate),
-                                    static_cast<const bf16*>(w.w_up), c.ffn_dim, c.d, hh, false,
-                                    sgu, h->g2part, s, true)));
-    QL_STAGE(h, QL_STAGE_DOWN, s,
-             QL_HIP(ql_gemm2_resid_out(hh, N, static_cast<const bf16*>(w.w_down), c.d, c.ffn_dim,
-                                       h->r, y, false, sdn, h->g2part, s, true)));
-    h->ffn_pair = true;
-    return QL_OK;
-  }
-  // few rows on the dense path: RMSNorm2 rides inside the gate/up projection
-  // (z is then only formed when a tap asks for it)
-  const bool gemv = decode && c.n_experts == 0 && N <= kGemvMaxRows &&
-                    ql_gemv_ok(N, c.ffn_dim, c.d) && ql_gemv_ok(N, c.d, c.ffn_dim);
-  if (!gemv || h->taps.z)
-    QL_STAGE(h, QL_STAGE_RMSNORM2, s,
-             QL_HIP(ql_rmsnorm_f32in_bf16(h->r, g2, z, c.n_experts > 0 ? h->zf : nullptr, N,
-                                          c.d, c.rms_eps, s)));
-  if (c.n_experts > 0) return moe_core(h, N, h->r, 1, y, s);
   bf16* hh = static_cast<bf16*>(h->h);
   const bf16* wg = static_cast<const bf16*>(w.w_gate);
   const bf16* wu = static_cast<const bf16*>(w.w_up);
   const bf16* wd = static_cast<const bf16*>(w.w_down);
+  h->ffn_pair = false;
+  // Dense decode of a few rows: RMSNorm2 rides inside the gate/up GEMV, whose
+  // z is never rounded (it is only formed, in bf16, when a tap asks for it).
+  const bool gemv = decode && c.n_experts == 0 && N <= kGemvMaxRows &&
+                    ql_gemv_ok(N, c.ffn_dim, c.d) && ql_gemv_ok(N, c.d, c.ffn_dim);
   if (gemv) {
+    if (h->taps.z)
+      QL_STAGE(h, QL_STAGE_RMSNORM2, s,
+               QL_HIP(ql_rmsnorm_f32in_bf16(h->r, g2, static_cast<bf16*>(h->z), nullptr, N, c.d,
+                                            c.rms_eps, s)));
     QL_STAGE(h, QL_STAGE_GATE_UP, s,
              QL_HIP(ql_gemv_rmsnorm_swiglu(h->r, g2, c.rms_eps, N, wg, wu, c.ffn_dim, c.d, hh, s)));
     QL_STAGE(h, QL_STAGE_DOWN, s,
              QL_HIP(ql_gemv_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, s)));
     return QL_OK;
   }
-  // decode tiles (more rows than the GEMV takes) cut their work evenly over
-  // the CUs themselves
+  // Otherwise RMSNorm2's output and the FFN hidden stay fp32 as [hi | lo]
+  // bf16 pairs (the x-hat buffer is free once Q/K/V exist): gate/up and down
+  // read them over a doubled K (prefill tiles) or with hi and lo rows sharing
+  // each weight tile (decode tiles); the MoE router also gets fp32 z.
+  bf16* z2 = static_cast<bf16*>(h->xhat);
+  QL_STAGE(h, QL_STAGE_RMSNORM2, s,
+           QL_HIP(ql_rmsnorm_f32_to_hilo(h->r, g2, z2, N, c.d, c.rms_eps, s,
+                                         c.n_experts > 0 ? h->zf : nullptr)));
+  h->ffn_pair = c.n_experts == 0;
+  if (c.n_experts > 0) return moe_core(h, N, h->r, 1, y, decode, s);
+  const int sgu = decode ? 1 : gemm2_splits(N, 2 * c.ffn_dim, 2 * c.d);
+  const int sdn = decode ? 1 : gemm2_splits(N, c.d, 2 * c.ffn_dim);
   QL_STAGE(h, QL_STAGE_GATE_UP, s,
-           QL_HIP(ql_gemm2_swiglu(z, N, wg, wu, c.ffn_dim, c.d, hh, true, 1, h->g2part, s)));
+           QL_HIP(ql_gemm2_swiglu(z2, N, wg, wu, c.ffn_dim, c.d, hh, decode, sgu, h->g2part, s,
+                                  true)));
   QL_STAGE(h, QL_STAGE_DOWN, s,
-           QL_HIP(ql_gemm2_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, true, 1, h->g2part, s)));
+           QL_HIP(ql_gemm2_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, decode, sdn, h->g2part,
+                                     s, true)));
   return QL_OK;
 }
 
@@ -827,7 +885,7 @@ ql_status qlayer_set_taps(ql_handle* h, const ql_taps* taps) {
 
 ql_status qlayer_set_stage_events(ql_handle* h, int stage, void* start_event, void* stop_event) {
   if (!h) return fail(QL_EINVAL, "handle must not be NULL");
-  if (stage < QL_STAGE_NONE || stage > QL_STAGE_COMBINE)
+  if (stage < QL_STAGE_NONE || stage > QL_STAGE_SHARED_DOWN)
     return fail(QL_EINVAL, "unknown stage %d", stage);
   if (stage == QL_STAGE_NONE || !start_event || !stop_event) {
     h->ev_stage = QL_STAGE_NONE;
@@ -918,17 +976,19 @@ ql_status qlayer_moe_ffn(ql_handle* h, const void* r, int N, void* y, int* topk_
   if (r == y) return fail(QL_EINVAL, "moe_ffn: y must not alias r");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ql_config& c = h->cfg;
-  QL_HIP(ql_rmsnorm_bf16(static_cast<const bf16*>(r), static_cast<const bf16*>(h->w.ln2_g),
-                         static_cast<bf16*>(h->z), h->zf, N, c.d, c.rms_eps, s));
-  ql_status st = moe_core(h, N, r, 0, static_cast<bf16*>(y), s);
+  // RMSNorm2 as a [hi | lo] pair and in fp32; the N rows run as a prefill
+  QL_HIP(ql_rmsnorm_bf16_to_hilo(static_cast<const bf16*>(r), static_cast<const bf16*>(h->w.ln2_g),
+                                 static_cast<bf16*>(h->xhat), N, c.d, c.rms_eps, s, h->zf));
+  ql_status st = moe_core(h, N, r, 0, static_cast<bf16*>(y), false, s);
   if (st != QL_OK) return st;
   const size_t nk = (size_t)N * c.top_k;
   if (topk_idx)
     QL_HIP(hipMemcpyAsync(topk_idx, h->idx, nk * 4, hipMemcpyDeviceToDevice, s));
   if (topk_w) QL_HIP(hipMemcpyAsync(topk_w, h->topw, nk * 4, hipMemcpyDeviceToDevice, s));
-  if (h->taps.logits)
-    QL_HIP(hipMemcpyAsync(h->taps.logits, h->logits, (size_t)N * c.n_experts * 4,
-                          hipMemcpyDeviceToDevice, s));
+  if (h->taps.logits) {
+    st = copy_logits(h, N, h->taps.logits, s);
+    if (st != QL_OK) return st;
+  }
   if (h->taps.z)
     QL_HIP(hipMemcpyAsync(h->taps.z, h->zf, (size_t)N * c.d * 4, hipMemcpyDeviceToDevice, s));
   return QL_OK;

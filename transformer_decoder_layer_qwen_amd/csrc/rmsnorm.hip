@@ -88,6 +88,7 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict_
         for (int j = 0; j < V; ++j) lo[j] = o[j] - (float)(bf16)o[j];
         storev<TOut, V>(orow + c, o);
         storev<TOut, V>(orow + d + c, lo);
+        if (out_f32) storev<float, V>(out_f32 + row * d + c, o);
       } else {
         storev<TOut, V>(out + row * d + c, o);
         if (out_f32) storev<float, V>(out_f32 + row * d + c, o);
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const TIn* __restrict__ x,
     const float o = to_f32(gamma[c]) * (to_f32(xr[c]) * inv);
     orow[c] = from_f32<TOut>(o);
     if constexpr (HILO) orow[d + c] = from_f32<TOut>(o - to_f32(from_f32<TOut>(o)));
-    else if (out_f32) out_f32[(size_t)row * d + c] = o;
+    if (out_f32) out_f32[(size_t)row * d + c] = o;
   }
 }
 
@@ -155,8 +156,8 @@ hipError_t ql_rmsnorm_bf16(const bf16* x, const bf16* gamma, bf16* out, float* o
   return launch<bf16, bf16, bf16>(x, gamma, out, out_f32, rows, d, eps, s);
 }
 hipError_t ql_rmsnorm_bf16_to_hilo(const bf16* x, const bf16* gamma, bf16* out, int rows, int d,
-                                   float eps, hipStream_t s) {
-  return launch<bf16, bf16, bf16, true>(x, gamma, out, nullptr, rows, d, eps, s);
+                                   float eps, hipStream_t s, float* out_f32) {
+  return launch<bf16, bf16, bf16, true>(x, gamma, out, out_f32, rows, d, eps, s);
 }
 
 namespace {
@@ -181,8 +182,8 @@ hipError_t ql_rmsnorm_f32in_bf16(const float* x, const bf16* gamma, bf16* out, f
   return launch<float, bf16, bf16>(x, gamma, out, out_f32, rows, d, eps, s);
 }
 hipError_t ql_rmsnorm_f32_to_hilo(const float* x, const bf16* gamma, bf16* out, int rows, int d,
-                                  float eps, hipStream_t s) {
-  return launch<float, bf16, bf16, true>(x, gamma, out, nullptr, rows, d, eps, s);
+                                  float eps, hipStream_t s, float* out_f32) {
+  return launch<float, bf16, bf16, true>(x, gamma, out, out_f32, rows, d, eps, s);
 }
 
 namespace {
