@@ -279,6 +279,36 @@ def time_stage(setup, hip, stage, steps):
     return tot / steps
 
 
+def time_stage_graph(setup, hip, stage, reps):
+    """Mean duration of one stage inside graph replay: the library's stage
+    events are captured into the graph with the calls (one event pair per
+    weight copy), the graph is replayed `reps` times and each replay's pairs
+    are read after it completes. No host launch gap can fall inside a
+    window, and the kernels run back to back as in the timed loop."""
+    import torch
+    n = len(setup.layers)
+    evs = hip.create(2 * n)
+    for c, layer in enumerate(setup.layers):
+        layer.set_stage_events(stage, evs[2 * c], evs[2 * c + 1])
+    try:
+        g = setup.capture()
+    finally:
+        for layer in setup.layers:
+            layer.set_stage_events(None, None, None)
+    tot, cnt = 0.0, 0
+    for r in range(reps + 1):
+        g.replay()
+        torch.cuda.synchronize()
+        if r == 0:
+            continue   # the first replay warms up
+        for c in range(n):
+            tot += hip.elapsed_ms(evs[2 * c], evs[2 * c + 1])
+            cnt += 1
+    del g
+    hip.destroy(evs)
+    return tot / cnt
+
+
 GEMV_MAX_ROWS = 4   # dense decode with this many rows or fewer folds RMSNorm2 into gate/up
 
 
@@ -350,7 +380,8 @@ def roofline_entry(cfg, wl, stage, ms):
             "algorithmic_flops": int(fl), "kernel_ms": round(ms, 5), "stage": stage}
 
 
-def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_graph=True):
+def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_graph=True,
+                 graph_stage_probe=False):
     setup = Setup(cid, wl)
     cfg = setup.cfg
     graph = setup.capture() if use_graph else None
@@ -373,6 +404,9 @@ def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_g
             st[s] = round(max(time_stage(setup, hip, s, stage_steps) - empty, 1e-6), 5)
         out["stage_ms"] = st
         out["event_span_overhead_ms"] = round(empty, 5)
+        if graph_stage_probe:
+            out["stage_ms_graph"] = {s: round(time_stage_graph(setup, hip, s, stage_steps), 5)
+                                     for s in st}
         dom = max(st, key=st.get)
         out["dominant"] = roofline_entry(cfg, wl, dom, st[dom])
         gemms = [s for s in ("qkv", "o_proj", "gate_up", "down", "expert_gate_up",
@@ -488,6 +522,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-steps", type=int, default=10)
     ap.add_argument("--eager", action="store_true", help="no HIP graph replay")
+    ap.add_argument("--graph-stage-probe", action="store_true",
+                    help="also time every stage with events captured in graph replay")
     ap.add_argument("--only", default=None,
                     help="time one workload CID:INDEX of the config table instead of the headline")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
@@ -523,7 +559,7 @@ def main():
         print(json.dumps(r), flush=True)
         return
     head, _ = run_workload(cid, wl, hip, args.steps, args.warmup, args.stage_steps,
-                           use_graph=not args.eager)
+                           use_graph=not args.eager, graph_stage_probe=args.graph_stage_probe)
     log(f"[bench] headline {head['workload']}: {head['tokens_per_s']} tok/s, "
         f"{head['ms_per_step']} ms/step")
     secondary = []

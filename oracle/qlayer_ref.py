@@ -432,3 +432,36 @@ def layer_decode(x, k_cache, v_cache, cache_len, w, spec: LayerSpec,
            "z": z, "f": F}
     out.update(extra)
     return out
+
+
+def layer_prefill_chunk(x_new, k_cache, v_cache, cache_len, w, spec: LayerSpec,
+                        pos_offset: int = 0) -> Dict[str, np.ndarray]:
+    """Prefill of new tokens over an existing cache prefix, one sequence
+    ([P1 §09.1]: the cache grows by the new rows; [P3 §8]: causal).
+
+    x_new: [S, d] new-token hidden rows; k_cache/v_cache: [T_max, Hkv, dh]
+    holding rows 0..cache_len-1 as stored (post-norm, post-RoPE keys). New
+    row t sits at cache row cache_len + t, position cache_len + t +
+    pos_offset, and attends to cache rows 0..cache_len-1 and new rows 0..t.
+
+    The projections and the FFN take the S rows as one matrix (rows never
+    interact, [P1 §03.2]). Returns y, r, q, attn, z, f [S, ...] and the new
+    cache rows k_new, v_new [S, Hkv, dh].
+    """
+    x = f64(x_new)
+    S, d = x.shape
+    Hq, dh = spec.n_q_heads, spec.head_dim
+    P = int(cache_len)
+    pos = np.arange(S, dtype=np.float64) + P + pos_offset
+    xhat = rmsnorm(x, w["ln1_g"], spec.eps)
+    q, k, v = _project_qkv(xhat, w, spec, pos)
+    K = np.concatenate([f64(k_cache[:P]), k], axis=0)
+    V = np.concatenate([f64(v_cache[:P]), v], axis=0)
+    o = attention(q, K, V, np.arange(S) + P, np.arange(P + S), spec.n_kv_heads)
+    attn = o.reshape(S, Hq * dh)                                      # concat heads [P3 §9]
+    r = x + linear(attn, w["wo"])
+    z = rmsnorm(r, w["ln2_g"], spec.eps)
+    F, extra = _ffn(z, w, spec)
+    out = {"y": r + F, "r": r, "q": q, "k_new": k, "v_new": v, "attn": attn, "z": z, "f": F}
+    out.update(extra)
+    return out

@@ -30,8 +30,8 @@ def spec_of(cfg, **kw):
     s = dict(d=cfg.d, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
              head_dim=cfg.head_dim, ffn_dim=cfg.ffn_dim, n_experts=cfg.n_experts,
              top_k=cfg.top_k, norm_topk_prob=cfg.norm_topk_prob,
-             qkv_bias=cfg.qkv_bias, qk_norm=cfg.qk_norm, eps=cfg.rms_eps,
-             theta=cfg.rope_theta)
+             shared_ffn_dim=cfg.shared_ffn_dim, qkv_bias=cfg.qkv_bias, qk_norm=cfg.qk_norm,
+             eps=cfg.rms_eps, theta=cfg.rope_theta)
     s.update(kw)
     return ref.LayerSpec(**s)
 
@@ -455,6 +455,35 @@ def test_decode_equals_prefill_last_row():
         assert np.max(np.abs(dec["y"] - full["y"][:, T - 1])) < 1e-12
         assert np.max(np.abs(dec["k_new"] - full["k"][:, T - 1])) < 1e-12
         assert np.max(np.abs(dec["v_new"] - full["v"][:, T - 1])) < 1e-12
+
+
+def test_chunked_prefill_equals_the_whole_sequence():
+    """A prefix of P rows prefilled into the cache, then the remaining S rows
+    as a chunk over it, gives rows P..P+S-1 of the prefill of all P+S rows
+    ("Qwen2.5-7B 结构拆解" §09.1); a one-row chunk is the decode step."""
+    for cfg in (configs.TOY, small_cfg(qk_norm=True, qkv_bias=True),
+                small_cfg(n_experts=8, top_k=3, ffn_dim=24, norm_topk_prob=False,
+                          shared_ffn_dim=40, router_std=0.3)):
+        spec = spec_of(cfg)
+        w = f32_weights(synth.make_weights(cfg, 1000))
+        T, P = 9, 5
+        x = synth.to_f32(synth.make_prefill_input(cfg, 1002, 1, T))[0]
+        full = ref.layer_prefill(x[None], w, spec, pos_offset=2)
+        part = ref.layer_prefill(x[None, :P], w, spec, pos_offset=2)
+        kc = np.full((T + 3, cfg.n_kv_heads, cfg.head_dim), np.nan)  # rows >= P never read
+        vc = np.full_like(kc, np.nan)
+        kc[:P], vc[:P] = part["k"][0], part["v"][0]
+        ch = ref.layer_prefill_chunk(x[P:], kc, vc, P, w, spec, pos_offset=2)
+        assert np.max(np.abs(ch["y"] - full["y"][0, P:])) < 1e-12
+        assert np.max(np.abs(ch["k_new"] - full["k"][0, P:])) < 1e-12
+        assert np.max(np.abs(ch["v_new"] - full["v"][0, P:])) < 1e-12
+        one = ref.layer_prefill_chunk(x[P:P + 1], kc, vc, P, w, spec, pos_offset=2)
+        dec = ref.layer_decode(x[None, P], kc[None], vc[None], np.array([P]), w, spec,
+                               pos_offset=2)
+        assert np.max(np.abs(one["y"][0] - dec["y"][0])) < 1e-12
+        # an empty prefix is the plain prefill
+        zero = ref.layer_prefill_chunk(x, kc, vc, 0, w, spec, pos_offset=2)
+        assert np.max(np.abs(zero["y"] - full["y"][0])) < 1e-12
 
 
 def test_prefill_row_subset_matches_full():
