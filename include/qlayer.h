@@ -156,6 +156,30 @@ size_t qlayer_workspace_bytes(const ql_handle* h);
 ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offset,
                          void* k_cache, void* v_cache, int T_max, void* y, void* stream);
 
+/* Prefill of new rows over existing cache prefixes, for a batch of
+ * sequences of different lengths (chunked prefill: "Qwen2.5-7B 结构拆解"
+ * §09.1, the cache grows by the new rows; causal as in "推理系统 03" §8).
+ *
+ * x          [N, d]  the new rows of every sequence, concatenated
+ * seq_start  [B + 1] int32 DEVICE: sequence b's new rows are x rows
+ *            seq_start[b] .. seq_start[b + 1] - 1 (seq_start[0] = 0,
+ *            non-decreasing, N = seq_start[B]; a sequence may have none)
+ * cache_len  [B] int32 DEVICE: rows 0 .. cache_len[b] - 1 of sequence b's
+ *            cache hold earlier keys/values (keys normed and rotated). New
+ *            row t is written at cache row cache_len[b] + t, has RoPE position
+ *            cache_len[b] + t + pos_offset and attends to cache rows
+ *            0 .. cache_len[b] + t. The caller advances cache_len afterwards.
+ * seq_start_host, cache_len_host  HOST copies of both (required): the
+ *            launch shapes come from them and the bounds are checked there.
+ * k_cache, v_cache [B, T_max, Hkv, dh];  y [N, d] (may not alias x)
+ * Errors: QL_EINVAL (NULL, bad seq_start, N = 0 or > max_tokens),
+ * QL_ECACHE_FULL (cache_len[b] + new rows > T_max), QL_EUNSUPPORTED
+ * (QL_F32), QL_EHIP. */
+ql_status qlayer_prefill_varlen(ql_handle* h, const void* x, int B, const int* seq_start,
+                                const int* cache_len, const int* seq_start_host,
+                                const int* cache_len_host, int pos_offset, void* k_cache,
+                                void* v_cache, int T_max, void* y, void* stream);
+
 /* Decode: one new token per sequence ("Qwen2.5-7B 结构拆解" §09.1).
  *
  * x          [B, d]     hidden row of the new token of each sequence

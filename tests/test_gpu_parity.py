@@ -608,6 +608,125 @@ def test_full_size_moe_ffn_routing():
     assert e <= BF16_TOL and ef <= MOE_BRANCH_TOL
 
 
+# ---------------------------------------- chunked and variable-length prefill ----
+
+def check_varlen(cfg, layer, w64, lens, prefix, seed, T_max, label, prefill_prefix=False):
+    """qlayer_prefill_varlen on sequences with `lens` new rows over `prefix`
+    cached rows each, against the oracle's chunked prefill per sequence fed
+    the same cache prefix: every new row of y, every new cache row, all other
+    cache rows untouched. The prefix rows are N(0, 1) synthetic cache rows, or
+    (prefill_prefix) written by qlayer_prefill of earlier rows of the same
+    sequences, in which case y must also match the whole-sequence prefill."""
+    Bn = len(lens)
+    spec = spec_of(cfg)
+    ss = [0]
+    for n in lens:
+        ss.append(ss[-1] + n)
+    N = ss[-1]
+    full_x = [synth.make_prefill_input(cfg, seed + b, 1, prefix[b] + lens[b])[0]
+              for b in range(Bn)]
+    if prefill_prefix:
+        kc = torch.zeros(Bn, T_max, cfg.n_kv_heads, cfg.head_dim, dtype=torch.bfloat16,
+                         device="cuda")
+        vc = torch.zeros_like(kc)
+        for b in range(Bn):   # one sequence at a time: the prefixes differ in length
+            if prefix[b]:
+                kb, vb = kc[b:b + 1].clone(), vc[b:b + 1].clone()
+                layer.prefill(B.to_device(np.ascontiguousarray(full_x[b][None, :prefix[b]])),
+                              kb, vb)
+                kc[b:b + 1], vc[b:b + 1] = kb, vb
+        torch.cuda.synchronize()
+        kc_np, vc_np = host(kc), host(vc)
+    else:
+        _, kc_b, vc_b, _ = synth.make_decode_input(cfg, seed + 99, Bn, max(prefix), T_max=T_max,
+                                                   canary="nan")
+        for b in range(Bn):
+            kc_b[b, prefix[b]:] = synth.BF16_NAN_BITS
+            vc_b[b, prefix[b]:] = synth.BF16_NAN_BITS
+        kc, vc = B.to_device(kc_b), B.to_device(vc_b)
+        kc_np, vc_np = synth.to_f32(kc_b), synth.to_f32(vc_b)
+    x_new = np.concatenate([full_x[b][prefix[b]:] for b in range(Bn)], axis=0)
+    r_t = torch.empty(N, cfg.d, dtype=torch.float32, device="cuda")
+    layer.set_taps(r=r_t)
+    y = layer.prefill_varlen(B.to_device(x_new), ss, prefix, kc, vc)
+    torch.cuda.synchronize()
+    layer.clear_taps()
+    yg, rg, kg, vg = host(y), host(r_t), host(kc), host(vc)
+    y_ref, r_ref, f_ref, x64 = [], [], [], []
+    for b in range(Bn):
+        if lens[b] == 0:
+            continue
+        xb = synth.to_f32(full_x[b][prefix[b]:]).astype(np.float64)
+        o = ref.layer_prefill_chunk(xb, kc_np[b], vc_np[b], prefix[b], w64, spec)
+        y_ref.append(o["y"]), r_ref.append(o["r"]), f_ref.append(o["f"]), x64.append(xb)
+        rows = slice(prefix[b], prefix[b] + lens[b])
+        assert rounding_err(kg[b, rows], o["k_new"]) <= 1.0, b
+        assert rounding_err(vg[b, rows], o["v_new"]) <= 1.0, b
+        # rows outside the new ones are untouched
+        assert np.array_equal(kg[b, :prefix[b]], kc_np[b, :prefix[b]], equal_nan=True)
+        assert np.array_equal(kg[b, prefix[b] + lens[b]:], kc_np[b, prefix[b] + lens[b]:],
+                              equal_nan=True)
+        if prefill_prefix:   # the chunk is the tail of the whole-sequence prefill
+            whole = ref.layer_prefill(synth.to_f32(full_x[b][None]).astype(np.float64), w64, spec,
+                                      rows=np.arange(prefix[b], prefix[b] + lens[b]))
+            assert rel_err(yg[ss[b]:ss[b + 1]], whole["y"][0]) <= BF16_TOL, b
+    y_ref, r_ref, f_ref, x64 = (np.concatenate(a) for a in (y_ref, r_ref, f_ref, x64))
+    e = rel_err(yg, y_ref)
+    ea = rowwise_err(rg - x64, r_ref - x64)
+    ef = branch_err(yg, rg, f_ref)
+    log(f"[gpu] {label}: {N} new rows over prefixes {prefix}: y {e:.2e}  attention branch "
+        f"(worst row) {ea:.2e}  ffn branch {ef:.2e}")
+    assert e <= BF16_TOL and ea <= ATT_ROW_TOL
+    assert ef <= (MOE_BRANCH_TOL if cfg.is_moe else FFN_BRANCH_TOL)
+
+
+# (lens, prefix, T_max): one chunk over a prefix; ragged batches with empty,
+# one-row and multi-tile sequences, prefixes that are not tile multiples
+VARLEN_SMALL = {
+    "chunk_1seq": ([130], [300], 448),
+    "batch4": ([37, 200, 0, 129], [100, 17, 64, 250], 400),
+    "batch5_no_prefix": ([1, 300, 5, 128, 77], [0, 0, 0, 0, 0], 320),
+    "batch3_one_row": ([1, 1, 260], [299, 0, 40], 320),
+}
+
+
+@pytest.mark.parametrize("case", list(VARLEN_SMALL))
+def test_small_prefill_varlen(case):
+    lens, prefix, T_max = VARLEN_SMALL[case]
+    cfg = small_cfg()
+    layer, w64 = make_layer(cfg, max_tokens=max(sum(lens), 1) + 300, max_batch=1)
+    check_varlen(cfg, layer, w64, lens, prefix, 1100, T_max, f"small varlen {case}")
+    layer.close()
+
+
+def test_small_chunked_prefill_continues_a_prefill():
+    cfg = small_cfg()
+    layer, w64 = make_layer(cfg, max_tokens=512, max_batch=1)
+    check_varlen(cfg, layer, w64, [90, 200], [211, 128], 1200, 420, "small chunk after prefill",
+                 prefill_prefix=True)
+    layer.close()
+
+
+def test_small_moe_prefill_varlen():
+    cfg = small_moe_cfg(n_experts=16, top_k=4, norm_topk_prob=False, shared_ffn_dim=512)
+    layer, w64 = make_layer(cfg, max_tokens=600, max_batch=1)
+    check_varlen(cfg, layer, w64, [150, 0, 290], [40, 7, 200], 1300, 512, "small MoE varlen")
+    layer.close()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cid,lens,prefix,T_max", [
+    (4, [512], [2048], 2560),                                  # a chunk over a 2048-row prefix
+    (3, [700, 300, 1024, 24], [0, 512, 100, 2000], 2048),      # a varlen batch, 2048 new rows
+], ids=["qwen3-8b_chunk512_over_2048", "qwen2.5-7b_varlen4"])
+def test_full_size_prefill_varlen(cid, lens, prefix, T_max):
+    cfg = configs.CONFIGS[cid]
+    layer, w64 = make_layer(cfg, seed=configs.weight_seed(cid), max_tokens=sum(lens), max_batch=1)
+    check_varlen(cfg, layer, w64, lens, prefix, 100 * cid + 70, T_max,
+                 f"{cfg.name} varlen {lens}")
+    layer.close()
+
+
 # A handle sized for more rows than the call: the split-K partial space must
 # cover every row count up to max_tokens (the plans split fewer row tiles
 # more ways), and one handle serves calls of several sizes in turn.

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "QL_OK", -1: "QL_EINVAL", -2: "QL_EUNSUPPORTED", -3: "QL_ENOM
 
 # every function include/qlayer.h declares
 EXPORTS = ("qlayer_create", "qlayer_destroy", "qlayer_workspace_bytes", "qlayer_prefill",
-           "qlayer_decode", "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
+           "qlayer_prefill_varlen", "qlayer_decode", "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
            "qlayer_set_stage_events", "qlayer_last_error", "qlayer_abi_version")
 NOALLOC_MAX_WORKSPACE = 64 << 20
 
@@ -92,6 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qlayer_workspace_bytes.restype = ctypes.c_size_t
     lib.qlayer_prefill.argtypes = [vp, vp, ci, ci, ci, vp, vp, ci, vp, vp]
     lib.qlayer_decode.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, ci, vp, vp]
+    lib.qlayer_prefill_varlen.argtypes = [vp, vp, ci, vp, vp, vp, vp, ci, vp, vp, ci, vp, vp]
     lib.qlayer_decode_noalloc.argtypes = [ctypes.POINTER(QlConfig), ctypes.POINTER(QlWeights), vp,
                                           ci, vp, vp, ci, vp, vp, ci, vp, vp]
     lib.qlayer_moe_ffn.argtypes = [vp, vp, ci, vp, vp, vp, vp]
@@ -100,7 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qlayer_last_error.restype = ctypes.c_char_p
     lib.qlayer_last_error.argtypes = []
     lib.qlayer_abi_version.restype = ci
-    for name in ("qlayer_create", "qlayer_destroy", "qlayer_prefill", "qlayer_decode",
+    for name in ("qlayer_create", "qlayer_destroy", "qlayer_prefill", "qlayer_prefill_varlen",
+                 "qlayer_decode",
                  "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
                  "qlayer_set_stage_events"):
         getattr(lib, name).restype = ci
@@ -141,6 +143,13 @@ def qlayer_workspace_bytes(h: int) -> int:
 def qlayer_prefill(h, x, B, S, pos_offset, k_cache, v_cache, T_max, y, stream) -> None:
     _check(load_library().qlayer_prefill(h, x, B, S, pos_offset, k_cache, v_cache, T_max, y,
                                          stream))
+
+
+def qlayer_prefill_varlen(h, x, B, seq_start, cache_len, seq_start_host, cache_len_host,
+                          pos_offset, k_cache, v_cache, T_max, y, stream) -> None:
+    _check(load_library().qlayer_prefill_varlen(h, x, B, seq_start, cache_len, seq_start_host,
+                                                cache_len_host, pos_offset, k_cache, v_cache,
+                                                T_max, y, stream))
 
 
 def qlayer_decode(h, x, B, cache_len, cache_len_host, pos_offset, k_cache, v_cache, T_max, y,
@@ -257,6 +266,31 @@ class QLayer:
         qlayer_decode(self.handle, x.data_ptr(), B, cache_len.data_ptr(), host, pos_offset,
                       k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1], y.data_ptr(),
                       _stream(stream))
+        return y
+
+    def prefill_varlen(self, x, seq_start, cache_len, k_cache, v_cache, pos_offset: int = 0,
+                       y=None, stream=None):
+        """x [N, d]; seq_start [B + 1] and cache_len [B] as Python int lists (the
+        device copies are made here)."""
+        torch = _torch()
+        N = x.shape[0]
+        B = len(cache_len)
+        self._check_act(x, (N, self.cfg.d))
+        self._check_cache(k_cache, v_cache, B)
+        if len(seq_start) != B + 1 or seq_start[-1] != N:
+            raise ValueError("seq_start: need B + 1 offsets ending at N")
+        ss_d = torch.tensor(seq_start, dtype=torch.int32, device=x.device)
+        cl_d = torch.tensor(cache_len, dtype=torch.int32, device=x.device)
+        ss_h = (ctypes.c_int * (B + 1))(*[int(v) for v in seq_start])
+        cl_h = (ctypes.c_int * B)(*[int(v) for v in cache_len])
+        self._varlen_keep = (ss_d, cl_d)   # alive until the stream has used them
+        if y is None:
+            y = torch.empty_like(x)
+        qlayer_prefill_varlen(self.handle, x.data_ptr(), B, ss_d.data_ptr(), cl_d.data_ptr(),
+                              ctypes.cast(ss_h, ctypes.c_void_p).value,
+                              ctypes.cast(cl_h, ctypes.c_void_p).value, pos_offset,
+                              k_cache.data_ptr(), v_cache.data_ptr(), k_cache.shape[1],
+                              y.data_ptr(), _stream(stream))
         return y
 
     def moe_ffn(self, r, y=None, topk_idx=None, topk_w=None, stream=None):

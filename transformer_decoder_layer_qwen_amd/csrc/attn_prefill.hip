@@ -2,6 +2,10 @@
 //
 // For query head h of sequence b, rows t and keys u <= t:
 //   o_t = sum_u softmax_u(q_t . k_u / sqrt(dh)) v_u,  KV head g = h / (Hq/Hkv)
+// A sequence may start over a cache prefix of P rows (chunked prefill): its
+// new row t is then key position P + t and sees the P prefix keys too
+// ("Qwen2.5-7B 结构拆解" §09.1), and sequences of one call may differ in
+// length (a varlen batch, rows concatenated).
 // ("推理系统 03：逐项算清一个真实 Qwen3 Transformer 层" §7-§9; "Qwen2.5-7B 结构拆解"
 // §05, §05.2: the KV head is indexed, never copied; §05.4: tiles above the
 // diagonal are skipped in both products). The [S, S] probability matrix is
@@ -57,24 +61,37 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int g = h / (p.n_q_heads / p.n_kv_heads);
+  // Sequence b: S new query rows from q row qbase, keys = its cache rows
+  // 0 .. P + S - 1, the first P of them an earlier prefix; new row t is at
+  // key position P + t and sees keys <= P + t. Uniform batches: qbase = b S,
+  // P = 0.
+  const int qbase = p.seq_start ? p.seq_start[b] : b * p.S;
+  const int S = p.seq_start ? p.seq_start[b + 1] - qbase : p.S;
+  const int P = p.prefix ? p.prefix[b] : 0;
+  const int L = P + S;  // keys of the sequence
   // Causal work grows with the query tile, so with p.pair a block takes tile
   // nqt-1-x and then tile x: every block then does about the same work.
-  // Otherwise a block takes one tile, the longest first.
-  const int nqt = (p.S + kBQ - 1) / kBQ;
-  const int qt_first = p.pair ? nqt - 1 - (int)blockIdx.x : (int)(gridDim.x - 1 - blockIdx.x);
+  // Otherwise a block takes one tile, the longest first. (Grids are sized
+  // for the longest sequence; a shorter one's extra blocks have no tile.)
+  const int nqt = (S + kBQ - 1) / kBQ;
+  const int qt_first = p.pair ? nqt - 1 - (int)blockIdx.x
+                              : (int)(gridDim.x - 1 - blockIdx.x) - ((int)gridDim.x - nqt);
+  // block-uniform, before any barrier: no tile, or (pairs) a tile that a
+  // lower block already takes as its second
+  if (qt_first < 0 || (p.pair && (int)blockIdx.x > qt_first)) return;
   const int npass = (p.pair && (int)blockIdx.x < qt_first) ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
   if (pass > 0) __syncthreads();  // the LDS ring is reused
   const int qt = pass == 0 ? qt_first : (int)blockIdx.x;
   const int q0 = qt * kBQ;
-  const int S = p.S;
-  const int my_q = q0 + wave * 32 + col;
-  const int wave_qmax = q0 + wave * 32 + 31;
+  const int my_q = q0 + wave * 32 + col;         // new row of this lane's query
+  const int my_pos = P + my_q;                   // its key position
+  const int wave_qmax = P + q0 + wave * 32 + 31;
 
   // Q^T fragments (B operand): lane (query col, group hi) holds dh [16s+8hi, +8)
   bf16x8 qf[8];
   {
-    const bf16* qrow = p.q + (size_t)(b * S + min(my_q, S - 1)) * p.ldq + h * kDh;
+    const bf16* qrow = p.q + (size_t)(qbase + min(my_q, S - 1)) * p.ldq + h * kDh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = load_bf16x8(qrow + 16 * s + 8 * hi);
   }
@@ -82,7 +99,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const size_t kv_row_stride = (size_t)p.n_kv_heads * kDh;
   const bf16* kbase = p.k_cache + ((size_t)b * p.T_max) * kv_row_stride + g * kDh;
   const bf16* vbase = p.v_cache + ((size_t)b * p.T_max) * kv_row_stride + g * kDh;
-  const int kend = min(q0 + kBQ, S);  // keys needed by this block
+  const int kend = min(P + q0 + kBQ, L);  // keys needed by this block
   const int ntiles = (kend + kBK - 1) / kBK;
   // this group's key tiles [kt_lo, kt_hi); both groups step niter times
   const int kt_lo = !KSPLIT ? 0 : grp == 0 ? 0 : ntiles / 2;
@@ -98,7 +115,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   u32x4 rk[4], rv[4];
   auto gload = [&](int kt) {
     const int k0 = kt * kBK;
-    if (k0 + kBK <= S) {  // whole tile inside the sequence: no per-lane checks
+    if (k0 + kBK <= L) {  // whole tile inside the sequence: no per-lane checks
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ch = tid + 256 * i;
@@ -111,20 +128,20 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
                                                  vc * 8);
       return;
     }
-    // ragged last tile: rows past S are zero (they may hold anything, and a
-    // NaN would survive a zero softmax weight in P V)
+    // ragged last tile: rows past the sequence are zero (they may hold
+    // anything, and a NaN would survive a zero softmax weight in P V)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = tid + 256 * i;
       const int key = k0 + (ch >> 4);
-      rk[i] = key < S ? *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kv_row_stride +
+      rk[i] = key < L ? *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kv_row_stride +
                                                          (ch & 15) * 8)
                       : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = k0 + vk + j;
-      rv[j] = key < S ? *reinterpret_cast<const u32x4*>(vbase + (size_t)key * kv_row_stride +
+      rv[j] = key < L ? *reinterpret_cast<const u32x4*>(vbase + (size_t)key * kv_row_stride +
                                                          vc * 8)
                       : u32x4{0u, 0u, 0u, 0u};
     }
@@ -191,14 +208,14 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
       // The mask test is wave-uniform (readfirstlane), so the common unmasked
       // tile carries no per-element code.
       const bool need_mask = __builtin_amdgcn_readfirstlane(
-          (k0 + kBK - 1 > q0 + wave * 32) || (k0 + kBK > S));
+          (k0 + kBK - 1 > P + q0 + wave * 32) || (k0 + kBK > L));
       if (need_mask) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-            sc[t][r] = (key > my_q || key >= S) ? -INFINITY : sc[t][r];
+            sc[t][r] = (key > my_pos || key >= L) ? -INFINITY : sc[t][r];
           }
       }
       float mt = -INFINITY;
@@ -213,15 +230,23 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
       // rescale of the accumulators runs only when some lane moved.
       const bool grow = mt > m_run + kSlack;  // first tile: m_run = -inf
       if (__any(grow)) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        // lanes that do not grow keep their reference (alpha = 1; their
+        // m_run may still be -inf, where m_run - m_run is not 0)
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+        m_run = grow ? mt : m_run;
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
       }
+      // A lane whose keys so far were all in its future still has m_run =
+      // -inf, and then so is every score of this tile (a finite one would
+      // have moved m_run): its weights are 0, not exp2(-inf + inf). This
+      // happens with a cache prefix, whose length need not be a multiple of
+      // the tile, in the second key group of a split tile, and in the
+      // rescale above.
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
       float lsum = 0.f;
       bf16x8 pf[4];
 #pragma unroll
@@ -229,7 +254,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           // the sum takes the rounded weights P*V is formed with
-          const bf16 pb = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][r], p.scale_log2, -m_run));
+          const bf16 pb = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][r], p.scale_log2, -m_ref));
           lsum += (float)pb;
           pf[2 * t + (r >> 3)][r & 7] = pb;
         }
@@ -284,7 +309,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const float inv = 1.0f / l_tot;
   // the fp32 output as a bf16 pair: hi = RNE(o) at column c, lo = RNE(o - hi)
   // at column c + lo_off (the O projection multiplies both)
-  bf16* orow = p.out + (size_t)(b * S + my_q) * p.ldo + h * kDh;
+  bf16* orow = p.out + (size_t)(qbase + my_q) * p.ldo + h * kDh;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -306,6 +331,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
 
 hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
+  // (a.S: the longest sequence's new rows when seq_start is set)
   const int nqt = (a.S + kBQ - 1) / kBQ;
   const long pairs = (long)((nqt + 1) / 2) * a.n_q_heads * a.B;
   const long tiles = (long)nqt * a.n_q_heads * a.B;

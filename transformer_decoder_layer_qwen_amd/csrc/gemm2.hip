@@ -86,6 +86,9 @@ struct G2Args {
   // fused into the epilogue
   int S, pos_offset, T_max, n_q_heads, n_kv_heads;
   const int* cache_len;  // decode: row b is sequence b at cache row cache_len[b]
+  const int* seq_start;  // varlen prefill: [nseq + 1] first row of each sequence
+  const int* prefix;     // varlen prefill: [nseq] cache rows before each sequence's new ones
+  int nseq;
   float eps;
   const double* omega;  // [64] RoPE frequencies
   const bf16* q_norm_g;
@@ -125,10 +128,20 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
     c = col - qd;
   }
   const int head = c >> 7, d0 = c & 127;
-  int b, t;
+  int b, t;  // sequence, cache row
   if constexpr (DEC) {
     b = (int)row;
     t = p.cache_len[b];
+  } else if (p.seq_start) {
+    // varlen: the last sequence starting at or before the row
+    int lo = 0, hi = p.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seq_start[mid] <= (int)row) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+    t = (int)row - p.seq_start[b] + (p.prefix ? p.prefix[b] : 0);
   } else {
     b = (int)(row / p.S);
     t = (int)(row % p.S);
@@ -1156,6 +1169,9 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
   a.pos_offset = f.pos_offset;
   a.T_max = f.T_max;
   a.cache_len = f.cache_len;
+  a.seq_start = f.seq_start;
+  a.prefix = f.prefix;
+  a.nseq = f.nseq;
   a.n_q_heads = q / 128;
   a.n_kv_heads = kv / 128;
   a.eps = f.eps;

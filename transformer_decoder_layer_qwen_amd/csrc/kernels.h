@@ -65,6 +65,9 @@ bool ql_gemm2_ok(int N, int Kb, bool dual);
 struct QkvFinish {
   int S, pos_offset, T_max;
   const int* cache_len;  // decode: [M] device, or NULL
+  const int* seq_start;  // varlen prefill: [nseq + 1] device (row -> sequence), or NULL
+  const int* prefix;     // varlen prefill: [nseq] cache rows before the new ones
+  int nseq;
   float eps;
   const double* omega;   // [64]
   const bf16* q_norm_g;  // or NULL
@@ -160,10 +163,12 @@ struct AttnPrefillArgs {
   const float* vf;
   float* outf;
   int ldq, ldo;
-  int B, S, T_max;
+  int B, S, T_max;       // S: new rows per sequence (varlen: the most of any sequence)
   int n_q_heads, n_kv_heads, head_dim;
   float scale_log2;      // log2(e) / sqrt(dh)
   int pair;              // set by the launcher: a block takes query tiles nqt-1-x and x
+  const int* seq_start;  // varlen [B + 1] device: sequence b's q rows, or NULL (b S)
+  const int* prefix;     // [B] device: cache rows before the new ones, or NULL (0)
 };
 hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s);
 hipError_t ql_attn_prefill_f32(const AttnPrefillArgs& a, hipStream_t s);

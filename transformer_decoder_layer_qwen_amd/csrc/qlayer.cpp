@@ -531,13 +531,22 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
   return QL_OK;
 }
 
+// A varlen prefill: sequence b's new rows are rows seq_start[b] ..
+// seq_start[b + 1] - 1 of the call, written after prefix[b] cache rows.
+struct Varlen {
+  const int* seq_start;  // [B + 1] device, or NULL: B sequences of S rows each
+  const int* prefix;     // [B] device, or NULL: no prefix
+  int N;                 // total new rows
+};
+
 // Prefill: RMSNorm1 -> QKV GEMM (+bias) -> QK-norm/RoPE/cache -> attention ->
-// O GEMM + residual -> FFN half.
+// O GEMM + residual -> FFN half. S is the rows per sequence, or with a
+// varlen batch the most new rows of any sequence.
 ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset, void* kc,
-                       void* vc, int T_max, bf16* y, hipStream_t s) {
+                       void* vc, int T_max, bf16* y, hipStream_t s, const Varlen& vl = Varlen{}) {
   const ql_config& c = h->cfg;
   const ql_weights& w = h->w;
-  const int N = B * S;
+  const int N = vl.seq_start ? vl.N : B * S;
   if (gemm2_call_part_bytes(c, h->q_dim, h->qkv_dim, N, false) > h->g2part_bytes)
     return fail(QL_EUNSUPPORTED, "prefill: %d rows need more GEMM partial space than the handle holds",
                 N);
@@ -560,6 +569,9 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   f.q_out = static_cast<bf16*>(h->q);
   f.k_cache = static_cast<bf16*>(kc);
   f.v_cache = static_cast<bf16*>(vc);
+  f.seq_start = vl.seq_start;
+  f.prefix = vl.prefix;
+  f.nseq = B;
   QL_STAGE(h, QL_STAGE_QKV, s,
            QL_HIP(ql_gemm2_qkv(xhat, N, static_cast<const bf16*>(w.wq),
                                static_cast<const bf16*>(w.wk), static_cast<const bf16*>(w.wv),
@@ -580,6 +592,8 @@ ql_status prefill_bf16(ql_handle* h, const bf16* x, int B, int S, int pos_offset
   pa.n_kv_heads = c.n_kv_heads;
   pa.head_dim = c.head_dim;
   pa.scale_log2 = scale_log2(c.head_dim);
+  pa.seq_start = vl.seq_start;
+  pa.prefix = vl.prefix;
   QL_STAGE(h, QL_STAGE_ATTENTION, s, QL_HIP(ql_attn_prefill_bf16(pa, s)));
   h->attn_hilo = true;
   QL_STAGE(h, QL_STAGE_O_PROJ, s,
@@ -918,6 +932,39 @@ ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offs
     st = prefill_bf16(h, static_cast<const bf16*>(x), B, S, pos_offset, k_cache, v_cache, T_max,
                       static_cast<bf16*>(y), s);
   }
+  if (st == QL_OK) st = copy_taps(h, N, s);
+  return st;
+}
+
+ql_status qlayer_prefill_varlen(ql_handle* h, const void* x, int B, const int* seq_start,
+                                const int* cache_len, const int* seq_start_host,
+                                const int* cache_len_host, int pos_offset, void* k_cache,
+                                void* v_cache, int T_max, void* y, void* stream) {
+  if (!h || !x || !seq_start || !cache_len || !seq_start_host || !cache_len_host || !k_cache ||
+      !v_cache || !y)
+    return fail(QL_EINVAL, "prefill_varlen: NULL argument");
+  if (B <= 0) return fail(QL_EINVAL, "prefill_varlen: B must be positive");
+  if (x == y) return fail(QL_EINVAL, "prefill_varlen: y must not alias x");
+  if (h->cfg.dtype != QL_BF16)
+    return fail(QL_EUNSUPPORTED, "prefill_varlen: needs dtype QL_BF16");
+  if (seq_start_host[0] != 0) return fail(QL_EINVAL, "prefill_varlen: seq_start[0] must be 0");
+  int S_max = 0;
+  for (int b = 0; b < B; ++b) {
+    const int n = seq_start_host[b + 1] - seq_start_host[b];
+    if (n < 0) return fail(QL_EINVAL, "prefill_varlen: seq_start must not decrease (at %d)", b);
+    S_max = std::max(S_max, n);
+    if (cache_len_host[b] < 0 || (long long)cache_len_host[b] + n > T_max)
+      return fail(QL_ECACHE_FULL, "prefill_varlen: sequence %d: %d cached + %d new rows exceed "
+                  "T_max = %d", b, cache_len_host[b], n, T_max);
+  }
+  const int N = seq_start_host[B];
+  if (N <= 0) return fail(QL_EINVAL, "prefill_varlen: no new rows");
+  if (N > h->cfg.max_tokens)
+    return fail(QL_EINVAL, "prefill_varlen: %d rows exceed max_tokens %d", N, h->cfg.max_tokens);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Varlen vl{seq_start, cache_len, N};
+  ql_status st = prefill_bf16(h, static_cast<const bf16*>(x), B, S_max, pos_offset, k_cache,
+                              v_cache, T_max, static_cast<bf16*>(y), s, vl);
   if (st == QL_OK) st = copy_taps(h, N, s);
   return st;
 }
