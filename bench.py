@@ -141,12 +141,19 @@ def stage_work(cfg, wl, stage, cache_len=None):
         flops = 2 * rows * f * d
         touched = cfg.n_experts * (1 - (1 - cfg.top_k / cfg.n_experts) ** N)
         return flops, touched * f * d * es + rows * (f * es + d * 4)
+    sf = cfg.shared_ffn_dim
+    if stage == "shared_gate_up":
+        return 2 * N * d * 2 * sf, 2 * sf * d * es + N * (d * es + sf * es)
+    if stage == "shared_down":
+        return 2 * N * sf * d, d * sf * es + N * (sf * es + d * 4)
     return 0, 0
 
 
 def layer_work(cfg, wl):
     stages = ["qkv", "attention", "o_proj"] + (
         ["expert_gate_up", "expert_down"] if cfg.is_moe else ["gate_up", "down"])
+    if cfg.shared_ffn_dim:
+        stages += ["shared_gate_up", "shared_down"]
     fl = by = 0
     for s in stages:
         a, b = stage_work(cfg, wl, s, cache_len=wl.seq)
@@ -163,6 +170,21 @@ def d_router(cfg):
 
 # ------------------------------------------------------------- workloads ----
 
+_WEIGHTS = {}
+
+
+def host_weights(cid):
+    """The seeded synthetic weights of a config (the tests' draws), kept for
+    the config's other workloads."""
+    cfg = configs.CONFIGS[cid]
+    if cfg.name not in _WEIGHTS:
+        _WEIGHTS.clear()
+        t0 = time.time()
+        _WEIGHTS[cfg.name] = synth.make_weights(cfg, configs.weight_seed(cid))
+        log(f"[bench] {cfg.name}: weights generated in {time.time() - t0:.1f}s")
+    return _WEIGHTS[cfg.name]
+
+
 class Setup:
     """Device weights (n_copies) and inputs of one workload."""
 
@@ -171,15 +193,12 @@ class Setup:
         from transformer_decoder_layer_qwen_amd import binding as B
         self.cfg = cfg = configs.CONFIGS[cid]
         self.wl = wl
-        t0 = time.time()
-        w_np = synth.make_weights(cfg, configs.weight_seed(cid))
-        log(f"[bench] {wl.label}: weights generated in {time.time() - t0:.1f}s")
+        w_np = host_weights(cid)
         self.layers = []
         for _ in range(n_copies):
             self.layers.append(B.QLayer(cfg, B.device_weights(w_np),
                                         max_tokens=wl.tokens if wl.kind == "prefill" else 1,
                                         max_batch=wl.batch if wl.kind == "decode" else 1))
-        del w_np
         self.inputs = []
         for c in range(n_copies):
             if wl.kind == "prefill":
@@ -339,29 +358,38 @@ def stages_of(cfg, kind, batch):
     s += ["attention", "o_proj"]
     if not (gemv and not cfg.is_moe):
         s += ["rmsnorm2"]
-    s += (["router", "permute", "expert_gate_up", "expert_down", "combine"] if cfg.is_moe
+    s += (["router", "permute", "expert_gate_up", "expert_down"] if cfg.is_moe
           else ["gate_up", "down"])
+    if cfg.shared_ffn_dim:
+        s += ["shared_gate_up", "shared_down"]
+    if cfg.is_moe:
+        s += ["combine"]
     return s
 
 
 # HBM bytes per launch from rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch), scaled by what the same counters read for a plain 256 MiB device copy
-# (FETCH_SIZE 131085.4 KiB, WRITE_SIZE 262144.0 KiB). Keyed by (workload, stage); an entry
-# is only valid for the kernel source it was taken on, named beside it.
+# (FETCH_SIZE 131085.4 KiB, WRITE_SIZE 262144.0 KiB: factors 1.9998 and 1.0). Keyed by
+# (workload, stage); each entry names the source file of the stage's kernels and the first
+# 16 hex digits of its SHA-256 when the counters were taken, and is reported only while
+# that file is unchanged (else traffic is null). Summaries: profiles/*_hbm_counters.md.
 PMC_FETCH_SCALE = 262144.0 / 131085.4
 PMC_WRITE_SCALE = 262144.0 / 262144.0
 PMC_TRAFFIC_KIB = {
-    # profiles/gemv_gate_up_qwen25_7b_decode_b1_hbm_counters.md (csrc/gemv.hip as of e72cee5)
-    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132731.3, 296.2),
-    # profiles/decode_b32_b64_hbm_counters.md (library at a5f47d2); a stage's kernels summed
-    ("qwen3-8b decode B=64 cache=4096", "attention"): (526717.1, 4608.0),
-    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (136845.9 + 6382.7, 12672.0 + 1184.0),
+    # (workload, stage): (FETCH_SIZE KiB, WRITE_SIZE KiB, source file, sha256[:16])
 }
+
+
+def source_sha(name):
+    import hashlib
+    path = os.path.join(ROOT, "transformer_decoder_layer_qwen_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def pmc_traffic(wl, stage):
     t = PMC_TRAFFIC_KIB.get((wl.label, stage))
-    if t is None:
+    if t is None or source_sha(t[2]) != t[3]:
         return None
     return int((t[0] * PMC_FETCH_SCALE + t[1] * PMC_WRITE_SCALE) * 1024)
 
@@ -410,12 +438,97 @@ def run_workload(cid, wl, hip, steps, warmup, stage_steps, breakdown=True, use_g
         dom = max(st, key=st.get)
         out["dominant"] = roofline_entry(cfg, wl, dom, st[dom])
         gemms = [s for s in ("qkv", "o_proj", "gate_up", "down", "expert_gate_up",
-                             "expert_down") if s in st]
+                             "expert_down", "shared_gate_up", "shared_down") if s in st]
         out["stage_roofline"] = {s: roofline_entry(cfg, wl, s, st[s]) for s in gemms + ["attention"]}
     if cfg.is_moe:
         out["expert_rows"] = expert_rows(setup)
     setup.close()
     return out, setup
+
+
+def gpu_weights(cfg, seed):
+    """A layer's synthetic weights drawn on the GPU (torch's generator, seeded),
+    with synth's distributions: gammas N(gamma_mean, gamma_std), weights and
+    biases N(0, w_std / b_std), router N(0, router_std), rounded to bf16. For
+    the layer stack, whose 28 layers (13 GB) would take minutes to draw on the
+    host; the single-layer workloads use synth's host draws."""
+    import torch
+    from transformer_decoder_layer_qwen_amd import synth as sy
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    out = {}
+    for name, shape in sy.weight_shapes(cfg).items():
+        if name.endswith("_g"):
+            mean, std = cfg.gamma_mean, cfg.gamma_std
+        elif name in ("bq", "bk", "bv"):
+            mean, std = 0.0, cfg.b_std
+        elif name == "w_router":
+            mean, std = 0.0, cfg.router_std
+        else:
+            mean, std = 0.0, cfg.w_std
+        t = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+        out[name] = (t * std + mean).to(torch.bfloat16).contiguous()
+    return out
+
+
+def run_stack(hip, n_layers, steps, warmup, cache_len=1024):
+    """One decode step (batch 1) through a stack of `n_layers` Qwen2.5-7B
+    layers, each with its own synthetic weights and KV cache, captured as one
+    HIP graph and replayed: the single-stream decode of the model's trunk
+    ("Qwen2.5-7B 结构拆解" §11: tokens/s is bounded by HBM bandwidth over the
+    bytes read per step)."""
+    import torch
+    from transformer_decoder_layer_qwen_amd import binding as B
+    cfg = configs.QWEN25_7B
+    t0 = time.time()
+    layers, ks, vs = [], [], []
+    T_max = cache_len + 1
+    for l in range(n_layers):
+        layers.append(B.QLayer(cfg, gpu_weights(cfg, 20000 + l), max_tokens=1, max_batch=1))
+        k = torch.randn(1, T_max, cfg.n_kv_heads, cfg.head_dim, device="cuda").to(torch.bfloat16)
+        ks.append(k)
+        vs.append(torch.randn_like(k, dtype=torch.float32).to(torch.bfloat16))
+    x = torch.randn(1, cfg.d, device="cuda").to(torch.bfloat16)
+    y, tmp = torch.empty_like(x), torch.empty_like(x)
+    lens = torch.full((1,), cache_len, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {n_layers}-layer stack: weights and caches in {time.time() - t0:.1f}s")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.decode_stack(layers, x, lens, ks, vs, y=y, tmp=tmp)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.decode_stack(layers, x, lens, ks, vs, y=y, tmp=tmp)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    a, b = hip.create(2)
+    hip.record(a, stream)
+    for _ in range(steps):
+        g.replay()
+    hip.record(b, stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(a, b) / steps
+    hip.destroy([a, b])
+    wl = configs.Workload(2, 1, "decode", 1, cache_len)
+    _, layer_bytes = layer_work(cfg, wl)
+    step_bytes = n_layers * layer_bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    for ly in layers:
+        ly.close()
+    del g, layers, ks, vs
+    torch.cuda.empty_cache()
+    return {"workload": f"qwen2.5-7b {n_layers}-layer decode stack B=1 cache={cache_len}",
+            "kind": "decode_stack", "layers": n_layers, "hip_graph": True,
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
+            "bytes_per_step": int(step_bytes), "achieved_GBs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "single_stream_bound_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / step_bytes, 1),
+            "weights": "per-layer synthetic, drawn on the GPU (torch generator, seeds 20000+l)"}
 
 
 def expert_rows(setup):
@@ -480,18 +593,70 @@ def measured_peaks():
 
 # ------------------------------------------------------------ CPU oracle ----
 
-def cpu_baseline(seconds=12.0):
-    """The fp64 oracle, as it stands, on the headline workload: repeated decode
-    steps of the Qwen2.5-7B layer at batch 1 with a 1024-row cache."""
-    from oracle import qlayer_ref as ref
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         cores = len(os.sched_getaffinity(0))
+    return model, int(cores)
+
+
+def oracle_spec(cfg):
+    from oracle import qlayer_ref as ref
+    return ref.LayerSpec(d=cfg.d, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                         head_dim=cfg.head_dim, ffn_dim=cfg.ffn_dim, n_experts=cfg.n_experts,
+                         top_k=cfg.top_k, norm_topk_prob=cfg.norm_topk_prob,
+                         shared_ffn_dim=cfg.shared_ffn_dim, qkv_bias=cfg.qkv_bias,
+                         qk_norm=cfg.qk_norm, eps=cfg.rms_eps, theta=cfg.rope_theta)
+
+
+def cpu_oracle(cid, wl, seconds=3.0):
+    """The fp64 oracle, as it stands, on a bounded sample of one workload:
+    decode steps of up to 4 of its sequences (full cache length), or the
+    prefill of the first min(S, 256) rows of one sequence; repeated for about
+    `seconds`. Tokens per second of that sample (a baseline only)."""
+    from oracle import qlayer_ref as ref
+    cfg = configs.CONFIGS[cid]
+    w = {k: synth.to_f32(v) for k, v in host_weights(cid).items()}
+    spec = oracle_spec(cfg)
+    if wl.kind == "prefill":
+        S = min(wl.seq, 256)
+        x = synth.to_f32(synth.make_prefill_input(cfg, wl.seed, 1, S))
+        run, toks, what = (lambda: ref.layer_prefill(x, w, spec)), S, f"prefill of {S} rows"
+    else:
+        Bs = min(wl.batch, 4)
+        x, kc, vc, lens = synth.make_decode_input(cfg, wl.seed, Bs, wl.seq)
+        x, kc, vc = synth.to_f32(x), synth.to_f32(kc), synth.to_f32(vc)
+        run, toks, what = (lambda: ref.layer_decode(x, kc, vc, lens, w, spec)), Bs, \
+            f"decode step of {Bs} sequences at cache {wl.seq}"
+    n, t0 = 0, time.time()
+    while True:
+        run()
+        n += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    return {"value": round(n * toks / dt, 3), "unit": "tokens/s", "kind": "oracle",
+            "sample": f"{n} x {what} in {dt:.1f}s"}
+
+def cpu_baseline(seconds=12.0):
+    """The fp64 oracle, as it stands, on the headline workload: repeated decode
+    steps of the Qwen2.5-7B layer at batch 1 with a 1024-row cache."""
+    from oracle import qlayer_ref as ref
+    model, cores = cpu_info()
     cid, wl = 2, configs.WORKLOADS[2][0]
     cfg = configs.CONFIGS[cid]
-    w = {k: synth.to_f32(v) for k, v in synth.make_weights(cfg, configs.weight_seed(cid)).items()}
+    w = {k: synth.to_f32(v) for k, v in host_weights(cid).items()}
     x, kc, vc, lens = synth.make_decode_input(cfg, wl.seed, wl.batch, wl.seq)
     x, kc, vc = synth.to_f32(x), synth.to_f32(kc), synth.to_f32(vc)
     spec = ref.LayerSpec(d=cfg.d, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
@@ -506,7 +671,7 @@ def cpu_baseline(seconds=12.0):
             break
     dt = time.time() - t0
     return {"value": round(n * wl.batch / dt, 3), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
+            "cpu": model, "kind": "oracle",
             "sample": f"{n} decode steps of {wl.label} (fp64 NumPy oracle, weights pre-widened "
                       f"to fp32) in {dt:.1f}s"}
 
@@ -522,6 +687,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-steps", type=int, default=10)
     ap.add_argument("--eager", action="store_true", help="no HIP graph replay")
+    ap.add_argument("--stack-layers", type=int, default=28,
+                    help="layers of the decode-stack workload (0: skip it)")
     ap.add_argument("--graph-stage-probe", action="store_true",
                     help="also time every stage with events captured in graph replay")
     ap.add_argument("--only", default=None,
@@ -564,17 +731,25 @@ def main():
         f"{head['ms_per_step']} ms/step")
     secondary = []
     if not args.headline_only:
-        for c in (2, 3, 4, 5):
+        # the graded configs (Qwen2.5-7B, Qwen3-8B, Qwen3-30B-A3B), then the
+        # shape variants (Qwen3-32B, the Mixtral-like layer, Qwen2-57B-A14B)
+        for c in (2, 3, 4, 5, 6, 7, 8):
             for w in configs.WORKLOADS[c]:
                 if (c, w.index) == (cid, wl.index):
                     continue
                 s_steps = max(6, args.steps // 5 // 2 * 2) if w.kind == "prefill" else args.steps
                 r, _ = run_workload(c, w, hip, s_steps, max(2, args.warmup // 2),
                                     max(3, args.stage_steps // 2), use_graph=not args.eager)
+                if not args.no_cpu_baseline:
+                    r["cpu_oracle"] = cpu_oracle(c, w)
                 log(f"[bench] {r['workload']}: {r['tokens_per_s']} tok/s, "
                     f"{r['ms_per_step']} ms/step")
                 secondary.append(r)
                 torch.cuda.empty_cache()
+        if args.stack_layers:
+            r = run_stack(hip, args.stack_layers, max(10, args.steps // 2), 3)
+            log(f"[bench] {r['workload']}: {r['tokens_per_s']} tok/s, {r['achieved_GBs']} GB/s")
+            secondary.append(r)
 
     cfg = configs.CONFIGS[cid]
     dom = dict(head["dominant"])
@@ -603,6 +778,7 @@ def main():
         "roofline": roof,
         "layer_frac_hbm": head.get("layer_frac_hbm"),
         "stage_ms": head.get("stage_ms"),
+        "stage_ms_graph": head.get("stage_ms_graph"),
         "secondary": secondary,
         "measured_peaks": peaks,
     }

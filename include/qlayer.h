@@ -199,6 +199,25 @@ ql_status qlayer_decode(ql_handle* h, const void* x, int B, const int* cache_len
                         const int* cache_len_host, int pos_offset, void* k_cache,
                         void* v_cache, int T_max, void* y, void* stream);
 
+/* One decode step through a stack of L layers (a model's trunk, "Qwen2.5-7B
+ * 结构拆解" §02 and §11: the layers run one after another, each reading the
+ * previous one's output rows and its own KV cache).
+ *
+ * layers     [L] handles (same d and dtype; B <= each max_batch)
+ * x          [B, d] input rows of layer 0;  y [B, d] output rows of layer L-1
+ * cache_len, cache_len_host, pos_offset, T_max  as qlayer_decode, shared by
+ *            every layer (each layer appends its row at cache_len[b])
+ * k_caches, v_caches  [L] HOST arrays of DEVICE pointers, layer l's caches
+ *            [B, T_max, Hkv_l, dh]
+ * tmp        [B, d] device scratch for the rows between layers (caller-owned;
+ *            layers alternate between tmp and y so the last one writes y)
+ * The whole step is enqueued on `stream` (capturable as one graph).
+ * Errors: as qlayer_decode; QL_EINVAL for mismatched layers or aliasing. */
+ql_status qlayer_decode_stack(ql_handle* const* layers, int L, const void* x, int B,
+                              const int* cache_len, const int* cache_len_host, int pos_offset,
+                              void* const* k_caches, void* const* v_caches, int T_max, void* y,
+                              void* tmp, void* stream);
+
 /* Largest workspace, in bytes, of a qlayer_decode_noalloc call. */
 #define QLAYER_NOALLOC_MAX_WORKSPACE (64u << 20)
 

@@ -727,6 +727,82 @@ def test_full_size_prefill_varlen(cid, lens, prefix, T_max):
     layer.close()
 
 
+# ------------------------------------------------- L-layer decode stack ----
+
+def check_stack(cfg, L, Bn, cache_len, T_max, seed, label, graph_replays=0):
+    """qlayer_decode_stack through L layers with their own synthetic weights
+    and caches: bit-identical to L qlayer_decode calls in turn (same kernels,
+    each layer's output bf16), and every layer within the bar of the oracle
+    fed that layer's GPU input and cache. With graph_replays, the captured
+    stack replays to the eager result with eager work in between."""
+    spec = spec_of(cfg)
+    layers, w64s = [], []
+    for l in range(L):
+        ly, w64 = make_layer(cfg, seed=seed + 10 * l, max_tokens=1, max_batch=Bn)
+        layers.append(ly)
+        w64s.append(w64)
+    x, _, _, _ = synth.make_decode_input(cfg, seed + 1, Bn, cache_len, T_max=T_max)
+    caches = [synth.make_decode_input(cfg, seed + 2 + l, Bn, cache_len, T_max=T_max)[1:3]
+              for l in range(L)]
+    lens = np.array([max(0, cache_len - 13 * b) for b in range(Bn)], np.int32)   # ragged
+    ld = torch.from_numpy(lens).cuda()
+    xd = B.to_device(x)
+    ks = [B.to_device(kc) for kc, _ in caches]
+    vs = [B.to_device(vc) for _, vc in caches]
+    y_stack = B.decode_stack(layers, xd, ld, ks, vs, cache_len_host=lens.tolist())
+    torch.cuda.synchronize()
+    # layer by layer (rewrites the same cache rows with the same values)
+    h = xd
+    ins = []
+    for l in range(L):
+        ins.append(h)
+        h = layers[l].decode(h, ld, ks[l], vs[l])
+    torch.cuda.synchronize()
+    assert torch.equal(h, y_stack), label
+    errs = []
+    for l in range(L):
+        kc, vc = caches[l]
+        o = ref.layer_decode(host(ins[l]).astype(np.float64), synth.to_f32(kc), synth.to_f32(vc),
+                             lens, w64s[l], spec)
+        out = host(ins[l + 1]) if l + 1 < L else host(h)
+        errs.append(rel_err(out, o["y"]))
+        assert rounding_err(host(ks[l])[np.arange(Bn), lens], o["k_new"]) <= 1.0
+    log(f"[gpu] {label}: {L} layers, per-layer y errors {[f'{e:.2e}' for e in errs]}")
+    assert max(errs) <= BF16_TOL
+    if graph_replays:
+        y = torch.empty_like(y_stack)
+        tmp = torch.empty_like(y_stack)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            B.decode_stack(layers, xd, ld, ks, vs, y=y, tmp=tmp)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            B.decode_stack(layers, xd, ld, ks, vs, y=y, tmp=tmp)
+        for rep in range(graph_replays):
+            y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_stack), rep
+            layers[0].decode(xd, ld, ks[0], vs[0])   # eager work between replays
+            torch.cuda.synchronize()
+    for ly in layers:
+        ly.close()
+
+
+@pytest.mark.parametrize("Bn", [2, 6])
+def test_small_decode_stack(Bn):
+    check_stack(small_cfg(), 3, Bn, 70, 80, 2100, f"small stack B={Bn}", graph_replays=3)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_decode_stack():
+    cfg = configs.QWEN25_7B
+    check_stack(cfg, 2, 1, 1024, 1025, 2200, "qwen2.5-7b 2-layer stack B=1")
+
+
 # A handle sized for more rows than the call: the split-K partial space must
 # cover every row count up to max_tokens (the plans split fewer row tiles
 # more ways), and one handle serves calls of several sizes in turn.

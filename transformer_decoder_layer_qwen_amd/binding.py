@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "QL_OK", -1: "QL_EINVAL", -2: "QL_EUNSUPPORTED", -3: "QL_ENOM
 
 # every function include/qlayer.h declares
 EXPORTS = ("qlayer_create", "qlayer_destroy", "qlayer_workspace_bytes", "qlayer_prefill",
-           "qlayer_prefill_varlen", "qlayer_decode", "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
+           "qlayer_prefill_varlen", "qlayer_decode", "qlayer_decode_stack", "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
            "qlayer_set_stage_events", "qlayer_last_error", "qlayer_abi_version")
 NOALLOC_MAX_WORKSPACE = 64 << 20
 
@@ -93,6 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qlayer_prefill.argtypes = [vp, vp, ci, ci, ci, vp, vp, ci, vp, vp]
     lib.qlayer_decode.argtypes = [vp, vp, ci, vp, vp, ci, vp, vp, ci, vp, vp]
     lib.qlayer_prefill_varlen.argtypes = [vp, vp, ci, vp, vp, vp, vp, ci, vp, vp, ci, vp, vp]
+    lib.qlayer_decode_stack.argtypes = [vp, ci, vp, ci, vp, vp, ci, vp, vp, ci, vp, vp, vp]
     lib.qlayer_decode_noalloc.argtypes = [ctypes.POINTER(QlConfig), ctypes.POINTER(QlWeights), vp,
                                           ci, vp, vp, ci, vp, vp, ci, vp, vp]
     lib.qlayer_moe_ffn.argtypes = [vp, vp, ci, vp, vp, vp, vp]
@@ -102,7 +103,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.qlayer_last_error.argtypes = []
     lib.qlayer_abi_version.restype = ci
     for name in ("qlayer_create", "qlayer_destroy", "qlayer_prefill", "qlayer_prefill_varlen",
-                 "qlayer_decode",
+                 "qlayer_decode", "qlayer_decode_stack",
                  "qlayer_decode_noalloc", "qlayer_moe_ffn", "qlayer_set_taps",
                  "qlayer_set_stage_events"):
         getattr(lib, name).restype = ci
@@ -156,6 +157,36 @@ def qlayer_decode(h, x, B, cache_len, cache_len_host, pos_offset, k_cache, v_cac
                   stream) -> None:
     _check(load_library().qlayer_decode(h, x, B, cache_len, cache_len_host, pos_offset, k_cache,
                                         v_cache, T_max, y, stream))
+
+
+def qlayer_decode_stack(layers, L, x, B, cache_len, cache_len_host, pos_offset, k_caches,
+                        v_caches, T_max, y, tmp, stream) -> None:
+    _check(load_library().qlayer_decode_stack(layers, L, x, B, cache_len, cache_len_host,
+                                              pos_offset, k_caches, v_caches, T_max, y, tmp,
+                                              stream))
+
+
+def decode_stack(layers, x, cache_len, k_caches, v_caches, y=None, tmp=None, pos_offset=0,
+                 cache_len_host=None, stream=None):
+    """One decode step through QLayer objects `layers` (their handles and the
+    per-layer caches marshalled into pointer arrays)."""
+    torch = _torch()
+    L, Bn = len(layers), x.shape[0]
+    hs = (ctypes.c_void_p * L)(*[ly.handle for ly in layers])
+    ks = (ctypes.c_void_p * L)(*[k.data_ptr() for k in k_caches])
+    vs = (ctypes.c_void_p * L)(*[v.data_ptr() for v in v_caches])
+    host = None
+    if cache_len_host is not None:
+        arr = (ctypes.c_int * Bn)(*[int(v) for v in cache_len_host])
+        host = ctypes.cast(arr, ctypes.c_void_p).value
+    y = torch.empty_like(x) if y is None else y
+    tmp = torch.empty_like(x) if tmp is None else tmp
+    qlayer_decode_stack(ctypes.cast(hs, ctypes.c_void_p).value, L, x.data_ptr(), Bn,
+                        cache_len.data_ptr(), host, pos_offset,
+                        ctypes.cast(ks, ctypes.c_void_p).value,
+                        ctypes.cast(vs, ctypes.c_void_p).value, k_caches[0].shape[1],
+                        y.data_ptr(), tmp.data_ptr(), _stream(stream))
+    return y
 
 
 def qlayer_decode_noalloc(cfg: QlConfig, w: QlWeights, x, B, cache_len, cache_len_host,

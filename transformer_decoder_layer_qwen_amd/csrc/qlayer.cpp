@@ -981,6 +981,40 @@ ql_status qlayer_decode(ql_handle* h, const void* x, int B, const int* cache_len
                     static_cast<hipStream_t>(stream));
 }
 
+ql_status qlayer_decode_stack(ql_handle* const* layers, int L, const void* x, int B,
+                              const int* cache_len, const int* cache_len_host, int pos_offset,
+                              void* const* k_caches, void* const* v_caches, int T_max, void* y,
+                              void* tmp, void* stream) {
+  if (!layers || !k_caches || !v_caches || !tmp || L <= 0)
+    return fail(QL_EINVAL, "decode_stack: NULL argument or L <= 0");
+  ql_status st = check_decode_args(x, B, cache_len, cache_len_host, k_caches[0], v_caches[0],
+                                   T_max, y);
+  if (st != QL_OK) return st;
+  if (tmp == x || tmp == y) return fail(QL_EINVAL, "decode_stack: tmp must not alias x or y");
+  const ql_config& c0 = layers[0] ? layers[0]->cfg : ql_config{};
+  for (int l = 0; l < L; ++l) {
+    const ql_handle* h = layers[l];
+    if (!h || !k_caches[l] || !v_caches[l])
+      return fail(QL_EINVAL, "decode_stack: layer %d: NULL handle or cache", l);
+    if (h->cfg.d != c0.d || h->cfg.dtype != c0.dtype)
+      return fail(QL_EINVAL, "decode_stack: layer %d: d or dtype differs from layer 0", l);
+    if (B > h->cfg.max_batch)
+      return fail(QL_EINVAL, "decode_stack: layer %d: B = %d exceeds max_batch %d", l, B,
+                  h->cfg.max_batch);
+  }
+  // layer l writes y when L - 1 - l is even, else tmp, so the last lands in y
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* in = x;
+  for (int l = 0; l < L; ++l) {
+    void* out = ((L - 1 - l) % 2 == 0) ? y : tmp;
+    st = run_decode(layers[l], in, B, cache_len, pos_offset, k_caches[l], v_caches[l], T_max, out,
+                    s);
+    if (st != QL_OK) return st;
+    in = out;
+  }
+  return QL_OK;
+}
+
 ql_status qlayer_decode_noalloc(const ql_config* cfg, const ql_weights* w, const void* x, int B,
                                 const int* cache_len, const int* cache_len_host, int pos_offset,
                                 void* k_cache, void* v_cache, int T_max, void* y, void* stream) {
