@@ -376,7 +376,15 @@ def stages_of(cfg, kind, batch):
 PMC_FETCH_SCALE = 262144.0 / 131085.4
 PMC_WRITE_SCALE = 262144.0 / 262144.0
 PMC_TRAFFIC_KIB = {
-    # (workload, stage): (FETCH_SIZE KiB, WRITE_SIZE KiB, source file, sha256[:16])
+    # (workload, stage): (FETCH_SIZE KiB, WRITE_SIZE KiB, source file, sha256[:16]);
+    # profiles/hbm_counters_decode_workloads.md (a stage's kernels summed)
+    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132732.1, 296.1, "gemv.hip", "63d297e1fbf69e6a"),
+    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140848.9 + 6384.0, 12672.0 + 2368.0,
+                                                        "gemm2.hip", "3b9ef4bd13e1c181"),
+    ("qwen3-8b decode B=64 cache=4096", "attention"): (526664.6, 4608.0, "attn_decode.hip",
+                                                       "bb0bcad24b0cb6bb"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (526907.8, 5632.0, "attn_decode.hip",
+                                                             "bb0bcad24b0cb6bb"),
 }
 
 
@@ -778,6 +786,7 @@ def main():
         "roofline": roof,
         "layer_frac_hbm": head.get("layer_frac_hbm"),
         "stage_ms": head.get("stage_ms"),
+        "event_span_overhead_ms": head.get("event_span_overhead_ms"),
         "stage_ms_graph": head.get("stage_ms_graph"),
         "secondary": secondary,
         "measured_peaks": peaks,
