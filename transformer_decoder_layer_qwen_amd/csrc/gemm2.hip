@@ -977,8 +977,7 @@ hipError_t launch(const G2Args& a, dim3 grid, hipStream_t s) {
   constexpr bool kPairOnly = MODE == G2_BIAS || MODE == G2_RESID_F32;
   constexpr bool kMoe = MODE == G2_MOE_GU || MODE == G2_MOE_DOWN;
   constexpr bool kDec = SHAPE != T256 && SHAPE != P128_HL;
-  if constexpr (SHAPE != T256 &&
-                (kMoe || SHAPE == D32_HL || (kPairOnly && !HL) || (SHAPE == P128_HL && !kPairOnly))) {
+  if constexpr (SHAPE != T256 && (kMoe || SHAPE == D32_HL || (kPairOnly && !HL))) {
     return hipErrorInvalidValue;
   } else if constexpr (kDec) {  // decode tiles: stream-K partials
     hipLaunchKernelGGL((gemm2_dec_kernel<MODE, HL, shape_ra(SHAPE)>), grid, dim3(256), 0, s, a);
@@ -1208,33 +1207,47 @@ hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K
   return run_pair<G2_RESID_F32>(a, pl, s);
 }
 
-// A of a plain-input GEMM: a pair doubles K on the 256-row prefill tiles
-// (hi then lo k steps against the same weights) and puts hi and lo rows side
-// by side on the decode tiles (each weight tile serves both)
-G2Args base_ab(const bf16* A, int M, const bf16* W, int K, bool pair, bool rows128, int splits,
-               void* part) {
-  G2Args a = base(A, M, pair && !rows128 ? 2 * K : K, W, K, splits, part);
+// A of a gate/up, down or shared-expert GEMM, and its launch plan. A pair
+// input on the prefill tiles takes the same plan as Q/K/V and O (256-row
+// tiles over a doubled K or 128-row hi/lo tiles, split count, and a split-K
+// tail when the last wave of tiles would be nearly empty); on the decode
+// tiles hi and lo rows sit side by side (each weight tile serves both). A
+// plain bf16 input on the prefill tiles splits `splits` ways.
+namespace {
+struct AbPlan {
+  G2Args a;
+  PairPlan pl;
+};
+AbPlan base_ab(const bf16* A, int M, const bf16* W, int N, int K, bool pair, bool rows128,
+               int splits, void* part) {
+  PairPlan pl{T256, splits, 0, 1};
+  if (rows128) pl = PairPlan{decode_shape(M, pair), 1, 0, 1};
+  else if (pair) pl = pair_plan(M, N, K);
+  G2Args a = base(A, M, pair && pl.shape == T256 ? 2 * K : K, W, K, pl.splits, part);
   if (pair) a.lda = 2 * K;
-  return a;
+  return {a, pl};
 }
+}  // namespace
 
 hipError_t ql_gemm2_resid_out(const bf16* A, int M, const bf16* W, int N, int K,
                               const float* resid, bf16* out, bool rows128, int splits, void* part,
                               hipStream_t s, bool pair_in) {
-  G2Args a = base_ab(A, M, W, K, pair_in, rows128, splits, part);
+  AbPlan ab = base_ab(A, M, W, N, K, pair_in, rows128, splits, part);
+  G2Args& a = ab.a;
   a.resid_f32 = resid;
   a.ldr = N;
   a.out_bf16 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_RESID_OUT>(a, rows128 ? decode_shape(M, pair_in) : T256, s);
+  return run_pair<G2_RESID_OUT>(a, ab.pl, s);
 }
 
 hipError_t ql_gemm2_gated_out(const bf16* A, int M, const bf16* W, int N, int K,
                               const float* gate_logit, int gate_ld, const float* resid_f32,
                               const bf16* resid_bf16, float* out, bool rows128, int splits,
                               void* part, hipStream_t s, bool pair_in) {
-  G2Args a = base_ab(A, M, W, K, pair_in, rows128, splits, part);
+  AbPlan ab = base_ab(A, M, W, N, K, pair_in, rows128, splits, part);
+  G2Args& a = ab.a;
   a.gate_logit = gate_logit;
   a.gate_ld = gate_ld;
   a.resid_f32 = resid_f32;
@@ -1243,19 +1256,20 @@ hipError_t ql_gemm2_gated_out(const bf16* A, int M, const bf16* W, int N, int K,
   a.out_f32 = out;
   a.ldo = N;
   a.tiles_n = N / BN;
-  return run<G2_GATED_F32>(a, rows128 ? decode_shape(M, pair_in) : T256, s);
+  return run_pair<G2_GATED_F32>(a, ab.pl, s);
 }
 
 hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu, int F, int K,
                            bf16* out, bool rows128, int splits, void* part, hipStream_t s,
                            bool pair) {
-  G2Args a = base_ab(A, M, Wg, K, pair, rows128, splits, part);
+  AbPlan ab = base_ab(A, M, Wg, 2 * F, K, pair, rows128, splits, part);
+  G2Args& a = ab.a;
   a.B2 = Wu;
   a.out_bf16 = out;
   a.ldo = pair ? 2 * F : F;
   a.out_lo = pair ? F : 0;
   a.tiles_n = F / (BN / 2);
-  return run<G2_SWIGLU>(a, rows128 ? decode_shape(M, pair) : T256, s);
+  return run_pair<G2_SWIGLU>(a, ab.pl, s);
 }
 
 hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg, const bf16* Wu,

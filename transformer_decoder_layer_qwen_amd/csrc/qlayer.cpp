@@ -176,14 +176,6 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
   return QL_OK;
 }
 
-// Prefill GEMM split-K: enough (tile, split) blocks for about one per CU,
-// each split keeping at least 512 of K.
-constexpr int kGemmTargetBlocks = 256;
-int gemm2_splits(int M, int b_rows, int K) {
-  const int tiles = ((M + 255) / 256) * ((b_rows + 255) / 256);
-  int sp = std::max(1, kGemmTargetBlocks / std::max(tiles, 1));
-  return std::max(1, std::min(sp, K / 512));
-}
 // Partial-tile bytes one call of M rows needs: the pair-input QKV and O
 // GEMMs and the two dense FFN GEMMs (prefill: the split-K plans; decode with
 // rows past the VALU GEMV: the stream-K cut). The bytes are not monotone in M
@@ -195,11 +187,11 @@ size_t gemm2_call_part_bytes(const ql_config& c, int q_dim, int qkv_dim, int M, 
   if (!decode) {
     b = std::max(b, ql_gemm2_pair_part_bytes(M, qkv_dim, c.d));
     b = std::max(b, ql_gemm2_pair_part_bytes(M, c.d, q_dim));
-    // dense FFN or shared expert: [hi | lo] pair inputs, doubled K
+    // dense FFN or shared expert: [hi | lo] pair inputs, planned as Q/K/V and O
     const int f = c.n_experts == 0 ? c.ffn_dim : c.shared_ffn_dim;
     if (f > 0) {
-      b = std::max(b, ql_gemm2_part_bytes(M, 2 * f, gemm2_splits(M, 2 * f, 2 * c.d)));
-      b = std::max(b, ql_gemm2_part_bytes(M, c.d, gemm2_splits(M, c.d, 2 * f)));
+      b = std::max(b, ql_gemm2_pair_part_bytes(M, 2 * f, c.d));
+      b = std::max(b, ql_gemm2_pair_part_bytes(M, c.d, f));
     }
     return b;
   }
@@ -446,15 +438,14 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
     const bf16* sg = static_cast<const bf16*>(w.ws_gate);
     const bf16* su = static_cast<const bf16*>(w.ws_up);
     const bf16* sd = static_cast<const bf16*>(w.ws_down);
-    const int sgu = decode ? 1 : gemm2_splits(N, 2 * sf, 2 * c.d);
-    const int sdn = decode ? 1 : gemm2_splits(N, c.d, 2 * sf);
+    // (pair inputs: the launchers plan tile shape and split count themselves)
     QL_STAGE(h, QL_STAGE_SHARED_GATE_UP, s,
-             QL_HIP(ql_gemm2_swiglu(z2, N, sg, su, sf, c.d, hs, decode, sgu, h->g2part, s, true)));
+             QL_HIP(ql_gemm2_swiglu(z2, N, sg, su, sf, c.d, hs, decode, 1, h->g2part, s, true)));
     QL_STAGE(h, QL_STAGE_SHARED_DOWN, s,
              QL_HIP(ql_gemm2_gated_out(
                  hs, N, sd, c.d, sf, h->logits + c.n_experts, c.n_experts + 1,
                  resid_is_f32 ? static_cast<const float*>(resid) : nullptr,
-                 resid_is_f32 ? nullptr : static_cast<const bf16*>(resid), h->rs, decode, sdn,
+                 resid_is_f32 ? nullptr : static_cast<const bf16*>(resid), h->rs, decode, 1,
                  h->g2part, s, true)));
     resid = h->rs;
     resid_is_f32 = 1;
@@ -520,14 +511,13 @@ ql_status ffn_dense_or_moe(ql_handle* h, int N, bool decode, bf16* y, hipStream_
                                          c.n_experts > 0 ? h->zf : nullptr)));
   h->ffn_pair = c.n_experts == 0;
   if (c.n_experts > 0) return moe_core(h, N, h->r, 1, y, decode, s);
-  const int sgu = decode ? 1 : gemm2_splits(N, 2 * c.ffn_dim, 2 * c.d);
-  const int sdn = decode ? 1 : gemm2_splits(N, c.d, 2 * c.ffn_dim);
+  // (pair inputs: the launchers plan tile shape and split count themselves)
   QL_STAGE(h, QL_STAGE_GATE_UP, s,
-           QL_HIP(ql_gemm2_swiglu(z2, N, wg, wu, c.ffn_dim, c.d, hh, decode, sgu, h->g2part, s,
+           QL_HIP(ql_gemm2_swiglu(z2, N, wg, wu, c.ffn_dim, c.d, hh, decode, 1, h->g2part, s,
                                   true)));
   QL_STAGE(h, QL_STAGE_DOWN, s,
-           QL_HIP(ql_gemm2_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, decode, sdn, h->g2part,
-                                     s, true)));
+           QL_HIP(ql_gemm2_resid_out(hh, N, wd, c.d, c.ffn_dim, h->r, y, decode, 1, h->g2part, s,
+                                     true)));
   return QL_OK;
 }
 
