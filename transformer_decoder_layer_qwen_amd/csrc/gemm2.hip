@@ -225,6 +225,13 @@ QL_HD int sk_owner(long long u, long long U, int G) { return (int)(((u + 1) * G 
 // chunk; with 128-byte rows this puts them on 16 distinct 16-byte positions of
 // a 256-byte bank line, so the read is free of bank conflicts.
 QL_DEV int swz(int r) { return (r >> 1) & 7; }
+// The same for 64-byte rows (4 chunks): rows r and r + 4 share a 64-byte
+// position of the bank line, so the chunk order turns with r / 4.
+template <int RC>
+QL_DEV int swz_rc(int r) {
+  static_assert(RC == 8 || RC == 4, "row chunks");
+  return RC == 8 ? swz(r) : (r >> 2) & 3;
+}
 
 // Typed address-space casts for the direct-to-LDS load builtin.
 typedef const void __attribute__((address_space(1)))* gptr_t;
@@ -243,30 +250,45 @@ QL_DEV void wait_vmcnt() {
 }
 
 // Prefill tiles. PART: write this split's fp32 partial tile instead of
-// MODE's epilogue. 8 waves as 2 (rows) x 4 (columns), a wave owns 128 x 64;
-// two waves share each SIMD, so one wave's MFMAs run while the other waits.
-// Two ring stages (2 x 64 KiB).
-// HL: A is a [hi | lo] pair and a tile covers 128 token rows: LDS rows
-// 0..127 hold the hi halves, 128..255 the lo halves at the same k, so each B
-// tile serves both and the k loop runs over Kb only; the lo accumulators
-// (waves wm = 1) are added to the hi ones through LDS in the epilogue. Same
-// MFMA work as the doubled K, twice the tiles at half the k steps, which
-// evens out the last wave of tiles on some shapes.
-template <int MODE, bool PART, bool HL>
+// MODE's epilogue. KIND selects the tile:
+//  0  256 token rows, A plain bf16 (or a pair over the doubled K); 8 waves as
+//     2 (rows) x 4 (columns), a wave owns 128 x 64; two 64-deep ring stages
+//     (2 x 64 KiB).
+//  1  [hi | lo] pair, 128 token rows: LDS rows 0..127 hold the hi halves,
+//     128..255 the lo halves at the same k, so each B tile serves both and the
+//     k loop runs over Kb only; the lo accumulators (waves wm = 1) are added to
+//     the hi ones through LDS in the epilogue. Same MFMA work as the doubled K,
+//     twice the tiles at half the k steps.
+//  2  [hi | lo] pair, 256 token rows: a stage holds 32 k of the 256 hi rows,
+//     of the 256 lo rows and of the 256 weight rows (48 KiB), so each weight
+//     fragment feeds a hi and a lo MFMA into the same accumulators; three ring
+//     stages (two in flight while one is multiplied). 8 waves as 4 x 2, a wave
+//     owns 64 token rows x 128 columns: per 16-deep step it reads 8 fragments
+//     for 16 MFMAs (kind 0 reads 6 for 8), and the block moves 48 KiB from L2
+//     per 256 x 256 x 64 of MFMA work instead of 64.
+// Two waves share each SIMD, so one wave's MFMAs run while the other waits.
+template <int MODE, bool PART, int KIND>
 __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
+  constexpr bool HL = KIND == 1;
+  constexpr bool P2 = KIND == 2;
   constexpr int BMT = 256;
   constexpr int NW = BMT / 32;          // waves
   constexpr int NT = NW * 64;           // threads
-  constexpr int WMW = BMT / 128;        // waves along M
+  constexpr int WMW = P2 ? 4 : BMT / 128;  // waves along M
   constexpr int WNW = NW / WMW;         // waves along N
+  constexpr int WROWS = P2 ? 64 : 128;  // LDS A rows per wave (per half for P2)
   constexpr int WCOLS = BN / WNW;       // columns per wave
+  constexpr int TI = WROWS / 32;        // 32-row MFMA tiles per wave along M
   constexpr int TJ = WCOLS / 32;        // 32-wide MFMA tiles per wave along N
-  constexpr int AC = BMT * kRowChunks;  // A chunks per stage
-  constexpr int CH = AC + BN * kRowChunks;
+  constexpr int SBK = P2 ? 32 : BK;     // k depth of a stage
+  constexpr int RC = SBK / 8;           // 16-byte chunks per LDS row
+  constexpr int AROWS = P2 ? 2 * BMT : BMT;  // LDS rows of A per stage
+  constexpr int AC = AROWS * RC;        // A chunks per stage
+  constexpr int CH = AC + BN * RC;
   constexpr int LPT = CH / NT;          // direct loads per thread per stage
   constexpr int LPA = AC / NT;          // ... of which A
   constexpr int SB = CH * 16;           // stage bytes
-  constexpr int NS = 2;                 // ring stages
+  constexpr int NS = P2 ? 3 : 2;        // ring stages
   constexpr int kLds = NS * SB > kEpiBytes ? NS * SB : kEpiBytes;
   constexpr bool kDual = MODE == G2_SWIGLU || MODE == G2_MOE_GU;
   constexpr bool kMoe = MODE == G2_MOE_GU || MODE == G2_MOE_DOWN;
@@ -354,13 +376,14 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     const int P = (NW * j + wave) * 64 + lane;
     const bool is_a = j < LPA;
     const int Q = is_a ? P : P - AC;
-    const int row = Q / kRowChunks;
-    const int c = (Q % kRowChunks) ^ swz(row);
+    const int row = Q / RC;
+    const int c = (Q % RC) ^ swz_rc<RC>(row);
     if (is_a) {
-      // rows past the tile re-read a valid row; HL: rows RT.. are the lo halves
-      const int rr = min(HL ? row % RT : row, rows_valid - 1);
+      // rows past the tile re-read a valid row; pairs: rows RT.. are the lo halves
+      const bool lo = (HL || P2) && row >= RT;
+      const int rr = min(lo ? row - RT : row, rows_valid - 1);
       const size_t ar = MODE == G2_MOE_GU ? (size_t)p.row_index[m0 + rr] : (size_t)(m0 + rr);
-      src[j] = p.A + ar * p.lda + (HL && row >= RT ? p.Kb : 0) + c * 8;
+      src[j] = p.A + ar * p.lda + (lo ? p.Kb : 0) + c * 8;
     } else {
       const bf16* base;
       if constexpr (kDual) {
@@ -374,42 +397,45 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   }
 
   auto issue = [&](int kt) {  // stage kt of this split -> ring slot kt % NS
-    const int ka = (ks0 + kt) * BK;
+    const int ka = (ks0 + kt) * SBK;
     int kb = ka;
-    if (kb >= p.Kb) kb -= p.Kb;  // [hi | lo] A: B is read twice
+    if (!P2 && kb >= p.Kb) kb -= p.Kb;  // [hi | lo] A over the doubled K: B is read twice
     char* slot = smem + (kt % NS) * SB;
 #pragma unroll
     for (int j = 0; j < LPT; ++j)
       load_lds16(src[j] + (j < LPA ? ka : kb), slot + (NW * j + wave) * 1024);
   };
 
-  f32x16 acc[4][TJ];
+  f32x16 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment read offsets (bytes within a stage) for k16 step ks
+  // fragment read offsets (bytes within a stage) for k16 step ks; P2: the lo
+  // row of a hi row sits BMT LDS rows further
   const int fr = lane & 31;
   const int fk = lane >> 5;
-  constexpr int KS = BK / 16;  // 16-deep MFMA steps per stage
-  int aoff[KS][4], boff[KS][TJ];
+  constexpr int KS = SBK / 16;  // 16-deep MFMA steps per stage
+  int aoff[KS][TI], boff[KS][TJ];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int c = 2 * ks + fk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + 32 * i + fr;
-      aoff[ks][i] = (ra * kRowChunks + (c ^ swz(ra))) * 16;
+    for (int i = 0; i < TI; ++i) {
+      const int ra = wm * WROWS + 32 * i + fr;
+      aoff[ks][i] = (ra * RC + (c ^ swz_rc<RC>(ra))) * 16;
     }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int rb = wn * WCOLS + 32 * j + fr;
-      boff[ks][j] = AC * 16 + (rb * kRowChunks + (c ^ swz(rb))) * 16;
+      boff[ks][j] = AC * 16 + (rb * RC + (c ^ swz_rc<RC>(rb))) * 16;
     }
   }
+  static_assert(!P2 || (BMT % 16 == 0 && ((BMT >> 2) & 3) == 0), "lo rows keep the hi rows' swizzle");
+  constexpr int kLoOff = BMT * RC * 16;  // P2: bytes from a hi row to its lo row
 
   // One stage: the fragments of k steps (0, 1) are read, then those of (2, 3)
   // are requested before the MFMAs of (0, 1) run, so only the first reads of
@@ -418,74 +444,128 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   // only (the fragment reads stay unconditional: reads inside the branches
   // made the compiler wait for them before every pair of MFMAs; the padding
   // rows hold copies of a valid row).
-  bool act[4];
+  bool act[TI];
   {
     const int wmu = __builtin_amdgcn_readfirstlane(wm);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) act[i] = !kMoe || wmu * 128 + 32 * i < rows_valid;
+    for (int i = 0; i < TI; ++i) act[i] = !kMoe || wmu * WROWS + 32 * i < rows_valid;
     (void)wmu;
   }
-  auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][4], bf16x8 (&bfr)[2][TJ]) {
+  if constexpr (!P2) {
+    auto read2 = [&](const char* st, int kh, bf16x8 (&af)[2][TI], bf16x8 (&bfr)[2][TJ]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
+        for (int i = 0; i < TI; ++i) af[ks][i] = *reinterpret_cast<const bf16x8*>(st + aoff[kh + ks][i]);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
+        for (int j = 0; j < TJ; ++j)
+          bfr[ks][j] = *reinterpret_cast<const bf16x8*>(st + boff[kh + ks][j]);
+      }
+    };
+    auto mma2 = [&](const bf16x8 (&af)[2][TI], const bf16x8 (&bfr)[2][TJ]) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+          if (act[i])
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+    };
+    static_assert(KS == 4, "two halves of two k steps per stage");
+
+    // Two stages; stage kt+1 is requested right after the barrier that
+    // publishes stage kt and lands while stage kt is multiplied.
+    if (nk > 0) issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();  // this wave's part of stage kt (the only stage in flight)
+      // every wave's part of stage kt has landed and every wave is done with
+      // the other slot. A bare s_barrier: __syncthreads' release fence adds
+      // nothing here; the acquire fence keeps the LDS reads below it.
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (kt + 1 < nk) issue(kt + 1);
+      const char* st = smem + (kt % NS) * SB;
+      bf16x8 a0[2][TI], b0[2][TJ], a1[2][TI], b1[2][TJ];
+      read2(st, 0, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      read2(st, 2, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma2(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma2(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  auto mma2 = [&](const bf16x8 (&af)[2][4], const bf16x8 (&bfr)[2][TJ]) {
+  } else {
+    static_assert(KS == 2 && NS == 3, "two k steps per stage, three ring slots");
+    // one 16-deep step: hi and lo fragments of the wave's rows, weight fragments
+    auto read1 = [&](const char* st, int ks, bf16x8 (&ah)[TI], bf16x8 (&al)[TI], bf16x8 (&bw)[TJ]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int i = 0; i < TI; ++i) {
+        ah[i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks][i]);
+        al[i] = *reinterpret_cast<const bf16x8*>(st + aoff[ks][i] + kLoOff);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < TJ; ++j) bw[j] = *reinterpret_cast<const bf16x8*>(st + boff[ks][j]);
+    };
+    // all hi products, then all lo products: eight independent MFMAs sit
+    // between two that update the same accumulators
+    auto mma1 = [&](const bf16x8 (&ah)[TI], const bf16x8 (&al)[TI], const bf16x8 (&bw)[TJ]) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
         if (act[i])
 #pragma unroll
-          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
-  };
-  static_assert(KS == 4, "two halves of two k steps per stage");
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(ah[i], bw[j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        if (act[i])
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_32x32x16(al[i], bw[j], acc[i][j]);
+    };
 
-  // Two stages; stage kt+1 is requested right after the barrier that publishes
-  // stage kt and lands while stage kt is multiplied.
-  if (nk > 0) issue(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmcnt<0>();  // this wave's part of stage kt (the only stage in flight)
-    // every wave's part of stage kt has landed and every wave is done with
-    // the other slot. A bare s_barrier: __syncthreads' release fence adds
-    // nothing here; the acquire fence keeps the LDS reads below it.
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (kt + 1 < nk) issue(kt + 1);
-    const char* st = smem + (kt % NS) * SB;
-    bf16x8 a0[2][4], b0[2][TJ], a1[2][4], b1[2][TJ];
-    read2(st, 0, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    read2(st, 2, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma2(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma2(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
+    // Three slots: stages kt+1 and kt+2 are in flight while stage kt is
+    // multiplied. Stage kt+2 goes to the slot stage kt-1 used, which every
+    // wave has finished reading once it passes the barrier of stage kt.
+    if (nk > 0) issue(0);
+    if (nk > 1) issue(1);
+    for (int kt = 0; kt < nk; ++kt) {
+      // this wave's part of stage kt (loads complete in order: only stage
+      // kt+1's may still be out)
+      if (kt + 1 < nk) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (kt + 2 < nk) issue(kt + 2);
+      const char* st = smem + (kt % NS) * SB;
+      bf16x8 h0[TI], l0[TI], w0[TJ], h1[TI], l1[TI], w1[TJ];
+      read1(st, 0, h0, l0, w0);
+      __builtin_amdgcn_sched_barrier(0);
+      read1(st, 1, h1, l1, w1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma1(h0, l0, w0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma1(h1, l1, w1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __syncthreads();  // the ring is reused for the epilogue
 
   // ---- epilogue: 128 rows (one row of waves) at a time through LDS ----
   float* C = reinterpret_cast<float*>(smem);
-  constexpr int NH = HL ? 1 : WMW;  // 128-row halves written out
+  constexpr int NH = HL ? 1 : 2;  // 128-row halves written out
+  constexpr int WPH = 128 / WROWS;  // wave rows per half
 #pragma unroll
   for (int half = 0; half < NH; ++half) {
     // HL: the hi rows (wm 0) are stored, then the lo rows (wm 1) added on top
 #pragma unroll
     for (int pass = 0; pass < (HL ? 2 : 1); ++pass) {
-      if (wm == (HL ? pass : half)) {
+      if ((HL ? wm == pass : wm / WPH == half)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              const int row = (wm % WPH) * WROWS + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
               float* dst = C + row * kPitch + wn * WCOLS + 32 * j + (lane & 31);
               *dst = (HL && pass == 1) ? *dst + acc[i][j][r] : acc[i][j][r];
             }
@@ -955,12 +1035,15 @@ __global__ __launch_bounds__(256) void gemm2_reduce_kernel(const G2Args p) {
   }
 }
 
-// Tile shapes: 256 token rows (8 waves); 128 token rows from a [hi | lo] pair
-// (8 waves); the 4-wave decode tiles with an A tile of 32, 64 or 128 LDS
-// rows, from a plain bf16 A or from a [hi | lo] pair (16, 32 or 64 token rows).
-enum : int { T256 = 0, P128_HL, D32, D64, D128, D32_HL, D64_HL, D128_HL };
+// Tile shapes: 256 token rows of a plain bf16 A (8 waves); 128 or 256 token
+// rows from a [hi | lo] pair (8 waves); the 4-wave decode tiles with an A tile
+// of 32, 64 or 128 LDS rows, from a plain bf16 A or from a [hi | lo] pair (16,
+// 32 or 64 token rows).
+enum : int { T256 = 0, P128_HL, P256, D32, D64, D128, D32_HL, D64_HL, D128_HL };
 constexpr int shape_ra(int sh) { return sh == D32 || sh == D32_HL ? 32 : (sh == D64 || sh == D64_HL ? 64 : 128); }
-constexpr bool shape_hl(int sh) { return sh >= D32_HL || sh == P128_HL; }
+constexpr bool shape_hl(int sh) { return sh >= D32_HL || sh == P128_HL || sh == P256; }
+constexpr bool shape_dec(int sh) { return sh >= D32; }
+constexpr int shape_kind(int sh) { return sh == P256 ? 2 : (sh == P128_HL ? 1 : 0); }
 // (a pair needs its hi and lo rows in different 32-row MFMA tiles: RA >= 64)
 int decode_shape(int M, bool pair) {
   if (pair) return M <= 32 ? D64_HL : D128_HL;
@@ -970,29 +1053,27 @@ int decode_shape(int M, bool pair) {
 template <int MODE, int SHAPE>
 hipError_t launch(const G2Args& a, dim3 grid, hipStream_t s) {
   constexpr bool HL = shape_hl(SHAPE);
-  // hi/lo inputs feed Q/K/V and O; plain bf16 inputs feed gate/up and down
-  // Q/K/V and O always take a pair; gate/up, down and the gated shared-expert
-  // down take a pair or plain bf16 on the decode tiles, and only the pair on
-  // the 128-row prefill tiles is reserved for Q/K/V and O
+  // Q/K/V and O always take a [hi | lo] pair; gate/up, down and the gated
+  // shared-expert down take a pair or plain bf16
   constexpr bool kPairOnly = MODE == G2_BIAS || MODE == G2_RESID_F32;
   constexpr bool kMoe = MODE == G2_MOE_GU || MODE == G2_MOE_DOWN;
-  constexpr bool kDec = SHAPE != T256 && SHAPE != P128_HL;
-  if constexpr (SHAPE != T256 && (kMoe || SHAPE == D32_HL || (kPairOnly && !HL))) {
+  constexpr bool kDec = shape_dec(SHAPE);
+  if constexpr ((kPairOnly && !HL) || (SHAPE != T256 && (kMoe || SHAPE == D32_HL))) {
     return hipErrorInvalidValue;
   } else if constexpr (kDec) {  // decode tiles: stream-K partials
     hipLaunchKernelGGL((gemm2_dec_kernel<MODE, HL, shape_ra(SHAPE)>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
   } else {
     if (a.splits == 1)
-      hipLaunchKernelGGL((gemm2_kernel<MODE, false, HL>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gemm2_kernel<MODE, false, shape_kind(SHAPE)>), grid, dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm2_kernel<MODE, true, HL>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gemm2_kernel<MODE, true, shape_kind(SHAPE)>), grid, dim3(512), 0, s, a);
     return hipGetLastError();
   }
 }
 
 int rows_per_tile(int shape) {
-  if (shape == T256) return 256;
+  if (shape == T256 || shape == P256) return 256;
   if (shape == P128_HL) return 128;
   return shape_hl(shape) ? shape_ra(shape) / 2 : shape_ra(shape);
 }
@@ -1017,7 +1098,7 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
   a.tiles_m = (a.M + rt - 1) / rt;
   const int nks = a.Ka / BK;
   dim3 grid;
-  if (shape != T256 && shape != P128_HL) {  // decode tiles: stream-K, always through the partials
+  if (shape_dec(shape)) {  // decode tiles: stream-K, always through the partials
     a.streamk = 1;
     a.sk_grid = sk_grid((long long)a.tiles_m * a.tiles_n * nks);
     a.splits = 1;
@@ -1033,6 +1114,7 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
   switch (shape) {
     case T256: e = launch<MODE, T256>(a, grid, s); break;
     case P128_HL: e = launch<MODE, P128_HL>(a, grid, s); break;
+    case P256: e = launch<MODE, P256>(a, grid, s); break;
     case D32: e = launch<MODE, D32>(a, grid, s); break;
     case D64: e = launch<MODE, D64>(a, grid, s); break;
     case D128: e = launch<MODE, D128>(a, grid, s); break;
@@ -1047,10 +1129,11 @@ hipError_t run(G2Args a, int shape, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Prefill GEMMs of a [hi | lo] pair A: 256-row tiles over the doubled K, or
-// 128-row tiles holding hi and lo rows over K (same MFMA work, twice the
-// tiles, half the k steps). Shape and split count minimise an estimate in
-// units of one 256 x 256 x 64 k step of a block (about 1.9 us measured):
+// Prefill GEMMs of a [hi | lo] pair A: 256-row tiles (32-deep stages of hi,
+// lo and weight rows), or 128-row tiles holding hi and lo rows over 64-deep
+// stages (same MFMA work per stage, twice the tiles at half the stages).
+// Shape and split count minimise an estimate in units of one stage of a
+// block (256 x 256 x 64 of MFMA work, about 1.9 us measured):
 // waves of up to 256 blocks times k steps per block, plus, with split-K, a
 // reduce launch and the partials' write and read back at ~5 TB/s. A tile
 // count just past a whole number of waves leaves most CUs idle in the last
@@ -1061,13 +1144,13 @@ struct PairPlan {
   int shape, splits, tail_cols, tail_splits;
 };
 PairPlan pair_plan(int M, int N, int K) {
-  PairPlan best{T256, 1, 0, 1};
+  PairPlan best{P256, 1, 0, 1};
   double best_c = 1e30;
   auto waves = [](long long blocks) { return (double)((blocks + 255) / 256); };
   auto part_cost = [&](int sp, int cols) { return (5.0 + 2.0 * sp * M * (double)cols * 4 / 5e6) / 1.9; };
-  for (int shape : {T256, P128_HL}) {
-    const int rows = shape == T256 ? 256 : 128;
-    const int ks = (shape == T256 ? 2 * K : K) / BK;
+  for (int shape : {P256, P128_HL}) {
+    const int rows = shape == P256 ? 256 : 128;
+    const int ks = (shape == P256 ? 2 * K : K) / BK;
     const int tiles_m = (M + rows - 1) / rows, tiles_n = N / BN;
     auto consider = [&](double c, PairPlan pl) {
       if (c < best_c - 1e-9) {
@@ -1162,7 +1245,7 @@ hipError_t ql_gemm2_qkv(const bf16* A2, int M, const bf16* Wq, const bf16* Wk, c
   if (rows128 != (f.cache_len != nullptr)) return hipErrorInvalidValue;  // decode <=> 128 rows
   const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1, 0, 1} : pair_plan(M, q + 2 * kv, K);
   (void)splits;
-  G2Args a = base(A2, M, pl.shape == T256 ? 2 * K : K, Wq, K, pl.splits, part);
+  G2Args a = base(A2, M, pl.shape == P256 ? 2 * K : K, Wq, K, pl.splits, part);
   a.lda = 2 * K;
   a.S = f.S;
   a.pos_offset = f.pos_offset;
@@ -1197,7 +1280,7 @@ hipError_t ql_gemm2_resid_f32(const bf16* A2, int M, const bf16* W, int N, int K
                               hipStream_t s) {
   const PairPlan pl = rows128 ? PairPlan{decode_shape(M, true), 1, 0, 1} : pair_plan(M, N, K);
   (void)splits;
-  G2Args a = base(A2, M, pl.shape == T256 ? 2 * K : K, W, K, pl.splits, part);
+  G2Args a = base(A2, M, pl.shape == P256 ? 2 * K : K, W, K, pl.splits, part);
   a.lda = 2 * K;
   a.resid_bf16 = resid;
   a.ldr = N;
@@ -1223,7 +1306,7 @@ AbPlan base_ab(const bf16* A, int M, const bf16* W, int N, int K, bool pair, boo
   PairPlan pl{T256, splits, 0, 1};
   if (rows128) pl = PairPlan{decode_shape(M, pair), 1, 0, 1};
   else if (pair) pl = pair_plan(M, N, K);
-  G2Args a = base(A, M, pair && pl.shape == T256 ? 2 * K : K, W, K, pl.splits, part);
+  G2Args a = base(A, M, pl.shape == P256 ? 2 * K : K, W, K, pl.splits, part);
   if (pair) a.lda = 2 * K;
   return {a, pl};
 }
@@ -1277,7 +1360,7 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg
                            const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H2,
                            hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  G2Args a = base(Z2, 0, 2 * d, Wg, d, 1, nullptr);  // [hi | lo] rows over a doubled K
+  G2Args a = base(Z2, 0, 2 * d, Wg, d, 1, nullptr);  // [hi | lo] rows, 256-row pair tiles
   a.B2 = Wu;
   a.b_expert_stride = (size_t)mf * d;
   a.row_index = slot_token;
@@ -1290,7 +1373,7 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg
   a.out_lo = mf;
   a.tiles_n = mf / (BN / 2);
   const int total = max_tiles * a.tiles_n;
-  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, false>), dim3(8 * ((total + 7) / 8)), dim3(512), 0,
+  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, 2>), dim3(8 * ((total + 7) / 8)), dim3(512), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -1299,7 +1382,7 @@ hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
                              const int* tile_expert, const int* tile_row0, const int* tile_rows,
                              const int* num_tiles, int max_tiles, float* out, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  G2Args a = base(H2, 0, 2 * mf, Wd, mf, 1, nullptr);  // [hi | lo] rows over a doubled K
+  G2Args a = base(H2, 0, 2 * mf, Wd, mf, 1, nullptr);  // [hi | lo] rows, 256-row pair tiles
   a.b_expert_stride = (size_t)d * mf;
   a.tile_expert = tile_expert;
   a.tile_row0 = tile_row0;
@@ -1309,7 +1392,7 @@ hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
   a.ldo = d;
   a.tiles_n = d / BN;
   const int total = max_tiles * a.tiles_n;
-  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, false>), dim3(8 * ((total + 7) / 8)), dim3(512),
+  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, 2>), dim3(8 * ((total + 7) / 8)), dim3(512),
                      0, s, a);
   return hipGetLastError();
 }
