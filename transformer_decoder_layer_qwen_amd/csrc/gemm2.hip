@@ -454,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   {
     const int wmu = __builtin_amdgcn_readfirstlane(wm);
 #pragma unroll
-    for (int i = 0; i < TI; ++i) act[i] = !kMoe || wmu * WROWS + 32 * i < rows_valid;
+    for (int i = 0; i < TI; ++i) act[i] = !kMoe || (wmu * WROWS + 32 * i) % RT < rows_valid;
     (void)wmu;
   }
   if constexpr (!P2) {
@@ -1368,10 +1368,14 @@ hipError_t ql_gemm2_swiglu(const bf16* A, int M, const bf16* Wg, const bf16* Wu,
 
 hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg, const bf16* Wu,
                            int mf, int d, const int* tile_expert, const int* tile_row0,
-                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H2,
-                           hipStream_t s) {
+                           const int* tile_rows, const int* num_tiles, int max_tiles, int bm,
+                           bf16* H2, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  G2Args a = base(Z2, 0, 2 * d, Wg, d, 1, nullptr);  // [hi | lo] rows, 256-row pair tiles
+  if (bm != 128 && bm != 256) return hipErrorInvalidValue;
+  // [hi | lo] rows: 256-row pair tiles over 32-deep stages (2 x Kb for the
+  // step count), or 128-row hi/lo tiles over 64-deep stages
+  G2Args a = base(Z2, 0, bm == 256 ? 2 * d : d, Wg, d, 1, nullptr);
+  a.lda = 2 * d;
   a.B2 = Wu;
   a.b_expert_stride = (size_t)mf * d;
   a.row_index = slot_token;
@@ -1384,16 +1388,23 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg
   a.out_lo = mf;
   a.tiles_n = mf / (BN / 2);
   const int total = max_tiles * a.tiles_n;
-  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, 2>), dim3(8 * ((total + 7) / 8)), dim3(512), 0,
-                     s, a);
+  if (bm == 256)
+    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, 2>), dim3(8 * ((total + 7) / 8)), dim3(512),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, 1>), dim3(8 * ((total + 7) / 8)), dim3(512),
+                       0, s, a);
   return hipGetLastError();
 }
 
 hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
                              const int* tile_expert, const int* tile_row0, const int* tile_rows,
-                             const int* num_tiles, int max_tiles, float* out, hipStream_t s) {
+                             const int* num_tiles, int max_tiles, int bm, float* out,
+                             hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  G2Args a = base(H2, 0, 2 * mf, Wd, mf, 1, nullptr);  // [hi | lo] rows, 256-row pair tiles
+  if (bm != 128 && bm != 256) return hipErrorInvalidValue;
+  G2Args a = base(H2, 0, bm == 256 ? 2 * mf : mf, Wd, mf, 1, nullptr);  // as for gate/up
+  a.lda = 2 * mf;
   a.b_expert_stride = (size_t)d * mf;
   a.tile_expert = tile_expert;
   a.tile_row0 = tile_row0;
@@ -1403,7 +1414,11 @@ hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
   a.ldo = d;
   a.tiles_n = d / BN;
   const int total = max_tiles * a.tiles_n;
-  hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, 2>), dim3(8 * ((total + 7) / 8)), dim3(512),
-                     0, s, a);
+  if (bm == 256)
+    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, 2>), dim3(8 * ((total + 7) / 8)),
+                       dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, 1>), dim3(8 * ((total + 7) / 8)),
+                       dim3(512), 0, s, a);
   return hipGetLastError();
 }

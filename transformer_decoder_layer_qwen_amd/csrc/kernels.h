@@ -98,17 +98,18 @@ hipError_t ql_gemm2_gated_out(const bf16* A, int M, const bf16* W, int N, int K,
                               const float* gate_logit, int gate_ld, const float* resid_f32,
                               const bf16* resid_bf16, float* out, bool rows128, int splits,
                               void* part, hipStream_t s, bool pair_in);
-// MoE expert GEMMs on 256-row expert tiles (the permute's tile table built
-// with bm = 256; max_tiles bounds *num_tiles; mf % 128 == 0, d % 256 == 0).
-// Z2 [N, 2d] and H2 [N*k, 2mf] are [hi | lo] pairs read over a doubled K;
-// out [N*k, d] fp32 in slot order.
+// MoE expert GEMMs on expert tiles of bm = 128 or 256 token rows (the
+// permute's tile table built with the same bm; max_tiles bounds *num_tiles;
+// mf % 128 == 0, d % 256 == 0). Z2 [N, 2d] and H2 [N*k, 2mf] are [hi | lo]
+// pairs; out [N*k, d] fp32 in slot order.
 hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg, const bf16* Wu,
                            int mf, int d, const int* tile_expert, const int* tile_row0,
-                           const int* tile_rows, const int* num_tiles, int max_tiles, bf16* H2,
-                           hipStream_t s);
+                           const int* tile_rows, const int* num_tiles, int max_tiles, int bm,
+                           bf16* H2, hipStream_t s);
 hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
                              const int* tile_expert, const int* tile_row0, const int* tile_rows,
-                             const int* num_tiles, int max_tiles, float* out, hipStream_t s);
+                             const int* num_tiles, int max_tiles, int bm, float* out,
+                             hipStream_t s);
 
 // ---- decode GEMVs for M <= kGemvMaxRows rows (N % 2 == 0, K % 8 == 0) ----
 // qkv_raw: out[M, q+2kv] fp32 = raw sums of (x * gamma) [Wq; Wk; Wv]^T (x,

@@ -38,6 +38,7 @@ ql_status fail(ql_status st, const char* fmt, ...) {
 }
 
 constexpr int kMinMoeTile = 32;
+constexpr int kBigMoeTile = 128;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -359,7 +360,7 @@ ql_status copy_taps(ql_handle* h, int N, hipStream_t s) {
 
 // y = resid + MoE(z). RMSNorm2 of the residual rows is in zf (fp32: the
 // router and the 32-row expert tiles) and in h->xhat as a [hi | lo] bf16
-// pair (the 256-row expert tiles and the shared expert). `decode`: the
+// pair (the 128-row expert tiles and the shared expert). `decode`: the
 // shared expert runs on the decode tiles.
 ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf16* y,
                    bool decode, hipStream_t s) {
@@ -381,11 +382,13 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
   ra.w = h->topw;
   QL_STAGE(h, QL_STAGE_ROUTER, s, QL_HIP(ql_router_topk(ra, s)));
 
-  // Expert tiles: 256 rows on the 8-wave MFMA tiles when experts see many
-  // rows (the prefill), 32 rows on the small-tile kernel for decode-sized
-  // batches.
+  // Expert tiles: 128 token rows on the 8-wave MFMA tiles when experts see
+  // many rows (the prefill), 32 rows on the small-tile kernel for
+  // decode-sized batches. (A tile's stages cost the same however few of its
+  // rows are live; around 256 rows per expert, 256-row tiles leave a third
+  // of the tile rows empty, 128-row tiles a fifth.)
   const bool big = (long long)N * c.top_k >= 64LL * c.n_experts;
-  const int bm = big ? 256 : kMinMoeTile;
+  const int bm = big ? kBigMoeTile : kMinMoeTile;
   const int max_tiles = (int)(((long long)N * c.top_k + bm - 1) / bm + c.n_experts);
   PermuteArgs pa{};
   pa.idx = h->idx;
@@ -405,9 +408,9 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
   QL_STAGE(h, QL_STAGE_PERMUTE, s, QL_HIP(ql_moe_permute(pa, s)));
 
   // The experts see z at fp32 precision and keep h and their outputs so:
-  // 256-row tiles read the [hi | lo] pair of z (x-hat buffer) over a doubled
-  // K and store h as a pair; 32-row tiles stage fp32 z and h as pairs
-  // themselves. Outputs are fp32 in slot order.
+  // 128-row tiles read the [hi | lo] pair of z (x-hat buffer), hi and lo
+  // rows sharing each weight tile, and store h as a pair; 32-row tiles stage
+  // fp32 z and h as pairs themselves. Outputs are fp32 in slot order.
   const bf16* z2 = static_cast<const bf16*>(h->xhat);
   const bf16* wg = static_cast<const bf16*>(w.we_gate);
   const bf16* wu = static_cast<const bf16*>(w.we_up);
@@ -416,10 +419,11 @@ ql_status moe_core(ql_handle* h, int N, const void* resid, int resid_is_f32, bf1
     bf16* hm = static_cast<bf16*>(h->hm);
     QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
              QL_HIP(ql_gemm2_moe_gu(z2, h->slot_token, wg, wu, c.ffn_dim, c.d, h->tile_expert,
-                                    h->tile_row0, h->tile_rows, h->num_tiles, max_tiles, hm, s)));
+                                    h->tile_row0, h->tile_rows, h->num_tiles, max_tiles, bm, hm,
+                                    s)));
     QL_STAGE(h, QL_STAGE_EXPERT_DOWN, s,
              QL_HIP(ql_gemm2_moe_down(hm, wd, c.ffn_dim, c.d, h->tile_expert, h->tile_row0,
-                                      h->tile_rows, h->num_tiles, max_tiles, h->out_slot, s)));
+                                      h->tile_rows, h->num_tiles, max_tiles, bm, h->out_slot, s)));
   } else {
     float* hm = static_cast<float*>(h->hm);
     QL_STAGE(h, QL_STAGE_EXPERT_GATE_UP, s,
