@@ -254,12 +254,19 @@ hipError_t launch_cfg(const GemvArgs& a, int M, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Two output rows per block, four waves, two chunks in flight per row stream:
-// the best of a sweep over (rows, waves, chunks) on the decode projections of
-// d = 3584 / ffn = 18944 (5.4-5.9 TB/s on the large ones).
+// Launch shapes, the best of sweeps over (rows per block, waves, chunks in
+// flight per row stream) on the batch-1 projections of d = 3584 / ffn = 18944
+// with non-temporal weight loads: gate/up takes four output rows (eight
+// weight row streams) with one chunk in flight each, 38.9 us for 272 MB
+// (two rows and two chunks: 43.4 us); Q/K/V, O and down take two rows, four
+// waves and two chunks (6.5, 4.3 and 19.7 us; no other shape tried was
+// faster on them).
 template <int MODE, int XM>
 hipError_t launch(const GemvArgs& a, int M, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
+  if constexpr (MODE == GV_SWIGLU) {
+    if (a.N % 4 == 0) return launch_cfg<MODE, XM, 4, 4, 1>(a, M, s);
+  }
   return launch_cfg<MODE, XM, 2, 4, 2>(a, M, s);
 }
 
