@@ -87,7 +87,7 @@ typedef enum { QL_BF16 = 0, QL_F32 = 1 } ql_dtype;
  *              MoE layers only; sf % 128 == 0.
  *
  * QL_BF16 shape limits: head_dim == 128, d % 256 == 0, Hq and Hkv even,
- * ffn_dim % 128 == 0, Hq/Hkv <= 16, max_batch <= 128, and with experts
+ * ffn_dim % 128 == 0, Hq/Hkv <= 16, max_batch <= 1024, and with experts
  * n_experts <= 256.
  */
 typedef struct {

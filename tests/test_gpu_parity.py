@@ -552,6 +552,20 @@ def check_decode_full(cfg, layer, w64, x, kc, vc, lens, label=""):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("cid,Bn,T", [(2, 200, 128), (5, 256, 96)],
+                         ids=["qwen2.5-7b_B200", "qwen3-30b-a3b_B256"])
+def test_decode_large_batch(cid, Bn, T):
+    """Batches past 128 rows: several 64-token decode tile rows (the last one
+    ragged at 200), a 256-row attention grid, and for the MoE layer 2048 routed
+    rows on the 32-row expert tiles; every sequence checked."""
+    cfg = configs.CONFIGS[cid]
+    layer, w64 = make_layer(cfg, seed=configs.weight_seed(cid), max_tokens=1, max_batch=Bn)
+    x, kc, vc, lens = synth.make_decode_input(cfg, 4242 + Bn, Bn, T)
+    check_decode_full(cfg, layer, w64, x, kc, vc, lens, label=f"{cfg.name} decode B={Bn} T={T}")
+    layer.close()
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cid,wl", FULL, ids=[w.label.replace(" ", "_") for _, w in FULL])
 def test_full_size(cid, wl):
     cfg = configs.CONFIGS[cid]

@@ -169,7 +169,7 @@ ql_status validate(const ql_config* c, const ql_weights* w) {
       return fail(QL_EUNSUPPORTED, "QL_BF16 needs even n_q_heads and n_kv_heads");
     if (c->ffn_dim % 128) return fail(QL_EUNSUPPORTED, "QL_BF16 needs ffn_dim %% 128 == 0");
     if (G > 16) return fail(QL_EUNSUPPORTED, "QL_BF16 needs n_q_heads / n_kv_heads <= 16");
-    if (c->max_batch > 128) return fail(QL_EUNSUPPORTED, "QL_BF16 decode needs max_batch <= 128");
+    if (c->max_batch > 1024) return fail(QL_EUNSUPPORTED, "QL_BF16 decode needs max_batch <= 1024");
   } else {
     if (!is_pow2(c->head_dim) || c->head_dim < 2 || c->head_dim > 128)
       return fail(QL_EUNSUPPORTED, "QL_F32 needs a power-of-two head_dim in [2, 128]");
