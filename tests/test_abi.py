@@ -61,7 +61,7 @@ def _weights(moe=False):
     (dict(ffn_dim=100), b.QL_EUNSUPPORTED),
     (dict(ffn_dim=192), b.QL_EUNSUPPORTED),
     (dict(n_q_heads=34, n_kv_heads=2), b.QL_EUNSUPPORTED),
-    (dict(max_batch=129), b.QL_EUNSUPPORTED),
+    (dict(max_batch=1025), b.QL_EUNSUPPORTED),
     (dict(max_tokens=0, max_batch=0), b.QL_EINVAL),
     (dict(dtype=7), b.QL_EINVAL),
     (dict(qkv_bias=1), b.QL_EINVAL),          # bias pointers missing
