@@ -58,8 +58,18 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const int wave = tid >> 6;          // query rows 32 wave .. +31 of the tile
   const int col = lane & 31;
   const int hi = lane >> 5;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // XCD-aware order: the work items (tile slot x fastest, then query head,
+  // then sequence) are cut into 8 contiguous stretches and block L runs item
+  // (L mod 8) * stretch + L / 8; consecutive blocks go to the 8 XCDs in turn,
+  // so each XCD walks whole heads and the query heads of one KV group find
+  // its K/V tiles in that XCD's L2 (attention 2-5 % faster)
+  const int wl = (int)blockIdx.x;
+  const int wchunk = (p.gtotal + 7) / 8;
+  const int wi = (wl % 8) * wchunk + wl / 8;
+  if (wi >= p.gtotal) return;  // block-uniform, before any barrier
+  const int bx = wi % p.gx;
+  const int h = (wi / p.gx) % p.gy;
+  const int b = wi / (p.gx * p.gy);
   const int g = h / (p.n_q_heads / p.n_kv_heads);
   // Sequence b: S new query rows from q row qbase, keys = its cache rows
   // 0 .. P + S - 1, the first P of them an earlier prefix; new row t is at
@@ -74,15 +84,14 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   // Otherwise a block takes one tile, the longest first. (Grids are sized
   // for the longest sequence; a shorter one's extra blocks have no tile.)
   const int nqt = (S + kBQ - 1) / kBQ;
-  const int qt_first = p.pair ? nqt - 1 - (int)blockIdx.x
-                              : (int)(gridDim.x - 1 - blockIdx.x) - ((int)gridDim.x - nqt);
+  const int qt_first = p.pair ? nqt - 1 - bx : (p.gx - 1 - bx) - (p.gx - nqt);
   // block-uniform, before any barrier: no tile, or (pairs) a tile that a
   // lower block already takes as its second
-  if (qt_first < 0 || (p.pair && (int)blockIdx.x > qt_first)) return;
-  const int npass = (p.pair && (int)blockIdx.x < qt_first) ? 2 : 1;
+  if (qt_first < 0 || (p.pair && bx > qt_first)) return;
+  const int npass = (p.pair && bx < qt_first) ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
   if (pass > 0) __syncthreads();  // the LDS ring is reused
-  const int qt = pass == 0 ? qt_first : (int)blockIdx.x;
+  const int qt = pass == 0 ? qt_first : bx;
   const int q0 = qt * kBQ;
   const int my_q = q0 + wave * 32 + col;         // new row of this lane's query
   const int my_pos = P + my_q;                   // its key position
@@ -339,19 +348,28 @@ hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
   if (pairs >= 2L * kCUs) {
     // enough tile pairs (equal work each) for two 4-wave blocks per CU
     b.pair = true;
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3((nqt + 1) / 2, a.n_q_heads, a.B),
-                       dim3(256), 0, s, b);
+    b.gx = (nqt + 1) / 2;
+    b.gy = a.n_q_heads;
+    b.gtotal = b.gx * b.gy * a.B;
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(256), 0,
+                       s, b);
   } else if (pairs >= kCUs || tiles <= kCUs) {
     // one 8-wave block per CU, each tile's keys split between its two groups:
     // tile pairs when they fill the CUs, else single tiles
     b.pair = pairs >= kCUs;
-    hipLaunchKernelGGL(attn_prefill_kernel<true>,
-                       dim3(b.pair ? (nqt + 1) / 2 : nqt, a.n_q_heads, a.B), dim3(512), 0, s, b);
+    b.gx = b.pair ? (nqt + 1) / 2 : nqt;
+    b.gy = a.n_q_heads;
+    b.gtotal = b.gx * b.gy * a.B;
+    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(512), 0,
+                       s, b);
   } else {
     // single tiles, longest first, two 4-wave blocks per CU
     b.pair = false;
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(nqt, a.n_q_heads, a.B), dim3(256), 0, s,
-                       b);
+    b.gx = nqt;
+    b.gy = a.n_q_heads;
+    b.gtotal = b.gx * b.gy * a.B;
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(256), 0,
+                       s, b);
   }
   return hipGetLastError();
 }

@@ -168,6 +168,7 @@ struct AttnPrefillArgs {
   int n_q_heads, n_kv_heads, head_dim;
   float scale_log2;      // log2(e) / sqrt(dh)
   int pair;              // set by the launcher: a block takes query tiles nqt-1-x and x
+  int gx, gy, gtotal;    // set by the launcher: the (tile, head, sequence) work grid
   const int* seq_start;  // varlen [B + 1] device: sequence b's q rows, or NULL (b S)
   const int* prefix;     // [B] device: cache rows before the new ones, or NULL (0)
 };
