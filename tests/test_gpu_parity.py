@@ -75,6 +75,40 @@ def test_toy_prefill_f32(variant):
     assert np.all(host(kc)[:, 3:] == 0)
 
 
+F32_SHAPES = {
+    # fp32 layers past the toy's head_dim 2: the generic fp32 kernels at
+    # head_dim 16 (GQA 3:1, bias, QK-norm) and 128 (one KV head)
+    "dh16": dict(d=96, n_q_heads=6, n_kv_heads=2, head_dim=16, ffn_dim=80, qkv_bias=True,
+                 qk_norm=True, b_std=0.1, gamma_std=0.1),
+    "dh128": dict(d=256, n_q_heads=2, n_kv_heads=1, head_dim=128, ffn_dim=64),
+}
+
+
+@pytest.mark.parametrize("shape", list(F32_SHAPES))
+def test_f32_wider_heads_prefill_then_decode(shape):
+    """The QL_F32 path at head_dim 16 and 128 against the oracle: a prefill
+    of 2 x 37 rows (the caches written), then one decode step per sequence
+    over those caches, every element at the fp32 bar."""
+    cfg = configs.with_dims(configs.TOY, name=f"f32-{shape}", w_std=0.1, x_std=1.0,
+                            cache_std=1.0, **F32_SHAPES[shape])
+    spec = spec_of(cfg)
+    layer, w32 = make_layer(cfg, max_tokens=2 * 37, max_batch=2)
+    x = synth.make_prefill_input(cfg, 1003, 2, 38)
+    T_max = 40
+    y, kc, vc = run_prefill(layer, cfg, x[:, :37], T_max=T_max)
+    o = ref.layer_prefill(x[:, :37], w32, spec)
+    assert rel_err(host(y), o["y"]) <= F32_TOL
+    assert rel_err(host(kc)[:, :37], o["k"]) <= F32_TOL
+    assert rel_err(host(vc)[:, :37], o["v"]) <= F32_TOL
+    lens = torch.tensor([37, 37], dtype=torch.int32, device="cuda")
+    yd = layer.decode(B.to_device(x[:, 37]), lens, kc, vc, cache_len_host=[37, 37])
+    torch.cuda.synchronize()
+    full = ref.layer_prefill(x, w32, spec)
+    assert rel_err(host(yd), full["y"][:, 37]) <= F32_TOL
+    assert rel_err(host(kc)[:, 37], full["k"][:, 37]) <= F32_TOL
+    layer.close()
+
+
 def test_toy_decode_f32():
     cfg = configs.TOY
     layer, w32 = make_layer(cfg, max_tokens=16, max_batch=4)
