@@ -1165,11 +1165,12 @@ PairPlan pair_plan(int M, int N, int K) {
   for (int shape : {P256, P128_HL}) {
     const int rows = shape == P256 ? 256 : 128;
     const int ks = (shape == P256 ? 2 * K : K) / BK;
-    // a 256-row stage (hi, lo and weight rows together) runs a little faster
-    // than a 128-row one: with this weight the plans moved to them cut the
-    // dense prefill layers by 2-5 % (Qwen2.5-7B 1 x 1024 1044 -> 991 us,
-    // 4 x 512 1839 -> 1749, Qwen3-32B 2048 3666 -> 3533)
-    const double unit = shape == P256 ? 0.93 : 1.0;
+    // a 256-row stage (hi, lo and weight rows together) runs faster than a
+    // 128-row one: weighing it at 0.93 moved plans that cut the dense prefill
+    // layers by 2-5 % (Qwen2.5-7B 1 x 1024 1044 -> 991 us, 4 x 512 1839 ->
+    // 1749, Qwen3-32B 2048 3666 -> 3533); 0.88 gained another 0-6 % on single
+    // GEMMs (Qwen3-8B down 384 -> 361 us), 0.97 lost 3-6 %
+    const double unit = shape == P256 ? 0.88 : 1.0;
     const int tiles_m = (M + rows - 1) / rows, tiles_n = N / BN;
     auto consider = [&](double c, PairPlan pl) {
       if (c < best_c - 1e-9) {
