@@ -391,21 +391,29 @@ QL_DEV void store_out4(const AttnDecodeArgs& p, size_t idx, const f32x4& v) {
 // W > 1: the block's W waves are the splits of one (KV head, sequence) and
 // merge in LDS at the end (waves past nsplit have no keys), so no combine
 // kernel runs; W = 1: one wave per split, merged by the combine kernel.
-template <int G, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_mfma_kernel(const AttnDecodeArgs p) {
+// HM (head-major): the block's waves are the Hkv <= HMW KV heads of one
+// (split, sequence), so the block's loads of a key cover the key's whole
+// cache row across heads (Hkv x 256 contiguous bytes) at once; the splits
+// merge in the combine kernel. (A load-only probe of the Qwen3-8B B = 64
+// cache: 6.7 TB/s head-major against 5.9 TB/s split-major.)
+constexpr int kHmMaxHeads = 8;
+template <int G, int W, bool HM = false>
+__global__ __launch_bounds__(HM ? 64 * kHmMaxHeads : 64 * W) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_mfma_kernel(const AttnDecodeArgs p) {
   static_assert(G >= 1 && G <= 16, "query heads per KV head");
   static_assert(16 * kDh * sizeof(float) <= kDh * kVtP * sizeof(bf16), "merge rows fit a V^T slot");
-  __shared__ __attribute__((aligned(16))) bf16 vt_all[W][kDh * kVtP];
+  static_assert(!HM || W == 1, "head-major blocks merge through the combine kernel");
+  constexpr int NWV = HM ? kHmMaxHeads : W;  // waves of the block
+  __shared__ __attribute__((aligned(16))) bf16 vt_all[NWV][kDh * kVtP];
 
-  const int wave = W == 1 ? 0 : (int)(threadIdx.x >> 6);
+  const int wave = NWV == 1 ? 0 : (int)(threadIdx.x >> 6);
   bf16* vt_lds = vt_all[wave];
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
   // KV heads fastest: the Hkv waves of one key range read neighbouring bytes
-  const int g = blockIdx.x;
-  const int split = W == 1 ? (int)blockIdx.y : wave;
-  const int b = blockIdx.z;
+  const int g = HM ? wave : (int)blockIdx.x;
+  const int split = HM ? (int)blockIdx.x : (W == 1 ? (int)blockIdx.y : wave);
+  const int b = HM ? (int)blockIdx.y : (int)blockIdx.z;
   const bool idle = split >= p.nsplit;  // W > 1 only
 
   // splits of `chunk` keys; the last one also takes the remainder
@@ -707,13 +715,22 @@ hipError_t ql_attn_decode_bf16(const AttnDecodeArgs& a, hipStream_t s) {
   const dim3 grid_kv(a.n_kv_heads, a.nsplit, a.B);
   // finished queries with up to 8 splits: the splits are the waves of one
   // block and merge there
-  const int wm = !a.q_in || a.nsplit == 1 || a.nsplit > 8 ? 1 : (a.nsplit <= 2 ? 2 : a.nsplit <= 4 ? 4 : 8);
+  // finished queries: head-major blocks (all KV heads of one split and
+  // sequence) when the heads fit one block, else the splits of one head as
+  // the waves of a block (<= 8 splits) or one wave per split
+  const bool hm = a.q_in && a.n_kv_heads >= 2 && a.n_kv_heads <= kHmMaxHeads;
+  const int wm = hm || !a.q_in || a.nsplit == 1 || a.nsplit > 8
+                     ? 1 : (a.nsplit <= 2 ? 2 : a.nsplit <= 4 ? 4 : 8);
   const dim3 grid_wg(a.n_kv_heads, 1, a.B);
+  const dim3 grid_hm(a.nsplit, a.B);
   switch (a.n_q_heads / a.n_kv_heads) {
 #define QL_G(V)                                                                                 \
   case V:                                                                                       \
     if (!a.q_in)                                                                                \
       hipLaunchKernelGGL((attn_decode_kernel<V>), grid, dim3(64), 0, s, a);                     \
+    else if (hm)                                                                                \
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<V, 1, true>), grid_hm, dim3(64 * a.n_kv_heads), \
+                         0, s, a);                                                              \
     else if (wm == 1)                                                                           \
       hipLaunchKernelGGL((attn_decode_mfma_kernel<V, 1>), grid_kv, dim3(64), 0, s, a);          \
     else if (wm == 2)                                                                           \
