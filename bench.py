@@ -384,23 +384,23 @@ PMC_TRAFFIC_KIB = {
     ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132730.0, 148.0, "gemv.hip", "1c873011e5d3fd21"),
     ("qwen2.5-7b decode B=1 cache=1024", "down"): (66526.3, 56.0, "gemv.hip", "1c873011e5d3fd21"),
     ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm1"): (157.0, 448.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22436.5, 9152.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22436.5, 9152.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen2.5-7b decode B=32 cache=1024", "attention"): (37915.7, 8064.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18577.4, 8896.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18577.4, 8896.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm2"): (268.7, 448.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140879.4, 15040.0, "gemm2.hip", "916da4e01f53f4ec"),
-    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79233.5, 8800.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140879.4, 15040.0, "gemm2.hip", "2262baeccb5a8fc2"),
+    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79233.5, 8800.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-8b decode B=64 cache=4096", "rmsnorm1"): (305.0, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35102.2, 18944.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35102.2, 18944.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-8b decode B=64 cache=4096", "attention"): (532684.4, 5376.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25486.0, 17408.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25486.0, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-8b decode B=64 cache=4096", "rmsnorm2"): (560.7, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110267.6, 23552.0, "gemm2.hip", "916da4e01f53f4ec"),
-    ("qwen3-8b decode B=64 cache=4096", "down"): (59532.7, 16896.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110267.6, 23552.0, "gemm2.hip", "2262baeccb5a8fc2"),
+    ("qwen3-8b decode B=64 cache=4096", "down"): (59532.7, 16896.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32544.8, 20992.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32544.8, 20992.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (536267.6, 10752.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17805.6, 17408.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17805.6, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "router"): (2650.9, 72.0, "moe.hip", "9df6017876fa8ad8"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "permute"): (4.9, 10.1, "moe.hip", "9df6017876fa8ad8"),
@@ -408,9 +408,9 @@ PMC_TRAFFIC_KIB = {
     ("qwen3-30b-a3b decode B=128 cache=4096", "expert_down"): (208941.2, 8192.0, "gemm.hip", "61d3a5bc75f21aff"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "combine"): (4645.6, 512.0, "moe.hip", "9df6017876fa8ad8"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32544.0, 20992.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32544.0, 20992.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "attention"): (139504.6, 10752.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17805.6, 17408.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17805.6, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "router"): (2650.9, 72.0, "moe.hip", "9df6017876fa8ad8"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "permute"): (4.9, 10.1, "moe.hip", "9df6017876fa8ad8"),
@@ -418,16 +418,16 @@ PMC_TRAFFIC_KIB = {
     ("qwen3-30b-a3b decode B=128 cache=1024", "expert_down"): (207405.1, 8192.1, "gemm.hip", "61d3a5bc75f21aff"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "combine"): (4645.6, 512.0, "moe.hip", "9df6017876fa8ad8"),
     ("qwen3-32b decode B=32 cache=4096", "rmsnorm1"): (230.0, 640.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57638.2, 10496.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57638.2, 10496.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-32b decode B=32 cache=4096", "attention"): (271521.6, 9728.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48161.9, 9344.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48161.9, 9344.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen3-32b decode B=32 cache=4096", "rmsnorm2"): (391.7, 640.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265873.3, 17536.0, "gemm2.hip", "916da4e01f53f4ec"),
-    ("qwen3-32b decode B=32 cache=4096", "down"): (140801.5, 9024.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265873.3, 17536.0, "gemm2.hip", "2262baeccb5a8fc2"),
+    ("qwen3-32b decode B=32 cache=4096", "down"): (140801.5, 9024.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("mixtral-like decode B=64 cache=2048", "rmsnorm1"): (304.8, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("mixtral-like decode B=64 cache=2048", "qkv"): (35099.6, 18944.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("mixtral-like decode B=64 cache=2048", "qkv"): (35099.6, 18944.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("mixtral-like decode B=64 cache=2048", "attention"): (268484.5, 5376.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25485.9, 17408.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25485.9, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("mixtral-like decode B=64 cache=2048", "rmsnorm2"): (560.7, 2048.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
     ("mixtral-like decode B=64 cache=2048", "router"): (694.9, 3.0, "moe.hip", "9df6017876fa8ad8"),
     ("mixtral-like decode B=64 cache=2048", "permute"): (3.2, 1.2, "moe.hip", "9df6017876fa8ad8"),
@@ -435,16 +435,16 @@ PMC_TRAFFIC_KIB = {
     ("mixtral-like decode B=64 cache=2048", "expert_down"): (139303.0, 2048.0, "gemm.hip", "61d3a5bc75f21aff"),
     ("mixtral-like decode B=64 cache=2048", "combine"): (1561.5, 512.0, "moe.hip", "9df6017876fa8ad8"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm1"): (268.8, 896.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28564.0, 18304.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28564.0, 18304.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "attention"): (72458.7, 8512.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24502.9, 17792.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24502.9, 17792.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm2"): (492.8, 1792.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "router"): (1973.5, 24.2, "moe.hip", "9df6017876fa8ad8"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "permute"): (3.9, 5.1, "moe.hip", "9df6017876fa8ad8"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "expert_gate_up"): (1150530.4, 5120.0, "gemm.hip", "61d3a5bc75f21aff"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "expert_down"): (594008.6, 7168.0, "gemm.hip", "61d3a5bc75f21aff"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158066.7, 29696.0, "gemm2.hip", "916da4e01f53f4ec"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98812.5, 18048.0, "gemm2.hip", "916da4e01f53f4ec"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158066.7, 29696.0, "gemm2.hip", "2262baeccb5a8fc2"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98812.5, 18048.0, "gemm2.hip", "2262baeccb5a8fc2"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "combine"): (4067.5, 448.0, "moe.hip", "9df6017876fa8ad8"),
 }
 

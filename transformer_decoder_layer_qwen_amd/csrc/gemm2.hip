@@ -1,39 +1,41 @@
-// Large-tile bf16 GEMM on MFMA for the prefill projections, C = A * B^T.
+// Large-tile bf16 GEMMs on MFMA for the projections, C = A * B^T.
 //
 // A is [M, Ka] (token rows), B is [N, Kb] (a weight in the [out, in] storage
 // convention of "Qwen2.5-7B 结构拆解" §03.1); both K-contiguous. Token rows never
 // interact in a projection (§03.2 of the same page), so M = B*S rows form one
-// GEMM. Ka is Kb, or 2 Kb when A carries an fp32 activation as a bf16 pair
-// [hi | lo] (hi = RNE(a), lo = RNE(a - hi)): then the k loop runs over 2 Kb and
-// reads B at k mod Kb, which sums hi*W + lo*W with the activation kept to about
-// 16 significant bits. Used for the projections of the RMSNorm1 output and of
-// the attention output.
+// GEMM. A plain bf16 A has Ka = Kb; an fp32 activation arrives as a bf16 pair
+// [hi | lo] (hi = RNE(a), lo = RNE(a - hi), row pitch 2 Kb), and the tile sums
+// hi*W + lo*W, keeping the activation to about 16 significant bits.
 //
-// Design (gfx950, wave64):
-// * tile 256 x 256 x 64; 4 or 8 waves, each owning 128 x 128 (or 128 x 64) of
-//   the tile as 32x32x16 MFMAs with fp32 accumulators.
+// Design (gfx950, wave64), prefill tiles (gemm2_kernel, three kinds, see there):
+// * 8 waves on a 256-column weight tile, 32x32x16 MFMAs with fp32 accumulators;
+//   256 token rows (plain A, or a pair whose 32-deep stages hold the hi, lo and
+//   weight rows together) or 128 token rows of a pair.
 // * global -> LDS directly (global_load_lds_dwordx4: 16 B per lane, lane i
 //   writes 16 i bytes past a wave-uniform LDS base); each load instruction
-//   moves 8 whole 128-byte rows (full cache lines). Two stages: stage t+1 is
-//   requested while stage t is multiplied.
-// * LDS rows are 32 bf16 (4 chunks of 16 B), chunks XOR-swizzled by row (swz)
-//   so fragment reads are free of bank conflicts. A direct load cannot
-//   scatter, so each lane picks the global chunk that belongs at its fixed
-//   LDS slot.
-// * split-K over blockIdx.y when the tile grid alone is too small for the
+//   moves whole 128-byte (or 64-byte) row pieces. A ring of two or three
+//   stages: the next stages are requested while one is multiplied.
+// * LDS chunks XOR-swizzled by row so fragment reads are free of bank
+//   conflicts. A direct load cannot scatter, so each lane picks the global
+//   chunk that belongs at its fixed LDS slot.
+// * split-K over work items when the tile grid alone is too small for the
 //   chip: each split writes an fp32 partial tile and a second kernel sums the
-//   partials and applies the epilogue.
+//   partials and applies the epilogue; a host plan picks the tile kind, the
+//   split count and an optional split-K tail launch.
 // * epilogue through LDS, half a tile at a time (the ring is reused): every
 //   thread then handles 8 consecutive columns of one row, so stores are
 //   16/32-byte contiguous and SwiGLU can pair a gate column with its up column.
+// Decode tiles (gemm2_dec_kernel): 4 waves, an A tile of the batch's rows, a
+// 3-4 slot ring of weight stages, work cut stream-K over 256 blocks with fp32
+// partials summed by the reduce kernel.
 //
 // Epilogues (one rounding at the stored tensor):
 //   BIAS      Q/K/V projection: + bias, QK-norm, RoPE; q -> q_out, k/v -> cache
 //   RESID_F32 out_f32 = resid_bf16 + acc        R = X + O W_O^T
 //   RESID_OUT out     = bf16(resid_f32 + acc)   Y = R + H W_down^T
-//   SWIGLU    out     = bf16(SiLU(g) * u)       B tile = [128 W_gate rows | 128 W_up rows]
+//   SWIGLU    h = SiLU(g) * u (bf16, or a [hi | lo] pair)  B tile = [128 W_gate rows | 128 W_up rows]
 //   MOE_GU    SWIGLU on gathered token rows with one expert's weights per tile
-//   MOE_DOWN  out     = bf16(acc) for one expert's slot rows
+//   MOE_DOWN  out     = fp32 (or bf16) acc for one expert's slot rows
 //   GATED_F32 out_f32 = resid + sigmoid(gate_logit[row]) * acc  (a shared
 //             expert scaled by its per-token gate; resid fp32, bf16 or none)
 // With split-K each split stores its fp32 partial tile and the reduce kernel
