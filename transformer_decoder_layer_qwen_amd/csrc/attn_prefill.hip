@@ -43,6 +43,10 @@ constexpr int kStage = kKElems + kVElems;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
 constexpr int kCUs = 256;
 
+typedef float f32v2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+constexpr bf16v2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 // Two 4-wave blocks per CU (one 68 KiB ring each), or one KSPLIT block with
 // two rings: the register budget of two waves per SIMD keeps every
 // accumulator in VGPRs, and one wave's MFMAs run while the other works
@@ -187,6 +191,12 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
     gload(kt_lo);
     lstore(0);
   }
+  // Drain the Q-fragment loads on every path into the key loop. Left to
+  // itself the compiler cannot tell, inside the loop, that they have landed,
+  // and waits on the vector-memory counter before the first score MFMAs,
+  // which then also waits for the next tile's prefetch issued just above
+  // them: the tile load's latency is exposed in every iteration.
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0) only
   __syncthreads();
 
   for (int it = 0; it < niter; ++it) {
@@ -256,18 +266,27 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
       // the tile, in the second key group of a split tile, and in the
       // rescale above.
       const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-      float lsum = 0.f;
-      bf16x8 pf[4];
+      // Weights are rounded to bf16 two at a time (one packed convert), and
+      // the row sum is taken from those rounded pairs by a two-term dot
+      // product with (1, 1), so it sums exactly the weights P*V is formed
+      // with, at one instruction per pair.
+      float lsum0 = 0.f, lsum1 = 0.f;
+      u32x4 pfw[4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // the sum takes the rounded weights P*V is formed with
-          const bf16 pb = (bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][r], p.scale_log2, -m_ref));
-          lsum += (float)pb;
-          pf[2 * t + (r >> 3)][r & 7] = pb;
+        for (int r = 0; r < 16; r += 2) {
+          const f32v2 e = {__builtin_amdgcn_exp2f(fmaf(sc[t][r], p.scale_log2, -m_ref)),
+                           __builtin_amdgcn_exp2f(fmaf(sc[t][r + 1], p.scale_log2, -m_ref))};
+          const bf16v2 pb = __builtin_convertvector(e, bf16v2);
+          if (r & 2) lsum1 = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, lsum1, false);
+          else lsum0 = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes2, lsum0, false);
+          pfw[2 * t + (r >> 3)][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pb);
         }
-      l_run += lsum;
+      l_run += lsum0 + lsum1;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pf[u] = __builtin_bit_cast(bf16x8, pfw[u]);
       // O^T[d][q] += sum_key V^T[d][key] P^T[key][q]; k-step u covers keys
       // 32(u/2) + 16(u%2) + {4hi..4hi+3, 8+4hi..8+4hi+3} in slot order.
 #pragma unroll
