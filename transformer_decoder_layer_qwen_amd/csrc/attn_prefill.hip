@@ -126,40 +126,36 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const int vk = (tid & 15) * 4;
   const int vc = tid >> 4;
   u32x4 rk[4], rv[4];
-  auto gload = [&](int kt) {
+  // piece idx of tile kt's prefetch (0-3: K, 4-7: V). Rows at or past the
+  // sequence's end read its last row (an in-bounds address, so the load
+  // needs no branch) and are zeroed at the LDS store: they may hold
+  // anything, and a NaN would survive a zero softmax weight in P V.
+  auto gload1 = [&](int kt, int idx) {
     const int k0 = kt * kBK;
-    if (k0 + kBK <= L) {  // whole tile inside the sequence: no per-lane checks
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ch = tid + 256 * i;
-        rk[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(k0 + (ch >> 4)) * kv_row_stride +
-                                                 (ch & 15) * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        rv[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(k0 + vk + j) * kv_row_stride +
-                                                 vc * 8);
-      return;
-    }
-    // ragged last tile: rows past the sequence are zero (they may hold
-    // anything, and a NaN would survive a zero softmax weight in P V)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i;
-      const int key = k0 + (ch >> 4);
-      rk[i] = key < L ? *reinterpret_cast<const u32x4*>(kbase + (size_t)key * kv_row_stride +
-                                                         (ch & 15) * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + vk + j;
-      rv[j] = key < L ? *reinterpret_cast<const u32x4*>(vbase + (size_t)key * kv_row_stride +
-                                                         vc * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
+    if (idx < 4) {
+      const int ch = tid + 256 * idx;
+      rk[idx] = *reinterpret_cast<const u32x4*>(
+          kbase + (size_t)min(k0 + (ch >> 4), L - 1) * kv_row_stride + (ch & 15) * 8);
+    } else {
+      const int j = idx - 4;
+      rv[j] = *reinterpret_cast<const u32x4*>(
+          vbase + (size_t)min(k0 + vk + j, L - 1) * kv_row_stride + vc * 8);
     }
   };
-  auto lstore = [&](int st) {
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) gload1(kt, idx);
+  };
+  auto lstore = [&](int st, int kt) {
+    const int k0 = kt * kBK;
+    if (k0 + kBK > L) {  // ragged last tile (block-uniform)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + ((tid + 256 * i) >> 4) >= L) rk[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (k0 + vk + j >= L) rv[j] = u32x4{0u, 0u, 0u, 0u};
+    }
     bf16* Ks = ring + st * kStage;
     bf16* Vt = Ks + kKElems;
 #pragma unroll
@@ -189,7 +185,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
 
   if (kt_lo < kt_hi) {
     gload(kt_lo);
-    lstore(0);
+    lstore(0, kt_lo);
   }
   // Drain the Q-fragment loads on every path into the key loop. Left to
   // itself the compiler cannot tell, inside the loop, that they have landed,
@@ -203,7 +199,9 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
     const int kt = kt_lo + it;
     const int st = it & 1;
     const bool more = kt + 1 < kt_hi;
-    if (more) gload(kt + 1);
+    // the next tile's prefetch (the last step re-reads its own tile, unused,
+    // so the loads need no branch and can sit among the score MFMAs)
+    const int ktn = more ? kt + 1 : kt;
     const int k0 = kt * kBK;
     // skip tiles past the group's range (its last step when it has one tile
     // fewer) and tiles whose every key is in this wave's future (wave-uniform)
@@ -220,7 +218,18 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
         for (int s = 0; s < 8; ++s) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
           sc[t] = mfma_32x32x16(kf, qf[s], sc[t]);
+          if (s & 1) gload1(ktn, 4 * t + (s >> 1));
         }
+      }
+      // issue order: per pair of score MFMAs, their two K-fragment reads,
+      // the MFMAs and one 16-byte global load of the next tile, so the
+      // loads' issue overlaps the matrix work instead of stalling the wave
+      // ahead of it
+#pragma unroll
+      for (int g8 = 0; g8 < 8; ++g8) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
       }
       // mask, tile max (raw scores; the scale is positive and applied in the
       // exponent). Register r of half t holds key 32t + 8(r/4) + 4hi + r%4.
@@ -301,8 +310,10 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
           acc_o[dt] = mfma_32x32x16(vf, pf[u], acc_o[dt]);
         }
       }
+    } else {
+      gload(ktn);
     }
-    if (more) lstore(st ^ 1);
+    if (more) lstore(st ^ 1, kt + 1);
     __syncthreads();
   }
 
