@@ -332,7 +332,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
     mst[65 * 64] = l_run;
   }
   if (KSPLIT) __syncthreads();
-  if (grp == 1 || my_q >= S) continue;  // (the next pass starts with a barrier)
+  if (grp == 1) continue;  // (the next pass starts with a barrier)
   if (KSPLIT) {
     const float m1 = mst[64 * 64], l1 = mst[65 * 64];
     const float m = fmaxf(m_run, m1);  // finite: every query sees key 0
@@ -346,9 +346,16 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   const float inv = 1.0f / l_tot;
-  // the fp32 output as a bf16 pair: hi = RNE(o) at column c, lo = RNE(o - hi)
-  // at column c + lo_off (the O projection multiplies both)
-  bf16* orow = p.out + (size_t)(qbase + my_q) * p.ldo + h * kDh;
+  // The fp32 output as a bf16 pair: hi = RNE(o) at column c, lo = RNE(o - hi)
+  // at column c + lo_off (the O projection multiplies both). A lane holds 16
+  // pieces of 4 values of one query row, so the rows are staged through LDS
+  // as [query][dh] (in the ring of group 1, or of the only group: every tile
+  // read ended before the loop's last barrier) and stored as whole 256-byte
+  // rows, 16 lanes to a row, rather than as 8-byte pieces of 32 rows. Rows
+  // past the sequence (a ragged last tile) are computed and not stored.
+  constexpr int kOP = kDh + 8;  // staging pitch, bf16 elements
+  static_assert(4 * 2 * 32 * kOP <= 2 * kStage, "output staging fits one ring");
+  bf16* so = lds + (KSPLIT ? 2 * kStage : 0) + wave * (2 * 32 * kOP);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -360,9 +367,29 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
         vh[e] = (bf16)v;
         vl[e] = (bf16)(v - (float)vh[e]);
       }
-      *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * c + 4 * hi) = vh;
-      *reinterpret_cast<bf16x4*>(orow + p.lo_off + 32 * dt + 8 * c + 4 * hi) = vl;
+      *reinterpret_cast<bf16x4*>(so + col * kOP + 32 * dt + 8 * c + 4 * hi) = vh;
+      *reinterpret_cast<bf16x4*>(so + (32 + col) * kOP + 32 * dt + 8 * c + 4 * hi) = vl;
     }
+  // (the wave's own LDS writes and reads run in order; the fences keep the
+  // compiler from moving the reads above the writes)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  bf16x8 h8[8], l8[8];  // query rows 4 i + lane / 16, columns 8 (lane % 16) ..
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    h8[i] = *reinterpret_cast<const bf16x8*>(so + r * kOP + 8 * (lane & 15));
+    l8[i] = *reinterpret_cast<const bf16x8*>(so + (32 + r) * kOP + 8 * (lane & 15));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int qr = q0 + wave * 32 + 4 * i + (lane >> 4);
+    if (qr < S) {
+      bf16* o = p.out + (size_t)(qbase + qr) * p.ldo + h * kDh + 8 * (lane & 15);
+      *reinterpret_cast<bf16x8*>(o) = h8[i];
+      *reinterpret_cast<bf16x8*>(o + p.lo_off) = l8[i];
+    }
+  }
   }  // pass
 }
 
