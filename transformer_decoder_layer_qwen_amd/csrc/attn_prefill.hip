@@ -17,16 +17,20 @@
 // two partial softmax states are merged through LDS at the end. That halves
 // the longest tiles' time when the causal work would otherwise leave most
 // CUs idle behind them (grids of at most one block per CU).
-// Key tiles of 64 rows stream through LDS, double-buffered per group.
-// Scores are formed transposed, S^T = K Q^T, with 32x32x16 MFMAs: the query
-// is the MFMA column, so a lane owns one query and its running max / sum
-// need only one cross-lane exchange per tile. P^T stays in registers and is
-// the B operand of O^T += V^T P^T; V is stored transposed in LDS (pitch 68
-// elements, which spreads the rows read together over distinct banks; the
-// 16 lanes of a store cover 64 keys of one row). K rows are padded to 136
-// elements, so the 16 lanes of a fragment read fall on distinct banks and a
-// lane's fragments sit at fixed offsets from one base. The fp32 output is
-// stored as a bf16 pair hi + lo, the form in which the O projection reads it.
+// Key tiles of 64 rows stream through LDS, double-buffered per group, by
+// direct global-to-LDS loads (no registers hold them on the way): K and V
+// rows of 256 bytes as they sit in the cache, each 16-byte chunk c of row r
+// at chunk position c ^ f(r) of the row, f(r) = r mod 16 for K and
+// 4 (r mod 4) for V, which puts the lanes of every fragment read on
+// distinct banks. Scores are formed transposed, S^T = K Q^T, with 32x32x16
+// MFMAs: the query is the MFMA column, so a lane owns one query and its
+// running max / sum need only one cross-lane exchange per tile. P^T stays
+// in registers and is the B operand of O^T += V^T P^T; the V^T fragments
+// come from the row-major V tile by gfx950's transposing LDS read
+// (ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+// i mod 4 of the 4-element pieces addressed by lanes 4 e + i / 4, e = 0..3),
+// so no transpose is stored. The fp32 output is stored as a bf16 pair
+// hi + lo, the form in which the O projection reads it.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,19 +39,31 @@ namespace {
 constexpr int kDh = 128;
 constexpr int kBQ = 128;      // queries per block
 constexpr int kBK = 64;       // keys per tile
-constexpr int kVtPitch = 68;  // bf16 elements per transposed-V row
-constexpr int kKPitch = kDh + 8;  // bf16 elements per K row
-constexpr int kKElems = kBK * kKPitch;
-constexpr int kVElems = kDh * kVtPitch;
-constexpr int kStage = kKElems + kVElems;
+constexpr int kTileBytes = kBK * kDh * 2;  // one K or V tile, 256-byte rows
+constexpr int kStageBytes = 2 * kTileBytes;  // K then V
+constexpr int kRingBytes = 2 * kStageBytes;  // two stages per wave group
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
 constexpr int kCUs = 256;
 
 typedef float f32v2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 constexpr bf16v2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+typedef s16x4 __attribute__((address_space(3)))* lptr4_t;
 
-// Two 4-wave blocks per CU (one 68 KiB ring each), or one KSPLIT block with
+QL_DEV int kswz(int r) { return r & 15; }        // K chunk position = c ^ kswz(row)
+QL_DEV int vswz(int r) { return 4 * (r & 3); }   // V chunk position = c ^ vswz(row)
+
+// 16 bytes from global memory straight into LDS: lane i of the wave writes
+// lds_wave_base + 16 i (the base is wave-uniform)
+QL_DEV void load_lds16(const bf16* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)lds_wave_base, 16, 0, 0);
+}
+
+// Two 4-wave blocks per CU (one 64 KiB ring each), or one KSPLIT block with
 // two rings: the register budget of two waves per SIMD keeps every
 // accumulator in VGPRs, and one wave's MFMAs run while the other works
 // through its softmax.
@@ -55,7 +71,12 @@ template <bool KSPLIT>
 __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefill_kernel(
     const AttnPrefillArgs p) {
   constexpr int NG = KSPLIT ? 2 : 1;  // wave groups
-  __shared__ __attribute__((aligned(16))) bf16 lds[NG * 2 * kStage];  // [group][stage]
+  // [group][stage][K | V], then (KSPLIT) group 1's running max and sum for
+  // the merge, per wave and lane. One LDS object: with a second one the
+  // compiler no longer tells the tile reads from the in-flight direct loads
+  // and waits for those loads before every fragment read.
+  constexpr int kMlBytes = KSPLIT ? 4 * 2 * 64 * 4 : 0;
+  __shared__ __attribute__((aligned(1024))) char lds[NG * kRingBytes + kMlBytes];
   const int lane = threadIdx.x & 63;
   const int grp = KSPLIT ? (int)(threadIdx.x >> 8) : 0;  // key half
   const int tid = threadIdx.x & 255;                     // thread within the group
@@ -118,61 +139,38 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const int kt_lo = !KSPLIT ? 0 : grp == 0 ? 0 : ntiles / 2;
   const int kt_hi = !KSPLIT ? ntiles : grp == 0 ? ntiles / 2 : ntiles;
   const int niter = !KSPLIT ? ntiles : ntiles - ntiles / 2;
-  bf16* ring = lds + grp * 2 * kStage;
+  char* ring = lds + grp * kRingBytes;
 
-  // tile-load assignment
-  //   K: chunk = tid + 256*i, key = chunk >> 4, 16-byte piece c = chunk & 15
-  //   V: keys 4*(tid & 15) .. +3, 8-wide dh piece c = tid >> 4
-  const int vk = (tid & 15) * 4;
-  const int vc = tid >> 4;
-  u32x4 rk[4], rv[4];
-  // piece idx of tile kt's prefetch (0-3: K, 4-7: V). Rows at or past the
-  // sequence's end read its last row (an in-bounds address, so the load
-  // needs no branch) and are zeroed at the LDS store: they may hold
-  // anything, and a NaN would survive a zero softmax weight in P V.
-  auto gload1 = [&](int kt, int idx) {
-    const int k0 = kt * kBK;
-    if (idx < 4) {
-      const int ch = tid + 256 * idx;
-      rk[idx] = *reinterpret_cast<const u32x4*>(
-          kbase + (size_t)min(k0 + (ch >> 4), L - 1) * kv_row_stride + (ch & 15) * 8);
-    } else {
-      const int j = idx - 4;
-      rv[j] = *reinterpret_cast<const u32x4*>(
-          vbase + (size_t)min(k0 + vk + j, L - 1) * kv_row_stride + vc * 8);
-    }
+  // Load j (0..3) of wave w fills LDS chunks 64 (4 j + w) + lane of the K
+  // (then the V) tile: row 4 (4 j + w) + lane / 16, chunk position lane % 16,
+  // which holds chunk (lane % 16) ^ f(row) of that key row. Rows at or past
+  // the sequence's end read its last row instead (an in-bounds address; K
+  // rows there are masked in the scores, V rows meet a zero weight).
+  const int lrow = 4 * wave + (lane >> 4);  // + 16 j
+  const int lpos = lane & 15;
+  auto gload1 = [&](int kt, int st, int idx) {  // idx 0-3: K, 4-7: V
+    const int j = idx & 3;
+    const int row = lrow + 16 * j;
+    const int key = min(kt * kBK + row, L - 1);
+    char* dst = ring + st * kStageBytes + (idx >= 4 ? kTileBytes : 0) + (4 * j + wave) * 1024;
+    if (idx < 4)
+      load_lds16(kbase + (size_t)key * kv_row_stride + 8 * (lpos ^ kswz(row)), dst);
+    else
+      load_lds16(vbase + (size_t)key * kv_row_stride + 8 * (lpos ^ vswz(row)), dst);
   };
-  auto gload = [&](int kt) {
+  auto gload = [&](int kt, int st) {
 #pragma unroll
-    for (int idx = 0; idx < 8; ++idx) gload1(kt, idx);
+    for (int idx = 0; idx < 8; ++idx) gload1(kt, st, idx);
   };
-  auto lstore = [&](int st, int kt) {
-    const int k0 = kt * kBK;
-    if (k0 + kBK > L) {  // ragged last tile (block-uniform)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (k0 + ((tid + 256 * i) >> 4) >= L) rk[i] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (k0 + vk + j >= L) rv[j] = u32x4{0u, 0u, 0u, 0u};
-    }
-    bf16* Ks = ring + st * kStage;
-    bf16* Vt = Ks + kKElems;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i;
-      const int key = ch >> 4, c = ch & 15;
-      *reinterpret_cast<u32x4*>(Ks + key * kKPitch + c * 8) = rk[i];
-    }
-    const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(&rv[0]);
-    const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(&rv[1]);
-    const bf16x8 v2 = *reinterpret_cast<const bf16x8*>(&rv[2]);
-    const bf16x8 v3 = *reinterpret_cast<const bf16x8*>(&rv[3]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bf16x4 t = {v0[e], v1[e], v2[e], v3[e]};
-      *reinterpret_cast<bf16x4*>(Vt + (vc * 8 + e) * kVtPitch + vk) = t;
-    }
+  // V^T fragment addresses (see the transposing read above): for keys
+  // kb + 4 (lane / 32) + 0..3 (and + 8) of dh rows 32 dt + lane % 32, lane
+  // s supplies key row kb + 4 (s / 32) + (s % 16) / 4, dh column
+  // 32 dt + 16 ((s / 16) % 2) + 4 (s % 4)
+  const int vtr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);  // + kb
+  const int vtr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 dt
+  auto vtr_addr = [&](const char* Vs, int row, int dcol) {
+    const int c = dcol >> 3;
+    return Vs + row * 256 + ((c ^ vswz(row)) << 4) + ((dcol & 7) << 1);
   };
 
   f32x16 acc_o[4];
@@ -183,15 +181,11 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  if (kt_lo < kt_hi) {
-    gload(kt_lo);
-    lstore(0, kt_lo);
-  }
-  // Drain the Q-fragment loads on every path into the key loop. Left to
-  // itself the compiler cannot tell, inside the loop, that they have landed,
-  // and waits on the vector-memory counter before the first score MFMAs,
-  // which then also waits for the next tile's prefetch issued just above
-  // them: the tile load's latency is exposed in every iteration.
+  if (kt_lo < kt_hi) gload(kt_lo, 0);
+  // This wave's tile loads and Q fragments have landed (and, after the
+  // barrier, every wave's). Draining on every path into the key loop also
+  // keeps the compiler from waiting on the vector-memory counter before the
+  // first score MFMAs, which would wait for the next tile's loads too.
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0) only
   __syncthreads();
 
@@ -206,19 +200,21 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
     // skip tiles past the group's range (its last step when it has one tile
     // fewer) and tiles whose every key is in this wave's future (wave-uniform)
     if (__builtin_amdgcn_readfirstlane(kt < kt_hi && k0 <= wave_qmax)) {
-      const bf16* Ks = ring + st * kStage;
-      const bf16* Vt = Ks + kKElems;
+      const char* Ks = ring + st * kStageBytes;
+      const char* Vs = Ks + kTileBytes;
       f32x16 sc[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
-        const bf16* kr = Ks + (32 * t + col) * kKPitch + 8 * hi;
+        const int krow = 32 * t + col;
+        const char* kr = Ks + krow * 256;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(kr + (((2 * s + hi) ^ kswz(krow)) << 4));
           sc[t] = mfma_32x32x16(kf, qf[s], sc[t]);
-          if (s & 1) gload1(ktn, 4 * t + (s >> 1));
+          if (s & 1) gload1(ktn, st ^ 1, 4 * t + (s >> 1));
         }
       }
       // issue order: per pair of score MFMAs, their two K-fragment reads,
@@ -300,20 +296,24 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
       // 32(u/2) + 16(u%2) + {4hi..4hi+3, 8+4hi..8+4hi+3} in slot order.
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int kb = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
+        const int kb = 32 * (u >> 1) + 16 * (u & 1);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16* vr = Vt + (32 * dt + col) * kVtPitch + kb;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-          const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vr + 8);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lptr4_t)vtr_addr(Vs, kb + vtr_row, 32 * dt + vtr_col));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lptr4_t)vtr_addr(Vs, kb + 8 + vtr_row, 32 * dt + vtr_col));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, (s16x8){lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]});
           acc_o[dt] = mfma_32x32x16(vf, pf[u], acc_o[dt]);
         }
       }
     } else {
-      gload(ktn);
+      gload(ktn, st ^ 1);
     }
-    if (more) lstore(st ^ 1, kt + 1);
+    // this wave's loads of the next tile have landed; after the barrier every
+    // wave's have, and every wave is done with this tile's slot
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0) only
     __syncthreads();
   }
 
@@ -321,20 +321,21 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   // free: every tile read ended before the loop's last barrier). A lane's
   // state is relative to its own reference maximum m_run; a group that saw
   // no key of this query has m_run = -inf and contributes nothing.
-  static_assert(4 * 66 * 64 * 4 <= 2 * kStage * 2, "merge state fits group 0's ring");
-  float* mst = reinterpret_cast<float*>(lds) + wave * (66 * 64) + lane;
+  static_assert(4 * 64 * 64 * 4 <= kRingBytes, "merge state fits group 0's ring");
+  float* mst = reinterpret_cast<float*>(lds) + wave * (64 * 64) + lane;
+  float* mls = reinterpret_cast<float*>(lds + NG * kRingBytes) + wave * 128 + lane;
   if (KSPLIT && grp == 1) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mst[(16 * dt + r) * 64] = acc_o[dt][r];
-    mst[64 * 64] = m_run;
-    mst[65 * 64] = l_run;
+    mls[0] = m_run;
+    mls[64] = l_run;
   }
   if (KSPLIT) __syncthreads();
   if (grp == 1) continue;  // (the next pass starts with a barrier)
   if (KSPLIT) {
-    const float m1 = mst[64 * 64], l1 = mst[65 * 64];
+    const float m1 = mls[0], l1 = mls[64];
     const float m = fmaxf(m_run, m1);  // finite: every query sees key 0
     const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
@@ -353,9 +354,10 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   // read ended before the loop's last barrier) and stored as whole 256-byte
   // rows, 16 lanes to a row, rather than as 8-byte pieces of 32 rows. Rows
   // past the sequence (a ragged last tile) are computed and not stored.
-  constexpr int kOP = kDh + 8;  // staging pitch, bf16 elements
-  static_assert(4 * 2 * 32 * kOP <= 2 * kStage, "output staging fits one ring");
-  bf16* so = lds + (KSPLIT ? 2 * kStage : 0) + wave * (2 * 32 * kOP);
+  // staging: 64 rows (hi, then lo) of 256 bytes per wave, chunk c of row r
+  // at position c ^ (r mod 16)
+  static_assert(4 * 64 * 256 <= kRingBytes, "output staging fits one ring");
+  char* so = lds + (KSPLIT ? kRingBytes : 0) + wave * (64 * 256);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -367,8 +369,9 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
         vh[e] = (bf16)v;
         vl[e] = (bf16)(v - (float)vh[e]);
       }
-      *reinterpret_cast<bf16x4*>(so + col * kOP + 32 * dt + 8 * c + 4 * hi) = vh;
-      *reinterpret_cast<bf16x4*>(so + (32 + col) * kOP + 32 * dt + 8 * c + 4 * hi) = vl;
+      const int pos = ((4 * dt + c) ^ kswz(col)) << 4;
+      *reinterpret_cast<bf16x4*>(so + col * 256 + pos + 8 * hi) = vh;
+      *reinterpret_cast<bf16x4*>(so + (32 + col) * 256 + pos + 8 * hi) = vl;
     }
   // (the wave's own LDS writes and reads run in order; the fences keep the
   // compiler from moving the reads above the writes)
@@ -378,8 +381,9 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 4 * i + (lane >> 4);
-    h8[i] = *reinterpret_cast<const bf16x8*>(so + r * kOP + 8 * (lane & 15));
-    l8[i] = *reinterpret_cast<const bf16x8*>(so + (32 + r) * kOP + 8 * (lane & 15));
+    const int pos = ((lane & 15) ^ kswz(r)) << 4;
+    h8[i] = *reinterpret_cast<const bf16x8*>(so + r * 256 + pos);
+    l8[i] = *reinterpret_cast<const bf16x8*>(so + (32 + r) * 256 + pos);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
