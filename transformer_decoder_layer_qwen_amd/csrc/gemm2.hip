@@ -109,6 +109,13 @@ struct G2Args {
   size_t b_expert_stride;
 };
 
+// The value of the lane 8 places away within its row of 16 lanes (lane
+// i ^ 8): a DPP row rotate by 8, no LDS round trip. Both lanes of a pair
+// are active together wherever it is used.
+QL_DEV float xor8_lane(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
 // QKV epilogue for 8 columns [col, col + 8) of token row `row`, bias added.
 // The 16 lanes of an aligned lane group hold one head (128 columns), so the
 // per-head sum of squares of QK-norm is a 16-lane reduction and the RoPE
@@ -161,18 +168,38 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = g[e] * (v[e] * inv);
     }
+    // rotate_half partner of column d0 + e: column d0 + e +- 64, held by the
+    // lane 8 places away in the head's 16-lane group
     float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = __shfl_xor(v[e], 8, kWave);
+    for (int e = 0; e < 8; ++e) o[e] = xor8_lane(v[e]);
+    // Columns d0 + e and d0 + e + 64 turn by the same angle pos * omega_i,
+    // i = (d0 + e) mod 64, so the two partner lanes each take four of the
+    // eight angles and swap the results. An angle is taken in turns, reduced
+    // to [-1/2, 1/2] in fp64 (pos may be large), and the hardware sine and
+    // cosine of that fraction of a turn are used: their error, ~1e-6, is far
+    // below the bf16 rounding of q and k (a full-precision sincosf per
+    // element dominated the epilogue of a 256-row tile).
     const double pos = (double)t + (double)p.pos_offset;
-    const double two_pi = 6.283185307179586476925286766559;
+    constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+    const bool upper = d0 >= 64;
+    float sn_own[4], cs_own[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      double ang = pos * p.omega[(d0 + e) & 63];
-      ang -= two_pi * rint(ang * (1.0 / two_pi));
-      float sn, cs;
-      sincosf((float)ang, &sn, &cs);
-      v[e] = d0 < 64 ? v[e] * cs - o[e] * sn : v[e] * cs + o[e] * sn;
+    for (int i = 0; i < 4; ++i) {
+      const int e = upper ? i + 4 : i;
+      double turns = pos * (p.omega[(d0 + e) & 63] * kInvTwoPi);
+      turns -= rint(turns);
+      const float r = (float)turns;
+      sn_own[i] = __builtin_amdgcn_sinf(r);
+      cs_own[i] = __builtin_amdgcn_cosf(r);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sn_p = xor8_lane(sn_own[i]), cs_p = xor8_lane(cs_own[i]);
+      const float sn_a = upper ? sn_p : sn_own[i], cs_a = upper ? cs_p : cs_own[i];  // e = i
+      const float sn_b = upper ? sn_own[i] : sn_p, cs_b = upper ? cs_own[i] : cs_p;  // e = i + 4
+      v[i] = upper ? v[i] * cs_a + o[i] * sn_a : v[i] * cs_a - o[i] * sn_a;
+      v[i + 4] = upper ? v[i + 4] * cs_b + o[i + 4] * sn_b : v[i + 4] * cs_b - o[i + 4] * sn_b;
     }
   }
   if (part == 0) {
