@@ -766,7 +766,10 @@ def test_small_moe_prefill_varlen():
 @pytest.mark.parametrize("cid,lens,prefix,T_max", [
     (4, [512], [2048], 2560),                                  # a chunk over a 2048-row prefix
     (3, [700, 300, 1024, 24], [0, 512, 100, 2000], 2048),      # a varlen batch, 2048 new rows
-], ids=["qwen3-8b_chunk512_over_2048", "qwen2.5-7b_varlen4"])
+    # enough query-tile pairs for the attention blocks whose two wave groups
+    # are two query heads sharing each K/V tile; ragged tiles and prefixes
+    (4, [1500, 37, 900, 1024], [0, 300, 1111, 64], 2048),
+], ids=["qwen3-8b_chunk512_over_2048", "qwen2.5-7b_varlen4", "qwen3-8b_varlen4_head_pairs"])
 def test_full_size_prefill_varlen(cid, lens, prefix, T_max):
     cfg = configs.CONFIGS[cid]
     layer, w64 = make_layer(cfg, seed=configs.weight_seed(cid), max_tokens=sum(lens), max_batch=1)

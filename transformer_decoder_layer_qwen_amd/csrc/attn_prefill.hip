@@ -42,6 +42,10 @@ constexpr int kBK = 64;       // keys per tile
 constexpr int kTileBytes = kBK * kDh * 2;  // one K or V tile, 256-byte rows
 constexpr int kStageBytes = 2 * kTileBytes;  // K then V
 constexpr int kRingBytes = 2 * kStageBytes;  // two stages per wave group
+// Block kinds: 4 waves on one head; 8 waves whose two groups split one
+// head's key tiles (KSPLIT); 8 waves whose two groups are two query heads of
+// one KV group sharing every K/V tile (HEADS2).
+enum : int { kPlain = 0, kKsplit = 1, kHeads2 = 2 };
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
 constexpr int kCUs = 256;
 
@@ -63,24 +67,39 @@ QL_DEV void load_lds16(const bf16* g, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)lds_wave_base, 16, 0, 0);
 }
 
-// Two 4-wave blocks per CU (one 64 KiB ring each), or one KSPLIT block with
-// two rings: the register budget of two waves per SIMD keeps every
-// accumulator in VGPRs, and one wave's MFMAs run while the other works
-// through its softmax.
-template <bool KSPLIT>
-__global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefill_kernel(
+// Two 4-wave blocks per CU (one 64 KiB ring each), or one 8-wave block
+// (KSPLIT: two rings; HEADS2: one shared ring of four stages): the register
+// budget of two waves per SIMD keeps every accumulator in VGPRs, and one
+// wave's MFMAs run while the other works through its softmax. HEADS2 halves
+// the K/V bytes each CU moves per unit of work (the direct loads cost about
+// a quarter of the kernel's time when two 4-wave blocks each fetch their own
+// copy) and keeps three tiles in flight instead of one.
+template <int VAR>
+__global__ __launch_bounds__(VAR != kPlain ? 512 : 256, VAR != kPlain ? 1 : 2) void attn_prefill_kernel(
     const AttnPrefillArgs p) {
-  constexpr int NG = KSPLIT ? 2 : 1;  // wave groups
-  // [group][stage][K | V], then (KSPLIT) group 1's running max and sum for
-  // the merge, per wave and lane. One LDS object: with a second one the
-  // compiler no longer tells the tile reads from the in-flight direct loads
-  // and waits for those loads before every fragment read.
+  constexpr bool KSPLIT = VAR == kKsplit;
+  constexpr bool HEADS2 = VAR == kHeads2;
+  constexpr int NG = KSPLIT ? 2 : 1;      // rings
+  constexpr int NS = HEADS2 ? 4 : 2;      // stages per ring
+  constexpr int kRing = NS * kStageBytes;
+  constexpr int LW = HEADS2 ? 8 : 4;      // waves sharing a ring's loads
+  constexpr int NLW = 16 / LW;            // 1 KiB loads per wave per K (or V) tile
+  constexpr int kMpl = 16 / (2 * NLW);    // score MFMAs per interleaved load
+  // [ring][stage][K | V], then (KSPLIT) group 1's running max and sum for
+  // the merge, per wave and lane; the output staging (64 rows of 256 bytes
+  // per storing wave) reuses the space. One LDS object: with a second one
+  // the compiler no longer tells the tile reads from the in-flight direct
+  // loads and waits for those loads before every fragment read.
   constexpr int kMlBytes = KSPLIT ? 4 * 2 * 64 * 4 : 0;
-  __shared__ __attribute__((aligned(1024))) char lds[NG * kRingBytes + kMlBytes];
+  constexpr int kStage = HEADS2 ? 8 * 64 * 256 : 0;
+  constexpr int kLds = NG * kRing + kMlBytes > kStage ? NG * kRing + kMlBytes : kStage;
+  static_assert(kLds <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[kLds];
   const int lane = threadIdx.x & 63;
-  const int grp = KSPLIT ? (int)(threadIdx.x >> 8) : 0;  // key half
+  const int grp = VAR != kPlain ? (int)(threadIdx.x >> 8) : 0;  // key half, or head of the pair
   const int tid = threadIdx.x & 255;                     // thread within the group
   const int wave = tid >> 6;          // query rows 32 wave .. +31 of the tile
+  const int lw = HEADS2 ? (int)(threadIdx.x >> 6) : wave;  // the wave's share of the loads
   const int col = lane & 31;
   const int hi = lane >> 5;
   // XCD-aware order: the work items (tile slot x fastest, then query head,
@@ -93,7 +112,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const int wi = (wl % 8) * wchunk + wl / 8;
   if (wi >= p.gtotal) return;  // block-uniform, before any barrier
   const int bx = wi % p.gx;
-  const int h = (wi / p.gx) % p.gy;
+  const int h = HEADS2 ? 2 * ((wi / p.gx) % p.gy) + grp : (wi / p.gx) % p.gy;
   const int b = wi / (p.gx * p.gy);
   const int g = h / (p.n_q_heads / p.n_kv_heads);
   // Sequence b: S new query rows from q row qbase, keys = its cache rows
@@ -139,28 +158,29 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   const int kt_lo = !KSPLIT ? 0 : grp == 0 ? 0 : ntiles / 2;
   const int kt_hi = !KSPLIT ? ntiles : grp == 0 ? ntiles / 2 : ntiles;
   const int niter = !KSPLIT ? ntiles : ntiles - ntiles / 2;
-  char* ring = lds + grp * kRingBytes;
+  char* ring = lds + (KSPLIT ? grp * kRing : 0);
 
-  // Load j (0..3) of wave w fills LDS chunks 64 (4 j + w) + lane of the K
-  // (then the V) tile: row 4 (4 j + w) + lane / 16, chunk position lane % 16,
-  // which holds chunk (lane % 16) ^ f(row) of that key row. Rows at or past
-  // the sequence's end read its last row instead (an in-bounds address; K
-  // rows there are masked in the scores, V rows meet a zero weight).
-  const int lrow = 4 * wave + (lane >> 4);  // + 16 j
+  // Load j (0 .. NLW-1) of load wave w fills LDS chunks 64 (LW j + w) + lane
+  // of the K (then the V) tile: row 4 (LW j + w) + lane / 16, chunk position
+  // lane % 16, which holds chunk (lane % 16) ^ f(row) of that key row. Rows
+  // at or past the sequence's end read its last row instead (an in-bounds
+  // address; K rows there are masked in the scores, V rows meet a zero
+  // weight).
+  const int lrow = 4 * lw + (lane >> 4);  // + 4 LW j
   const int lpos = lane & 15;
-  auto gload1 = [&](int kt, int st, int idx) {  // idx 0-3: K, 4-7: V
-    const int j = idx & 3;
-    const int row = lrow + 16 * j;
+  auto gload1 = [&](int kt, int st, int idx) {  // idx < NLW: K, else V
+    const int j = idx % NLW;
+    const int row = lrow + 4 * LW * j;
     const int key = min(kt * kBK + row, L - 1);
-    char* dst = ring + st * kStageBytes + (idx >= 4 ? kTileBytes : 0) + (4 * j + wave) * 1024;
-    if (idx < 4)
+    char* dst = ring + st * kStageBytes + (idx >= NLW ? kTileBytes : 0) + (LW * j + lw) * 1024;
+    if (idx < NLW)
       load_lds16(kbase + (size_t)key * kv_row_stride + 8 * (lpos ^ kswz(row)), dst);
     else
       load_lds16(vbase + (size_t)key * kv_row_stride + 8 * (lpos ^ vswz(row)), dst);
   };
   auto gload = [&](int kt, int st) {
 #pragma unroll
-    for (int idx = 0; idx < 8; ++idx) gload1(kt, st, idx);
+    for (int idx = 0; idx < 2 * NLW; ++idx) gload1(kt, st, idx);
   };
   // V^T fragment addresses (see the transposing read above): for keys
   // kb + 4 (lane / 32) + 0..3 (and + 8) of dh rows 32 dt + lane % 32, lane
@@ -181,21 +201,30 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  if (kt_lo < kt_hi) gload(kt_lo, 0);
-  // This wave's tile loads and Q fragments have landed (and, after the
-  // barrier, every wave's). Draining on every path into the key loop also
-  // keeps the compiler from waiting on the vector-memory counter before the
-  // first score MFMAs, which would wait for the next tile's loads too.
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0) only
+  // the first NS - 1 tiles (a tile past the range re-reads the last one,
+  // unused, so the vector-memory count per tile stays fixed)
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (kt_lo < kt_hi) gload(min(kt_lo + j, kt_hi - 1), j);
+  // This wave's first tile and Q fragments have landed (and, after the
+  // barrier, every wave's); only the later tiles' loads may remain. Waiting
+  // on every path into the key loop also keeps the compiler from waiting on
+  // the vector-memory counter before the first score MFMAs, which would wait
+  // for the next tiles' loads too.
+  if constexpr (NS == 2)
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0) only
+  else
+    __builtin_amdgcn_s_waitcnt(((NS - 2) * 2 * NLW) | (0x7 << 4) | (0xF << 8));
   __syncthreads();
 
   for (int it = 0; it < niter; ++it) {
     const int kt = kt_lo + it;
-    const int st = it & 1;
-    const bool more = kt + 1 < kt_hi;
-    // the next tile's prefetch (the last step re-reads its own tile, unused,
-    // so the loads need no branch and can sit among the score MFMAs)
-    const int ktn = more ? kt + 1 : kt;
+    const int st = it % NS;
+    // the prefetch of tile kt + NS - 1 into the slot tile kt - 1 used (a
+    // tile past the range re-reads the last one, unused, so the loads need
+    // no branch and can sit among the score MFMAs)
+    const int ktn = max(min(kt + NS - 1, kt_hi - 1), 0);
+    const int stn = (it + NS - 1) % NS;
     const int k0 = kt * kBK;
     // skip tiles past the group's range (its last step when it has one tile
     // fewer) and tiles whose every key is in this wave's future (wave-uniform)
@@ -214,18 +243,17 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
           const bf16x8 kf =
               *reinterpret_cast<const bf16x8*>(kr + (((2 * s + hi) ^ kswz(krow)) << 4));
           sc[t] = mfma_32x32x16(kf, qf[s], sc[t]);
-          if (s & 1) gload1(ktn, st ^ 1, 4 * t + (s >> 1));
+          if (s % kMpl == kMpl - 1) gload1(ktn, stn, (8 / kMpl) * t + s / kMpl);
         }
       }
-      // issue order: per pair of score MFMAs, their two K-fragment reads,
-      // the MFMAs and one 16-byte global load of the next tile, so the
-      // loads' issue overlaps the matrix work instead of stalling the wave
-      // ahead of it
+      // issue order: per kMpl score MFMAs, their K-fragment reads, the MFMAs
+      // and one 16-byte global load of a later tile, so the loads' issue
+      // overlaps the matrix work instead of stalling the wave ahead of it
 #pragma unroll
-      for (int g8 = 0; g8 < 8; ++g8) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+      for (int g8 = 0; g8 < 16 / kMpl; ++g8) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kMpl, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, kMpl, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // global load
       }
       // mask, tile max (raw scores; the scale is positive and applied in the
       // exponent). Register r of half t holds key 32t + 8(r/4) + 4hi + r%4.
@@ -309,10 +337,19 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
         }
       }
     } else {
-      gload(ktn, st ^ 1);
+      gload(ktn, stn);
     }
-    // this wave's loads of the next tile have landed; after the barrier every
-    // wave's have, and every wave is done with this tile's slot
+    // this wave's loads of the next tile have landed (only the NS - 2 tiles
+    // after it may still be out); after the barrier every wave's have, and
+    // every wave is done with this tile's slot
+    if constexpr (NS == 2)
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0) only
+    else
+      __builtin_amdgcn_s_waitcnt(((NS - 2) * 2 * NLW) | (0x7 << 4) | (0xF << 8));
+    __syncthreads();
+  }
+  if constexpr (NS > 2) {
+    // the last steps' unused re-reads land before the LDS is reused
     __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0) only
     __syncthreads();
   }
@@ -321,9 +358,9 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   // free: every tile read ended before the loop's last barrier). A lane's
   // state is relative to its own reference maximum m_run; a group that saw
   // no key of this query has m_run = -inf and contributes nothing.
-  static_assert(4 * 64 * 64 * 4 <= kRingBytes, "merge state fits group 0's ring");
+  static_assert(!KSPLIT || 4 * 64 * 64 * 4 <= kRing, "merge state fits group 0's ring");
   float* mst = reinterpret_cast<float*>(lds) + wave * (64 * 64) + lane;
-  float* mls = reinterpret_cast<float*>(lds + NG * kRingBytes) + wave * 128 + lane;
+  float* mls = reinterpret_cast<float*>(lds + NG * kRing) + wave * 128 + lane;
   if (KSPLIT && grp == 1) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -333,7 +370,7 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
     mls[64] = l_run;
   }
   if (KSPLIT) __syncthreads();
-  if (grp == 1) continue;  // (the next pass starts with a barrier)
+  if (KSPLIT && grp == 1) continue;  // (the next pass starts with a barrier)
   if (KSPLIT) {
     const float m1 = mls[0], l1 = mls[64];
     const float m = fmaxf(m_run, m1);  // finite: every query sees key 0
@@ -356,8 +393,8 @@ __global__ __launch_bounds__(KSPLIT ? 512 : 256, KSPLIT ? 1 : 2) void attn_prefi
   // past the sequence (a ragged last tile) are computed and not stored.
   // staging: 64 rows (hi, then lo) of 256 bytes per wave, chunk c of row r
   // at position c ^ (r mod 16)
-  static_assert(4 * 64 * 256 <= kRingBytes, "output staging fits one ring");
-  char* so = lds + (KSPLIT ? kRingBytes : 0) + wave * (64 * 256);
+  static_assert(HEADS2 || 4 * 64 * 256 <= kRing, "output staging fits one ring");
+  char* so = lds + (KSPLIT ? kRing : 0) + (HEADS2 ? (int)(threadIdx.x >> 6) : wave) * (64 * 256);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -406,13 +443,23 @@ hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
   const long pairs = (long)((nqt + 1) / 2) * a.n_q_heads * a.B;
   const long tiles = (long)nqt * a.n_q_heads * a.B;
   AttnPrefillArgs b = a;
-  if (pairs >= 2L * kCUs) {
+  const int G = a.n_kv_heads > 0 ? a.n_q_heads / a.n_kv_heads : 0;
+  if (pairs >= 2L * kCUs && G % 2 == 0) {
+    // enough tile pairs (equal work each) for one 8-wave block per CU whose
+    // two groups are two query heads of one KV group sharing each K/V tile
+    b.pair = true;
+    b.gx = (nqt + 1) / 2;
+    b.gy = a.n_q_heads / 2;
+    b.gtotal = b.gx * b.gy * a.B;
+    hipLaunchKernelGGL(attn_prefill_kernel<kHeads2>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(512), 0,
+                       s, b);
+  } else if (pairs >= 2L * kCUs) {
     // enough tile pairs (equal work each) for two 4-wave blocks per CU
     b.pair = true;
     b.gx = (nqt + 1) / 2;
     b.gy = a.n_q_heads;
     b.gtotal = b.gx * b.gy * a.B;
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(256), 0,
+    hipLaunchKernelGGL(attn_prefill_kernel<kPlain>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(256), 0,
                        s, b);
   } else if (pairs >= kCUs || tiles <= kCUs) {
     // one 8-wave block per CU, each tile's keys split between its two groups:
@@ -421,7 +468,7 @@ hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
     b.gx = b.pair ? (nqt + 1) / 2 : nqt;
     b.gy = a.n_q_heads;
     b.gtotal = b.gx * b.gy * a.B;
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(512), 0,
+    hipLaunchKernelGGL(attn_prefill_kernel<kKsplit>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(512), 0,
                        s, b);
   } else {
     // single tiles, longest first, two 4-wave blocks per CU
@@ -429,7 +476,7 @@ hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
     b.gx = nqt;
     b.gy = a.n_q_heads;
     b.gtotal = b.gx * b.gy * a.B;
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(256), 0,
+    hipLaunchKernelGGL(attn_prefill_kernel<kPlain>, dim3(8 * ((b.gtotal + 7) / 8)), dim3(256), 0,
                        s, b);
   }
   return hipGetLastError();
