@@ -262,13 +262,14 @@ __global__ __launch_bounds__(VAR != kPlain ? 512 : 256, VAR != kPlain ? 1 : 2) v
       const bool need_mask = __builtin_amdgcn_readfirstlane(
           (k0 + kBK - 1 > P + q0 + wave * 32) || (k0 + kBK > L));
       if (need_mask) {
+        // keys past min(my_pos, L - 1), relative to this lane's first key:
+        // one compare per score against a constant offset
+        const int lim = min(my_pos, L - 1) - (k0 + 4 * hi);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-            sc[t][r] = (key > my_pos || key >= L) ? -INFINITY : sc[t][r];
-          }
+          for (int r = 0; r < 16; ++r)
+            sc[t][r] = 32 * t + 8 * (r >> 2) + (r & 3) > lim ? -INFINITY : sc[t][r];
       }
       float mt = -INFINITY;
 #pragma unroll
