@@ -166,17 +166,29 @@ __global__ __launch_bounds__(VAR != kPlain ? 512 : 256, VAR != kPlain ? 1 : 2) v
   // at or past the sequence's end read its last row instead (an in-bounds
   // address; K rows there are masked in the scores, V rows meet a zero
   // weight).
-  const int lrow = 4 * lw + (lane >> 4);  // + 4 LW j
+  // The lane's key row and byte position in the row are fixed per load j;
+  // per tile a load adds the key row's offset (a 24-bit multiply, the cache
+  // of one sequence being far below 4 GiB) to the block's K or V base, so the
+  // load takes a scalar base and a 32-bit vector offset.
+  const int lw_s = __builtin_amdgcn_readfirstlane(lw);
   const int lpos = lane & 15;
+  const uint32_t row_bytes = (uint32_t)p.n_kv_heads * kDh * 2;
+  int lrow_j[NLW];
+  uint32_t kpos_j[NLW], vpos_j[NLW];
+#pragma unroll
+  for (int j = 0; j < NLW; ++j) {
+    lrow_j[j] = 4 * (LW * j + lw) + (lane >> 4);
+    kpos_j[j] = 16 * (lpos ^ kswz(lrow_j[j]));
+    vpos_j[j] = 16 * (lpos ^ vswz(lrow_j[j]));
+  }
+  const char* kb8 = reinterpret_cast<const char*>(kbase);
+  const char* vb8 = reinterpret_cast<const char*>(vbase);
   auto gload1 = [&](int kt, int st, int idx) {  // idx < NLW: K, else V
     const int j = idx % NLW;
-    const int row = lrow + 4 * LW * j;
-    const int key = min(kt * kBK + row, L - 1);
-    char* dst = ring + st * kStageBytes + (idx >= NLW ? kTileBytes : 0) + (LW * j + lw) * 1024;
-    if (idx < NLW)
-      load_lds16(kbase + (size_t)key * kv_row_stride + 8 * (lpos ^ kswz(row)), dst);
-    else
-      load_lds16(vbase + (size_t)key * kv_row_stride + 8 * (lpos ^ vswz(row)), dst);
+    const int key = min(kt * kBK + lrow_j[j], L - 1);
+    const uint32_t off = __umul24((uint32_t)key, row_bytes) + (idx < NLW ? kpos_j[j] : vpos_j[j]);
+    char* dst = ring + st * kStageBytes + (idx >= NLW ? kTileBytes : 0) + (LW * j + lw_s) * 1024;
+    load_lds16(reinterpret_cast<const bf16*>((idx < NLW ? kb8 : vb8) + off), dst);
   };
   auto gload = [&](int kt, int st) {
 #pragma unroll
@@ -439,6 +451,9 @@ __global__ __launch_bounds__(VAR != kPlain ? 512 : 256, VAR != kPlain ? 1 : 2) v
 
 hipError_t ql_attn_prefill_bf16(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.B <= 0 || a.S <= 0) return hipSuccess;
+  // key-row offsets within one sequence's cache are 32-bit (24-bit factors)
+  if ((long long)a.T_max * a.n_kv_heads * kDh * 2 >= (1LL << 32) || a.T_max >= (1 << 24))
+    return hipErrorInvalidValue;
   // (a.S: the longest sequence's new rows when seq_start is set)
   const int nqt = (a.S + kBQ - 1) / kBQ;
   const long pairs = (long)((nqt + 1) / 2) * a.n_q_heads * a.B;
