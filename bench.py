@@ -369,91 +369,98 @@ def stages_of(cfg, kind, batch):
 
 # HBM bytes per launch from rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch), scaled by what the same counters read for a plain 256 MiB device copy
-# (FETCH_SIZE 131085.4 KiB, WRITE_SIZE 262144.0 KiB: factors 1.9998 and 1.0). Keyed by
+# (FETCH_SIZE 131084.6 KiB, WRITE_SIZE 262144.0 KiB: factors 1.9998 and 1.0). Keyed by
 # (workload, stage); each entry names the source file of the stage's kernels and the first
-# 16 hex digits of its SHA-256 when the counters were taken, and is reported only while
-# that file is unchanged (else traffic is null). Summaries: profiles/*_hbm_counters.md.
-PMC_FETCH_SCALE = 262144.0 / 131085.4
+# 16 hex digits of the SHA-256 of that file with common.h and kernels.h when the counters
+# were taken, and is reported only while they are unchanged (else traffic is null).
+# Summary: profiles/hbm_counters_decode_workloads.md.
+PMC_FETCH_SCALE = 262144.0 / 131084.6
 PMC_WRITE_SCALE = 262144.0 / 262144.0
 PMC_TRAFFIC_KIB = {
     # (workload, stage): (FETCH_SIZE KiB, WRITE_SIZE KiB, source file, sha256[:16]) per layer
     # call, the stage's kernels summed; profiles/hbm_counters_decode_workloads.md
-    ("qwen2.5-7b decode B=1 cache=1024", "qkv"): (16212.3, 72.0, "gemv.hip", "1c873011e5d3fd21"),
-    ("qwen2.5-7b decode B=1 cache=1024", "attention"): (1760.3, 975.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen2.5-7b decode B=1 cache=1024", "o_proj"): (12651.1, 56.0, "gemv.hip", "1c873011e5d3fd21"),
-    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132730.0, 148.0, "gemv.hip", "1c873011e5d3fd21"),
-    ("qwen2.5-7b decode B=1 cache=1024", "down"): (66526.3, 56.0, "gemv.hip", "1c873011e5d3fd21"),
-    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm1"): (157.0, 448.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22436.5, 9152.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen2.5-7b decode B=32 cache=1024", "attention"): (37915.7, 8064.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18577.4, 8896.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm2"): (268.7, 448.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140879.4, 15040.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79233.5, 8800.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-8b decode B=64 cache=4096", "rmsnorm1"): (305.0, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35102.2, 18944.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-8b decode B=64 cache=4096", "attention"): (532684.4, 5376.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25486.0, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-8b decode B=64 cache=4096", "rmsnorm2"): (560.7, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110267.6, 23552.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-8b decode B=64 cache=4096", "down"): (59532.7, 16896.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32544.8, 20992.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (536267.6, 10752.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17805.6, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "router"): (2650.9, 72.0, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "permute"): (4.9, 10.1, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_gate_up"): (397950.0, 3072.6, "gemm.hip", "61d3a5bc75f21aff"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_down"): (208941.2, 8192.0, "gemm.hip", "61d3a5bc75f21aff"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "combine"): (4645.6, 512.0, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32544.0, 20992.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "attention"): (139504.6, 10752.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17805.6, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "router"): (2650.9, 72.0, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "permute"): (4.9, 10.1, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_gate_up"): (394923.2, 3072.6, "gemm.hip", "61d3a5bc75f21aff"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_down"): (207405.1, 8192.1, "gemm.hip", "61d3a5bc75f21aff"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "combine"): (4645.6, 512.0, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen3-32b decode B=32 cache=4096", "rmsnorm1"): (230.0, 640.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57638.2, 10496.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-32b decode B=32 cache=4096", "attention"): (271521.6, 9728.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48161.9, 9344.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-32b decode B=32 cache=4096", "rmsnorm2"): (391.7, 640.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265873.3, 17536.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen3-32b decode B=32 cache=4096", "down"): (140801.5, 9024.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("mixtral-like decode B=64 cache=2048", "rmsnorm1"): (304.8, 1024.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("mixtral-like decode B=64 cache=2048", "qkv"): (35099.6, 18944.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("mixtral-like decode B=64 cache=2048", "attention"): (268484.5, 5376.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25485.9, 17408.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("mixtral-like decode B=64 cache=2048", "rmsnorm2"): (560.7, 2048.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("mixtral-like decode B=64 cache=2048", "router"): (694.9, 3.0, "moe.hip", "9df6017876fa8ad8"),
-    ("mixtral-like decode B=64 cache=2048", "permute"): (3.2, 1.2, "moe.hip", "9df6017876fa8ad8"),
-    ("mixtral-like decode B=64 cache=2048", "expert_gate_up"): (266288.7, 2048.0, "gemm.hip", "61d3a5bc75f21aff"),
-    ("mixtral-like decode B=64 cache=2048", "expert_down"): (139303.0, 2048.0, "gemm.hip", "61d3a5bc75f21aff"),
-    ("mixtral-like decode B=64 cache=2048", "combine"): (1561.5, 512.0, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm1"): (268.8, 896.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28564.0, 18304.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "attention"): (72458.7, 8512.0, "attn_decode.hip", "131fb980e0aece5b"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24502.9, 17792.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm2"): (492.8, 1792.0, "rmsnorm.hip", "f2f7400f5c0ddf7e"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "router"): (1973.5, 24.2, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "permute"): (3.9, 5.1, "moe.hip", "9df6017876fa8ad8"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_gate_up"): (1150530.4, 5120.0, "gemm.hip", "61d3a5bc75f21aff"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_down"): (594008.6, 7168.0, "gemm.hip", "61d3a5bc75f21aff"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158066.7, 29696.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98812.5, 18048.0, "gemm2.hip", "2262baeccb5a8fc2"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "combine"): (4067.5, 448.0, "moe.hip", "9df6017876fa8ad8"),
+    ("qwen2.5-7b decode B=1 cache=1024", "qkv"): (16212.3, 72.0, "gemv.hip", "56b4af1dcf5d3206"),
+    ("qwen2.5-7b decode B=1 cache=1024", "attention"): (1760.4, 975.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("qwen2.5-7b decode B=1 cache=1024", "o_proj"): (12651.1, 56.0, "gemv.hip", "56b4af1dcf5d3206"),
+    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132729.9, 148.0, "gemv.hip", "56b4af1dcf5d3206"),
+    ("qwen2.5-7b decode B=1 cache=1024", "down"): (66526.3, 56.0, "gemv.hip", "56b4af1dcf5d3206"),
+    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm1"): (156.9, 448.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22397.2, 9152.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen2.5-7b decode B=32 cache=1024", "attention"): (37918.3, 8064.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18573.3, 8896.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm2"): (268.7, 448.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140876.8, 15040.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79234.0, 8800.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-8b decode B=64 cache=4096", "rmsnorm1"): (304.9, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35062.7, 18944.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-8b decode B=64 cache=4096", "attention"): (532699.5, 5376.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25488.5, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-8b decode B=64 cache=4096", "rmsnorm2"): (560.7, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110263.2, 23552.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-8b decode B=64 cache=4096", "down"): (59545.0, 16896.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32506.2, 20992.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (536260.8, 10752.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17808.1, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "router"): (2650.9, 72.0, "moe.hip", "d4d322f69feeb112"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "permute"): (4.9, 10.1, "moe.hip", "d4d322f69feeb112"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_gate_up"): (397933.9, 3072.4, "gemm.hip", "20d2966d912f0b5d"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_down"): (208941.1, 8192.0, "gemm.hip", "20d2966d912f0b5d"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "combine"): (4645.6, 512.0, "moe.hip", "d4d322f69feeb112"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32505.1, 20992.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "attention"): (139494.5, 10752.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17808.1, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "router"): (2650.9, 72.0, "moe.hip", "d4d322f69feeb112"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "permute"): (4.9, 10.1, "moe.hip", "d4d322f69feeb112"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_gate_up"): (394908.5, 3072.5, "gemm.hip", "20d2966d912f0b5d"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_down"): (207405.2, 8192.1, "gemm.hip", "20d2966d912f0b5d"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "combine"): (4645.6, 512.0, "moe.hip", "d4d322f69feeb112"),
+    ("qwen3-32b decode B=32 cache=4096", "rmsnorm1"): (230.0, 640.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57599.6, 10496.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-32b decode B=32 cache=4096", "attention"): (271549.2, 9728.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48157.9, 9344.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-32b decode B=32 cache=4096", "rmsnorm2"): (391.7, 640.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265871.0, 17536.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen3-32b decode B=32 cache=4096", "down"): (140803.0, 9024.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("mixtral-like decode B=64 cache=2048", "rmsnorm1"): (304.8, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("mixtral-like decode B=64 cache=2048", "qkv"): (35059.8, 18944.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("mixtral-like decode B=64 cache=2048", "attention"): (268511.4, 5376.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25488.4, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("mixtral-like decode B=64 cache=2048", "rmsnorm2"): (560.7, 2048.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("mixtral-like decode B=64 cache=2048", "router"): (694.9, 3.0, "moe.hip", "d4d322f69feeb112"),
+    ("mixtral-like decode B=64 cache=2048", "permute"): (3.2, 1.2, "moe.hip", "d4d322f69feeb112"),
+    ("mixtral-like decode B=64 cache=2048", "expert_gate_up"): (266284.7, 2048.0, "gemm.hip", "20d2966d912f0b5d"),
+    ("mixtral-like decode B=64 cache=2048", "expert_down"): (139301.9, 2048.0, "gemm.hip", "20d2966d912f0b5d"),
+    ("mixtral-like decode B=64 cache=2048", "combine"): (1561.5, 512.0, "moe.hip", "d4d322f69feeb112"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm1"): (268.8, 896.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28525.7, 18304.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "attention"): (72450.7, 8512.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24505.6, 17792.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm2"): (492.8, 1792.0, "rmsnorm.hip", "4822ce368199ba82"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "router"): (1973.5, 24.2, "moe.hip", "d4d322f69feeb112"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "permute"): (3.9, 5.1, "moe.hip", "d4d322f69feeb112"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_gate_up"): (1150526.4, 5120.0, "gemm.hip", "20d2966d912f0b5d"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_down"): (594008.9, 7168.0, "gemm.hip", "20d2966d912f0b5d"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158059.9, 29696.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98815.9, 18048.0, "gemm2.hip", "9cfde967086ef01f"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "combine"): (4067.5, 448.0, "moe.hip", "d4d322f69feeb112"),
 }
 
 
 def source_sha(name):
+    """First 16 hex digits of the SHA-256 of a kernel source together with the
+    headers every kernel includes (common.h, kernels.h): a change to either
+    changes the kernel, and its counter readings no longer apply."""
     import hashlib
-    path = os.path.join(ROOT, "transformer_decoder_layer_qwen_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    csrc = os.path.join(ROOT, "transformer_decoder_layer_qwen_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (name, "common.h", "kernels.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def pmc_traffic(wl, stage):
