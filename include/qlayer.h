@@ -150,9 +150,12 @@ size_t qlayer_workspace_bytes(const ql_handle* h);
  * k_cache, v_cache  [B, T_max, Hkv, dh]  rows 0..S-1 of each sequence are
  *          written: K after QK-norm and RoPE, V as projected ("推理系统 03"
  *          §12); other rows are untouched. Attention reads only these S rows.
- * T_max    rows per sequence in the caches (S <= T_max)
+ * T_max    rows per sequence in the caches (S <= T_max; one sequence's K or V
+ *          cache, T_max * Hkv * dh * 2 bytes, must stay below 4 GiB and T_max
+ *          below 2^24 on the bf16 path)
  * y        [B, S, d]                output hidden rows (may not alias x)
- * Errors: QL_EINVAL (NULL, B*S > max_tokens, S > T_max), QL_EHIP. */
+ * Errors: QL_EINVAL (NULL, B*S > max_tokens, S > T_max), QL_EUNSUPPORTED
+ * (T_max beyond the limit above), QL_EHIP. */
 ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offset,
                          void* k_cache, void* v_cache, int T_max, void* y, void* stream);
 
@@ -171,10 +174,11 @@ ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offs
  *            0 .. cache_len[b] + t. The caller advances cache_len afterwards.
  * seq_start_host, cache_len_host  HOST copies of both (required): the
  *            launch shapes come from them and the bounds are checked there.
- * k_cache, v_cache [B, T_max, Hkv, dh];  y [N, d] (may not alias x)
+ * k_cache, v_cache [B, T_max, Hkv, dh];  y [N, d] (may not alias x); T_max
+ *            within the limit of qlayer_prefill
  * Errors: QL_EINVAL (NULL, bad seq_start, N = 0 or > max_tokens),
  * QL_ECACHE_FULL (cache_len[b] + new rows > T_max), QL_EUNSUPPORTED
- * (QL_F32), QL_EHIP. */
+ * (QL_F32, T_max beyond the limit), QL_EHIP. */
 ql_status qlayer_prefill_varlen(ql_handle* h, const void* x, int B, const int* seq_start,
                                 const int* cache_len, const int* seq_start_host,
                                 const int* cache_len_host, int pos_offset, void* k_cache,

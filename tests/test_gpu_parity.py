@@ -248,8 +248,8 @@ def test_small_bf16_decode_ragged_lengths(case):
 
 def test_entry_points_reject_bad_arguments_before_any_launch():
     """Argument errors on a live handle return their status and write nothing: sizes beyond
-    the handle's workspace, S > T_max, empty batches, y aliasing x, and the MoE entry point
-    on a dense layer."""
+    the handle's workspace, S > T_max, a T_max past the cache addressing limit, empty
+    batches, y aliasing x, and the MoE entry point on a dense layer."""
     cfg = small_cfg()
     layer, _ = make_layer(cfg, max_tokens=16, max_batch=4)
     h, dt = layer.handle, tdt(cfg)
@@ -268,6 +268,9 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
         "prefill S = 0": (lambda: B.qlayer_prefill(h, X, 1, 0, 0, K, V, 8, Y, s), B.QL_EINVAL),
         "prefill y aliases x": (lambda: B.qlayer_prefill(h, X, 1, 8, 0, K, V, 8, X, s),
                                 B.QL_EINVAL),
+        # one sequence's cache past the prefill attention's 32-bit row offsets
+        "prefill T_max 2^24": (lambda: B.qlayer_prefill(h, X, 1, 8, 0, K, V, 1 << 24, Y, s),
+                               B.QL_EUNSUPPORTED),
         "decode B > max_batch": (lambda: B.qlayer_decode(h, X, 5, L, None, 0, K, V, 8, Y, s),
                                  B.QL_EINVAL),
         "decode B = 0": (lambda: B.qlayer_decode(h, X, 0, L, None, 0, K, V, 8, Y, s), B.QL_EINVAL),

@@ -104,6 +104,12 @@ namespace {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// The bf16 prefill attention addresses one sequence's cache rows with 32-bit
+// offsets from 24-bit factors.
+bool prefill_cache_fits(const ql_config& c, int T_max) {
+  return T_max < (1 << 24) && (long long)T_max * c.n_kv_heads * c.head_dim * 2 < (1LL << 32);
+}
+
 // Stage markers for qlayer_set_stage_events.
 ql_status mark(ql_handle* h, int stage, bool begin, hipStream_t s) {
   if (h->ev_stage == QL_STAGE_NONE || h->ev_stage != stage) return QL_OK;
@@ -916,6 +922,9 @@ ql_status qlayer_prefill(ql_handle* h, const void* x, int B, int S, int pos_offs
                 h->cfg.max_tokens);
   if (S > T_max) return fail(QL_EINVAL, "prefill: S (%d) > T_max (%d)", S, T_max);
   if (x == y) return fail(QL_EINVAL, "prefill: y must not alias x");
+  if (h->cfg.dtype == QL_BF16 && !prefill_cache_fits(h->cfg, T_max))
+    return fail(QL_EUNSUPPORTED, "prefill: T_max = %d: one sequence's cache must stay below 4 GiB",
+                T_max);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int N = B * S;
   ql_status st;
@@ -941,6 +950,9 @@ ql_status qlayer_prefill_varlen(ql_handle* h, const void* x, int B, const int* s
   if (x == y) return fail(QL_EINVAL, "prefill_varlen: y must not alias x");
   if (h->cfg.dtype != QL_BF16)
     return fail(QL_EUNSUPPORTED, "prefill_varlen: needs dtype QL_BF16");
+  if (!prefill_cache_fits(h->cfg, T_max))
+    return fail(QL_EUNSUPPORTED,
+                "prefill_varlen: T_max = %d: one sequence's cache must stay below 4 GiB", T_max);
   if (seq_start_host[0] != 0) return fail(QL_EINVAL, "prefill_varlen: seq_start[0] must be 0");
   int S_max = 0;
   for (int b = 0; b < B; ++b) {
