@@ -1218,12 +1218,14 @@ PairPlan pair_plan(int M, int N, int K) {
       for (int st = 2; st <= 8 && st * 8 <= ks; ++st) {
         const int per = (ks + st - 1) / st;
         if ((ks + per - 1) / per != st) continue;
-        // + the second GEMM launch and its partial epilogue, ~20 units as
-        // measured (a half-empty last wave is better left alone; a nearly
-        // empty one is worth the split)
+        // + the second GEMM launch, 5 units beyond the partials' traffic
+        // (weighed at 20, the plans kept Qwen3-30B-A3B 4096-token Q/K/V on
+        // 2.5 waves of 128-row tiles: 209.5 us; at 5 it takes one wave of
+        // 256-row tiles and a 4-way split tail: 196.4 us; Qwen3-8B Q/K/V
+        // 224.9 -> 219.7 us, Qwen3-32B O 336.0 -> 329.2 us)
         const double c = (waves((long long)tiles_m * (tiles_n - tc)) * ks +
                           waves((long long)tiles_m * tc * st) * per) * unit +
-                         part_cost(st, tc * BN) + 20.0;
+                         part_cost(st, tc * BN) + 5.0;
         consider(c, {shape, 1, tc, st});
       }
   }
