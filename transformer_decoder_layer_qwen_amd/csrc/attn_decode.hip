@@ -263,8 +263,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
       sc[r] = x;
       mt = fmaxf(mt, x);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = xor32_max(xor16_max(mt));
     const float m_new = fmaxf(m_run, mt);  // finite: key k0 < kend is valid
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
@@ -275,8 +274,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
       ps += pv;
       p_lds[(4 * grp + r) * 16 + col] = pv;
     }
-    ps += __shfl_xor(ps, 16, kWave);
-    ps += __shfl_xor(ps, 32, kWave);
+    ps = xor32_sum(xor16_sum(ps));
     l_run = l_run * alpha + ps;
     if (grp == 0) a_lds[col] = alpha;
     __builtin_amdgcn_wave_barrier();
@@ -523,8 +521,7 @@ __global__ __launch_bounds__(HM ? 64 * kHmMaxHeads : 64 * W) __attribute__((amdg
         sc[h][r] = x;
         mt = fmaxf(mt, x);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    mt = xor32_max(xor16_max(mt));
     const float m_new = fmaxf(m_run, mt);  // finite: key k0 < kend is live
     const float alpha = exp2f(m_run - m_new);
     m_run = m_new;
@@ -575,8 +572,7 @@ __global__ __launch_bounds__(HM ? 64 * kHmMaxHeads : 64 * W) __attribute__((amdg
     }
   }
 
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = xor32_sum(xor16_sum(l_run));
   if constexpr (W > 1) {
     // each wave's partial (m, l, O) to LDS (O in its own V^T slot, which only
     // this wave has used), then the block merges: thread t takes elements

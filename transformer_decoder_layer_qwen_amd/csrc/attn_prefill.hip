@@ -288,7 +288,7 @@ __global__ __launch_bounds__(VAR != kPlain ? 512 : 256, VAR != kPlain ? 1 : 2) v
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[t][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave)) * p.scale_log2;
+      mt = xor32_max(mt) * p.scale_log2;
       // Lazy rescaling: the reference maximum only moves when a score exceeds
       // it by more than kSlack (log2 units), so p <= 2^kSlack and the output
       // is unchanged (numerator and denominator use the same reference); the
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(VAR != kPlain ? 512 : 256, VAR != kPlain ? 1 : 2) v
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[dt][r] = a0 * acc_o[dt][r] + a1 * mst[(16 * dt + r) * 64];
   }
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = xor32_sum(l_run);
   const float inv = 1.0f / l_tot;
   // The fp32 output as a bf16 pair: hi = RNE(o) at column c, lo = RNE(o - hi)
   // at column c + lo_off (the O projection multiplies both). A lane holds 16

@@ -64,6 +64,28 @@ QL_DEV float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
   return v;
 }
+// A lane's value combined with the lane 16 (or 32) places away, i ^ 16 (i ^ 32),
+// by gfx950's row swaps (v_permlane16_swap / v_permlane32_swap: no LDS round
+// trip). Swapping a register with itself leaves each lane holding its own
+// value and its partner's, in an order that differs by half; max and sum do
+// not depend on it.
+QL_DEV float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+QL_DEV float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+QL_DEV float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+QL_DEV float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 QL_DEV float group_sum(float v, int width) {
   for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
