@@ -54,16 +54,6 @@ QL_DEV f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-QL_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
-}
-QL_DEV float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
-}
 // A lane's value combined with the lane 16 (or 32) places away, i ^ 16 (i ^ 32),
 // by gfx950's row swaps (v_permlane16_swap / v_permlane32_swap: no LDS round
 // trip). Swapping a register with itself leaves each lane holding its own
@@ -85,6 +75,31 @@ QL_DEV float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// Value of the lane k places earlier in its row of 16 lanes (a DPP row rotate).
+template <int K>
+QL_DEV float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + K, 0xF, 0xF, false));
+}
+// Sum / max over the lane's row of 16 lanes, left in every lane of the row:
+// rotations by 8, 4, 2 and 1 reach every lane of the row (no LDS round trip).
+QL_DEV float row16_sum(float x) {
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  return x + row_ror<1>(x);
+}
+QL_DEV float row16_max(float x) {
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  return fmaxf(x, row_ror<1>(x));
+}
+// Sum / max over the wave, in every lane. These and the row and half exchanges
+// above read other lanes' registers directly, so every lane of the wave must
+// be active where they are used (all call sites are wave-uniform).
+QL_DEV float wave_sum(float v) { return xor32_sum(xor16_sum(row16_sum(v))); }
+QL_DEV float wave_max(float v) { return xor32_max(xor16_max(row16_max(v))); }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 QL_DEV float group_sum(float v, int width) {

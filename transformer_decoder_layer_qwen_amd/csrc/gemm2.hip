@@ -161,8 +161,8 @@ QL_DEV void qkv_finish(const G2Args& p, size_t row, int col, float (&v)[8]) {
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-      ss = group_sum(ss, 16);
-      const float inv = 1.0f / sqrtf(ss / 128.f + p.eps);
+      ss = row16_sum(ss);
+      const float inv = __builtin_amdgcn_rsqf(ss / 128.f + p.eps);
       float g[8];
       unpack8(load_bf16x8(gam + d0), g);
 #pragma unroll
