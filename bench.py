@@ -374,79 +374,79 @@ def stages_of(cfg, kind, batch):
 # 16 hex digits of the SHA-256 of that file with common.h and kernels.h when the counters
 # were taken, and is reported only while they are unchanged (else traffic is null).
 # Summary: profiles/hbm_counters_decode_workloads.md.
-PMC_FETCH_SCALE = 262144.0 / 131084.6
+PMC_FETCH_SCALE = 262144.0 / 131084.5
 PMC_WRITE_SCALE = 262144.0 / 262144.0
 PMC_TRAFFIC_KIB = {
     # (workload, stage): (FETCH_SIZE KiB, WRITE_SIZE KiB, source file, sha256[:16]) per layer
     # call, the stage's kernels summed; profiles/hbm_counters_decode_workloads.md
-    ("qwen2.5-7b decode B=1 cache=1024", "qkv"): (16212.3, 72.0, "gemv.hip", "56b4af1dcf5d3206"),
-    ("qwen2.5-7b decode B=1 cache=1024", "attention"): (1760.4, 975.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("qwen2.5-7b decode B=1 cache=1024", "o_proj"): (12651.1, 56.0, "gemv.hip", "56b4af1dcf5d3206"),
-    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132729.9, 148.0, "gemv.hip", "56b4af1dcf5d3206"),
-    ("qwen2.5-7b decode B=1 cache=1024", "down"): (66526.3, 56.0, "gemv.hip", "56b4af1dcf5d3206"),
-    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm1"): (156.9, 448.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22397.2, 9152.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen2.5-7b decode B=32 cache=1024", "attention"): (37918.3, 8064.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18573.3, 8896.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm2"): (268.7, 448.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140876.8, 15040.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79234.0, 8800.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-8b decode B=64 cache=4096", "rmsnorm1"): (304.9, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35062.7, 18944.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-8b decode B=64 cache=4096", "attention"): (532699.5, 5376.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25488.5, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-8b decode B=64 cache=4096", "rmsnorm2"): (560.7, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110263.2, 23552.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-8b decode B=64 cache=4096", "down"): (59545.0, 16896.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32506.2, 20992.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (536260.8, 10752.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17808.1, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "router"): (2650.9, 72.0, "moe.hip", "d4d322f69feeb112"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "permute"): (4.9, 10.1, "moe.hip", "d4d322f69feeb112"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_gate_up"): (397933.9, 3072.4, "gemm.hip", "20d2966d912f0b5d"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_down"): (208941.1, 8192.0, "gemm.hip", "20d2966d912f0b5d"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "combine"): (4645.6, 512.0, "moe.hip", "d4d322f69feeb112"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm1"): (291.3, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32505.1, 20992.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "attention"): (139494.5, 10752.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17808.1, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm2"): (546.7, 2048.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "router"): (2650.9, 72.0, "moe.hip", "d4d322f69feeb112"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "permute"): (4.9, 10.1, "moe.hip", "d4d322f69feeb112"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_gate_up"): (394908.5, 3072.5, "gemm.hip", "20d2966d912f0b5d"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_down"): (207405.2, 8192.1, "gemm.hip", "20d2966d912f0b5d"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "combine"): (4645.6, 512.0, "moe.hip", "d4d322f69feeb112"),
-    ("qwen3-32b decode B=32 cache=4096", "rmsnorm1"): (230.0, 640.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57599.6, 10496.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-32b decode B=32 cache=4096", "attention"): (271549.2, 9728.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48157.9, 9344.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-32b decode B=32 cache=4096", "rmsnorm2"): (391.7, 640.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265871.0, 17536.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen3-32b decode B=32 cache=4096", "down"): (140803.0, 9024.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("mixtral-like decode B=64 cache=2048", "rmsnorm1"): (304.8, 1024.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("mixtral-like decode B=64 cache=2048", "qkv"): (35059.8, 18944.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("mixtral-like decode B=64 cache=2048", "attention"): (268511.4, 5376.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25488.4, 17408.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("mixtral-like decode B=64 cache=2048", "rmsnorm2"): (560.7, 2048.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("mixtral-like decode B=64 cache=2048", "router"): (694.9, 3.0, "moe.hip", "d4d322f69feeb112"),
-    ("mixtral-like decode B=64 cache=2048", "permute"): (3.2, 1.2, "moe.hip", "d4d322f69feeb112"),
-    ("mixtral-like decode B=64 cache=2048", "expert_gate_up"): (266284.7, 2048.0, "gemm.hip", "20d2966d912f0b5d"),
-    ("mixtral-like decode B=64 cache=2048", "expert_down"): (139301.9, 2048.0, "gemm.hip", "20d2966d912f0b5d"),
-    ("mixtral-like decode B=64 cache=2048", "combine"): (1561.5, 512.0, "moe.hip", "d4d322f69feeb112"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm1"): (268.8, 896.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28525.7, 18304.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "attention"): (72450.7, 8512.0, "attn_decode.hip", "0aeaaa0dc74b3d5a"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24505.6, 17792.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm2"): (492.8, 1792.0, "rmsnorm.hip", "4822ce368199ba82"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "router"): (1973.5, 24.2, "moe.hip", "d4d322f69feeb112"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "permute"): (3.9, 5.1, "moe.hip", "d4d322f69feeb112"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_gate_up"): (1150526.4, 5120.0, "gemm.hip", "20d2966d912f0b5d"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_down"): (594008.9, 7168.0, "gemm.hip", "20d2966d912f0b5d"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158059.9, 29696.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98815.9, 18048.0, "gemm2.hip", "9cfde967086ef01f"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "combine"): (4067.5, 448.0, "moe.hip", "d4d322f69feeb112"),
+    ("qwen2.5-7b decode B=1 cache=1024", "qkv"): (16212.2, 72.0, "gemv.hip", "6a126318354a6a7d"),
+    ("qwen2.5-7b decode B=1 cache=1024", "attention"): (1766.3, 975.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen2.5-7b decode B=1 cache=1024", "o_proj"): (12643.6, 56.0, "gemv.hip", "6a126318354a6a7d"),
+    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132730.5, 148.0, "gemv.hip", "6a126318354a6a7d"),
+    ("qwen2.5-7b decode B=1 cache=1024", "down"): (66531.3, 56.0, "gemv.hip", "6a126318354a6a7d"),
+    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm1"): (161.0, 448.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22395.5, 9152.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen2.5-7b decode B=32 cache=1024", "attention"): (37937.8, 8064.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18576.9, 8896.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm2"): (273.7, 448.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140880.7, 15040.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79230.1, 8800.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-8b decode B=64 cache=4096", "rmsnorm1"): (308.9, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35057.6, 18944.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-8b decode B=64 cache=4096", "attention"): (531962.6, 5376.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25494.9, 17408.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-8b decode B=64 cache=4096", "rmsnorm2"): (565.7, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110260.7, 23552.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-8b decode B=64 cache=4096", "down"): (59542.2, 16896.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm1"): (289.8, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32501.2, 20992.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (535581.1, 10752.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17814.6, 17408.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm2"): (545.7, 2048.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "router"): (2652.9, 72.0, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "permute"): (4.9, 10.1, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_gate_up"): (397957.1, 3072.5, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_down"): (208941.2, 8192.0, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "combine"): (4645.6, 512.0, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm1"): (289.8, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32500.5, 20992.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "attention"): (139264.9, 10752.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17814.6, 17408.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm2"): (545.7, 2048.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "router"): (2652.9, 72.0, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "permute"): (4.9, 10.1, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_gate_up"): (394899.4, 3072.4, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_down"): (207405.1, 8192.1, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "combine"): (4645.6, 512.0, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-32b decode B=32 cache=4096", "rmsnorm1"): (228.8, 640.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57597.7, 10496.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-32b decode B=32 cache=4096", "attention"): (270920.7, 9728.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48161.4, 9344.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-32b decode B=32 cache=4096", "rmsnorm2"): (386.7, 640.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265874.9, 17536.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen3-32b decode B=32 cache=4096", "down"): (140799.0, 9024.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("mixtral-like decode B=64 cache=2048", "rmsnorm1"): (308.8, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("mixtral-like decode B=64 cache=2048", "qkv"): (35054.9, 18944.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("mixtral-like decode B=64 cache=2048", "attention"): (267870.8, 5376.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25494.8, 17408.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("mixtral-like decode B=64 cache=2048", "rmsnorm2"): (565.7, 2048.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("mixtral-like decode B=64 cache=2048", "router"): (692.9, 3.0, "moe.hip", "f52fec8eb3681e2a"),
+    ("mixtral-like decode B=64 cache=2048", "permute"): (3.2, 1.2, "moe.hip", "f52fec8eb3681e2a"),
+    ("mixtral-like decode B=64 cache=2048", "expert_gate_up"): (266285.3, 2048.0, "gemm.hip", "c4880637026b08aa"),
+    ("mixtral-like decode B=64 cache=2048", "expert_down"): (139302.3, 2048.0, "gemm.hip", "c4880637026b08aa"),
+    ("mixtral-like decode B=64 cache=2048", "combine"): (1561.5, 512.0, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm1"): (272.8, 896.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28521.0, 18304.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "attention"): (72274.4, 8512.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24511.8, 17792.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm2"): (497.8, 1792.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "router"): (1971.5, 24.2, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "permute"): (3.9, 5.1, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_gate_up"): (1150526.3, 5120.0, "gemm.hip", "c4880637026b08aa"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_down"): (594008.5, 7168.0, "gemm.hip", "c4880637026b08aa"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158060.4, 29696.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98823.0, 18048.0, "gemm2.hip", "e2ec7170c384b7b9"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "combine"): (4067.5, 448.0, "moe.hip", "f52fec8eb3681e2a"),
 }
 
 
