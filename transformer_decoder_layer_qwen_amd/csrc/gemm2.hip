@@ -334,7 +334,9 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform, so the direct loads' LDS addresses (M0) come from scalar
+  // arithmetic instead of a vector add and a lane read per load
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WNW, wn = wave % WNW;
 
   const int nks_all = p.Ka / BK;
@@ -737,7 +739,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_dec_kernel(const G2Args p) {
   __shared__ __attribute__((aligned(1024))) char smem[NS * SB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wn = tid >> 6;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar M0 addresses)
   const int nks = p.Ka / BK;
   const int U = p.tiles_m * p.tiles_n * nks;
   const int u0 = __builtin_amdgcn_readfirstlane((int)((long long)blockIdx.x * U / p.sk_grid));
