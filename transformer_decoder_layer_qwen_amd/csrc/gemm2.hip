@@ -7,7 +7,7 @@
 // [hi | lo] (hi = RNE(a), lo = RNE(a - hi), row pitch 2 Kb), and the tile sums
 // hi*W + lo*W, keeping the activation to about 16 significant bits.
 //
-// Design (gfx950, wave64), prefill tiles (gemm2_kernel, three kinds, see there):
+// Design (gfx950, wave64), prefill tiles (gemm2_kernel, four kinds, see there):
 // * 8 waves on a 256-column weight tile, 32x32x16 MFMAs with fp32 accumulators;
 //   256 token rows (plain A, or a pair whose 32-deep stages hold the hi, lo and
 //   weight rows together) or 128 token rows of a pair.
@@ -301,15 +301,24 @@ QL_DEV void wait_vmcnt() {
 //     owns 64 token rows x 128 columns: per 16-deep step it reads 8 fragments
 //     for 16 MFMAs (kind 0 reads 6 for 8), and the block moves 48 KiB from L2
 //     per 256 x 256 x 64 of MFMA work instead of 64.
-// Two waves share each SIMD, so one wave's MFMAs run while the other waits.
+//  3  [hi | lo] pair, 128 token rows, for the MoE down projection: a stage
+//     holds 32 k of the 128 hi, 128 lo and 256 weight rows (32 KiB); two ring
+//     slots and 64-row epilogue passes keep the block at 65 KiB of LDS and 128
+//     registers, so two blocks share a CU and one block's prologue and
+//     epilogue (short k loops: K = the expert width) overlap the other's
+//     MFMAs. 8 waves as 2 x 4, a wave owns 64 token rows x 64 columns.
+// Kinds 0-2: two waves share each SIMD, so one wave's MFMAs run while the
+// other waits; kind 3: four.
 template <int MODE, bool PART, int KIND>
-__global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
+__global__ __launch_bounds__(512, KIND == 3 ? 4 : 1) void gemm2_kernel(const G2Args p) {
   constexpr bool HL = KIND == 1;
-  constexpr bool P2 = KIND == 2;
+  constexpr bool K3 = KIND == 3;
+  constexpr bool P2 = KIND == 2 || K3;  // pair stages: hi, lo and weight rows together
   constexpr int BMT = 256;
+  constexpr int RT = HL || K3 ? BMT / 2 : BMT;  // token rows per tile
   constexpr int NW = BMT / 32;          // waves
   constexpr int NT = NW * 64;           // threads
-  constexpr int WMW = P2 ? 4 : BMT / 128;  // waves along M
+  constexpr int WMW = K3 ? 2 : (P2 ? 4 : BMT / 128);  // waves along M
   constexpr int WNW = NW / WMW;         // waves along N
   constexpr int WROWS = P2 ? 64 : 128;  // LDS A rows per wave (per half for P2)
   constexpr int WCOLS = BN / WNW;       // columns per wave
@@ -317,17 +326,18 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
   constexpr int TJ = WCOLS / 32;        // 32-wide MFMA tiles per wave along N
   constexpr int SBK = P2 ? 32 : BK;     // k depth of a stage
   constexpr int RC = SBK / 8;           // 16-byte chunks per LDS row
-  constexpr int AROWS = P2 ? 2 * BMT : BMT;  // LDS rows of A per stage
+  constexpr int AROWS = P2 ? 2 * RT : BMT;  // LDS rows of A per stage
   constexpr int AC = AROWS * RC;        // A chunks per stage
   constexpr int CH = AC + BN * RC;
   constexpr int LPT = CH / NT;          // direct loads per thread per stage
   constexpr int LPA = AC / NT;          // ... of which A
   constexpr int SB = CH * 16;           // stage bytes
-  constexpr int NS = P2 ? 3 : 2;        // ring stages
-  constexpr int kLds = NS * SB > kEpiBytes ? NS * SB : kEpiBytes;
+  constexpr int NS = KIND == 2 ? 3 : 2;  // ring stages
+  constexpr int kEpiRows = K3 ? 64 : 128;  // output rows per epilogue pass
+  constexpr int kEpiB = kEpiRows * kPitch * 4;
+  constexpr int kLds = NS * SB > kEpiB ? NS * SB : kEpiB;
   constexpr bool kDual = MODE == G2_SWIGLU || MODE == G2_MOE_GU;
   constexpr bool kMoe = MODE == G2_MOE_GU || MODE == G2_MOE_DOWN;
-  constexpr int RT = HL ? BMT / 2 : BMT;  // token rows per tile
   static_assert(CH % NT == 0 && AC % NT == 0, "whole loads per thread");
   static_assert(kLds <= 160 * 1024, "LDS");
   static_assert(!kMoe || !PART, "expert tiles run whole");
@@ -452,7 +462,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // fragment read offsets (bytes within a stage) for k16 step ks; P2: the lo
-  // row of a hi row sits BMT LDS rows further
+  // row of a hi row sits RT LDS rows further
   const int fr = lane & 31;
   const int fk = lane >> 5;
   constexpr int KS = SBK / 16;  // 16-deep MFMA steps per stage
@@ -471,8 +481,8 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
       boff[ks][j] = AC * 16 + (rb * RC + (c ^ swz_rc<RC>(rb))) * 16;
     }
   }
-  static_assert(!P2 || (BMT % 16 == 0 && ((BMT >> 2) & 3) == 0), "lo rows keep the hi rows' swizzle");
-  constexpr int kLoOff = BMT * RC * 16;  // P2: bytes from a hi row to its lo row
+  static_assert(!P2 || (RT % 16 == 0 && ((RT >> 2) & 3) == 0), "lo rows keep the hi rows' swizzle");
+  constexpr int kLoOff = RT * RC * 16;  // P2: bytes from a hi row to its lo row
 
   // One stage: the fragments of k steps (0, 1) are read, then those of (2, 3)
   // are requested before the MFMAs of (0, 1) run, so only the first reads of
@@ -533,7 +543,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
-    static_assert(KS == 2 && NS == 3, "two k steps per stage, three ring slots");
+    static_assert(KS == 2 && NS == (K3 ? 2 : 3), "two k steps per stage, three ring slots (two in kind 3)");
     // one 16-deep step: hi and lo fragments of the wave's rows, weight fragments
     auto read1 = [&](const char* st, int ks, bf16x8 (&ah)[TI], bf16x8 (&al)[TI], bf16x8 (&bw)[TJ]) {
 #pragma unroll
@@ -562,12 +572,13 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
     // Three slots: stages kt+1 and kt+2 are in flight while stage kt is
     // multiplied. Stage kt+2 goes to the slot stage kt-1 used, which every
     // wave has finished reading once it passes the barrier of stage kt.
+    // Kind 3 (two blocks per CU): two slots, stage kt+1 in flight.
     if (nk > 0) issue(0);
-    if (nk > 1) issue(1);
+    if (!K3 && nk > 1) issue(1);
     for (int kt = 0; kt < nk; ++kt) {
       // this wave's part of stage kt (loads complete in order: only stage
       // kt+1's may still be out)
-      if (kt + 1 < nk) wait_vmcnt<LPT>();
+      if (!K3 && kt + 1 < nk) wait_vmcnt<(K3 ? 0 : LPT)>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -578,7 +589,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
       bf16x8 h0[TI], l0[TI], w0[TJ], h1[TI], l1[TI], w1[TJ];
       read1(st, 0, h0, l0, w0);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + 2 < nk) issue(kt + 2);
+      if (kt + NS - 1 < nk) issue(kt + NS - 1);
       __builtin_amdgcn_sched_barrier(0);
       read1(st, 1, h1, l1, w1);
       mma1(h0, l0, w0);
@@ -591,8 +602,8 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
 
   // ---- epilogue: 128 rows (one row of waves) at a time through LDS ----
   float* C = reinterpret_cast<float*>(smem);
-  constexpr int NH = HL ? 1 : 2;  // 128-row halves written out
-  constexpr int WPH = 128 / WROWS;  // wave rows per half
+  constexpr int NH = HL ? 1 : RT / kEpiRows;  // epilogue passes
+  constexpr int WPH = kEpiRows / WROWS;  // wave rows per pass
 #pragma unroll
   for (int half = 0; half < NH; ++half) {
     // HL: the hi rows (wm 0) are stored, then the lo rows (wm 1) added on top
@@ -613,8 +624,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_kernel(const G2Args p) {
       if (HL && pass == 0) __syncthreads();
     }
     __syncthreads();
-    constexpr int kEpiRows = 128;
-    const int rbase = half * 128;
+    const int rbase = half * kEpiRows;
     if constexpr (PART) {
       const int ldp = p.tiles_n * BN;
       float* dst = p.part + (size_t)split * p.M * ldp;
@@ -1446,7 +1456,7 @@ hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
                              hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   if (bm != 128 && bm != 256) return hipErrorInvalidValue;
-  G2Args a = base(H2, 0, bm == 256 ? 2 * mf : mf, Wd, mf, 1, nullptr);  // as for gate/up
+  G2Args a = base(H2, 0, 2 * mf, Wd, mf, 1, nullptr);  // both kinds step over 2 mf
   a.lda = 2 * mf;
   a.b_expert_stride = (size_t)d * mf;
   a.tile_expert = tile_expert;
@@ -1461,7 +1471,7 @@ hipError_t ql_gemm2_moe_down(const bf16* H2, const bf16* Wd, int mf, int d,
     hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, 2>), dim3(8 * ((total + 7) / 8)),
                        dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, 1>), dim3(8 * ((total + 7) / 8)),
+    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_DOWN, false, 3>), dim3(8 * ((total + 7) / 8)),
                        dim3(512), 0, s, a);
   return hipGetLastError();
 }
