@@ -301,12 +301,13 @@ QL_DEV void wait_vmcnt() {
 //     owns 64 token rows x 128 columns: per 16-deep step it reads 8 fragments
 //     for 16 MFMAs (kind 0 reads 6 for 8), and the block moves 48 KiB from L2
 //     per 256 x 256 x 64 of MFMA work instead of 64.
-//  3  [hi | lo] pair, 128 token rows, for the MoE down projection: a stage
-//     holds 32 k of the 128 hi, 128 lo and 256 weight rows (32 KiB); two ring
-//     slots and 64-row epilogue passes keep the block at 65 KiB of LDS and 128
-//     registers, so two blocks share a CU and one block's prologue and
-//     epilogue (short k loops: K = the expert width) overlap the other's
-//     MFMAs. 8 waves as 2 x 4, a wave owns 64 token rows x 64 columns.
+//  3  [hi | lo] pair, 128 token rows, for the MoE expert projections: a
+//     stage holds 32 k of the 128 hi, 128 lo and 256 weight rows (32 KiB);
+//     two ring slots and 64-row epilogue passes keep the block at 65 KiB of
+//     LDS and 128 registers, so two blocks share a CU and one block's
+//     prologue, epilogue and barrier waits overlap the other's MFMAs (expert
+//     tiles are many and short). 8 waves as 2 x 4, a wave owns 64 token rows
+//     x 64 columns.
 // Kinds 0-2: two waves share each SIMD, so one wave's MFMAs run while the
 // other waits; kind 3: four.
 template <int MODE, bool PART, int KIND>
@@ -1425,9 +1426,9 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg
                            bf16* H2, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
   if (bm != 128 && bm != 256) return hipErrorInvalidValue;
-  // [hi | lo] rows: 256-row pair tiles over 32-deep stages (2 x Kb for the
-  // step count), or 128-row hi/lo tiles over 64-deep stages
-  G2Args a = base(Z2, 0, bm == 256 ? 2 * d : d, Wg, d, 1, nullptr);
+  // [hi | lo] rows: 256- or 128-row pair tiles over 32-deep stages (2 x Kb
+  // for the step count; the 128-row ones two blocks per CU)
+  G2Args a = base(Z2, 0, 2 * d, Wg, d, 1, nullptr);
   a.lda = 2 * d;
   a.B2 = Wu;
   a.b_expert_stride = (size_t)mf * d;
@@ -1445,7 +1446,7 @@ hipError_t ql_gemm2_moe_gu(const bf16* Z2, const int* slot_token, const bf16* Wg
     hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, 2>), dim3(8 * ((total + 7) / 8)), dim3(512),
                        0, s, a);
   else
-    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, 1>), dim3(8 * ((total + 7) / 8)), dim3(512),
+    hipLaunchKernelGGL((gemm2_kernel<G2_MOE_GU, false, 3>), dim3(8 * ((total + 7) / 8)), dim3(512),
                        0, s, a);
   return hipGetLastError();
 }
