@@ -374,78 +374,78 @@ def stages_of(cfg, kind, batch):
 # 16 hex digits of the SHA-256 of that file with common.h and kernels.h when the counters
 # were taken, and is reported only while they are unchanged (else traffic is null).
 # Summary: profiles/hbm_counters_decode_workloads.md.
-PMC_FETCH_SCALE = 262144.0 / 131084.5
+PMC_FETCH_SCALE = 262144.0 / 131084.4
 PMC_WRITE_SCALE = 262144.0 / 262144.0
 PMC_TRAFFIC_KIB = {
     # (workload, stage): (FETCH_SIZE KiB, WRITE_SIZE KiB, source file, sha256[:16]) per layer
     # call, the stage's kernels summed; profiles/hbm_counters_decode_workloads.md
-    ("qwen2.5-7b decode B=1 cache=1024", "qkv"): (16212.4, 72.0, "gemv.hip", "6a126318354a6a7d"),
+    ("qwen2.5-7b decode B=1 cache=1024", "qkv"): (16212.3, 72.0, "gemv.hip", "6a126318354a6a7d"),
     ("qwen2.5-7b decode B=1 cache=1024", "attention"): (1766.4, 975.0, "attn_decode.hip", "5eaf26c64e4f6327"),
     ("qwen2.5-7b decode B=1 cache=1024", "o_proj"): (12643.6, 56.0, "gemv.hip", "6a126318354a6a7d"),
-    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132730.0, 148.0, "gemv.hip", "6a126318354a6a7d"),
+    ("qwen2.5-7b decode B=1 cache=1024", "gate_up"): (132730.4, 148.1, "gemv.hip", "6a126318354a6a7d"),
     ("qwen2.5-7b decode B=1 cache=1024", "down"): (66531.3, 56.0, "gemv.hip", "6a126318354a6a7d"),
     ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm1"): (160.9, 448.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22392.9, 9152.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen2.5-7b decode B=32 cache=1024", "attention"): (37945.8, 8064.0, "attn_decode.hip", "5eaf26c64e4f6327"),
-    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18577.4, 8896.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen2.5-7b decode B=32 cache=1024", "qkv"): (22392.5, 9152.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen2.5-7b decode B=32 cache=1024", "attention"): (37940.6, 8064.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen2.5-7b decode B=32 cache=1024", "o_proj"): (18577.4, 8896.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen2.5-7b decode B=32 cache=1024", "rmsnorm2"): (273.7, 448.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140884.4, 15040.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79226.4, 8800.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen2.5-7b decode B=32 cache=1024", "gate_up"): (140884.4, 15040.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen2.5-7b decode B=32 cache=1024", "down"): (79226.5, 8800.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen3-8b decode B=64 cache=4096", "rmsnorm1"): (308.9, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35060.0, 18944.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen3-8b decode B=64 cache=4096", "attention"): (532005.4, 5376.0, "attn_decode.hip", "5eaf26c64e4f6327"),
-    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25491.5, 17408.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen3-8b decode B=64 cache=4096", "qkv"): (35060.0, 18944.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen3-8b decode B=64 cache=4096", "attention"): (532011.5, 5376.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-8b decode B=64 cache=4096", "o_proj"): (25491.5, 17408.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen3-8b decode B=64 cache=4096", "rmsnorm2"): (565.7, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110264.5, 23552.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen3-8b decode B=64 cache=4096", "down"): (59541.2, 16896.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen3-8b decode B=64 cache=4096", "gate_up"): (110272.2, 23552.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen3-8b decode B=64 cache=4096", "down"): (59540.8, 16896.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm1"): (289.8, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32503.4, 20992.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (535698.0, 10752.0, "attn_decode.hip", "5eaf26c64e4f6327"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17811.1, 17408.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "qkv"): (32503.5, 20992.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "attention"): (535739.6, 10752.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "o_proj"): (17811.1, 17408.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "rmsnorm2"): (545.7, 2048.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "router"): (2652.9, 72.0, "moe.hip", "f52fec8eb3681e2a"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "permute"): (4.9, 10.1, "moe.hip", "f52fec8eb3681e2a"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_gate_up"): (397850.1, 3072.4, "gemm.hip", "c4880637026b08aa"),
-    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_down"): (208941.2, 8192.0, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_gate_up"): (398320.1, 3073.4, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=4096", "expert_down"): (208941.1, 8192.0, "gemm.hip", "c4880637026b08aa"),
     ("qwen3-30b-a3b decode B=128 cache=4096", "combine"): (4645.6, 512.0, "moe.hip", "f52fec8eb3681e2a"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm1"): (289.8, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32502.8, 20992.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "attention"): (139272.6, 10752.0, "attn_decode.hip", "5eaf26c64e4f6327"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17811.1, 17408.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm1"): (289.9, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "qkv"): (32502.6, 20992.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "attention"): (139268.4, 10752.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "o_proj"): (17811.1, 17408.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "rmsnorm2"): (545.7, 2048.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
     ("qwen3-30b-a3b decode B=128 cache=1024", "router"): (2652.9, 72.0, "moe.hip", "f52fec8eb3681e2a"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "permute"): (5.1, 10.1, "moe.hip", "f52fec8eb3681e2a"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_gate_up"): (394878.2, 3072.6, "gemm.hip", "c4880637026b08aa"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_down"): (207405.1, 8192.1, "gemm.hip", "c4880637026b08aa"),
-    ("qwen3-30b-a3b decode B=128 cache=1024", "combine"): (4645.6, 512.0, "moe.hip", "f52fec8eb3681e2a"),
-    ("qwen3-32b decode B=32 cache=4096", "rmsnorm1"): (228.9, 640.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57594.7, 10496.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen3-32b decode B=32 cache=4096", "attention"): (270964.6, 9728.0, "attn_decode.hip", "5eaf26c64e4f6327"),
-    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48162.0, 9344.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "permute"): (4.9, 10.1, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_gate_up"): (395321.6, 3073.7, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "expert_down"): (207405.2, 8192.1, "gemm.hip", "c4880637026b08aa"),
+    ("qwen3-30b-a3b decode B=128 cache=1024", "combine"): (4645.5, 512.0, "moe.hip", "f52fec8eb3681e2a"),
+    ("qwen3-32b decode B=32 cache=4096", "rmsnorm1"): (229.0, 640.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
+    ("qwen3-32b decode B=32 cache=4096", "qkv"): (57594.7, 10496.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen3-32b decode B=32 cache=4096", "attention"): (270961.6, 9728.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen3-32b decode B=32 cache=4096", "o_proj"): (48161.9, 9344.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen3-32b decode B=32 cache=4096", "rmsnorm2"): (386.7, 640.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265878.7, 17536.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen3-32b decode B=32 cache=4096", "down"): (140794.8, 9024.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen3-32b decode B=32 cache=4096", "gate_up"): (265878.7, 17536.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen3-32b decode B=32 cache=4096", "down"): (140794.7, 9024.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("mixtral-like decode B=64 cache=2048", "rmsnorm1"): (308.8, 1024.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("mixtral-like decode B=64 cache=2048", "qkv"): (35057.3, 18944.0, "gemm2.hip", "189e2265121b259e"),
-    ("mixtral-like decode B=64 cache=2048", "attention"): (267890.1, 5376.0, "attn_decode.hip", "5eaf26c64e4f6327"),
-    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25491.4, 17408.0, "gemm2.hip", "189e2265121b259e"),
+    ("mixtral-like decode B=64 cache=2048", "qkv"): (35057.3, 18944.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("mixtral-like decode B=64 cache=2048", "attention"): (267923.5, 5376.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("mixtral-like decode B=64 cache=2048", "o_proj"): (25491.5, 17408.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("mixtral-like decode B=64 cache=2048", "rmsnorm2"): (565.7, 2048.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
     ("mixtral-like decode B=64 cache=2048", "router"): (692.9, 3.0, "moe.hip", "f52fec8eb3681e2a"),
     ("mixtral-like decode B=64 cache=2048", "permute"): (3.2, 1.2, "moe.hip", "f52fec8eb3681e2a"),
-    ("mixtral-like decode B=64 cache=2048", "expert_gate_up"): (266284.7, 2048.0, "gemm.hip", "c4880637026b08aa"),
-    ("mixtral-like decode B=64 cache=2048", "expert_down"): (139302.9, 2048.0, "gemm.hip", "c4880637026b08aa"),
+    ("mixtral-like decode B=64 cache=2048", "expert_gate_up"): (266353.2, 2048.0, "gemm.hip", "c4880637026b08aa"),
+    ("mixtral-like decode B=64 cache=2048", "expert_down"): (139305.1, 2048.0, "gemm.hip", "c4880637026b08aa"),
     ("mixtral-like decode B=64 cache=2048", "combine"): (1561.5, 512.0, "moe.hip", "f52fec8eb3681e2a"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm1"): (272.8, 896.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28523.2, 18304.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "attention"): (72266.8, 8512.0, "attn_decode.hip", "5eaf26c64e4f6327"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24511.3, 17792.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "qkv"): (28523.3, 18304.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "attention"): (72277.7, 8512.0, "attn_decode.hip", "5eaf26c64e4f6327"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "o_proj"): (24511.3, 17792.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "rmsnorm2"): (497.8, 1792.0, "rmsnorm.hip", "8b0d9a0232539a0f"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "router"): (1971.5, 24.2, "moe.hip", "f52fec8eb3681e2a"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "permute"): (3.9, 5.1, "moe.hip", "f52fec8eb3681e2a"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_gate_up"): (1150526.3, 5120.0, "gemm.hip", "c4880637026b08aa"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_down"): (594007.9, 7168.1, "gemm.hip", "c4880637026b08aa"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158065.1, 29696.0, "gemm2.hip", "189e2265121b259e"),
-    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98819.0, 18048.0, "gemm2.hip", "189e2265121b259e"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_gate_up"): (1150526.8, 5120.0, "gemm.hip", "c4880637026b08aa"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "expert_down"): (594007.0, 7168.0, "gemm.hip", "c4880637026b08aa"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_gate_up"): (158065.8, 29696.0, "gemm2.hip", "c99046ea5ffdae45"),
+    ("qwen2-57b-a14b decode B=64 cache=1024", "shared_down"): (98819.2, 18048.0, "gemm2.hip", "c99046ea5ffdae45"),
     ("qwen2-57b-a14b decode B=64 cache=1024", "combine"): (4067.5, 448.0, "moe.hip", "f52fec8eb3681e2a"),
 }
 
